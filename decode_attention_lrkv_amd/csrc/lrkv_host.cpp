@@ -1,0 +1,380 @@
+// C-ABI layer of liblrkv: argument validation, split planning, workspace
+// layout and kernel launches.  No device memory is allocated here.
+#include <atomic>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstdlib>
+#include <string>
+
+#include "lrkv.h"
+#include "lrkv_internal.h"
+
+using namespace lrkv;
+
+namespace {
+
+thread_local std::string g_last_error;
+
+lrkv_status fail(lrkv_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return st;
+}
+
+lrkv_status device_fail(const char* fn, hipError_t e) {
+  return fail(LRKV_ERR_DEVICE, "%s: kernel launch failed: %s", fn, hipGetErrorString(e));
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+// Compute units of the current device (cached); 256 when no device answers.
+int device_cu_count() {
+  static std::atomic<int> cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 256;
+  if (dev < 64) {
+    const int c = cache[dev].load(std::memory_order_relaxed);
+    if (c > 0) return c;
+  }
+  int n = 0;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+    n = 256;
+  if (dev < 64) cache[dev].store(n, std::memory_order_relaxed);
+  return n;
+}
+
+struct Plan {
+  int n_splits = 1;
+  int chunks_per_split = 1;
+};
+
+// Split a context of n_tokens over (units) independent (batch, kv head) rows so
+// that the whole chip gets about 16 waves per compute unit, with at least 4
+// chunks (128 tokens) per split.  LRKV_SPLITS forces the split count.
+Plan plan_splits(int64_t units, int64_t n_tokens, int cus, int max_splits) {
+  Plan p;
+  const int64_t n_chunks = n_tokens > 0 ? cdiv(n_tokens, kChunk) : 1;
+  int64_t s = cdiv((int64_t)cus * 16, units > 0 ? units : 1);
+  s = std::min<int64_t>(s, cdiv(n_chunks, 4));
+  if (const char* env = std::getenv("LRKV_SPLITS")) {
+    const long v = std::strtol(env, nullptr, 10);
+    if (v > 0) s = v;
+  }
+  s = std::max<int64_t>(1, std::min<int64_t>(s, n_chunks));
+  s = std::min<int64_t>(s, max_splits);
+  const int64_t cps = cdiv(n_chunks, s);
+  p.chunks_per_split = (int)cps;
+  p.n_splits = (int)cdiv(n_chunks, cps);
+  return p;
+}
+
+struct DecodeLayout {
+  Plan lr, side;
+  size_t acc_lr = 0, ml_lr = 0, acc_side = 0, ml_side = 0, total = 0;
+};
+
+DecodeLayout decode_layout(const lrkv_dims& d, int64_t n_lr_tokens, int64_t side_cap) {
+  DecodeLayout L;
+  const int cus = device_cu_count();
+  const int64_t units = (int64_t)d.batch * d.n_kv_heads;
+  const int64_t rows = (int64_t)d.batch * d.n_q_heads;
+  int max_lr = kMaxSplits;
+  if (side_cap > 0) {
+    L.side = plan_splits(units, side_cap, cus, kMaxSplits / 2);
+    max_lr = kMaxSplits - L.side.n_splits;
+  }
+  L.lr = plan_splits(units, n_lr_tokens, cus, max_lr);
+  size_t off = 0;
+  L.acc_lr = off; off = align256(off + sizeof(float) * rows * L.lr.n_splits * d.rank_v);
+  L.ml_lr = off;  off = align256(off + sizeof(float) * rows * L.lr.n_splits * 2);
+  if (side_cap > 0) {
+    L.acc_side = off; off = align256(off + sizeof(float) * rows * L.side.n_splits * d.head_dim);
+    L.ml_side = off;  off = align256(off + sizeof(float) * rows * L.side.n_splits * 2);
+  }
+  L.total = off;
+  return L;
+}
+
+lrkv_status check_rank(int32_t r, int32_t hd, lrkv_dtype dt, const char* fn, const char* what) {
+  const int mult = dt == LRKV_BF16 ? 8 : 4;
+  if (r < 1 || r > hd)
+    return fail(LRKV_ERR_UNSUPPORTED, "%s: %s = %d outside [1, head_dim = %d]", fn, what, r, hd);
+  if (r % mult)
+    return fail(LRKV_ERR_UNSUPPORTED, "%s: %s = %d is not a multiple of %d", fn, what, r, mult);
+  return LRKV_OK;
+}
+
+lrkv_status check_dims(const lrkv_dims* d, lrkv_dtype dt, const char* fn) {
+  if (!d) return fail(LRKV_ERR_INVALID_ARGUMENT, "%s: dims is NULL", fn);
+  if (dt != LRKV_F32 && dt != LRKV_BF16) return fail(LRKV_ERR_INVALID_ARGUMENT, "%s: unknown dtype %d", fn, (int)dt);
+  if (d->batch < 1 || d->n_kv_heads < 1 || d->n_q_heads < 1)
+    return fail(LRKV_ERR_INVALID_ARGUMENT, "%s: batch, n_q_heads and n_kv_heads must be >= 1", fn);
+  if (d->batch > 65535 || d->n_kv_heads > 65535)
+    return fail(LRKV_ERR_UNSUPPORTED, "%s: batch and n_kv_heads must be <= 65535", fn);
+  if (d->n_q_heads % d->n_kv_heads)
+    return fail(LRKV_ERR_INVALID_ARGUMENT, "%s: n_q_heads = %d is not a multiple of n_kv_heads = %d", fn,
+                d->n_q_heads, d->n_kv_heads);
+  if (d->n_q_heads / d->n_kv_heads > 8)
+    return fail(LRKV_ERR_UNSUPPORTED, "%s: more than 8 query heads per kv head", fn);
+  if (d->head_dim != 64 && d->head_dim != 128)
+    return fail(LRKV_ERR_UNSUPPORTED, "%s: head_dim = %d (supported: 64, 128)", fn, d->head_dim);
+  lrkv_status st = check_rank(d->rank_k, d->head_dim, dt, fn, "rank_k");
+  if (st != LRKV_OK) return st;
+  st = check_rank(d->rank_v, d->head_dim, dt, fn, "rank_v");
+  if (st != LRKV_OK) return st;
+  if (d->capacity < 8 || d->capacity % 8)
+    return fail(LRKV_ERR_INVALID_ARGUMENT, "%s: capacity = %lld must be a positive multiple of 8", fn,
+                (long long)d->capacity);
+  if (d->capacity > (int64_t)1 << 31)
+    return fail(LRKV_ERR_UNSUPPORTED, "%s: capacity above 2^31 tokens", fn);
+  return LRKV_OK;
+}
+
+#define LRKV_CHECK_PTR(p, fn)                                                              \
+  do {                                                                                     \
+    if (!(p)) return fail(LRKV_ERR_INVALID_ARGUMENT, "%s: %s is NULL", fn, #p);            \
+    if (!aligned16(p)) return fail(LRKV_ERR_INVALID_ARGUMENT, "%s: %s is not 16-byte aligned", fn, #p); \
+  } while (0)
+
+float resolve_scale(float scale, int head_dim) {
+  return scale == 0.f ? 1.f / std::sqrt((float)head_dim) : scale;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* lrkv_status_string(lrkv_status s) {
+  switch (s) {
+    case LRKV_OK: return "ok";
+    case LRKV_ERR_INVALID_ARGUMENT: return "invalid argument";
+    case LRKV_ERR_UNSUPPORTED: return "unsupported";
+    case LRKV_ERR_WORKSPACE_TOO_SMALL: return "workspace too small";
+    case LRKV_ERR_DEVICE: return "device error";
+  }
+  return "unknown status";
+}
+
+const char* lrkv_last_error(void) { return g_last_error.c_str(); }
+
+lrkv_status lrkv_compress(const void* x, const void* basis, void* coeff, lrkv_cache_kind kind,
+                          int32_t batch, int32_t n_kv_heads, int32_t head_dim, int32_t rank,
+                          int64_t n_tokens, int64_t pos, int64_t capacity, lrkv_dtype dtype,
+                          hipStream_t stream) {
+  const char* fn = "lrkv_compress";
+  if (dtype != LRKV_F32 && dtype != LRKV_BF16) return fail(LRKV_ERR_INVALID_ARGUMENT, "%s: unknown dtype", fn);
+  if (kind != LRKV_KEYS && kind != LRKV_VALUES) return fail(LRKV_ERR_INVALID_ARGUMENT, "%s: unknown cache kind", fn);
+  if (batch < 1 || n_kv_heads < 1) return fail(LRKV_ERR_INVALID_ARGUMENT, "%s: batch and n_kv_heads must be >= 1", fn);
+  if (batch > 65535 || n_kv_heads > 65535) return fail(LRKV_ERR_UNSUPPORTED, "%s: batch and n_kv_heads must be <= 65535", fn);
+  if (head_dim != 64 && head_dim != 128)
+    return fail(LRKV_ERR_UNSUPPORTED, "%s: head_dim = %d (supported: 64, 128)", fn, head_dim);
+  lrkv_status st = check_rank(rank, head_dim, dtype, fn, "rank");
+  if (st != LRKV_OK) return st;
+  if (capacity < 8 || capacity % 8)
+    return fail(LRKV_ERR_INVALID_ARGUMENT, "%s: capacity = %lld must be a positive multiple of 8", fn, (long long)capacity);
+  if (n_tokens < 0 || pos < 0 || pos + n_tokens > capacity)
+    return fail(LRKV_ERR_INVALID_ARGUMENT, "%s: rows [%lld, %lld) do not fit capacity %lld", fn, (long long)pos,
+                (long long)(pos + n_tokens), (long long)capacity);
+  LRKV_CHECK_PTR(x, fn);
+  LRKV_CHECK_PTR(basis, fn);
+  LRKV_CHECK_PTR(coeff, fn);
+  if (n_tokens == 0) return LRKV_OK;
+  CompressArgs a{x, basis, coeff, kind == LRKV_VALUES ? 1 : 0, batch, n_kv_heads, head_dim, rank,
+                 n_tokens, pos, capacity};
+  const hipError_t e = dtype == LRKV_BF16 ? launch_compress_bf16(a, stream) : launch_compress_f32(a, stream);
+  return e == hipSuccess ? LRKV_OK : device_fail(fn, e);
+}
+
+size_t lrkv_decode_workspace_bytes(const lrkv_dims* dims, int64_t n_ctx, int64_t side_cap) {
+  if (check_dims(dims, LRKV_F32, "lrkv_decode_workspace_bytes") != LRKV_OK &&
+      check_dims(dims, LRKV_BF16, "lrkv_decode_workspace_bytes") != LRKV_OK)
+    return 0;
+  if (side_cap < 0) return 0;
+  const int64_t n = side_cap > 0 ? dims->capacity : n_ctx;
+  if (n < 1) return 0;
+  return decode_layout(*dims, n, side_cap).total;
+}
+
+lrkv_status lrkv_decode_attn(const void* q, const void* basis_k, const void* coeff_k,
+                             const void* basis_v, const void* coeff_v, void* out, float* lse,
+                             const lrkv_dims* dims, int64_t n_ctx, float scale, lrkv_dtype dtype,
+                             void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  const char* fn = "lrkv_decode_attn";
+  lrkv_status st = check_dims(dims, dtype, fn);
+  if (st != LRKV_OK) return st;
+  if (n_ctx < 1 || n_ctx > dims->capacity)
+    return fail(LRKV_ERR_INVALID_ARGUMENT, "%s: n_ctx = %lld outside [1, capacity = %lld]", fn, (long long)n_ctx,
+                (long long)dims->capacity);
+  if (!std::isfinite(scale)) return fail(LRKV_ERR_INVALID_ARGUMENT, "%s: scale is not finite", fn);
+  LRKV_CHECK_PTR(q, fn);
+  LRKV_CHECK_PTR(basis_k, fn);
+  LRKV_CHECK_PTR(coeff_k, fn);
+  LRKV_CHECK_PTR(basis_v, fn);
+  LRKV_CHECK_PTR(coeff_v, fn);
+  LRKV_CHECK_PTR(out, fn);
+  LRKV_CHECK_PTR(workspace, fn);
+  if (lse && !aligned16(lse)) return fail(LRKV_ERR_INVALID_ARGUMENT, "%s: lse is not 16-byte aligned", fn);
+  const DecodeLayout L = decode_layout(*dims, n_ctx, 0);
+  if (workspace_bytes < L.total)
+    return fail(LRKV_ERR_WORKSPACE_TOO_SMALL, "%s: workspace of %zu bytes, %zu needed", fn, workspace_bytes, L.total);
+  char* ws = static_cast<char*>(workspace);
+  const int g = dims->n_q_heads / dims->n_kv_heads;
+  SplitArgs sa{};
+  sa.q = q; sa.basis_k = basis_k; sa.ck = coeff_k; sa.cv = coeff_v;
+  sa.cap = dims->capacity; sa.rk = dims->rank_k; sa.rv = dims->rank_v; sa.d = dims->head_dim;
+  sa.g = g; sa.hq = dims->n_q_heads; sa.hkv = dims->n_kv_heads; sa.batch = dims->batch;
+  sa.n_static = n_ctx; sa.n_dev = nullptr;
+  sa.chunks_per_split = L.lr.chunks_per_split; sa.n_splits = L.lr.n_splits;
+  sa.qscale = resolve_scale(scale, dims->head_dim) * kLog2eHost;
+  sa.part_acc = reinterpret_cast<float*>(ws + L.acc_lr);
+  sa.part_ml = reinterpret_cast<float*>(ws + L.ml_lr);
+  hipError_t e = dtype == LRKV_BF16 ? launch_split_bf16(sa, stream) : launch_split_f32(sa, stream);
+  if (e != hipSuccess) return device_fail(fn, e);
+  MergeArgs ma{};
+  ma.part_acc = sa.part_acc; ma.part_ml = sa.part_ml; ma.n_splits = L.lr.n_splits; ma.racc = dims->rank_v;
+  ma.side_acc = nullptr; ma.side_ml = nullptr; ma.n_side_splits = 0;
+  ma.basis_v = basis_v; ma.rv = dims->rank_v; ma.d = dims->head_dim; ma.g = g;
+  ma.hq = dims->n_q_heads; ma.hkv = dims->n_kv_heads; ma.batch = dims->batch;
+  ma.out = out; ma.lse = lse;
+  e = launch_merge(ma, dtype == LRKV_BF16, stream);
+  return e == hipSuccess ? LRKV_OK : device_fail(fn, e);
+}
+
+size_t lrkv_compress_hybrid_workspace_bytes(const lrkv_dims* dims, int64_t n_tokens) {
+  if (!dims || n_tokens < 0 || dims->batch < 1 || dims->n_kv_heads < 1) return 0;
+  const int64_t tiles = cdiv(n_tokens, kHybridTile);
+  const int64_t units = (int64_t)dims->batch * dims->n_kv_heads;
+  size_t off = align256((size_t)(units * tiles * kHybridTile));       // flags
+  off = align256(off + sizeof(int32_t) * units * tiles);              // counts
+  off = align256(off + sizeof(int32_t) * units * tiles * 2);          // offsets
+  return off;
+}
+
+lrkv_status lrkv_compress_hybrid(const void* k, const void* v, const void* basis_k,
+                                 const void* basis_v, float tau, void* coeff_k, void* coeff_v,
+                                 int32_t* n_lr, void* k_side, void* v_side, int32_t* side_idx,
+                                 int32_t* n_side, uint8_t* flags, int32_t* overflow,
+                                 const lrkv_dims* dims, int64_t n_tokens, int64_t pos,
+                                 int64_t side_cap, lrkv_dtype dtype, void* workspace,
+                                 size_t workspace_bytes, hipStream_t stream) {
+  const char* fn = "lrkv_compress_hybrid";
+  lrkv_status st = check_dims(dims, dtype, fn);
+  if (st != LRKV_OK) return st;
+  if (dtype != LRKV_BF16) return fail(LRKV_ERR_UNSUPPORTED, "%s: only bfloat16 caches are supported", fn);
+  if (std::isnan(tau) || tau < 0.f) return fail(LRKV_ERR_INVALID_ARGUMENT, "%s: tau must be >= 0", fn);
+  if (n_tokens < 0 || pos < 0 || pos + n_tokens > ((int64_t)1 << 31))
+    return fail(LRKV_ERR_INVALID_ARGUMENT, "%s: bad n_tokens / pos", fn);
+  if (side_cap < 8 || side_cap % 8 || side_cap > ((int64_t)1 << 31))
+    return fail(LRKV_ERR_INVALID_ARGUMENT, "%s: side_cap = %lld must be a positive multiple of 8", fn,
+                (long long)side_cap);
+  LRKV_CHECK_PTR(k, fn);
+  LRKV_CHECK_PTR(v, fn);
+  LRKV_CHECK_PTR(basis_k, fn);
+  LRKV_CHECK_PTR(basis_v, fn);
+  LRKV_CHECK_PTR(coeff_k, fn);
+  LRKV_CHECK_PTR(coeff_v, fn);
+  LRKV_CHECK_PTR(k_side, fn);
+  LRKV_CHECK_PTR(v_side, fn);
+  LRKV_CHECK_PTR(workspace, fn);
+  if (!n_lr || !n_side || !side_idx || !overflow)
+    return fail(LRKV_ERR_INVALID_ARGUMENT, "%s: n_lr, n_side, side_idx and overflow must not be NULL", fn);
+  if (n_tokens == 0) return LRKV_OK;
+  const size_t need = lrkv_compress_hybrid_workspace_bytes(dims, n_tokens);
+  if (workspace_bytes < need)
+    return fail(LRKV_ERR_WORKSPACE_TOO_SMALL, "%s: workspace of %zu bytes, %zu needed", fn, workspace_bytes, need);
+  const int64_t tiles = cdiv(n_tokens, kHybridTile);
+  if (tiles > 0x7fffffff) return fail(LRKV_ERR_UNSUPPORTED, "%s: too many tokens", fn);
+  const int64_t units = (int64_t)dims->batch * dims->n_kv_heads;
+  char* ws = static_cast<char*>(workspace);
+  HybridArgs a{};
+  a.k = k; a.v = v; a.bk = basis_k; a.bv = basis_v;
+  a.tau2 = std::isinf(tau) ? INFINITY : tau * tau;
+  a.ck = coeff_k; a.cv = coeff_v; a.n_lr = n_lr;
+  a.k_side = k_side; a.v_side = v_side; a.side_idx = side_idx; a.n_side = n_side;
+  a.flags = flags; a.overflow = overflow;
+  a.batch = dims->batch; a.hkv = dims->n_kv_heads; a.d = dims->head_dim;
+  a.rk = dims->rank_k; a.rv = dims->rank_v;
+  a.n_tokens = n_tokens; a.pos = pos; a.cap = dims->capacity; a.side_cap = side_cap;
+  size_t off = 0;
+  a.ws_flags = reinterpret_cast<uint8_t*>(ws + off); off = align256(off + (size_t)(units * tiles * kHybridTile));
+  a.ws_counts = reinterpret_cast<int32_t*>(ws + off); off = align256(off + sizeof(int32_t) * units * tiles);
+  a.ws_offsets = reinterpret_cast<int32_t*>(ws + off);
+  a.n_tiles = (int)tiles;
+  const hipError_t e = launch_hybrid_bf16(a, stream);
+  return e == hipSuccess ? LRKV_OK : device_fail(fn, e);
+}
+
+lrkv_status lrkv_decode_attn_hybrid(const void* q, const void* basis_k, const void* coeff_k,
+                                    const void* basis_v, const void* coeff_v,
+                                    const int32_t* n_lr, const void* k_side, const void* v_side,
+                                    const int32_t* n_side, int64_t side_cap, void* out,
+                                    float* lse, const lrkv_dims* dims, float scale,
+                                    lrkv_dtype dtype, void* workspace, size_t workspace_bytes,
+                                    hipStream_t stream) {
+  const char* fn = "lrkv_decode_attn_hybrid";
+  lrkv_status st = check_dims(dims, dtype, fn);
+  if (st != LRKV_OK) return st;
+  if (side_cap < 8 || side_cap % 8 || side_cap > ((int64_t)1 << 31))
+    return fail(LRKV_ERR_INVALID_ARGUMENT, "%s: side_cap = %lld must be a positive multiple of 8", fn,
+                (long long)side_cap);
+  if (!std::isfinite(scale)) return fail(LRKV_ERR_INVALID_ARGUMENT, "%s: scale is not finite", fn);
+  LRKV_CHECK_PTR(q, fn);
+  LRKV_CHECK_PTR(basis_k, fn);
+  LRKV_CHECK_PTR(coeff_k, fn);
+  LRKV_CHECK_PTR(basis_v, fn);
+  LRKV_CHECK_PTR(coeff_v, fn);
+  LRKV_CHECK_PTR(k_side, fn);
+  LRKV_CHECK_PTR(v_side, fn);
+  LRKV_CHECK_PTR(out, fn);
+  LRKV_CHECK_PTR(workspace, fn);
+  if (!n_lr || !n_side) return fail(LRKV_ERR_INVALID_ARGUMENT, "%s: n_lr and n_side must not be NULL", fn);
+  if (lse && !aligned16(lse)) return fail(LRKV_ERR_INVALID_ARGUMENT, "%s: lse is not 16-byte aligned", fn);
+  const DecodeLayout L = decode_layout(*dims, dims->capacity, side_cap);
+  if (workspace_bytes < L.total)
+    return fail(LRKV_ERR_WORKSPACE_TOO_SMALL, "%s: workspace of %zu bytes, %zu needed", fn, workspace_bytes, L.total);
+  char* ws = static_cast<char*>(workspace);
+  const int g = dims->n_q_heads / dims->n_kv_heads;
+  const bool bf16 = dtype == LRKV_BF16;
+  const float qscale = resolve_scale(scale, dims->head_dim) * kLog2eHost;
+
+  SplitArgs sa{};
+  sa.q = q; sa.basis_k = basis_k; sa.ck = coeff_k; sa.cv = coeff_v;
+  sa.cap = dims->capacity; sa.rk = dims->rank_k; sa.rv = dims->rank_v; sa.d = dims->head_dim;
+  sa.g = g; sa.hq = dims->n_q_heads; sa.hkv = dims->n_kv_heads; sa.batch = dims->batch;
+  sa.n_static = 0; sa.n_dev = n_lr;
+  sa.chunks_per_split = L.lr.chunks_per_split; sa.n_splits = L.lr.n_splits;
+  sa.qscale = qscale;
+  sa.part_acc = reinterpret_cast<float*>(ws + L.acc_lr);
+  sa.part_ml = reinterpret_cast<float*>(ws + L.ml_lr);
+  hipError_t e = bf16 ? launch_split_bf16(sa, stream) : launch_split_f32(sa, stream);
+  if (e != hipSuccess) return device_fail(fn, e);
+
+  SplitArgs ss = sa;   // side list: full-rank rows, no fold
+  ss.basis_k = nullptr; ss.ck = k_side; ss.cv = v_side; ss.cap = side_cap;
+  ss.rk = dims->head_dim; ss.rv = dims->head_dim; ss.n_dev = n_side;
+  ss.chunks_per_split = L.side.chunks_per_split; ss.n_splits = L.side.n_splits;
+  ss.part_acc = reinterpret_cast<float*>(ws + L.acc_side);
+  ss.part_ml = reinterpret_cast<float*>(ws + L.ml_side);
+  e = bf16 ? launch_split_bf16(ss, stream) : launch_split_f32(ss, stream);
+  if (e != hipSuccess) return device_fail(fn, e);
+
+  MergeArgs ma{};
+  ma.part_acc = sa.part_acc; ma.part_ml = sa.part_ml; ma.n_splits = L.lr.n_splits; ma.racc = dims->rank_v;
+  ma.side_acc = ss.part_acc; ma.side_ml = ss.part_ml; ma.n_side_splits = L.side.n_splits;
+  ma.basis_v = basis_v; ma.rv = dims->rank_v; ma.d = dims->head_dim; ma.g = g;
+  ma.hq = dims->n_q_heads; ma.hkv = dims->n_kv_heads; ma.batch = dims->batch;
+  ma.out = out; ma.lse = lse;
+  e = launch_merge(ma, bf16, stream);
+  return e == hipSuccess ? LRKV_OK : device_fail(fn, e);
+}
+
+}  // extern "C"

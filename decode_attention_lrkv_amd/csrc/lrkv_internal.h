@@ -1,0 +1,71 @@
+// Host-side launch interface between the C-ABI layer and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace lrkv {
+
+constexpr float kLog2eHost = 1.4426950408889634f;
+
+// Tokens per decode chunk: two 16-token matrix-core tiles.
+constexpr int kChunk = 32;
+// Largest number of splits one merge can combine (latent + side), bounded by its LDS.
+constexpr int kMaxSplits = 4096;
+
+struct SplitArgs {
+  const void* q;         // [B, Hq, d]
+  const void* basis_k;   // [Hkv, d, rk] (nullptr: keys are full rank, no fold)
+  const void* ck;        // key rows [B, Hkv, cap, rk]
+  const void* cv;        // value octets [B, Hkv, cap/8, rv, 8]
+  int64_t cap;
+  int rk, rv, d, g, hq, hkv, batch;
+  int64_t n_static;      // context length when n_dev is null
+  const int32_t* n_dev;  // per-(b, h) token counts on the device, or null
+  int chunks_per_split;
+  int n_splits;
+  float qscale;          // softmax scale * log2(e)
+  float* part_acc;       // [B, Hq, n_splits, rv]
+  float* part_ml;        // [B, Hq, n_splits, 2]  (running max in log2 units, sum)
+};
+
+struct MergeArgs {
+  const float* part_acc; const float* part_ml; int n_splits; int racc;
+  const float* side_acc; const float* side_ml; int n_side_splits;  // hybrid only
+  const void* basis_v;   // [Hkv, d, rv]
+  int rv, d, g, hq, hkv, batch;
+  void* out;             // [B, Hq, d]
+  float* lse;            // [B, Hq] or null
+};
+
+struct CompressArgs {
+  const void* x; const void* basis; void* coeff;
+  int values_layout;     // 0: row layout, 1: octet layout
+  int batch, hkv, d, rank;
+  int64_t n_tokens, pos, cap;
+};
+
+hipError_t launch_split_bf16(const SplitArgs& a, hipStream_t s);
+hipError_t launch_split_f32(const SplitArgs& a, hipStream_t s);
+hipError_t launch_merge(const MergeArgs& a, bool bf16, hipStream_t s);
+hipError_t launch_compress_bf16(const CompressArgs& a, hipStream_t s);
+hipError_t launch_compress_f32(const CompressArgs& a, hipStream_t s);
+
+struct HybridArgs {
+  const void* k; const void* v; const void* bk; const void* bv;
+  float tau2;
+  void* ck; void* cv; int32_t* n_lr;
+  void* k_side; void* v_side; int32_t* side_idx; int32_t* n_side;
+  uint8_t* flags; int32_t* overflow;
+  int batch, hkv, d, rk, rv;
+  int64_t n_tokens, pos, cap, side_cap;
+  uint8_t* ws_flags;     // [B, Hkv, n_tiles * 64]
+  int32_t* ws_counts;    // [B, Hkv, n_tiles] flagged tokens per tile
+  int32_t* ws_offsets;   // [B, Hkv, n_tiles, 2] (low-rank row, side row) of each tile's first token
+  int n_tiles;
+};
+
+constexpr int kHybridTile = 64;
+hipError_t launch_hybrid_bf16(const HybridArgs& a, hipStream_t s);
+
+}  // namespace lrkv

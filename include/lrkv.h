@@ -1,0 +1,197 @@
+/*
+ * lrkv.h -- decode attention over a low-rank KV cache, for AMD Instinct MI355X (gfx950).
+ *
+ * A low-rank KV cache stores, for every token and kv head, rank-r coefficients
+ * of the key and of the value against fixed per-kv-head bases:
+ *     C_K = K B_K,   C_V = V B_V,   B_K in R^{d x r_K}, B_V in R^{d x r_V}
+ * ("Llama-3.1-NovaKV" model card, introduction: a post-hoc low-rank
+ * factorisation of the K and V projections shrinks the cache; "OjaKV" README,
+ * Method Summary, StaticPCA: an offline basis, fixed at inference).  A decode
+ * step attends one query per q head over the cache without reconstructing K
+ * or V: the query is folded into the key latent space, scored against C_K,
+ * softmax-weighted, accumulated against C_V and lifted back through B_V^T.
+ * The result equals standard attention over K_hat = C_K B_K^T and
+ * V_hat = C_V B_V^T, which is how StaticPCA attends (same README section).
+ * The hybrid variant keeps tokens whose reconstruction error is high in full
+ * rank in a side list and attends both kinds in one softmax ("OjaKV" README,
+ * Method Summary, OjaKV).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - All pointers to tensors are DEVICE pointers, 16-byte aligned, to dense
+ *   row-major arrays in the layouts stated per argument.  The caller
+ *   allocates and owns every buffer (inputs, outputs, caches, counters,
+ *   workspace); the library allocates no device memory and keeps no state
+ *   beyond a per-device compute-unit count and a thread-local error string.
+ * - One storage dtype (lrkv_dtype) for every floating-point tensor of a call;
+ *   lse and workspaces are float32.  Arithmetic accumulates in float32;
+ *   rounding to bfloat16 is round-to-nearest-even.
+ * - Grouped-query attention: q head h reads kv head h / (Hq / Hkv).
+ * - Layouts ("B" batch, "Hq"/"Hkv" query/kv heads, "d" head_dim, "cap" cache
+ *   capacity in tokens):
+ *     keys, row layout:     key coefficient cache [B, Hkv, cap, r_K],
+ *                           full-rank key side list [B, Hkv, side_cap, d]
+ *     values, octet layout: value coefficient cache [B, Hkv, cap/8, r_V, 8],
+ *                           full-rank value side list [B, Hkv, side_cap/8, d, 8]
+ *   In the octet layout element (t, c) of a token-by-column matrix lives at
+ *   ((t / 8) * ncols + c) * 8 + t % 8: each column's 8 consecutive tokens are
+ *   contiguous.  cap and side_cap must be multiples of 8.
+ * - Every call is asynchronous on `stream` (0 = the null stream), allocates
+ *   nothing and synchronizes nothing, so it can be captured in a HIP graph.
+ * - Errors: arguments are validated before any HIP call; an invalid call
+ *   returns a non-zero lrkv_status, launches nothing and leaves a message in
+ *   lrkv_last_error().  A failed launch returns LRKV_ERR_DEVICE.  Faults
+ *   during kernel execution surface at the caller's next synchronization.
+ *   No C++ exception crosses this interface.
+ * - Supported shapes: head_dim in {64, 128}; 1 <= rank <= head_dim; ranks a
+ *   multiple of 8 for bfloat16 and of 4 for float32; Hq a multiple of Hkv with
+ *   Hq / Hkv <= 8; B, Hkv >= 1.
+ */
+#ifndef LRKV_H
+#define LRKV_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum lrkv_status {
+  LRKV_OK = 0,
+  LRKV_ERR_INVALID_ARGUMENT = 1,   /* null pointer, misaligned pointer, inconsistent sizes */
+  LRKV_ERR_UNSUPPORTED = 2,        /* valid request outside the supported shapes */
+  LRKV_ERR_WORKSPACE_TOO_SMALL = 3,
+  LRKV_ERR_DEVICE = 4              /* a HIP runtime call failed; see lrkv_last_error() */
+} lrkv_status;
+
+typedef enum lrkv_dtype { LRKV_F32 = 0, LRKV_BF16 = 1 } lrkv_dtype;
+
+/* Which cache a compress call writes: keys use the row layout, values the octet layout. */
+typedef enum lrkv_cache_kind { LRKV_KEYS = 0, LRKV_VALUES = 1 } lrkv_cache_kind;
+
+typedef struct lrkv_dims {
+  int32_t batch;        /* B */
+  int32_t n_q_heads;    /* Hq */
+  int32_t n_kv_heads;   /* Hkv */
+  int32_t head_dim;     /* d */
+  int32_t rank_k;       /* r_K */
+  int32_t rank_v;       /* r_V */
+  int64_t capacity;     /* cap: tokens the coefficient caches hold per (b, kv head) */
+} lrkv_dims;
+
+/*
+ * Compress / append (the cache write).
+ *   coeff[b, h, pos + t, :] = x[b, t, h, :] @ basis[h]      for t in [0, n_tokens)
+ * ("Llama-3.1-NovaKV" model card: the cache holds the low-rank factors of K
+ * and V; "OjaKV" README, StaticPCA: a fixed offline basis.)  One call writes
+ * one cache (K or V) with its own basis and rank.
+ *   x      [B, n_tokens, Hkv, d]   the new tokens' full keys or values
+ *   basis  [Hkv, d, rank]          orthonormal columns (not checked)
+ *   coeff  key row layout [B, Hkv, capacity, rank] (kind = LRKV_KEYS) or
+ *          value octet layout [B, Hkv, capacity/8, rank, 8] (kind = LRKV_VALUES)
+ * Rows outside [pos, pos + n_tokens) are not touched.  n_tokens = 0 is a no-op.
+ * Requires pos >= 0 and pos + n_tokens <= capacity.
+ */
+lrkv_status lrkv_compress(const void* x, const void* basis, void* coeff, lrkv_cache_kind kind,
+                          int32_t batch, int32_t n_kv_heads, int32_t head_dim, int32_t rank,
+                          int64_t n_tokens, int64_t pos, int64_t capacity, lrkv_dtype dtype,
+                          hipStream_t stream);
+
+/*
+ * Bytes of float32 workspace lrkv_decode_attn (side_cap = 0) or
+ * lrkv_decode_attn_hybrid (side_cap > 0) needs for these dims.  n_ctx is the
+ * context length of a plain decode; the hybrid decode plans for
+ * dims->capacity and side_cap instead.  Returns 0 for invalid dims.  The
+ * split plan depends on the current device's compute-unit count, so query on
+ * the device that will run the call.
+ */
+size_t lrkv_decode_workspace_bytes(const lrkv_dims* dims, int64_t n_ctx, int64_t side_cap);
+
+/*
+ * Decode attention of one query per q head over tokens [0, n_ctx) of a
+ * low-rank cache (the token appended at this step included):
+ *   q' = q B_K[h] * scale,  s_t = q' . C_K[t],  p = softmax(s),
+ *   acc = sum_t p_t C_V[t],  out = acc B_V[h]^T,  lse = log sum_t exp(s_t)
+ * which equals softmax(q K_hat^T * scale) V_hat with K_hat = C_K B_K^T and
+ * V_hat = C_V B_V^T ("OjaKV" README, StaticPCA: standard attention over
+ * keys and values reconstructed from the low-rank cache).  The context is
+ * split into chunks attended in parallel and merged by log-sum-exp.
+ *   q        [B, Hq, d]
+ *   basis_k  [Hkv, d, r_K];   coeff_k  key row layout [B, Hkv, capacity, r_K]
+ *   basis_v  [Hkv, d, r_V];   coeff_v  value octet layout [B, Hkv, capacity/8, r_V, 8]
+ *   out      [B, Hq, d] (storage dtype);  lse [B, Hq] float32 natural log, or NULL
+ *   scale    softmax scale; 0 selects 1/sqrt(head_dim)
+ *   workspace at least lrkv_decode_workspace_bytes(dims, n_ctx, 0) bytes
+ * Requires 1 <= n_ctx <= capacity.
+ */
+lrkv_status lrkv_decode_attn(const void* q, const void* basis_k, const void* coeff_k,
+                             const void* basis_v, const void* coeff_v, void* out, float* lse,
+                             const lrkv_dims* dims, int64_t n_ctx, float scale, lrkv_dtype dtype,
+                             void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Bytes of workspace lrkv_compress_hybrid needs for n_tokens new tokens. */
+size_t lrkv_compress_hybrid_workspace_bytes(const lrkv_dims* dims, int64_t n_tokens);
+
+/*
+ * Hybrid compress ("OjaKV" README, Method Summary, OjaKV: tokens with high
+ * reconstruction error are kept in full rank, the rest are compressed).
+ * For every new token t of (b, h) with key k and value v:
+ *   c = round(x B) (the stored coefficients), x_hat = c B^T,
+ *   selected(x) = ||x - x_hat||^2 > tau^2 ||x||^2   (float32),
+ *   flag_t = selected(k) or selected(v).
+ * Unflagged tokens are appended, in ascending t, to the low-rank caches at
+ * rows n_lr[b, h], n_lr[b, h] + 1, ...; flagged tokens are appended, in
+ * ascending t, to the full-rank side lists at n_side[b, h], ... with
+ * side_idx = pos + t.  n_lr and n_side are then advanced.  Selection and
+ * placement are deterministic (no dependence on execution order).
+ *   k, v      [B, n_tokens, Hkv, d]
+ *   tau       >= 0 (+inf keeps every token low rank); tokens of zero norm are never flagged
+ *   coeff_k / coeff_v   key row / value octet layout caches (dims->capacity tokens)
+ *   n_lr, n_side        [B, Hkv] int32, device, in/out (the caller zeroes them once)
+ *   k_side    key row layout [B, Hkv, side_cap, d]; v_side value octet layout
+ *             [B, Hkv, side_cap/8, d, 8]; side_idx [B, Hkv, side_cap] int32
+ *   flags     [B, Hkv, n_tokens] uint8 (1 = full rank), or NULL
+ *   overflow  device int32, set to 1 when a low-rank cache or a side list is
+ *             full; the tokens that do not fit are dropped and the counts stop
+ *             at the capacities.  The caller zeroes it.
+ *   workspace at least lrkv_compress_hybrid_workspace_bytes(dims, n_tokens) bytes
+ * Only bfloat16 is supported for the hybrid cache.
+ */
+lrkv_status lrkv_compress_hybrid(const void* k, const void* v, const void* basis_k,
+                                 const void* basis_v, float tau, void* coeff_k, void* coeff_v,
+                                 int32_t* n_lr, void* k_side, void* v_side, int32_t* side_idx,
+                                 int32_t* n_side, uint8_t* flags, int32_t* overflow,
+                                 const lrkv_dims* dims, int64_t n_tokens, int64_t pos,
+                                 int64_t side_cap, lrkv_dtype dtype, void* workspace,
+                                 size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * Hybrid decode: one softmax over the n_lr[b, h] low-rank tokens and the
+ * n_side[b, h] full-rank side-list tokens of each (b, kv head)
+ * ("OjaKV" README, Method Summary, OjaKV):
+ *   out = (sum_lr p_t C_V[t] B_V^T + sum_side p_j v_j),  p = softmax over both sets
+ * with s_t = q' . C_K[t] for low-rank tokens and s_j = scale q . k_j for side tokens.
+ * Counts are read on the device; an empty (b, h) gives out = 0, lse = -inf.
+ *   workspace at least lrkv_decode_workspace_bytes(dims, 0, side_cap) bytes.
+ */
+lrkv_status lrkv_decode_attn_hybrid(const void* q, const void* basis_k, const void* coeff_k,
+                                    const void* basis_v, const void* coeff_v,
+                                    const int32_t* n_lr, const void* k_side, const void* v_side,
+                                    const int32_t* n_side, int64_t side_cap, void* out,
+                                    float* lse, const lrkv_dims* dims, float scale,
+                                    lrkv_dtype dtype, void* workspace, size_t workspace_bytes,
+                                    hipStream_t stream);
+
+/* Static description of a status code. */
+const char* lrkv_status_string(lrkv_status status);
+
+/* Detail of the last non-OK status returned on this thread ("" if none). */
+const char* lrkv_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LRKV_H */
