@@ -1,0 +1,299 @@
+#!/usr/bin/env python3
+"""Benchmark: decode attention over a low-rank KV cache on one MI355X.
+
+Workload (default): Llama-3.1-8B geometry, 32 layers, batch 16, 32 query /
+8 kv heads, head_dim 128, context 32768, layer-varying ranks (r_K, r_V) =
+(32, 96) on even and (48, 112) on odd layers, bfloat16 cache.  One step is
+the whole hot path over one batch: for every layer, compress a 4096-token
+prefill chunk (K and V) into rows [N-1-4096, N-1); then for every layer,
+compress the appended token (K and V) into row N-1 and attend one query per
+head over all N tokens.
+All inputs are synthetic, seeded, and resident in HBM before timing.
+
+Reported `value`: decode microseconds per layer-step (appended-token
+compress of K and V in one launch + the attention kernel + the merge kernel),
+averaged over the 32 layers and the timed steps, measured with HIP events on
+the launch stream.  The roofline entry is for the attention kernel
+(split_bf16_kernel, the dominant one): its algorithmic bytes per launch (key
+and value coefficient rows, both bases, the queries) over its average launch
+time.  `cpu_baseline` times the float64 CPU oracle on a
+bounded sample of the same decode and scales it to a layer-step.
+
+Usage: python bench.py [--gpus 1] [--steps 10] [--warmup 3] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "decode attn μs/layer-step & achieved HBM GB/s (% peak) at ctx 8K-128K"
+HBM_PEAK_GBPS = 8000.0   # MI355X HBM3E, AMD's published figure
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=10)
+    p.add_argument("--warmup", type=int, default=3)
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-seconds", type=float, default=15.0,
+                   help="approximate CPU time budget of the oracle sample")
+    return p.parse_args()
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only: this build has no multi-GPU path "
+              f"(asked for --gpus {args.gpus}).", flush=True)
+        return 2
+
+    import torch
+    import decode_attention_lrkv_amd as lrkv
+    from decode_attention_lrkv_amd import bytes_model as bm
+    import lrkv_synth as synth
+
+    lrkv.library()   # fails loudly when the HIP library is missing
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    w = synth.BATCHED_32K
+    L, B, Hq, H, d = w.layers, w.batch, w.n_q_heads, w.n_kv_heads, w.head_dim
+    N = w.n_ctx[0]
+    cap = N
+    P = w.prefill
+    p0 = N - 1 - P                      # first row of the prefill chunk
+    threads = min(16, len(os.sched_getaffinity(0)))
+
+    def dev_bf16(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    # ---------------- inputs (generated once per layer parity, copied per layer)
+    t_gen = time.time()
+    base = {}
+    for par in (0, 1):
+        rk, rv = w.ranks(par)
+        ck = np.zeros((B, H, cap, rk), np.uint16)
+        cv = np.zeros((B, H, cap, rv), np.uint16)
+        ck[:, :, :p0] = synth.stack_heads(w, lambda b, h: synth.direct_coeffs(w, par, "k", b, h, p0, exact=False),
+                                          threads=threads).store
+        cv[:, :, :p0] = synth.stack_heads(w, lambda b, h: synth.direct_coeffs(w, par, "v", b, h, p0, exact=False),
+                                          threads=threads).store
+        xk = synth.tokens_major(synth.stack_heads(
+            w, lambda b, h: synth.full_tokens(w, par, "k", b, h, P, synth.PART_PREFILL), threads=threads)).store
+        xv = synth.tokens_major(synth.stack_heads(
+            w, lambda b, h: synth.full_tokens(w, par, "v", b, h, P, synth.PART_PREFILL), threads=threads)).store
+        base[par] = dict(
+            rk=rk, rv=rv,
+            ck=dev_bf16(ck), cv=dev_bf16(synth.to_value_octets(cv)),
+            xk=dev_bf16(xk), xv=dev_bf16(xv),
+            bk=dev_bf16(synth.basis(w, par, "k").store), bv=dev_bf16(synth.basis(w, par, "v").store))
+        del ck, cv, xk, xv
+    layers = []
+    for l in range(L):
+        bs = base[l % 2]
+        xa_k = synth.tokens_major(synth.stack_heads(
+            w, lambda b, h: synth.full_tokens(w, l, "k", b, h, 1, synth.PART_APPEND), threads=threads)).store
+        xa_v = synth.tokens_major(synth.stack_heads(
+            w, lambda b, h: synth.full_tokens(w, l, "v", b, h, 1, synth.PART_APPEND), threads=threads)).store
+        layers.append(dict(
+            rk=bs["rk"], rv=bs["rv"], bk=bs["bk"], bv=bs["bv"],
+            ck=bs["ck"].clone(), cv=bs["cv"].clone(),       # distinct addresses per layer
+            xk=bs["xk"].clone(), xv=bs["xv"].clone(),
+            ak=dev_bf16(xa_k), av=dev_bf16(xa_v),
+            q=dev_bf16(synth.query(w, l).store),
+            out=torch.empty((B, Hq, d), dtype=torch.bfloat16, device=dev),
+            lse=torch.empty((B, Hq), dtype=torch.float32, device=dev)))
+    del base
+    ws_bytes = max(lrkv.decode_workspace_bytes(B, Hq, H, d, lay["rk"], lay["rv"], cap, N) for lay in layers)
+    ws = torch.zeros(ws_bytes, dtype=torch.uint8, device=dev)   # decode workspaces start zero-filled
+    torch.cuda.synchronize()
+    log(f"inputs ready in {time.time() - t_gen:.1f}s: {torch.cuda.memory_allocated() / 2**30:.1f} GiB on device, "
+        f"workspace {ws_bytes / 2**20:.2f} MiB")
+
+    # ---------------- one step: prefill chunk of every layer, then one decode step of every layer
+    def step(ev=None):
+        for l, lay in enumerate(layers):
+            if ev: ev["pre"][l][0].record()
+            lrkv.compress_kv(lay["xk"], lay["xv"], lay["bk"], lay["bv"], lay["ck"], lay["cv"], p0)
+            if ev: ev["pre"][l][1].record()
+        for l, lay in enumerate(layers):
+            if ev: ev["dec"][l][0].record()
+            lrkv.compress_kv(lay["ak"], lay["av"], lay["bk"], lay["bv"], lay["ck"], lay["cv"], N - 1)
+            if ev: ev["dec"][l][1].record()
+            # lrkv_decode_attn as its two launches, so that the attention kernel is timed alone
+            lrkv.decode_attn_partial(lay["q"], lay["bk"], lay["ck"], lay["bv"], lay["cv"], N, ws)
+            if ev: ev["dec"][l][2].record()
+            lrkv.decode_attn_merge(lay["out"], lay["lse"], N, ws, H, lay["rk"], lay["rv"], cap)
+            if ev: ev["dec"][l][3].record()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    K = args.steps
+    mk = lambda n: [torch.cuda.Event(enable_timing=True) for _ in range(n)]
+    events = [{"pre": [mk(2) for _ in range(L)], "dec": [mk(4) for _ in range(L)]} for _ in range(K)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(K):
+        step(events[k])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    log(f"timed {K} steps in {wall:.3f}s")
+
+    prefill_us, decode_us, attn_us, merge_us, append_us = [], [], [], [], []
+    attn_by_par = {0: [], 1: []}
+    for k in range(K):
+        for l in range(L):
+            ep, ed = events[k]["pre"][l], events[k]["dec"][l]
+            prefill_us.append(ep[0].elapsed_time(ep[1]) * 1e3)
+            append_us.append(ed[0].elapsed_time(ed[1]) * 1e3)
+            attn_us.append(ed[1].elapsed_time(ed[2]) * 1e3)
+            merge_us.append(ed[2].elapsed_time(ed[3]) * 1e3)
+            decode_us.append(ed[0].elapsed_time(ed[3]) * 1e3)
+            attn_by_par[l % 2].append(attn_us[-1])
+
+    # ---------------- bytes and rates
+    app_bytes = {p: bm.compress_bytes(B, 1, H, d, w.ranks(p)[0]) + bm.compress_bytes(B, 1, H, d, w.ranks(p)[1])
+                 for p in (0, 1)}
+    dec_bytes = {p: bm.decode_bytes(B, Hq, H, d, *w.ranks(p), N) for p in (0, 1)}
+    attn_bytes = {p: bm.split_kernel_bytes(B, Hq, H, d, *w.ranks(p), N) for p in (0, 1)}
+    pre_bytes = {p: bm.compress_bytes(B, P, H, d, w.ranks(p)[0]) + bm.compress_bytes(B, P, H, d, w.ranks(p)[1])
+                 for p in (0, 1)}
+    mean = lambda xs: float(np.mean(xs))
+    dec_us = mean(decode_us)
+    dec_gbps = sum((dec_bytes[l % 2] + app_bytes[l % 2]) for l in range(L)) * K / (sum(decode_us) * 1e-6) / 1e9
+    attn_mean = {p: mean(attn_by_par[p]) for p in (0, 1)}
+    attn_gbps = sum(attn_bytes[l % 2] for l in range(L)) * K / (sum(attn_us) * 1e-6) / 1e9
+    pre_gbps = sum(pre_bytes[l % 2] for l in range(L)) * K / (sum(prefill_us) * 1e-6) / 1e9
+    step_decode_us = dec_us * L
+    tok_s = B / (step_decode_us * 1e-6)
+
+    # a plain device copy of 4 GiB for context (practical bandwidth ceiling)
+    src = torch.empty(2 ** 31, dtype=torch.uint16, device=dev)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(5):
+        dst.copy_(src)
+    e1.record()
+    torch.cuda.synchronize()
+    copy_gbps = 5 * 2 * src.numel() * 2 / (e0.elapsed_time(e1) * 1e-3) / 1e9
+    del src, dst
+
+    result = {
+        "metric": METRIC,
+        "value": round(dec_us, 3),
+        "unit": "us/layer-step",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall * 1e3 / K, 4),
+        "higher_is_better": False,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "layers": L, "batch": B, "n_q_heads": Hq, "n_kv_heads": H,
+                   "head_dim": d, "context": N, "ranks_even": list(w.ranks(0)), "ranks_odd": list(w.ranks(1)),
+                   "prefill_chunk": P, "cache_dtype": "bf16", "accumulate": "fp32"},
+        "decode_GBps": round(dec_gbps, 1),
+        "decode_pct_peak": round(100 * dec_gbps / HBM_PEAK_GBPS, 2),
+        "attn_tokens_per_s": round(tok_s, 1),
+        "decode_us_per_step_32_layers": round(step_decode_us, 1),
+        "attn_kernel_us": {"even": round(attn_mean[0], 3), "odd": round(attn_mean[1], 3)},
+        "merge_us": round(mean(merge_us), 3),
+        "append_compress_us": round(mean(append_us), 3),
+        "prefill_compress_us_per_layer": round(mean(prefill_us), 3),
+        "prefill_compress_GBps": round(pre_gbps, 1),
+        "device_copy_GBps": round(copy_gbps, 1),
+        "roofline": {"bound": "hbm", "kernel": "split_bf16_kernel",
+                     "achieved": round(attn_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(attn_gbps / HBM_PEAK_GBPS, 4), "traffic": measured_traffic(),
+                     "bytes_per_launch": round(sum(attn_bytes[l % 2] for l in range(L)) / L)},
+    }
+
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+def measured_traffic():
+    """HBM bytes per launch of the attention kernel from the committed counter
+    summary, or None when the kernel source changed since it was taken."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", "split_bf16_kernel_llama8b-b16-32k.md")
+    src = os.path.join(ROOT, "decode_attention_lrkv_amd", "csrc", "decode.hip")
+    try:
+        rec = next(json.loads(l.split("TRAFFIC", 1)[1]) for l in open(path) if l.strip().startswith("TRAFFIC"))
+        sha = hashlib.sha256(open(src, "rb").read()).hexdigest()
+    except (OSError, StopIteration, ValueError):
+        return None
+    return rec["mean_bytes_per_launch"] if rec.get("decode_hip_sha256") == sha else None
+
+
+def cpu_baseline(w, budget_s):
+    """Time the float64 CPU oracle on a bounded sample of the same decode layer-step.
+
+    Sample: whole (batch, kv head) units of the decode (reconstruct K_hat and
+    V_hat of all N tokens, attend the 4 query heads; plus compressing the
+    appended token), alternating odd and even layers, until the budget is
+    spent; the mean per unit times B * Hkv units is the layer-step estimate.
+    """
+    import lrkv_synth as synth
+    from oracle import lrkv_oracle as O
+    try:
+        from threadpoolctl import threadpool_info
+        n_threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        n_threads = None
+    N = w.n_ctx[0]
+    g = w.group
+    times = []
+    t_start = time.time()
+    u = 0
+    while time.time() - t_start < budget_s or len(times) < 2:
+        layer = u % 2
+        b, h = (u // 2) % w.batch, (u // (2 * w.batch)) % w.n_kv_heads
+        ck = synth.direct_coeffs(w, layer, "k", b, h, N - 1).exact
+        cv = synth.direct_coeffs(w, layer, "v", b, h, N - 1).exact
+        xk = synth.full_tokens(w, layer, "k", b, h, 1, synth.PART_APPEND).exact
+        xv = synth.full_tokens(w, layer, "v", b, h, 1, synth.PART_APPEND).exact
+        bk = synth.basis(w, layer, "k").exact
+        bv = synth.basis(w, layer, "v").exact
+        q = synth.query(w, layer).exact
+        t0 = time.perf_counter()
+        ak = O.round_storage(O.compress(xk[None, :, None, :], bk[h:h + 1]), "bf16")[0, 0]
+        av = O.round_storage(O.compress(xv[None, :, None, :], bv[h:h + 1]), "bf16")[0, 0]
+        rows = [(b, h * g + j) for j in range(g)]
+        O.decode_rows(q, bk, {(b, h): np.concatenate([ck, ak])}, bv, {(b, h): np.concatenate([cv, av])},
+                      N, rows)
+        times.append(time.perf_counter() - t0)
+        u += 1
+    per_unit = float(np.mean(times))
+    us = per_unit * w.batch * w.n_kv_heads * 1e6
+    return {"value": round(us, 1), "unit": "us/layer-step", "cores": n_threads, "kind": "oracle",
+            "host_cpus": len(os.sched_getaffinity(0)),
+            "sample": f"{len(times)} (batch, kv-head) units of the decode at N={N} (reconstruct K_hat, V_hat; "
+                      f"attend {g} query heads; compress the appended token), odd and even layers alternating, "
+                      f"mean {per_unit:.3f}s per unit, scaled x{w.batch * w.n_kv_heads} to one layer-step"}
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -20,9 +20,9 @@ from typing import Optional
 import torch
 
 __all__ = [
-    "LrkvError", "library", "compress", "decode_attn", "decode_workspace_bytes",
+    "LrkvError", "library", "compress", "compress_kv", "decode_attn", "decode_workspace_bytes",
     "compress_hybrid", "compress_hybrid_workspace_bytes", "decode_attn_hybrid",
-    "HybridCache", "value_cache_shape", "LIB_PATH",
+    "HybridCache", "value_cache_shape", "LIB_PATH", "decode_attn_partial", "decode_attn_merge",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "liblrkv.so")
@@ -50,6 +50,7 @@ _I32, _I64, _F = ctypes.c_int32, ctypes.c_int64, ctypes.c_float
 _SIG = {
     "lrkv_compress": (ctypes.c_int, [_P, _P, _P, ctypes.c_int, _I32, _I32, _I32, _I32, _I64, _I64, _I64,
                                      ctypes.c_int, _P]),
+    "lrkv_compress_kv": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, ctypes.POINTER(_Dims), _I64, _I64, ctypes.c_int, _P]),
     "lrkv_decode_workspace_bytes": (ctypes.c_size_t, [ctypes.POINTER(_Dims), _I64, _I64]),
     "lrkv_decode_attn": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, ctypes.POINTER(_Dims), _I64, _F,
                                         ctypes.c_int, _P, ctypes.c_size_t, _P]),
@@ -60,6 +61,10 @@ _SIG = {
     "lrkv_decode_attn_hybrid": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _I64, _P, _P,
                                                ctypes.POINTER(_Dims), _F, ctypes.c_int, _P,
                                                ctypes.c_size_t, _P]),
+    "lrkv_decode_attn_partial": (ctypes.c_int, [_P, _P, _P, _P, _P, ctypes.POINTER(_Dims), _I64, _F,
+                                                ctypes.c_int, _P, ctypes.c_size_t, _P]),
+    "lrkv_decode_attn_merge": (ctypes.c_int, [_P, _P, ctypes.POINTER(_Dims), _I64, ctypes.c_int, _P,
+                                              ctypes.c_size_t, _P]),
     "lrkv_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "lrkv_last_error": (ctypes.c_char_p, []),
 }
@@ -132,6 +137,15 @@ def compress(x: torch.Tensor, basis: torch.Tensor, coeff: torch.Tensor, pos: int
                                    B, H, d, r, T, pos, cap, _dtype_code(x), _stream(x.device)))
 
 
+def compress_kv(xk, xv, basis_k, basis_v, coeff_k, coeff_v, pos: int) -> None:
+    """Both caches at once: coeff_k rows (row layout) and coeff_v rows (octet layout) [pos, pos + T)."""
+    B, T, H, d = xk.shape
+    dims = _Dims(B, H, H, d, basis_k.shape[2], basis_v.shape[2], coeff_k.shape[2])
+    _check(library().lrkv_compress_kv(_ptr(xk), _ptr(xv), _ptr(basis_k), _ptr(basis_v), _ptr(coeff_k),
+                                      _ptr(coeff_v), ctypes.byref(dims), T, pos, _dtype_code(xk),
+                                      _stream(xk.device)))
+
+
 def decode_workspace_bytes(batch, n_q_heads, n_kv_heads, head_dim, rank_k, rank_v, capacity,
                            n_ctx, side_cap=0) -> int:
     dims = _Dims(batch, n_q_heads, n_kv_heads, head_dim, rank_k, rank_v, capacity)
@@ -139,6 +153,7 @@ def decode_workspace_bytes(batch, n_q_heads, n_kv_heads, head_dim, rank_k, rank_
 
 
 def _workspace(nbytes: int, device, workspace: Optional[torch.Tensor]) -> torch.Tensor:
+    """The caller's workspace, or a new one."""
     if workspace is not None:
         return workspace
     return torch.empty(max(nbytes, 16), dtype=torch.uint8, device=device)
@@ -229,3 +244,23 @@ def decode_attn_hybrid(q, basis_k, basis_v, cache: HybridCache, out=None, lse=No
                                        _ptr(out), _ptr(lse), ctypes.byref(dims), scale, _dtype_code(q),
                                        _ptr(ws), ws.numel(), _stream(q.device)))
     return out, lse
+
+
+def decode_attn_partial(q, basis_k, coeff_k, basis_v, coeff_v, n_ctx: int, workspace: torch.Tensor,
+                        scale: float = 0.0):
+    """First phase of decode_attn: per-workgroup lifted partial results into `workspace`."""
+    B, Hq, d = q.shape
+    H, _, rk = basis_k.shape
+    dims = _Dims(B, Hq, H, d, rk, basis_v.shape[2], coeff_k.shape[2])
+    _check(library().lrkv_decode_attn_partial(_ptr(q), _ptr(basis_k), _ptr(coeff_k), _ptr(basis_v),
+                                              _ptr(coeff_v), ctypes.byref(dims), n_ctx, scale, _dtype_code(q),
+                                              _ptr(workspace), workspace.numel(), _stream(q.device)))
+
+
+def decode_attn_merge(out, lse, n_ctx: int, workspace: torch.Tensor, n_kv_heads: int, rank_k: int,
+                      rank_v: int, capacity: int):
+    """Second phase of decode_attn: log-sum-exp merge of the partials into out and lse."""
+    B, Hq, d = out.shape
+    dims = _Dims(B, Hq, n_kv_heads, d, rank_k, rank_v, capacity)
+    _check(library().lrkv_decode_attn_merge(_ptr(out), _ptr(lse), ctypes.byref(dims), n_ctx, _dtype_code(out),
+                                            _ptr(workspace), workspace.numel(), _stream(out.device)))

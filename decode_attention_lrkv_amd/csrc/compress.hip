@@ -1,10 +1,12 @@
 // Compress / append: coeff[b, h, pos + t, :] = x[b, t, h, :] @ basis[h]  (gfx950).
 //
-// bfloat16: a 64-token tile per workgroup, 16 tokens per wave, on the matrix
-// cores.  The basis of the kv head is staged once per workgroup in LDS,
-// transposed, so that both operands are read as 16-byte runs along the
+// bfloat16: a 128-token tile per workgroup on the matrix cores, 16 tokens per
+// wave at a time.  The basis of the kv head is staged once per workgroup in
+// LDS, transposed, so that both operands are read as 16-byte runs along the
 // contraction (head_dim) axis: tokens' rows straight from HBM, basis columns
-// from LDS.  float32 accumulation, one rounding to bfloat16 at the store.
+// from LDS.  float32 accumulation, one rounding to bfloat16, and the tile's
+// coefficients leave through LDS as 16-byte stores (key rows, or whole value
+// octets; element stores only for octets cut by the tile's ends).
 // float32: one thread per (token, coefficient) on the vector ALU.
 #include "lrkv_device.h"
 #include "lrkv_internal.h"
@@ -13,7 +15,7 @@ namespace lrkv {
 
 namespace {
 
-constexpr int kTile = 64;
+constexpr int kTile = 128;   // tokens per workgroup (bfloat16 path)
 constexpr int kPad = 8;   // LDS row padding (elements) against bank conflicts
 
 __device__ __forceinline__ int64_t coeff_index(int values_layout, int64_t bh, int64_t cap, int r,
@@ -33,48 +35,182 @@ __global__ __launch_bounds__(256) void compress_bf16_kernel(CompressArgs a) {
   const int b = blockIdx.z;
   const int r = a.rank;
   const int64_t bh = (int64_t)b * a.hkv + h;
+  const int64_t t_base = (int64_t)blockIdx.x * kTile;
+  const int64_t left = a.n_tokens - t_base;
+  const int nt = left < kTile ? (int)left : kTile;
 
-  __shared__ uint16_t s_bt[NB * 16][D + kPad];
+  __shared__ __attribute__((aligned(16))) uint16_t s_bt[NB * 16][D + kPad];    // basis, transposed
+  // the tile's coefficients: keys as [token][column]; values as [column][slot]
+  // with slot = token + (p0 % 8), so each destination octet is 16 aligned bytes
+  constexpr int kOutRow = NB * 16 + kPad;
+  constexpr int kOutCol = kTile + 8 + kPad;
+  constexpr int kOutElems = kTile * kOutRow > NB * 16 * kOutCol ? kTile * kOutRow : NB * 16 * kOutCol;
+  __shared__ __attribute__((aligned(16))) uint16_t s_out[kOutElems];
+  const int64_t p0 = a.pos + t_base;                       // destination row of the tile's first token
+  const int shift = (int)(p0 & 7);
 
-  const uint16_t* bs = static_cast<const uint16_t*>(a.basis) + (int64_t)h * D * r;
-  for (int i = tid; i < D * r; i += 256) {
-    const int dd = i / r, c = i - dd * r;
-    s_bt[c][dd] = bs[i];
-  }
-  for (int i = tid; i < (NB * 16 - r) * D; i += 256) s_bt[r + i / D][i % D] = 0;
-  __syncthreads();
-
-  const int64_t t0 = (int64_t)blockIdx.x * kTile + wave * 16;
-  const int64_t tok = t0 + n16;
-  const bool valid = tok < a.n_tokens;
-  const uint16_t* xrow = static_cast<const uint16_t*>(a.x) + ((b * a.n_tokens + tok) * a.hkv + h) * D;
-
-  f32x4 acc[NB];
+  // basis rows arrive as 16-byte runs of 8 coefficients (all loads issued
+  // before the first wait) and are written transposed
+  {
+    // piece i = (8-column group, head_dim row); consecutive lanes take
+    // consecutive rows, so the transposed 2-byte LDS writes hit distinct banks
+    const uint16_t* bs = static_cast<const uint16_t*>(a.basis) + (int64_t)h * D * r;
+    const int n = D * (r / 8);
+    constexpr int kIter = (D * NB * 16 / 8 + 255) / 256;
+    u32x4 w[kIter];
 #pragma unroll
-  for (int nb = 0; nb < NB; ++nb) acc[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-  for (int c = 0; c < D / 32; ++c) {
-    const int k = 32 * c + 8 * grp;
-    const u32x4 xa = valid ? *reinterpret_cast<const u32x4*>(xrow + k) : u32x4{0u, 0u, 0u, 0u};
-#pragma unroll
-    for (int nb = 0; nb < NB; ++nb) {
-      const u32x4 bb = *reinterpret_cast<const u32x4*>(&s_bt[16 * nb + n16][k]);
-      acc[nb] = mfma_16x16x32(xa, bb, acc[nb]);
+    for (int it = 0; it < kIter; ++it) {
+      const int i = tid + 256 * it;
+      if (i < n) w[it] = *reinterpret_cast<const u32x4*>(bs + (i % D) * r + (i / D) * 8);
     }
-  }
-  // lane (n16, grp) holds coefficient 16*nb + n16 of tokens t0 + 4*grp + i
-  uint16_t* out = static_cast<uint16_t*>(a.coeff);
 #pragma unroll
-  for (int nb = 0; nb < NB; ++nb) {
-    const int col = 16 * nb + n16;
-    if (col < r) {
+    for (int it = 0; it < kIter; ++it) {
+      const int i = tid + 256 * it;
+      if (i < n) {
+        const int dd = i % D, c = (i / D) * 8;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int64_t t = t0 + 4 * grp + i;
-        if (t < a.n_tokens)
-          out[coeff_index(a.values_layout, bh, a.cap, r, a.pos + t, col)] = f32_to_bf16(acc[nb][i]);
+        for (int e = 0; e < 4; ++e) {
+          s_bt[c + 2 * e][dd] = (uint16_t)(w[it][e] & 0xFFFFu);
+          s_bt[c + 2 * e + 1][dd] = (uint16_t)(w[it][e] >> 16);
+        }
       }
     }
+    for (int i = tid; i < (NB * 16 - r) * D; i += 256) s_bt[r + i / D][i % D] = 0;
+  }
+  __syncthreads();
+
+  // each wave takes two 16-token sub-tiles; both sub-tiles' rows are loaded
+  // before either is multiplied, so each wave keeps 8 KB of loads in flight
+  constexpr int kSubs = kTile / 16 / 4;
+  u32x4 xa[kSubs][D / 32];
+#pragma unroll
+  for (int u = 0; u < kSubs; ++u) {
+    const int tl = 16 * (wave + 4 * u) + n16;
+    const bool valid = tl < nt;
+    const uint16_t* xrow =
+        static_cast<const uint16_t*>(a.x) + ((b * a.n_tokens + t_base + tl) * a.hkv + h) * D;
+#pragma unroll
+    for (int c = 0; c < D / 32; ++c)
+      xa[u][c] = valid ? *reinterpret_cast<const u32x4*>(xrow + 32 * c + 8 * grp) : u32x4{0u, 0u, 0u, 0u};
+  }
+#pragma unroll
+  for (int u = 0; u < kSubs; ++u) {
+    const int sub = wave + 4 * u;
+    if (16 * sub >= nt) break;
+    f32x4 acc[NB];
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) acc[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int c = 0; c < D / 32; ++c) {
+      const int k = 32 * c + 8 * grp;
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb)
+        acc[nb] = mfma_16x16x32(xa[u][c], *reinterpret_cast<const u32x4*>(&s_bt[16 * nb + n16][k]), acc[nb]);
+    }
+    // lane (n16, grp) holds coefficient 16*nb + n16 of tokens 16*sub + 4*grp + i
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int tl = 16 * sub + 4 * grp + i, col = 16 * nb + n16;
+        const int at = a.values_layout ? col * kOutCol + shift + tl : tl * kOutRow + col;
+        s_out[at] = f32_to_bf16(acc[nb][i]);
+      }
+  }
+  __syncthreads();
+
+  uint16_t* out = static_cast<uint16_t*>(a.coeff);
+  if (!a.values_layout) {
+    // key rows: each destination row is r/8 aligned 16-byte pieces
+    const int per_row = r / 8;
+    uint16_t* dst = out + (bh * a.cap + p0) * r;
+    for (int i = tid; i < nt * per_row; i += 256) {
+      const int tl = i / per_row, c = (i - tl * per_row) * 8;
+      *reinterpret_cast<u32x4*>(dst + (int64_t)tl * r + c) = *reinterpret_cast<const u32x4*>(&s_out[tl * kOutRow + c]);
+    }
+  } else {
+    // value octets: a whole octet is one 16-byte LDS read and one 16-byte
+    // store; octets cut by the tile's ends are written element by element
+    const int64_t o_first = p0 >> 3, o_last = (p0 + nt - 1) >> 3;
+    const int n_oct = (int)(o_last - o_first + 1);
+    uint16_t* dst = out + bh * a.cap * r;
+    for (int i = tid; i < n_oct * r; i += 256) {
+      const int oi = i / r, col = i - oi * r;
+      const int64_t o = o_first + oi;
+      const int first = 8 * oi - shift;                    // tile-local token of element 0
+      uint16_t* q = dst + (o * r + col) * 8;
+      const uint16_t* src = &s_out[col * kOutCol + 8 * oi];
+      if (first >= 0 && first + 8 <= nt) {
+        *reinterpret_cast<u32x4*>(q) = *reinterpret_cast<const u32x4*>(src);
+      } else {
+        for (int e = 0; e < 8; ++e) {
+          const int tl = first + e;
+          if (tl >= 0 && tl < nt) q[e] = src[e];
+        }
+      }
+    }
+  }
+}
+
+// Few tokens (an appended decode token): both caches in one launch, one
+// workgroup per (batch, kv head), no LDS staging of the bases.  Threads
+// 0..127 compute the key coefficients and 128..255 the value coefficients:
+// thread (8-column group, 16-row slice of head_dim) accumulates 8 columns
+// over 16 rows from 16-byte basis loads, and the slices are summed in LDS.
+template <int D>
+__global__ __launch_bounds__(256) void compress_kv_small_kernel(CompressKvArgs a) {
+  const int tid = threadIdx.x;
+  const int kind = tid >> 7;                 // 0: keys, 1: values
+  const int t7 = tid & 127;
+  const int h = blockIdx.x;
+  const int b = blockIdx.y;
+  const int r = kind ? a.rv : a.rk;
+  const int groups = r / 8;
+  constexpr int kSlices = 8, kRows = D / kSlices;
+  const int cg = t7 % 16, sl = t7 / 16;      // column group, head_dim slice
+  const int64_t bh = (int64_t)b * a.hkv + h;
+  const uint16_t* basis = static_cast<const uint16_t*>(kind ? a.bv : a.bk) + (int64_t)h * D * r;
+  const uint16_t* x = static_cast<const uint16_t*>(kind ? a.xv : a.xk);
+
+  __shared__ float s_x[2][kSmallT][D];
+  __shared__ float s_part[2][kSlices][kSmallT][128];
+  for (int i = t7; i < a.n_tokens * D; i += 128) {
+    const int t = i / D, e = i - t * D;
+    s_x[kind][t][e] = bf16_to_f32(x[((b * a.n_tokens + t) * a.hkv + h) * D + e]);
+  }
+  u32x4 w[kRows];
+  if (cg < groups) {
+#pragma unroll
+    for (int e = 0; e < kRows; ++e)
+      w[e] = *reinterpret_cast<const u32x4*>(basis + (sl * kRows + e) * r + cg * 8);
+  }
+  __syncthreads();
+  if (cg < groups) {
+    for (int t = 0; t < a.n_tokens; ++t) {
+      float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int e = 0; e < kRows; ++e) {
+        const float xv = s_x[kind][t][sl * kRows + e];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          acc[2 * k] = fmaf(xv, bf16_lo(w[e][k]), acc[2 * k]);
+          acc[2 * k + 1] = fmaf(xv, bf16_hi(w[e][k]), acc[2 * k + 1]);
+        }
+      }
+#pragma unroll
+      for (int k = 0; k < 8; ++k) s_part[kind][sl][t][cg * 8 + k] = acc[k];
+    }
+  }
+  __syncthreads();
+  uint16_t* out = static_cast<uint16_t*>(kind ? a.cv : a.ck);
+  for (int i = t7; i < a.n_tokens * r; i += 128) {
+    const int t = i / r, col = i - t * r;
+    float v = 0.f;
+#pragma unroll
+    for (int s2 = 0; s2 < kSlices; ++s2) v += s_part[kind][s2][t][col];
+    const int64_t p = a.pos + t;
+    const int64_t at = kind ? bh * a.cap * r + ((p >> 3) * r + col) * 8 + (p & 7) : (bh * a.cap + p) * r + col;
+    out[at] = f32_to_bf16(v);
   }
 }
 
@@ -113,6 +249,13 @@ hipError_t launch_compress_bf16(const CompressArgs& a, hipStream_t s) {
     default:
       return hipErrorInvalidValue;
   }
+  return hipGetLastError();
+}
+
+hipError_t launch_compress_kv_small_bf16(const CompressKvArgs& a, hipStream_t s) {
+  const dim3 grid(a.hkv, a.batch);
+  if (a.d == 128) hipLaunchKernelGGL(compress_kv_small_kernel<128>, grid, dim3(256), 0, s, a);
+  else hipLaunchKernelGGL(compress_kv_small_kernel<64>, grid, dim3(256), 0, s, a);
   return hipGetLastError();
 }
 

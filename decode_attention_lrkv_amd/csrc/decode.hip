@@ -1,8 +1,8 @@
 // Split-K decode attention over a low-rank KV cache (gfx950).
 //
-// One wave attends one split (a run of 32-token chunks) of one (batch, kv
-// head) for all g query heads of that kv head, so every coefficient row is
-// read from HBM once per kv head.  Per chunk:
+// Launch 1, the attention kernel: one wave attends one split (a run of
+// 32-token chunks) of one (batch, kv head) for all g query heads of that kv
+// head, so every coefficient row is read from HBM once per kv head.  Per chunk:
 //   scores  s = C_K q'             matrix cores, tokens as rows, heads as columns
 //   softmax running max / sum per head, rescaling the accumulator
 //   acc    += P C_V                matrix cores, heads as rows, value columns as columns
@@ -13,8 +13,12 @@
 // value product, so no data moves between lanes inside the loop.  bfloat16
 // operands that must keep float32 accuracy (q' and the weights p) are split
 // into a high and a low bfloat16 part: the two products sum to float32
-// precision.  A second kernel merges the splits by log-sum-exp and lifts the
-// latent accumulator through B_V^T.
+// precision.  At the end the workgroup's four waves are merged in LDS and the
+// merged latent accumulator is lifted through B_V^T, so each workgroup leaves
+// one head_dim-wide partial (running max, sum, unnormalised output) per query
+// head.
+// Launch 2, the merge kernel: log-sum-exp combination of those partials
+// (and of the full-rank side list's partials in the hybrid cache).
 #include "lrkv_device.h"
 #include "lrkv_internal.h"
 
@@ -23,14 +27,138 @@ namespace lrkv {
 namespace {
 
 constexpr int kWaves = 4;
+constexpr uint32_t kOob = 0x80000000u;   // a buffer offset past any valid range
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+
+__device__ __forceinline__ u32x4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t voff) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, 0, 0));
+}
+
+template <typename T>
+__device__ __forceinline__ float load_f(const T* p, int64_t i);
+template <>
+__device__ __forceinline__ float load_f<uint16_t>(const uint16_t* p, int64_t i) { return bf16_to_f32(p[i]); }
+template <>
+__device__ __forceinline__ float load_f<float>(const float* p, int64_t i) { return p[i]; }
+
+template <typename T>
+__device__ __forceinline__ void store_f(T* p, int64_t i, float v);
+template <>
+__device__ __forceinline__ void store_f<uint16_t>(uint16_t* p, int64_t i, float v) { p[i] = f32_to_bf16(v); }
+template <>
+__device__ __forceinline__ void store_f<float>(float* p, int64_t i, float v) { p[i] = v; }
 
 // ----------------------------------------------------------------------------
-// bfloat16 split kernel (matrix cores)
+// workgroup epilogue shared by the attention kernels
+// ----------------------------------------------------------------------------
+// In LDS on entry: wave w's unnormalised latent accumulator of head j at
+// s_acc[(w * 16 + j) * acc_ld + c] (c < rv), and s_ml[w][j] = {running max
+// (log2 units), sum}.  The four waves are merged (M = max_w m_w,
+// acc = sum_w 2^(m_w - M) acc_w, likewise the sum), the result is lifted
+// through B_V^T (or taken as is when the values are full rank, basis_v null)
+// and written as this workgroup's partial.
+// For bfloat16, s_stage must hold d x (rv + 8) elements; it may alias s_acc.
+template <typename T>
+__device__ void workgroup_partial(const SplitArgs& a, int b, int h, const float* s_acc, int acc_ld,
+                                  const float (*s_ml)[8][2], T* s_stage, float* s_merged) {
+  const int tid = threadIdx.x;
+  const int g = a.g, rv = a.rv, d = a.d;
+  constexpr int kVec = 16 / sizeof(T);
+  const int ldb = rv + kVec;
+  const bool lift = a.basis_v != nullptr;
+  __shared__ float s_w[kWaves][8];
+  __shared__ float s_mm[8][2];
+
+  // issue the B_V loads first; they land while the waves are merged
+  // (bfloat16 bases are staged in LDS; float32 ones are read from memory)
+  constexpr bool kStage = sizeof(T) == 2;
+  constexpr int kIter = kStage ? 128 * 128 / kVec / 256 : 1;
+  u32x4 wb[kIter];
+  const int per_row = rv / kVec, nb = (lift && kStage) ? d * per_row : 0;
+  const T* bv = lift ? static_cast<const T*>(a.basis_v) + (int64_t)h * d * rv : nullptr;
+#pragma unroll
+  for (int it = 0; it < kIter; ++it) {
+    const int i = tid + 256 * it;
+    if (i < nb) wb[it] = *reinterpret_cast<const u32x4*>(bv + (i / per_row) * rv + (i % per_row) * kVec);
+  }
+  if (tid < g) {
+    float M = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) M = fmaxf(M, s_ml[w][tid][0]);
+    float L = 0.f;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+      const float m = s_ml[w][tid][0];
+      const float wt = m == -INFINITY ? 0.f : exp2_fast(m - M);
+      s_w[w][tid] = wt;
+      L = fmaf(wt, s_ml[w][tid][1], L);
+    }
+    s_mm[tid][0] = M;
+    s_mm[tid][1] = L;
+  }
+  __syncthreads();
+  for (int i = tid; i < g * rv; i += 256) {
+    const int j = i / rv, c = i - j * rv;
+    float acc = 0.f;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) acc = fmaf(s_w[w][j], s_acc[(w * 16 + j) * acc_ld + c], acc);
+    s_merged[j * 128 + c] = acc;
+  }
+  __syncthreads();   // s_acc may share memory with s_stage
+  const int64_t row0 = (int64_t)b * a.hq + (int64_t)h * g;
+  const int part = blockIdx.x;
+  float* po = a.part_o;
+  if (lift) {
+    if (kStage) {
+#pragma unroll
+      for (int it = 0; it < kIter; ++it) {
+        const int i = tid + 256 * it;
+        if (i < nb) *reinterpret_cast<u32x4*>(s_stage + (i / per_row) * ldb + (i % per_row) * kVec) = wb[it];
+      }
+      __syncthreads();
+    }
+    for (int i = tid; i < g * d; i += 256) {
+      const int j = i / d, dd = i - j * d;
+      const T* br = kStage ? s_stage + dd * ldb : bv + (int64_t)dd * rv;
+      const float* ac = s_merged + j * 128;
+      float o = 0.f;
+      for (int c = 0; c < rv; ++c) o = fmaf(load_f(br, c), ac[c], o);
+      po[((row0 + j) * a.n_parts + part) * d + dd] = o;
+    }
+  } else {
+    for (int i = tid; i < g * d; i += 256) {
+      const int j = i / d, dd = i - j * d;
+      po[((row0 + j) * a.n_parts + part) * d + dd] = s_merged[j * 128 + dd];
+    }
+  }
+  if (tid < g) {
+    a.part_ml[((row0 + tid) * a.n_parts + part) * 2 + 0] = s_mm[tid][0];
+    a.part_ml[((row0 + tid) * a.n_parts + part) * 2 + 1] = s_mm[tid][1];
+  }
+}
+
+// ----------------------------------------------------------------------------
+// bfloat16 attention kernel (matrix cores)
 // ----------------------------------------------------------------------------
 // KC: 32-wide k chunks covering r_K;  VB: 16-wide column blocks covering r_V.
 // FOLD false: keys are full-rank rows (hybrid side list), q' = q * scale.
+//
+// Each chunk is read through buffer resources based at the chunk and sized to
+// its valid tokens: rows past the context, and lanes pointed past the end on
+// purpose (columns beyond the rank), read as zero without a branch.  Chunks
+// are double-buffered in registers: the loads of chunk i+1 are in flight while
+// chunk i is scored and accumulated.
+template <int KC, int VB>
+struct Chunk {
+  u32x4 k[2][KC];
+  u32x4 v[VB];
+};
+
 template <int KC, int VB, bool FOLD>
-__global__ __launch_bounds__(256) void split_bf16_kernel(SplitArgs a) {
+__device__ __forceinline__ void split_bf16_body(const SplitArgs& a) {
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
   const int lane = tid & 63;
@@ -43,25 +171,99 @@ __global__ __launch_bounds__(256) void split_bf16_kernel(SplitArgs a) {
   const int rk = a.rk, rv = a.rv, d = a.d;
   const int64_t bh = (int64_t)b * a.hkv + h;
 
-  __shared__ float s_q[8 * 128];          // q rows of this kv head's query heads
-  __shared__ float s_qf[8 * 128];         // folded queries q' [g][rk]
-  __shared__ float s_acc[kWaves][16][VB * 16];
+  // the prologue's B_K, the waves' accumulator rows and the epilogue's B_V share LDS
+  constexpr int kStageBytes = 128 * (128 + 8) * 2;
+  constexpr int kAccBytes = kWaves * 16 * VB * 16 * 4;
+  __shared__ __attribute__((aligned(16))) unsigned char s_raw[kStageBytes > kAccBytes ? kStageBytes : kAccBytes];
+  __shared__ float s_q[8 * 128];
+  __shared__ float s_qf[8 * 128];
+  __shared__ float s_ml[kWaves][8][2];
+  uint16_t* s_bk = reinterpret_cast<uint16_t*>(s_raw);
+  float (*s_acc)[16][VB * 16] = reinterpret_cast<float (*)[16][VB * 16]>(s_raw);
 
-  const uint16_t* q = static_cast<const uint16_t*>(a.q) + ((int64_t)b * a.hq + (int64_t)h * g) * d;
-  for (int i = tid; i < g * d; i += 256) s_q[i] = bf16_to_f32(q[i]);
-  __syncthreads();
-  if (FOLD) {
-    const uint16_t* bk = static_cast<const uint16_t*>(a.basis_k) + (int64_t)h * d * rk;
-    for (int i = tid; i < g * rk; i += 256) {
-      const int j = i / rk, k = i - j * rk;
-      float acc = 0.f;
-      for (int e = 0; e < d; ++e) acc = fmaf(s_q[j * d + e], bf16_to_f32(bk[e * rk + k]), acc);
-      s_qf[i] = acc * a.qscale;
-    }
-  } else {
-    for (int i = tid; i < g * d; i += 256) s_qf[i] = s_q[i] * a.qscale;
+  int64_t n_end = a.n_static;
+  if (a.n_dev) {
+    n_end = a.n_dev[bh];
+    if (n_end > a.cap) n_end = a.cap;
+    if (n_end < 0) n_end = 0;
   }
-  __syncthreads();
+  const int64_t n_chunks = (n_end + kChunk - 1) / kChunk;
+  const int64_t c_begin = (int64_t)split * a.chunks_per_split;
+  int64_t c_end = c_begin + a.chunks_per_split;
+  if (c_end > n_chunks) c_end = n_chunks;
+
+  const uint16_t* ck = static_cast<const uint16_t*>(a.ck) + bh * a.cap * rk;
+  const uint16_t* cv = static_cast<const uint16_t*>(a.cv) + bh * a.cap * rv;
+  // per-lane byte offsets inside a chunk; lanes past the rank point out of range
+  uint32_t vo_k[2][KC], vo_v[VB];
+#pragma unroll
+  for (int T = 0; T < 2; ++T)
+#pragma unroll
+    for (int c = 0; c < KC; ++c) {
+      const int col = 32 * c + 8 * grp;
+      const int row = 8 * (n16 >> 2) + 4 * T + (n16 & 3);   // tile T, row n16
+      vo_k[T][c] = col < rk ? (uint32_t)((row * rk + col) * 2) : kOob;
+    }
+#pragma unroll
+  for (int vb = 0; vb < VB; ++vb) {
+    const int col = 16 * vb + n16;
+    vo_v[vb] = col < rv ? (uint32_t)((grp * rv + col) * 16) : kOob;
+  }
+  auto load = [&](Chunk<KC, VB>& c, int64_t chunk) {
+    const int64_t t0 = chunk * kChunk;
+    const int64_t left = n_end - t0;
+    const int nt = left < kChunk ? (int)left : kChunk;
+    const __amdgpu_buffer_rsrc_t rs_k = make_rsrc(ck + t0 * rk, (uint32_t)(nt * rk * 2));
+    const __amdgpu_buffer_rsrc_t rs_v = make_rsrc(cv + t0 * rv, (uint32_t)(((nt + 7) >> 3) * rv * 16));
+#pragma unroll
+    for (int T = 0; T < 2; ++T)
+#pragma unroll
+      for (int cc = 0; cc < KC; ++cc) c.k[T][cc] = buf_load16(rs_k, vo_k[T][cc]);
+#pragma unroll
+    for (int vb = 0; vb < VB; ++vb) c.v[vb] = buf_load16(rs_v, vo_v[vb]);
+  };
+
+  // --- fold q' = q B_K * scale * log2(e) for the g query heads of this kv head
+  {
+    // every load of the prologue is issued before the first wait
+    const uint16_t* q = static_cast<const uint16_t*>(a.q) + ((int64_t)b * a.hq + (int64_t)h * g) * d;
+    const int nq = g * d / 8;                       // <= 128 sixteen-byte pieces
+    const u32x4 wq = tid < nq ? *reinterpret_cast<const u32x4*>(q + 8 * tid) : u32x4{0u, 0u, 0u, 0u};
+    constexpr int kBkIter = 8;                      // d * rk / 8 <= 2048 = 8 * 256
+    u32x4 wb[kBkIter];
+    const uint16_t* bk = FOLD ? static_cast<const uint16_t*>(a.basis_k) + (int64_t)h * d * rk : nullptr;
+    const int nb = FOLD ? d * rk / 8 : 0;
+#pragma unroll
+    for (int it = 0; it < kBkIter; ++it) {
+      const int i = tid + 256 * it;
+      if (i < nb) wb[it] = *reinterpret_cast<const u32x4*>(bk + 8 * i);
+    }
+    if (tid < nq) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        s_q[8 * tid + 2 * e] = bf16_lo(wq[e]);
+        s_q[8 * tid + 2 * e + 1] = bf16_hi(wq[e]);
+      }
+    }
+#pragma unroll
+    for (int it = 0; it < kBkIter; ++it) {
+      const int i = tid + 256 * it;
+      if (i < nb) *reinterpret_cast<u32x4*>(s_bk + 8 * i) = wb[it];
+    }
+    __syncthreads();
+    if (FOLD) {
+      for (int i = tid; i < g * rk; i += 256) {
+        const int j = i / rk, k = i - j * rk;
+        float acc = 0.f;
+#pragma unroll 8
+        for (int e = 0; e < d; ++e) acc = fmaf(s_q[j * d + e], bf16_to_f32(s_bk[e * rk + k]), acc);
+        s_qf[i] = acc * a.qscale;
+      }
+    } else {
+      for (int i = tid; i < g * d; i += 256) s_qf[i] = s_q[i] * a.qscale;
+    }
+    __syncthreads();
+  }
 
   // Query operand of the score product: column n16 is head n16 (high part in
   // the first MFMA, low part in the second); columns g..2g-1 repeat the heads
@@ -86,20 +288,6 @@ __global__ __launch_bounds__(256) void split_bf16_kernel(SplitArgs a) {
     bq_lo[c] = u32x4{lo[0], lo[1], lo[2], lo[3]};
   }
 
-  int64_t n_end = a.n_static;
-  if (a.n_dev) {
-    n_end = a.n_dev[bh];
-    if (n_end > a.cap) n_end = a.cap;
-    if (n_end < 0) n_end = 0;
-  }
-  const int64_t n_chunks = (n_end + kChunk - 1) / kChunk;
-  const int64_t c_begin = (int64_t)split * a.chunks_per_split;
-  int64_t c_end = c_begin + a.chunks_per_split;
-  if (c_end > n_chunks) c_end = n_chunks;
-
-  const uint16_t* ck = static_cast<const uint16_t*>(a.ck) + bh * a.cap * rk;
-  const uint16_t* cv = static_cast<const uint16_t*>(a.cv) + bh * a.cap * rv;
-
   f32x4 acc[VB];
 #pragma unroll
   for (int i = 0; i < VB; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -108,73 +296,49 @@ __global__ __launch_bounds__(256) void split_bf16_kernel(SplitArgs a) {
   const bool take_hi = n16 < g;
   const bool p_row = n16 < 2 * g;
 
-  for (int64_t chunk = c_begin; chunk < c_end; ++chunk) {
+  auto process = [&](Chunk<KC, VB>& c, int64_t chunk) {
     const int64_t t0 = chunk * kChunk;
-    // --- key tiles: tile T, row m holds token t0 + 8*(m/4) + 4*T + m%4
-    u32x4 kt[2][KC];
-#pragma unroll
-    for (int T = 0; T < 2; ++T) {
-      const int64_t tok = t0 + 8 * (n16 >> 2) + 4 * T + (n16 & 3);
-#pragma unroll
-      for (int c = 0; c < KC; ++c) {
-        const int col = 32 * c + 8 * grp;
-        kt[T][c] = (tok < n_end && col < rk)
-                       ? *reinterpret_cast<const u32x4*>(ck + tok * rk + col)
-                       : u32x4{0u, 0u, 0u, 0u};
-      }
-    }
-    // --- value octets: column 16*vb + n16, tokens t0 + 8*grp .. +7
-    u32x4 vt[VB];
     const int64_t oct_tok = t0 + 8 * grp;
-#pragma unroll
-    for (int vb = 0; vb < VB; ++vb) {
-      const int col = 16 * vb + n16;
-      vt[vb] = (oct_tok < n_end && col < rv)
-                   ? *reinterpret_cast<const u32x4*>(cv + ((oct_tok >> 3) * rv + col) * 8)
-                   : u32x4{0u, 0u, 0u, 0u};
-    }
-    if (t0 + kChunk > n_end) {
-      // tail chunk: zero value elements past the end (they may hold anything)
+    const bool tail = t0 + kChunk > n_end;
+    if (tail) {
+      // value elements past the end may hold anything: zero them
       const int64_t nv = n_end - oct_tok;
-      if (nv < 8) {
 #pragma unroll
-        for (int vb = 0; vb < VB; ++vb) {
+      for (int vb = 0; vb < VB; ++vb)
 #pragma unroll
-          for (int w = 0; w < 4; ++w) {
-            uint32_t m = 0u;
-            if (2 * w < nv) m |= 0x0000FFFFu;
-            if (2 * w + 1 < nv) m |= 0xFFFF0000u;
-            vt[vb][w] &= m;
-          }
+        for (int w = 0; w < 4; ++w) {
+          uint32_t m = 0u;
+          if (2 * w < nv) m |= 0x0000FFFFu;
+          if (2 * w + 1 < nv) m |= 0xFFFF0000u;
+          c.v[vb][w] &= m;
         }
-      }
     }
-
-    // --- scores
+    // scores: tile T, row m is token t0 + 8*(m/4) + 4*T + m%4
     f32x4 st[2];
 #pragma unroll
     for (int T = 0; T < 2; ++T) {
       f32x4 s = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int c = 0; c < KC; ++c) {
-        s = mfma_16x16x32(kt[T][c], bq_hi[c], s);
-        s = mfma_16x16x32(kt[T][c], bq_lo[c], s);
+      for (int cc = 0; cc < KC; ++cc) {
+        s = mfma_16x16x32(c.k[T][cc], bq_hi[cc], s);
+        s = mfma_16x16x32(c.k[T][cc], bq_lo[cc], s);
       }
       st[T] = s;
     }
     // lane (n16, grp) now holds, for head(n16), tokens t0 + 8*grp + 4*T + i
     float sv[8];
-    float cmax = -INFINITY;
 #pragma unroll
-    for (int T = 0; T < 2; ++T) {
+    for (int T = 0; T < 2; ++T)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int64_t tok = oct_tok + 4 * T + i;
-        const float s = tok < n_end ? st[T][i] : -INFINITY;
-        sv[4 * T + i] = s;
-        cmax = fmaxf(cmax, s);
-      }
+      for (int i = 0; i < 4; ++i) sv[4 * T + i] = st[T][i];
+    if (tail) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        if (oct_tok + e >= n_end) sv[e] = -INFINITY;
     }
+    float cmax = sv[0];
+#pragma unroll
+    for (int e = 1; e < 8; ++e) cmax = fmaxf(cmax, sv[e]);
     cmax = fmaxf(cmax, __shfl_xor(cmax, 16));
     cmax = fmaxf(cmax, __shfl_xor(cmax, 32));
     const float m_new = fmaxf(m_run, cmax);
@@ -193,7 +357,6 @@ __global__ __launch_bounds__(256) void split_bf16_kernel(SplitArgs a) {
     }
     l_run = l_run * alpha + psum;
     const u32x4 pop = u32x4{pw[0], pw[1], pw[2], pw[3]};
-
     // rescale the accumulator rows 4*grp + i by the alpha of their head
     float ar[4];
 #pragma unroll
@@ -202,34 +365,57 @@ __global__ __launch_bounds__(256) void split_bf16_kernel(SplitArgs a) {
     for (int vb = 0; vb < VB; ++vb) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) acc[vb][i] *= ar[i];
-      acc[vb] = mfma_16x16x32(pop, vt[vb], acc[vb]);
+      acc[vb] = mfma_16x16x32(pop, c.v[vb], acc[vb]);
     }
+  };
+
+  Chunk<KC, VB> ca, cb;
+  if (c_begin < c_end) load(ca, c_begin);
+  for (int64_t chunk = c_begin; chunk < c_end; chunk += 2) {
+    if (chunk + 1 < c_end) load(cb, chunk + 1);
+    process(ca, chunk);
+    if (chunk + 1 >= c_end) break;
+    if (chunk + 2 < c_end) load(ca, chunk + 2);
+    process(cb, chunk + 1);
   }
 
   // --- epilogue: rows j (high part) + rows g + j (low part) are head j
+  __syncthreads();   // the prologue's LDS is reused below
 #pragma unroll
   for (int vb = 0; vb < VB; ++vb)
 #pragma unroll
     for (int i = 0; i < 4; ++i) s_acc[wave][4 * grp + i][16 * vb + n16] = acc[vb][i];
   float l_tot = l_run + __shfl_xor(l_run, 16);
   l_tot += __shfl_xor(l_tot, 32);
-  __syncthreads();
-  if (split < a.n_splits) {
-    const int64_t row0 = ((int64_t)b * a.hq + (int64_t)h * g) * a.n_splits + split;
-    for (int i = lane; i < g * rv; i += 64) {
-      const int j = i / rv, c = i - j * rv;
-      a.part_acc[(row0 + (int64_t)j * a.n_splits) * rv + c] = s_acc[wave][j][c] + s_acc[wave][g + j][c];
-    }
-    if (lane < g) {
-      a.part_ml[(row0 + (int64_t)lane * a.n_splits) * 2 + 0] = m_run;
-      a.part_ml[(row0 + (int64_t)lane * a.n_splits) * 2 + 1] = l_tot;
-    }
+  if (lane < g) {
+    s_ml[wave][lane][0] = m_run;     // -inf for a wave without tokens
+    s_ml[wave][lane][1] = l_tot;
   }
+  __syncthreads();
+  for (int i = tid; i < kWaves * g * rv; i += 256) {
+    const int w = i / (g * rv), r = i - w * g * rv, j = r / rv, c = r - j * rv;
+    s_acc[w][j][c] += s_acc[w][g + j][c];
+  }
+  __syncthreads();
+  workgroup_partial<uint16_t>(a, b, h, &s_acc[0][0][0], VB * 16, s_ml, reinterpret_cast<uint16_t*>(s_raw), s_qf);
+}
+
+// Low-rank keys: two waves per SIMD (one round of workgroups fills the chip).
+template <int KC, int VB>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void split_bf16_kernel(SplitArgs a) {
+  split_bf16_body<KC, VB, true>(a);
+}
+
+// Full-rank side-list keys (r = d): the wider operands need one wave per SIMD.
+template <int KC, int VB>
+__global__ __launch_bounds__(256) void split_bf16_side_kernel(SplitArgs a) {
+  split_bf16_body<KC, VB, false>(a);
 }
 
 // ----------------------------------------------------------------------------
-// float32 split kernel (vector ALU): 64-token tiles, one token per lane for the
-// scores, one value column per lane for the accumulation.
+// float32 attention kernel (vector ALU): 64-token tiles, one token per lane for
+// the scores, one value column per lane for the accumulation.
 // ----------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void split_f32_kernel(SplitArgs a) {
   const int tid = threadIdx.x;
@@ -247,6 +433,8 @@ __global__ __launch_bounds__(256) void split_f32_kernel(SplitArgs a) {
   __shared__ float s_q[8 * 128];
   __shared__ float s_qf[8 * 128];
   __shared__ float s_p[kWaves][8][64];
+  __shared__ float s_ml[kWaves][8][2];
+  __shared__ __attribute__((aligned(16))) float s_acc[kWaves][16][128];   // rows 0..g-1 used
 
   const float* q = static_cast<const float*>(a.q) + ((int64_t)b * a.hq + (int64_t)h * g) * d;
   for (int i = tid; i < g * d; i += 256) s_q[i] = q[i];
@@ -335,124 +523,95 @@ __global__ __launch_bounds__(256) void split_f32_kernel(SplitArgs a) {
     __builtin_amdgcn_wave_barrier();
   }
 
-  if (split < a.n_splits) {
-    const int64_t row0 = ((int64_t)b * a.hq + (int64_t)h * g) * a.n_splits + split;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      if (j < g) {
-        for (int ci = 0; ci < 2; ++ci) {
-          const int c = lane + 64 * ci;
-          if (c < rv) a.part_acc[(row0 + (int64_t)j * a.n_splits) * rv + c] = acc[j][ci];
-        }
-        if (lane == 0) {
-          a.part_ml[(row0 + (int64_t)j * a.n_splits) * 2 + 0] = m_run[j];
-          a.part_ml[(row0 + (int64_t)j * a.n_splits) * 2 + 1] = l_run[j];
-        }
+  for (int j = 0; j < 8; ++j) {
+    if (j < g) {
+      for (int ci = 0; ci < 2; ++ci) {
+        const int c = lane + 64 * ci;
+        if (c < rv) s_acc[wave][j][c] = acc[j][ci];
+      }
+      if (lane == 0) {
+        s_ml[wave][j][0] = m_run[j];
+        s_ml[wave][j][1] = l_run[j];
       }
     }
   }
+  __syncthreads();
+  workgroup_partial<float>(a, b, h, &s_acc[0][0][0], 128, s_ml, nullptr, s_qf);
 }
 
 // ----------------------------------------------------------------------------
-// merge + lift: one workgroup per (batch, query head)
+// merge: one wave per (batch, query head), four rows per workgroup
 // ----------------------------------------------------------------------------
+//   M = max_s m_s,  w_s = 2^(m_s - M),  L = sum_s w_s l_s,
+//   out = sum_s w_s o_s / L,  lse = (M + log2 L) ln 2
+// over the low-rank partials and, for a hybrid cache, the side-list partials.
 template <typename T>
-__device__ __forceinline__ float load_f(const T* p, int64_t i);
-template <>
-__device__ __forceinline__ float load_f<uint16_t>(const uint16_t* p, int64_t i) { return bf16_to_f32(p[i]); }
-template <>
-__device__ __forceinline__ float load_f<float>(const float* p, int64_t i) { return p[i]; }
-
-template <typename T>
-__device__ __forceinline__ void store_f(T* p, int64_t i, float v);
-template <>
-__device__ __forceinline__ void store_f<uint16_t>(uint16_t* p, int64_t i, float v) { p[i] = f32_to_bf16(v); }
-template <>
-__device__ __forceinline__ void store_f<float>(float* p, int64_t i, float v) { p[i] = v; }
-
-__device__ __forceinline__ float block_max_128(float v, float* red) {
-  v = wave_max(v);
-  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
-  __syncthreads();
-  v = fmaxf(red[0], red[1]);
-  __syncthreads();
-  return v;
-}
-
-__device__ __forceinline__ float block_sum_128(float v, float* red) {
-  v = wave_sum(v);
-  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
-  __syncthreads();
-  v = red[0] + red[1];
-  __syncthreads();
-  return v;
-}
-
-template <typename T>
-__global__ __launch_bounds__(128) void merge_kernel(MergeArgs a) {
-  const int hq = blockIdx.x;
-  const int b = blockIdx.y;
-  const int h = hq / a.g;
-  const int tid = threadIdx.x;
-  const int S = a.n_splits, SS = a.n_side_splits;
-  const int64_t row = (int64_t)b * a.hq + hq;
-
-  __shared__ float s_w[kMaxSplits];
-  __shared__ float s_acc[128];
-  __shared__ float s_red[2];
-
+__global__ __launch_bounds__(256) void merge_kernel(MergeArgs a) {
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int64_t row = (int64_t)blockIdx.x * 4 + wave;
+  if (row >= (int64_t)a.batch * a.hq) return;
+  const int S = a.n_parts, SS = a.n_side_parts, d = a.d;
   const float* ml = a.part_ml + row * S * 2;
-  const float* sml = a.side_ml ? a.side_ml + row * SS * 2 : nullptr;
+  const float* sml = SS ? a.side_ml + row * SS * 2 : nullptr;
+
   float m = -INFINITY;
-  for (int s = tid; s < S; s += 128) m = fmaxf(m, ml[2 * s]);
-  for (int s = tid; s < SS; s += 128) m = fmaxf(m, sml[2 * s]);
-  const float M = block_max_128(m, s_red);
+  for (int s = lane; s < S; s += 64) m = fmaxf(m, ml[2 * s]);
+  for (int s = lane; s < SS; s += 64) m = fmaxf(m, sml[2 * s]);
+  const float M = wave_max(m);
   float l = 0.f;
-  for (int s = tid; s < S + SS; s += 128) {
-    const float ms = s < S ? ml[2 * s] : sml[2 * (s - S)];
-    const float ls = s < S ? ml[2 * s + 1] : sml[2 * (s - S) + 1];
-    const float w = (ms == -INFINITY) ? 0.f : exp2_fast(ms - M);
-    s_w[s] = w;
-    l = fmaf(w, ls, l);
-  }
-  const float L = block_sum_128(l, s_red);   // also orders the s_w writes
+  for (int s = lane; s < S; s += 64) l += ml[2 * s] == -INFINITY ? 0.f : exp2_fast(ml[2 * s] - M) * ml[2 * s + 1];
+  for (int s = lane; s < SS; s += 64)
+    l += sml[2 * s] == -INFINITY ? 0.f : exp2_fast(sml[2 * s] - M) * sml[2 * s + 1];
+  const float L = wave_sum(l);
   const float inv = L > 0.f ? 1.f / L : 0.f;
 
-  if (tid < a.rv) {
-    const float* pa = a.part_acc + row * (int64_t)S * a.racc + tid;
-    float acc = 0.f;
-    for (int s = 0; s < S; ++s) acc = fmaf(s_w[s], pa[(int64_t)s * a.racc], acc);
-    s_acc[tid] = acc * inv;
-  }
-  __syncthreads();
-  if (tid < a.d) {
-    const T* bv = static_cast<const T*>(a.basis_v) + ((int64_t)h * a.d + tid) * a.rv;
-    float o = 0.f;
-    for (int c = 0; c < a.rv; ++c) o = fmaf(load_f(bv, c), s_acc[c], o);
-    if (SS > 0) {
-      const float* sa = a.side_acc + row * (int64_t)SS * a.d + tid;
-      float os = 0.f;
-      for (int s = 0; s < SS; ++s) os = fmaf(s_w[S + s], sa[(int64_t)s * a.d], os);
-      o = fmaf(os, inv, o);
+  // each lane owns head_dim elements lane and lane + 64; eight partials in flight
+  float o[2] = {0.f, 0.f};
+  for (int pass = 0; pass < 2; ++pass) {
+    const int n = pass ? SS : S;
+    const float* pm = pass ? sml : ml;
+    const float* po = pass ? a.side_o + row * (int64_t)SS * d : a.part_o + row * (int64_t)S * d;
+    for (int s0 = 0; s0 < n; s0 += 8) {
+      float v[8][2], wt[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const bool ok = s0 + u < n;
+        const float ms = ok ? pm[2 * (s0 + u)] : -INFINITY;
+        wt[u] = ms == -INFINITY ? 0.f : exp2_fast(ms - M);
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+          const int dd = lane + 64 * e;
+          v[u][e] = (ok && dd < d) ? po[(int64_t)(s0 + u) * d + dd] : 0.f;
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+#pragma unroll
+        for (int e = 0; e < 2; ++e) o[e] = fmaf(wt[u], v[u][e], o[e]);
     }
-    store_f(static_cast<T*>(a.out), row * a.d + tid, o);
   }
-  if (tid == 0 && a.lse) a.lse[row] = L > 0.f ? (M + __log2f(L)) * kLn2 : -INFINITY;
+#pragma unroll
+  for (int e = 0; e < 2; ++e) {
+    const int dd = lane + 64 * e;
+    if (dd < d) store_f(static_cast<T*>(a.out), row * d + dd, o[e] * inv);
+  }
+  if (lane == 0 && a.lse) a.lse[row] = L > 0.f ? (M + __log2f(L)) * kLn2 : -INFINITY;
 }
 
 }  // namespace
 
 #define LRKV_SPLIT_CASE(KC, VB)                                                          \
   case (KC * 16 + VB):                                                                   \
-    hipLaunchKernelGGL((split_bf16_kernel<KC, VB, true>), grid, dim3(256), 0, s, a);     \
+    hipLaunchKernelGGL((split_bf16_kernel<KC, VB>), grid, dim3(256), 0, s, a);           \
     break;
 
 hipError_t launch_split_bf16(const SplitArgs& a, hipStream_t s) {
   const dim3 grid((a.n_splits + kWaves - 1) / kWaves, a.hkv, a.batch);
   const int kc = (a.rk + 31) / 32, vb = (a.rv + 15) / 16;
   if (a.basis_k == nullptr) {
-    if (a.d == 128) hipLaunchKernelGGL((split_bf16_kernel<4, 8, false>), grid, dim3(256), 0, s, a);
-    else hipLaunchKernelGGL((split_bf16_kernel<2, 4, false>), grid, dim3(256), 0, s, a);
+    if (a.d == 128) hipLaunchKernelGGL((split_bf16_side_kernel<4, 8>), grid, dim3(256), 0, s, a);
+    else hipLaunchKernelGGL((split_bf16_side_kernel<2, 4>), grid, dim3(256), 0, s, a);
     return hipGetLastError();
   }
   switch (kc * 16 + vb) {
@@ -477,9 +636,9 @@ hipError_t launch_split_f32(const SplitArgs& a, hipStream_t s) {
 }
 
 hipError_t launch_merge(const MergeArgs& a, bool bf16, hipStream_t s) {
-  const dim3 grid(a.hq, a.batch);
-  if (bf16) hipLaunchKernelGGL(merge_kernel<uint16_t>, grid, dim3(128), 0, s, a);
-  else hipLaunchKernelGGL(merge_kernel<float>, grid, dim3(128), 0, s, a);
+  const dim3 grid((unsigned)(((int64_t)a.batch * a.hq + 3) / 4));
+  if (bf16) hipLaunchKernelGGL(merge_kernel<uint16_t>, grid, dim3(256), 0, s, a);
+  else hipLaunchKernelGGL(merge_kernel<float>, grid, dim3(256), 0, s, a);
   return hipGetLastError();
 }
 

@@ -1,5 +1,6 @@
 // C-ABI layer of liblrkv: argument validation, split planning, workspace
 // layout and kernel launches.  No device memory is allocated here.
+#include <algorithm>
 #include <atomic>
 #include <cmath>
 #include <cstdarg>
@@ -58,12 +59,13 @@ struct Plan {
 };
 
 // Split a context of n_tokens over (units) independent (batch, kv head) rows so
-// that the whole chip gets about 16 waves per compute unit, with at least 4
-// chunks (128 tokens) per split.  LRKV_SPLITS forces the split count.
+// that one round of workgroups fills the chip (8 resident waves per compute
+// unit at the split kernel's register use), with at least 4 chunks (128
+// tokens) per split.  LRKV_SPLITS forces the split count.
 Plan plan_splits(int64_t units, int64_t n_tokens, int cus, int max_splits) {
   Plan p;
   const int64_t n_chunks = n_tokens > 0 ? cdiv(n_tokens, kChunk) : 1;
-  int64_t s = cdiv((int64_t)cus * 16, units > 0 ? units : 1);
+  int64_t s = cdiv((int64_t)cus * 8, units > 0 ? units : 1);
   s = std::min<int64_t>(s, cdiv(n_chunks, 4));
   if (const char* env = std::getenv("LRKV_SPLITS")) {
     const long v = std::strtol(env, nullptr, 10);
@@ -79,7 +81,8 @@ Plan plan_splits(int64_t units, int64_t n_tokens, int cus, int max_splits) {
 
 struct DecodeLayout {
   Plan lr, side;
-  size_t acc_lr = 0, ml_lr = 0, acc_side = 0, ml_side = 0, total = 0;
+  int parts_lr = 0, parts_side = 0;   // partials per (b, h): one per attention workgroup
+  size_t o_lr = 0, ml_lr = 0, o_side = 0, ml_side = 0, total = 0;
 };
 
 DecodeLayout decode_layout(const lrkv_dims& d, int64_t n_lr_tokens, int64_t side_cap) {
@@ -87,18 +90,18 @@ DecodeLayout decode_layout(const lrkv_dims& d, int64_t n_lr_tokens, int64_t side
   const int cus = device_cu_count();
   const int64_t units = (int64_t)d.batch * d.n_kv_heads;
   const int64_t rows = (int64_t)d.batch * d.n_q_heads;
-  int max_lr = kMaxSplits;
+  L.lr = plan_splits(units, n_lr_tokens, cus, kMaxSplits);
+  L.parts_lr = (int)cdiv(L.lr.n_splits, kSplitsPerPart);
   if (side_cap > 0) {
-    L.side = plan_splits(units, side_cap, cus, kMaxSplits / 2);
-    max_lr = kMaxSplits - L.side.n_splits;
+    L.side = plan_splits(units, side_cap, cus, kMaxSplits);
+    L.parts_side = (int)cdiv(L.side.n_splits, kSplitsPerPart);
   }
-  L.lr = plan_splits(units, n_lr_tokens, cus, max_lr);
   size_t off = 0;
-  L.acc_lr = off; off = align256(off + sizeof(float) * rows * L.lr.n_splits * d.rank_v);
-  L.ml_lr = off;  off = align256(off + sizeof(float) * rows * L.lr.n_splits * 2);
+  L.o_lr = off;  off = align256(off + sizeof(float) * rows * L.parts_lr * d.head_dim);
+  L.ml_lr = off; off = align256(off + sizeof(float) * rows * L.parts_lr * 2);
   if (side_cap > 0) {
-    L.acc_side = off; off = align256(off + sizeof(float) * rows * L.side.n_splits * d.head_dim);
-    L.ml_side = off;  off = align256(off + sizeof(float) * rows * L.side.n_splits * 2);
+    L.o_side = off;  off = align256(off + sizeof(float) * rows * L.parts_side * d.head_dim);
+    L.ml_side = off; off = align256(off + sizeof(float) * rows * L.parts_side * 2);
   }
   L.total = off;
   return L;
@@ -134,8 +137,12 @@ lrkv_status check_dims(const lrkv_dims* d, lrkv_dtype dt, const char* fn) {
   if (d->capacity < 8 || d->capacity % 8)
     return fail(LRKV_ERR_INVALID_ARGUMENT, "%s: capacity = %lld must be a positive multiple of 8", fn,
                 (long long)d->capacity);
-  if (d->capacity > (int64_t)1 << 31)
-    return fail(LRKV_ERR_UNSUPPORTED, "%s: capacity above 2^31 tokens", fn);
+  // the kernels address one (batch, kv head) of a cache with 31-bit byte offsets
+  const int64_t elem = dt == LRKV_BF16 ? 2 : 4;
+  const int64_t widest = std::max<int64_t>(d->rank_k, d->rank_v);
+  if (d->capacity * widest * elem >= ((int64_t)1 << 31))
+    return fail(LRKV_ERR_UNSUPPORTED, "%s: capacity %lld too large (capacity x rank x element size must be < 2^31)",
+                fn, (long long)d->capacity);
   return LRKV_OK;
 }
 
@@ -194,6 +201,38 @@ lrkv_status lrkv_compress(const void* x, const void* basis, void* coeff, lrkv_ca
   return e == hipSuccess ? LRKV_OK : device_fail(fn, e);
 }
 
+lrkv_status lrkv_compress_kv(const void* xk, const void* xv, const void* basis_k, const void* basis_v,
+                             void* coeff_k, void* coeff_v, const lrkv_dims* dims, int64_t n_tokens,
+                             int64_t pos, lrkv_dtype dtype, hipStream_t stream) {
+  const char* fn = "lrkv_compress_kv";
+  lrkv_status st = check_dims(dims, dtype, fn);
+  if (st != LRKV_OK) return st;
+  if (n_tokens < 0 || pos < 0 || pos + n_tokens > dims->capacity)
+    return fail(LRKV_ERR_INVALID_ARGUMENT, "%s: rows [%lld, %lld) do not fit capacity %lld", fn, (long long)pos,
+                (long long)(pos + n_tokens), (long long)dims->capacity);
+  LRKV_CHECK_PTR(xk, fn);
+  LRKV_CHECK_PTR(xv, fn);
+  LRKV_CHECK_PTR(basis_k, fn);
+  LRKV_CHECK_PTR(basis_v, fn);
+  LRKV_CHECK_PTR(coeff_k, fn);
+  LRKV_CHECK_PTR(coeff_v, fn);
+  if (n_tokens == 0) return LRKV_OK;
+  if (dtype == LRKV_BF16 && n_tokens <= kSmallT) {
+    CompressKvArgs a{xk, xv, basis_k, basis_v, coeff_k, coeff_v, dims->batch, dims->n_kv_heads, dims->head_dim,
+                     dims->rank_k, dims->rank_v, n_tokens, pos, dims->capacity};
+    const hipError_t e = launch_compress_kv_small_bf16(a, stream);
+    return e == hipSuccess ? LRKV_OK : device_fail(fn, e);
+  }
+  CompressArgs ak{xk, basis_k, coeff_k, 0, dims->batch, dims->n_kv_heads, dims->head_dim, dims->rank_k,
+                  n_tokens, pos, dims->capacity};
+  CompressArgs av{xv, basis_v, coeff_v, 1, dims->batch, dims->n_kv_heads, dims->head_dim, dims->rank_v,
+                  n_tokens, pos, dims->capacity};
+  hipError_t e = dtype == LRKV_BF16 ? launch_compress_bf16(ak, stream) : launch_compress_f32(ak, stream);
+  if (e != hipSuccess) return device_fail(fn, e);
+  e = dtype == LRKV_BF16 ? launch_compress_bf16(av, stream) : launch_compress_f32(av, stream);
+  return e == hipSuccess ? LRKV_OK : device_fail(fn, e);
+}
+
 size_t lrkv_decode_workspace_bytes(const lrkv_dims* dims, int64_t n_ctx, int64_t side_cap) {
   if (check_dims(dims, LRKV_F32, "lrkv_decode_workspace_bytes") != LRKV_OK &&
       check_dims(dims, LRKV_BF16, "lrkv_decode_workspace_bytes") != LRKV_OK)
@@ -204,16 +243,69 @@ size_t lrkv_decode_workspace_bytes(const lrkv_dims* dims, int64_t n_ctx, int64_t
   return decode_layout(*dims, n, side_cap).total;
 }
 
-lrkv_status lrkv_decode_attn(const void* q, const void* basis_k, const void* coeff_k,
-                             const void* basis_v, const void* coeff_v, void* out, float* lse,
-                             const lrkv_dims* dims, int64_t n_ctx, float scale, lrkv_dtype dtype,
-                             void* workspace, size_t workspace_bytes, hipStream_t stream) {
-  const char* fn = "lrkv_decode_attn";
+}  // extern "C"
+
+namespace {
+
+lrkv_status check_decode_common(const lrkv_dims* dims, int64_t n_ctx, lrkv_dtype dtype, void* workspace,
+                                size_t workspace_bytes, const char* fn, DecodeLayout* L) {
   lrkv_status st = check_dims(dims, dtype, fn);
   if (st != LRKV_OK) return st;
   if (n_ctx < 1 || n_ctx > dims->capacity)
     return fail(LRKV_ERR_INVALID_ARGUMENT, "%s: n_ctx = %lld outside [1, capacity = %lld]", fn, (long long)n_ctx,
                 (long long)dims->capacity);
+  LRKV_CHECK_PTR(workspace, fn);
+  *L = decode_layout(*dims, n_ctx, 0);
+  if (workspace_bytes < L->total)
+    return fail(LRKV_ERR_WORKSPACE_TOO_SMALL, "%s: workspace of %zu bytes, %zu needed", fn, workspace_bytes, L->total);
+  return LRKV_OK;
+}
+
+lrkv_status decode_partial(const void* q, const void* basis_k, const void* coeff_k, const void* basis_v,
+                           const void* coeff_v, const lrkv_dims* dims, int64_t n_ctx, float scale,
+                           lrkv_dtype dtype, void* workspace, const DecodeLayout& L, hipStream_t stream,
+                           const char* fn) {
+  char* ws = static_cast<char*>(workspace);
+  SplitArgs sa{};
+  sa.q = q; sa.basis_k = basis_k; sa.ck = coeff_k; sa.cv = coeff_v; sa.basis_v = basis_v;
+  sa.cap = dims->capacity; sa.rk = dims->rank_k; sa.rv = dims->rank_v; sa.d = dims->head_dim;
+  sa.g = dims->n_q_heads / dims->n_kv_heads; sa.hq = dims->n_q_heads; sa.hkv = dims->n_kv_heads;
+  sa.batch = dims->batch;
+  sa.n_static = n_ctx; sa.n_dev = nullptr;
+  sa.chunks_per_split = L.lr.chunks_per_split; sa.n_splits = L.lr.n_splits; sa.n_parts = L.parts_lr;
+  sa.qscale = resolve_scale(scale, dims->head_dim) * kLog2eHost;
+  sa.part_o = reinterpret_cast<float*>(ws + L.o_lr);
+  sa.part_ml = reinterpret_cast<float*>(ws + L.ml_lr);
+  const hipError_t e = dtype == LRKV_BF16 ? launch_split_bf16(sa, stream) : launch_split_f32(sa, stream);
+  return e == hipSuccess ? LRKV_OK : device_fail(fn, e);
+}
+
+lrkv_status decode_merge(void* out, float* lse, const lrkv_dims* dims, lrkv_dtype dtype, void* workspace,
+                         const DecodeLayout& L, hipStream_t stream, const char* fn) {
+  char* ws = static_cast<char*>(workspace);
+  MergeArgs ma{};
+  ma.part_o = reinterpret_cast<const float*>(ws + L.o_lr);
+  ma.part_ml = reinterpret_cast<const float*>(ws + L.ml_lr);
+  ma.n_parts = L.parts_lr;
+  ma.side_o = nullptr; ma.side_ml = nullptr; ma.n_side_parts = 0;
+  ma.d = dims->head_dim; ma.hq = dims->n_q_heads; ma.batch = dims->batch;
+  ma.out = out; ma.lse = lse;
+  const hipError_t e = launch_merge(ma, dtype == LRKV_BF16, stream);
+  return e == hipSuccess ? LRKV_OK : device_fail(fn, e);
+}
+
+}  // namespace
+
+extern "C" {
+
+lrkv_status lrkv_decode_attn(const void* q, const void* basis_k, const void* coeff_k,
+                             const void* basis_v, const void* coeff_v, void* out, float* lse,
+                             const lrkv_dims* dims, int64_t n_ctx, float scale, lrkv_dtype dtype,
+                             void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  const char* fn = "lrkv_decode_attn";
+  DecodeLayout L;
+  lrkv_status st = check_decode_common(dims, n_ctx, dtype, workspace, workspace_bytes, fn, &L);
+  if (st != LRKV_OK) return st;
   if (!std::isfinite(scale)) return fail(LRKV_ERR_INVALID_ARGUMENT, "%s: scale is not finite", fn);
   LRKV_CHECK_PTR(q, fn);
   LRKV_CHECK_PTR(basis_k, fn);
@@ -221,32 +313,39 @@ lrkv_status lrkv_decode_attn(const void* q, const void* basis_k, const void* coe
   LRKV_CHECK_PTR(basis_v, fn);
   LRKV_CHECK_PTR(coeff_v, fn);
   LRKV_CHECK_PTR(out, fn);
-  LRKV_CHECK_PTR(workspace, fn);
   if (lse && !aligned16(lse)) return fail(LRKV_ERR_INVALID_ARGUMENT, "%s: lse is not 16-byte aligned", fn);
-  const DecodeLayout L = decode_layout(*dims, n_ctx, 0);
-  if (workspace_bytes < L.total)
-    return fail(LRKV_ERR_WORKSPACE_TOO_SMALL, "%s: workspace of %zu bytes, %zu needed", fn, workspace_bytes, L.total);
-  char* ws = static_cast<char*>(workspace);
-  const int g = dims->n_q_heads / dims->n_kv_heads;
-  SplitArgs sa{};
-  sa.q = q; sa.basis_k = basis_k; sa.ck = coeff_k; sa.cv = coeff_v;
-  sa.cap = dims->capacity; sa.rk = dims->rank_k; sa.rv = dims->rank_v; sa.d = dims->head_dim;
-  sa.g = g; sa.hq = dims->n_q_heads; sa.hkv = dims->n_kv_heads; sa.batch = dims->batch;
-  sa.n_static = n_ctx; sa.n_dev = nullptr;
-  sa.chunks_per_split = L.lr.chunks_per_split; sa.n_splits = L.lr.n_splits;
-  sa.qscale = resolve_scale(scale, dims->head_dim) * kLog2eHost;
-  sa.part_acc = reinterpret_cast<float*>(ws + L.acc_lr);
-  sa.part_ml = reinterpret_cast<float*>(ws + L.ml_lr);
-  hipError_t e = dtype == LRKV_BF16 ? launch_split_bf16(sa, stream) : launch_split_f32(sa, stream);
-  if (e != hipSuccess) return device_fail(fn, e);
-  MergeArgs ma{};
-  ma.part_acc = sa.part_acc; ma.part_ml = sa.part_ml; ma.n_splits = L.lr.n_splits; ma.racc = dims->rank_v;
-  ma.side_acc = nullptr; ma.side_ml = nullptr; ma.n_side_splits = 0;
-  ma.basis_v = basis_v; ma.rv = dims->rank_v; ma.d = dims->head_dim; ma.g = g;
-  ma.hq = dims->n_q_heads; ma.hkv = dims->n_kv_heads; ma.batch = dims->batch;
-  ma.out = out; ma.lse = lse;
-  e = launch_merge(ma, dtype == LRKV_BF16, stream);
-  return e == hipSuccess ? LRKV_OK : device_fail(fn, e);
+  st = decode_partial(q, basis_k, coeff_k, basis_v, coeff_v, dims, n_ctx, scale, dtype, workspace, L, stream, fn);
+  if (st != LRKV_OK) return st;
+  return decode_merge(out, lse, dims, dtype, workspace, L, stream, fn);
+}
+
+lrkv_status lrkv_decode_attn_partial(const void* q, const void* basis_k, const void* coeff_k,
+                                     const void* basis_v, const void* coeff_v, const lrkv_dims* dims,
+                                     int64_t n_ctx, float scale, lrkv_dtype dtype, void* workspace,
+                                     size_t workspace_bytes, hipStream_t stream) {
+  const char* fn = "lrkv_decode_attn_partial";
+  DecodeLayout L;
+  lrkv_status st = check_decode_common(dims, n_ctx, dtype, workspace, workspace_bytes, fn, &L);
+  if (st != LRKV_OK) return st;
+  if (!std::isfinite(scale)) return fail(LRKV_ERR_INVALID_ARGUMENT, "%s: scale is not finite", fn);
+  LRKV_CHECK_PTR(q, fn);
+  LRKV_CHECK_PTR(basis_k, fn);
+  LRKV_CHECK_PTR(coeff_k, fn);
+  LRKV_CHECK_PTR(basis_v, fn);
+  LRKV_CHECK_PTR(coeff_v, fn);
+  return decode_partial(q, basis_k, coeff_k, basis_v, coeff_v, dims, n_ctx, scale, dtype, workspace, L, stream, fn);
+}
+
+lrkv_status lrkv_decode_attn_merge(void* out, float* lse, const lrkv_dims* dims, int64_t n_ctx,
+                                   lrkv_dtype dtype, void* workspace, size_t workspace_bytes,
+                                   hipStream_t stream) {
+  const char* fn = "lrkv_decode_attn_merge";
+  DecodeLayout L;
+  lrkv_status st = check_decode_common(dims, n_ctx, dtype, workspace, workspace_bytes, fn, &L);
+  if (st != LRKV_OK) return st;
+  LRKV_CHECK_PTR(out, fn);
+  if (lse && !aligned16(lse)) return fail(LRKV_ERR_INVALID_ARGUMENT, "%s: lse is not 16-byte aligned", fn);
+  return decode_merge(out, lse, dims, dtype, workspace, L, stream, fn);
 }
 
 size_t lrkv_compress_hybrid_workspace_bytes(const lrkv_dims* dims, int64_t n_tokens) {
@@ -273,9 +372,9 @@ lrkv_status lrkv_compress_hybrid(const void* k, const void* v, const void* basis
   if (std::isnan(tau) || tau < 0.f) return fail(LRKV_ERR_INVALID_ARGUMENT, "%s: tau must be >= 0", fn);
   if (n_tokens < 0 || pos < 0 || pos + n_tokens > ((int64_t)1 << 31))
     return fail(LRKV_ERR_INVALID_ARGUMENT, "%s: bad n_tokens / pos", fn);
-  if (side_cap < 8 || side_cap % 8 || side_cap > ((int64_t)1 << 31))
-    return fail(LRKV_ERR_INVALID_ARGUMENT, "%s: side_cap = %lld must be a positive multiple of 8", fn,
-                (long long)side_cap);
+  if (side_cap < 8 || side_cap % 8 || side_cap * dims->head_dim * 4 >= ((int64_t)1 << 31))
+    return fail(LRKV_ERR_INVALID_ARGUMENT, "%s: side_cap = %lld must be a positive multiple of 8 below 2^31 bytes",
+                fn, (long long)side_cap);
   LRKV_CHECK_PTR(k, fn);
   LRKV_CHECK_PTR(v, fn);
   LRKV_CHECK_PTR(basis_k, fn);
@@ -323,9 +422,9 @@ lrkv_status lrkv_decode_attn_hybrid(const void* q, const void* basis_k, const vo
   const char* fn = "lrkv_decode_attn_hybrid";
   lrkv_status st = check_dims(dims, dtype, fn);
   if (st != LRKV_OK) return st;
-  if (side_cap < 8 || side_cap % 8 || side_cap > ((int64_t)1 << 31))
-    return fail(LRKV_ERR_INVALID_ARGUMENT, "%s: side_cap = %lld must be a positive multiple of 8", fn,
-                (long long)side_cap);
+  if (side_cap < 8 || side_cap % 8 || side_cap * dims->head_dim * 4 >= ((int64_t)1 << 31))
+    return fail(LRKV_ERR_INVALID_ARGUMENT, "%s: side_cap = %lld must be a positive multiple of 8 below 2^31 bytes",
+                fn, (long long)side_cap);
   if (!std::isfinite(scale)) return fail(LRKV_ERR_INVALID_ARGUMENT, "%s: scale is not finite", fn);
   LRKV_CHECK_PTR(q, fn);
   LRKV_CHECK_PTR(basis_k, fn);
@@ -347,31 +446,30 @@ lrkv_status lrkv_decode_attn_hybrid(const void* q, const void* basis_k, const vo
   const float qscale = resolve_scale(scale, dims->head_dim) * kLog2eHost;
 
   SplitArgs sa{};
-  sa.q = q; sa.basis_k = basis_k; sa.ck = coeff_k; sa.cv = coeff_v;
+  sa.q = q; sa.basis_k = basis_k; sa.ck = coeff_k; sa.cv = coeff_v; sa.basis_v = basis_v;
   sa.cap = dims->capacity; sa.rk = dims->rank_k; sa.rv = dims->rank_v; sa.d = dims->head_dim;
   sa.g = g; sa.hq = dims->n_q_heads; sa.hkv = dims->n_kv_heads; sa.batch = dims->batch;
   sa.n_static = 0; sa.n_dev = n_lr;
-  sa.chunks_per_split = L.lr.chunks_per_split; sa.n_splits = L.lr.n_splits;
+  sa.chunks_per_split = L.lr.chunks_per_split; sa.n_splits = L.lr.n_splits; sa.n_parts = L.parts_lr;
   sa.qscale = qscale;
-  sa.part_acc = reinterpret_cast<float*>(ws + L.acc_lr);
+  sa.part_o = reinterpret_cast<float*>(ws + L.o_lr);
   sa.part_ml = reinterpret_cast<float*>(ws + L.ml_lr);
   hipError_t e = bf16 ? launch_split_bf16(sa, stream) : launch_split_f32(sa, stream);
   if (e != hipSuccess) return device_fail(fn, e);
 
-  SplitArgs ss = sa;   // side list: full-rank rows, no fold
-  ss.basis_k = nullptr; ss.ck = k_side; ss.cv = v_side; ss.cap = side_cap;
+  SplitArgs ss = sa;   // side list: full-rank rows, no fold and no lift
+  ss.basis_k = nullptr; ss.basis_v = nullptr; ss.ck = k_side; ss.cv = v_side; ss.cap = side_cap;
   ss.rk = dims->head_dim; ss.rv = dims->head_dim; ss.n_dev = n_side;
-  ss.chunks_per_split = L.side.chunks_per_split; ss.n_splits = L.side.n_splits;
-  ss.part_acc = reinterpret_cast<float*>(ws + L.acc_side);
+  ss.chunks_per_split = L.side.chunks_per_split; ss.n_splits = L.side.n_splits; ss.n_parts = L.parts_side;
+  ss.part_o = reinterpret_cast<float*>(ws + L.o_side);
   ss.part_ml = reinterpret_cast<float*>(ws + L.ml_side);
   e = bf16 ? launch_split_bf16(ss, stream) : launch_split_f32(ss, stream);
   if (e != hipSuccess) return device_fail(fn, e);
 
   MergeArgs ma{};
-  ma.part_acc = sa.part_acc; ma.part_ml = sa.part_ml; ma.n_splits = L.lr.n_splits; ma.racc = dims->rank_v;
-  ma.side_acc = ss.part_acc; ma.side_ml = ss.part_ml; ma.n_side_splits = L.side.n_splits;
-  ma.basis_v = basis_v; ma.rv = dims->rank_v; ma.d = dims->head_dim; ma.g = g;
-  ma.hq = dims->n_q_heads; ma.hkv = dims->n_kv_heads; ma.batch = dims->batch;
+  ma.part_o = sa.part_o; ma.part_ml = sa.part_ml; ma.n_parts = L.parts_lr;
+  ma.side_o = ss.part_o; ma.side_ml = ss.part_ml; ma.n_side_parts = L.parts_side;
+  ma.d = dims->head_dim; ma.hq = dims->n_q_heads; ma.batch = dims->batch;
   ma.out = out; ma.lse = lse;
   e = launch_merge(ma, bf16, stream);
   return e == hipSuccess ? LRKV_OK : device_fail(fn, e);

@@ -10,30 +10,33 @@ constexpr float kLog2eHost = 1.4426950408889634f;
 
 // Tokens per decode chunk: two 16-token matrix-core tiles.
 constexpr int kChunk = 32;
-// Largest number of splits one merge can combine (latent + side), bounded by its LDS.
-constexpr int kMaxSplits = 4096;
+// Waves (splits) per attention workgroup; a workgroup leaves one partial.
+constexpr int kSplitsPerPart = 4;
+// Upper bound on splits per (batch, kv head) the planner uses.
+constexpr int kMaxSplits = 1 << 16;
 
 struct SplitArgs {
   const void* q;         // [B, Hq, d]
   const void* basis_k;   // [Hkv, d, rk] (nullptr: keys are full rank, no fold)
   const void* ck;        // key rows [B, Hkv, cap, rk]
   const void* cv;        // value octets [B, Hkv, cap/8, rv, 8]
+  const void* basis_v;   // [Hkv, d, rv] (nullptr: values are full rank, no lift)
   int64_t cap;
   int rk, rv, d, g, hq, hkv, batch;
   int64_t n_static;      // context length when n_dev is null
   const int32_t* n_dev;  // per-(b, h) token counts on the device, or null
   int chunks_per_split;
   int n_splits;
+  int n_parts;           // workgroups per (b, h) = ceil(n_splits / kSplitsPerPart)
   float qscale;          // softmax scale * log2(e)
-  float* part_acc;       // [B, Hq, n_splits, rv]
-  float* part_ml;        // [B, Hq, n_splits, 2]  (running max in log2 units, sum)
+  float* part_o;         // [B, Hq, n_parts, d]  unnormalised outputs
+  float* part_ml;        // [B, Hq, n_parts, 2]  running max (log2 units), softmax sum
 };
 
 struct MergeArgs {
-  const float* part_acc; const float* part_ml; int n_splits; int racc;
-  const float* side_acc; const float* side_ml; int n_side_splits;  // hybrid only
-  const void* basis_v;   // [Hkv, d, rv]
-  int rv, d, g, hq, hkv, batch;
+  const float* part_o; const float* part_ml; int n_parts;
+  const float* side_o; const float* side_ml; int n_side_parts;   // hybrid only
+  int d, hq, batch;
   void* out;             // [B, Hq, d]
   float* lse;            // [B, Hq] or null
 };
@@ -45,7 +48,16 @@ struct CompressArgs {
   int64_t n_tokens, pos, cap;
 };
 
+// Both caches of a few new tokens in one launch.
+constexpr int kSmallT = 4;
+struct CompressKvArgs {
+  const void* xk; const void* xv; const void* bk; const void* bv; void* ck; void* cv;
+  int batch, hkv, d, rk, rv;
+  int64_t n_tokens, pos, cap;
+};
+
 hipError_t launch_split_bf16(const SplitArgs& a, hipStream_t s);
+hipError_t launch_compress_kv_small_bf16(const CompressKvArgs& a, hipStream_t s);
 hipError_t launch_split_f32(const SplitArgs& a, hipStream_t s);
 hipError_t launch_merge(const MergeArgs& a, bool bf16, hipStream_t s);
 hipError_t launch_compress_bf16(const CompressArgs& a, hipStream_t s);

@@ -100,6 +100,18 @@ lrkv_status lrkv_compress(const void* x, const void* basis, void* coeff, lrkv_ca
                           hipStream_t stream);
 
 /*
+ * Both caches of a layer in one call: lrkv_compress of the keys (row layout,
+ * rank_k) and of the values (octet layout, rank_v), with the shapes of dims
+ * (n_q_heads is not used).  Up to 4 tokens (an appended decode token) are
+ * compressed in a single launch that reads the bases straight from memory;
+ * longer chunks use the matrix-core path of lrkv_compress for each cache.
+ *   xk, xv  [B, n_tokens, Hkv, d]
+ */
+lrkv_status lrkv_compress_kv(const void* xk, const void* xv, const void* basis_k, const void* basis_v,
+                             void* coeff_k, void* coeff_v, const lrkv_dims* dims, int64_t n_tokens,
+                             int64_t pos, lrkv_dtype dtype, hipStream_t stream);
+
+/*
  * Bytes of float32 workspace lrkv_decode_attn (side_cap = 0) or
  * lrkv_decode_attn_hybrid (side_cap > 0) needs for these dims.  n_ctx is the
  * context length of a plain decode; the hybrid decode plans for
@@ -123,13 +135,35 @@ size_t lrkv_decode_workspace_bytes(const lrkv_dims* dims, int64_t n_ctx, int64_t
  *   basis_v  [Hkv, d, r_V];   coeff_v  value octet layout [B, Hkv, capacity/8, r_V, 8]
  *   out      [B, Hq, d] (storage dtype);  lse [B, Hq] float32 natural log, or NULL
  *   scale    softmax scale; 0 selects 1/sqrt(head_dim)
- *   workspace at least lrkv_decode_workspace_bytes(dims, n_ctx, 0) bytes
+ *   workspace at least lrkv_decode_workspace_bytes(dims, n_ctx, 0) bytes (scratch;
+ *            calls that share a workspace must not overlap in time)
  * Requires 1 <= n_ctx <= capacity.
  */
 lrkv_status lrkv_decode_attn(const void* q, const void* basis_k, const void* coeff_k,
                              const void* basis_v, const void* coeff_v, void* out, float* lse,
                              const lrkv_dims* dims, int64_t n_ctx, float scale, lrkv_dtype dtype,
                              void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * The two phases of lrkv_decode_attn, callable separately (same arguments,
+ * same workspace, same result when called back to back on one stream):
+ *   _partial  attends the context in splits; each workgroup of splits merges
+ *             its splits and lifts the result through B_V^T, leaving per
+ *             (b, q head, workgroup) a running max, a softmax sum and an
+ *             unnormalised head_dim-wide output in the workspace;
+ *   _merge    combines those by log-sum-exp into out and lse.
+ * The split plan is a function of dims, n_ctx and the device, so both phases
+ * must see the same values.  Splitting the call lets a caller time the phases
+ * or combine partial results computed elsewhere (for example on other GPUs,
+ * each holding a range of the context) before the merge.
+ */
+lrkv_status lrkv_decode_attn_partial(const void* q, const void* basis_k, const void* coeff_k,
+                                     const void* basis_v, const void* coeff_v, const lrkv_dims* dims,
+                                     int64_t n_ctx, float scale, lrkv_dtype dtype, void* workspace,
+                                     size_t workspace_bytes, hipStream_t stream);
+lrkv_status lrkv_decode_attn_merge(void* out, float* lse, const lrkv_dims* dims, int64_t n_ctx,
+                                   lrkv_dtype dtype, void* workspace, size_t workspace_bytes,
+                                   hipStream_t stream);
 
 /* Bytes of workspace lrkv_compress_hybrid needs for n_tokens new tokens. */
 size_t lrkv_compress_hybrid_workspace_bytes(const lrkv_dims* dims, int64_t n_tokens);

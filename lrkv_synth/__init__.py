@@ -188,16 +188,20 @@ def query(w: Workload, layer: int, batch: Optional[int] = None) -> Stored:
     return quantize(q, w.dtype)
 
 
-def direct_coeffs(w: Workload, layer: int, which: str, b: int, h: int, n_rows: int) -> Stored:
-    """Coefficient rows c ~ N(0, diag(rho^(2i))) for i < r, as an already-filled cache [n, r]."""
+def direct_coeffs(w: Workload, layer: int, which: str, b: int, h: int, n_rows: int,
+                  exact: bool = True) -> Stored:
+    """Coefficient rows c ~ N(0, diag(rho^(2i))) for i < r, as an already-filled cache [n, r].
+
+    exact=False skips the float64 image (``Stored.exact`` is None) for bulk inputs.
+    """
     r = w.ranks(layer)[0 if which == "k" else 1]
     tag = TAG_KEYS if which == "k" else TAG_VALUES
     z = rng(w, layer, b, h, tag, PART_DIRECT).standard_normal((n_rows, r), dtype=np.float32)
     c = z * spectrum(w, r).astype(np.float32)[None, :]
     if w.dtype == "bf16":
         bits = f32_to_bf16_bits(c)
-        return Stored(bits, bf16_bits_to_f64(bits))
-    return Stored(c, c.astype(np.float64))
+        return Stored(bits, bf16_bits_to_f64(bits) if exact else None)
+    return Stored(c, c.astype(np.float64) if exact else None)
 
 
 def full_tokens(w: Workload, layer: int, which: str, b: int, h: int, n_tokens: int,
@@ -219,6 +223,8 @@ def stack_heads(w: Workload, fn, batch: Optional[int] = None, threads: int = 8) 
     else:
         parts = [fn(b, h) for b, h in keys]
     store = np.stack([p.store for p in parts]).reshape((B, w.n_kv_heads) + parts[0].store.shape)
+    if parts[0].exact is None:
+        return Stored(store, None)
     exact = np.stack([p.exact for p in parts]).reshape((B, w.n_kv_heads) + parts[0].exact.shape)
     return Stored(store, exact)
 
@@ -226,7 +232,7 @@ def stack_heads(w: Workload, fn, batch: Optional[int] = None, threads: int = 8) 
 def tokens_major(s: Stored) -> Stored:
     """[B, Hkv, T, d] -> [B, T, Hkv, d] (the layout a K/V projection produces)."""
     return Stored(np.ascontiguousarray(s.store.transpose(0, 2, 1, 3)),
-                  np.ascontiguousarray(s.exact.transpose(0, 2, 1, 3)))
+                  None if s.exact is None else np.ascontiguousarray(s.exact.transpose(0, 2, 1, 3)))
 
 
 # ----------------------------------------------------------------------------

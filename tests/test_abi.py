@@ -1,0 +1,145 @@
+"""The C-ABI library: it loads without a GPU, exports what the header declares,
+and rejects invalid calls with a status before launching anything."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "lrkv.h")
+
+
+def _lib():
+    lrkv = pytest.importorskip("decode_attention_lrkv_amd")
+    if not os.path.exists(lrkv.LIB_PATH):
+        pytest.skip("liblrkv.so not built")
+    return lrkv, lrkv.library()
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(lrkv_[a-z_]+)\s*\(", text)))
+
+
+def test_header_declares_the_entry_points():
+    names = _declared()
+    for n in ("lrkv_compress", "lrkv_decode_attn", "lrkv_compress_hybrid", "lrkv_decode_attn_hybrid",
+              "lrkv_decode_workspace_bytes", "lrkv_status_string", "lrkv_last_error",
+              "lrkv_decode_attn_partial", "lrkv_decode_attn_merge", "lrkv_compress_hybrid_workspace_bytes"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol():
+    lrkv, lib = _lib()
+    out = subprocess.run(["nm", "-D", "--defined-only", lrkv.LIB_PATH], capture_output=True, text=True).stdout
+    exported = set(re.findall(r"\sT\s(lrkv_\w+)", out))
+    missing = [n for n in _declared() if n not in exported]
+    assert not missing, missing
+    for n in _declared():
+        assert getattr(lib, n) is not None
+
+
+def test_header_compiles_as_c():
+    """The header is plain C (a C caller needs no C++ or torch)."""
+    src = '#include "lrkv.h"\nint main(void) { lrkv_dims d = {0}; (void)d; return (int)LRKV_OK; }\n'
+    r = subprocess.run(["gcc", "-x", "c", "-std=c99", "-fsyntax-only", "-D__HIP_PLATFORM_AMD__",
+                        f"-I{os.path.dirname(HEADER)}", "-I/opt/rocm/include", "-"],
+                       input=src, capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr
+
+
+def test_status_strings():
+    _, lib = _lib()
+    assert lib.lrkv_status_string(0) == b"ok"
+    assert lib.lrkv_status_string(3) == b"workspace too small"
+    assert lib.lrkv_status_string(99) == b"unknown status"
+
+
+P = ctypes.c_void_p(16)          # a non-null, 16-byte aligned address that is never dereferenced
+MIS = ctypes.c_void_p(18)        # misaligned
+
+
+def _dims(lrkv, **kw):
+    base = dict(batch=1, n_q_heads=8, n_kv_heads=2, head_dim=128, rank_k=32, rank_v=64, capacity=256)
+    base.update(kw)
+    return lrkv._Dims(*[base[k] for k in ("batch", "n_q_heads", "n_kv_heads", "head_dim", "rank_k",
+                                            "rank_v", "capacity")])
+
+
+def _decode(lib, lrkv, dims, n_ctx=100, q=P, ws=P, ws_bytes=1 << 30, dtype=1, scale=0.0):
+    return lib.lrkv_decode_attn(q, P, P, P, P, P, None, ctypes.byref(dims), n_ctx, scale, dtype, ws,
+                                ws_bytes, None)
+
+
+@pytest.mark.parametrize("dims_kw,n_ctx,status,needle", [
+    (dict(head_dim=96), 100, 2, "head_dim"),
+    (dict(rank_k=36), 100, 2, "rank_k"),            # not a multiple of 8 for bf16
+    (dict(rank_v=0), 100, 2, "rank_v"),
+    (dict(rank_v=136), 100, 2, "rank_v"),
+    (dict(n_q_heads=9), 100, 1, "multiple"),
+    (dict(n_q_heads=32, n_kv_heads=2), 100, 2, "8 query heads"),
+    (dict(capacity=100), 100, 1, "capacity"),
+    (dict(batch=0), 100, 1, "batch"),
+    (dict(), 0, 1, "n_ctx"),
+    (dict(), 257, 1, "n_ctx"),
+])
+def test_decode_rejects_invalid_dims(dims_kw, n_ctx, status, needle):
+    lrkv, lib = _lib()
+    st = _decode(lib, lrkv, _dims(lrkv, **dims_kw), n_ctx=n_ctx)
+    assert st == status
+    assert needle in lib.lrkv_last_error().decode()
+
+
+def test_decode_rejects_bad_pointers_and_workspace():
+    lrkv, lib = _lib()
+    d = _dims(lrkv)
+    assert _decode(lib, lrkv, d, q=None) == 1 and b"NULL" in lib.lrkv_last_error()
+    assert _decode(lib, lrkv, d, q=MIS) == 1 and b"aligned" in lib.lrkv_last_error()
+    assert _decode(lib, lrkv, d, ws_bytes=16) == 3
+    assert _decode(lib, lrkv, d, dtype=7) == 1
+    assert _decode(lib, lrkv, d, scale=float("inf")) == 1
+    # fp32 accepts ranks that are multiples of 4 but not of 8
+    assert _decode(lib, lrkv, _dims(lrkv, rank_k=36), dtype=0, ws_bytes=16) == 3
+
+
+def test_compress_validation():
+    lrkv, lib = _lib()
+    c = lib.lrkv_compress
+    # x, basis, coeff, kind, B, Hkv, d, r, T, pos, cap, dtype, stream
+    assert c(P, P, P, 0, 1, 2, 128, 32, 10, 250, 256, 1, None) == 1      # rows past capacity
+    assert c(P, P, P, 2, 1, 2, 128, 32, 10, 0, 256, 1, None) == 1        # unknown cache kind
+    assert c(P, P, P, 0, 1, 2, 80, 32, 10, 0, 256, 1, None) == 2         # head_dim
+    assert c(None, P, P, 0, 1, 2, 128, 32, 10, 0, 256, 1, None) == 1     # null x
+    assert c(P, P, MIS, 1, 1, 2, 128, 32, 10, 0, 256, 1, None) == 1      # misaligned coeff
+    assert c(P, P, P, 1, 1, 2, 128, 32, 0, 0, 256, 1, None) == 0         # no tokens: nothing to do
+    assert c(P, P, P, 1, 1, 2, 128, 32, 10, 0, 252, 1, None) == 1        # capacity not a multiple of 8
+
+
+def test_hybrid_validation():
+    lrkv, lib = _lib()
+    d = _dims(lrkv)
+    f = lib.lrkv_compress_hybrid
+    args = lambda tau=0.5, side_cap=64, dtype=1, n_lr=P: (P, P, P, P, tau, P, P, n_lr, P, P, P, P, None, P,
+                                                           ctypes.byref(d), 100, 0, side_cap, dtype, P,
+                                                           1 << 30, None)
+    assert f(*args(tau=-1.0)) == 1
+    assert f(*args(tau=float("nan"))) == 1
+    assert f(*args(side_cap=60)) == 1
+    assert f(*args(dtype=0)) == 2
+    assert f(*args(n_lr=None)) == 1
+    g = lib.lrkv_decode_attn_hybrid
+    assert g(P, P, P, P, P, P, P, P, P, 0, P, None, ctypes.byref(d), 0.0, 1, P, 1 << 30, None) == 1
+
+
+def test_workspace_queries():
+    lrkv, lib = _lib()
+    d = _dims(lrkv)
+    n1 = lib.lrkv_decode_workspace_bytes(ctypes.byref(d), 256, 0)
+    assert n1 > 0 and n1 % 256 == 0
+    assert lib.lrkv_decode_workspace_bytes(ctypes.byref(d), 0, 0) == 0
+    assert lib.lrkv_decode_workspace_bytes(ctypes.byref(_dims(lrkv, head_dim=96)), 256, 0) == 0
+    assert lib.lrkv_decode_workspace_bytes(ctypes.byref(d), 256, 64) > n1
+    assert lib.lrkv_compress_hybrid_workspace_bytes(ctypes.byref(d), 1000) > 0

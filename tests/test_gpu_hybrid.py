@@ -1,0 +1,175 @@
+"""GPU parity of the hybrid (OjaKV-style) cache: selection, compaction and union decode.
+
+Selection is compared bit for bit (flags, counts, side-list indices, side
+rows); coefficients within the compress gate; decode within the bfloat16
+decode gate, on the oracle's cache contents and end to end.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import lrkv_synth as synth
+from oracle import lrkv_oracle as O
+from tests.gpu_helpers import DEV, bits, check_decode, round_store, to_dev, to_f64
+from tests.test_gpu_parity_small import check_compress
+
+pytestmark = pytest.mark.gpu
+lrkv = pytest.importorskip("decode_attention_lrkv_amd")
+
+TAU = 0.5
+
+
+def _round8(x):
+    return (x + 7) // 8 * 8
+
+
+def _inputs(n):
+    w = synth.scaled(synth.HYBRID_128K, n_ctx=(n,))
+    inj = synth.injected_set(w, 0, 0, n)
+    k = synth.tokens_major(synth.stack_heads(w, lambda b, h: synth.hybrid_tokens(w, 0, "k", b, h, n, inj)))
+    v = synth.tokens_major(synth.stack_heads(w, lambda b, h: synth.hybrid_tokens(w, 0, "v", b, h, n, inj)))
+    return w, inj, k, v, synth.basis(w, 0, "k"), synth.basis(w, 0, "v"), synth.query(w, 0)
+
+
+def _new_cache(w, cap, side_cap):
+    return lrkv.HybridCache(w.batch, w.n_q_heads, w.n_kv_heads, w.head_dim, *w.ranks(0), cap, side_cap, DEV)
+
+
+def _snapshot(c):
+    torch.cuda.synchronize()
+    return {name: bits(getattr(c, name)) for name in
+            ("coeff_k", "coeff_v", "k_side", "v_side", "side_idx", "n_lr", "n_side", "overflow")}
+
+
+def _valid_parts(snap, b, h):
+    n_lr, n_side = int(snap["n_lr"][b, h]), int(snap["n_side"][b, h])
+    return dict(
+        ck=snap["coeff_k"][b, h, :n_lr],
+        cv=synth.from_value_octets(snap["coeff_v"][b, h])[:n_lr],
+        ks=snap["k_side"][b, h, :n_side],
+        vs=synth.from_value_octets(snap["v_side"][b, h])[:n_side],
+        idx=snap["side_idx"][b, h, :n_side])
+
+
+@pytest.mark.parametrize("n", [8192, 131072])
+def test_hybrid_selection_compaction_and_decode(n):
+    w, inj, k, v, bk, bv, q = _inputs(n)
+    H, d = w.n_kv_heads, w.head_dim
+    cap = _round8(n)
+    side_cap = _round8(int(math.ceil(0.06 * n)))
+    ref = O.compress_hybrid(k.exact, v.exact, bk.exact, bv.exact, TAU, "bf16")
+
+    # --- one call
+    c1 = _new_cache(w, cap, side_cap)
+    flags = torch.zeros((1, H, n), dtype=torch.uint8, device=DEV)
+    kd, vd, bkd, bvd = to_dev(k, "bf16"), to_dev(v, "bf16"), to_dev(bk, "bf16"), to_dev(bv, "bf16")
+    lrkv.compress_hybrid(c1, kd, vd, bkd, bvd, TAU, 0, flags=flags)
+    s1 = _snapshot(c1)
+    fl = flags.cpu().numpy()
+    assert s1["overflow"][0] == 0
+    for h in range(H):
+        f_ref = ref["flags"][(0, h)]
+        assert np.array_equal(fl[0, h].astype(bool), f_ref), f"flags differ at head {h}"
+        assert np.array_equal(np.nonzero(f_ref)[0], inj)      # the injected tokens, exactly
+        part = _valid_parts(s1, 0, h)
+        assert s1["n_side"][0, h] == f_ref.sum() and s1["n_lr"][0, h] == n - f_ref.sum()
+        assert np.array_equal(part["idx"], ref["side_idx"][(0, h)])
+        side = np.nonzero(f_ref)[0]
+        lr = np.nonzero(~f_ref)[0]
+        assert np.array_equal(part["ks"], k.store[0, side, h])      # bit-identical copies
+        assert np.array_equal(part["vs"], v.store[0, side, h])
+        ck_gpu = synth.bf16_bits_to_f64(part["ck"])[None, None]
+        cv_gpu = synth.bf16_bits_to_f64(part["cv"])[None, None]
+        check_compress(ck_gpu, ref["ck"][(0, h)][None, None], k.exact[:, lr, h:h + 1], bk.exact[h:h + 1],
+                       "bf16", f"hybrid K h={h}")
+        check_compress(cv_gpu, ref["cv"][(0, h)][None, None], v.exact[:, lr, h:h + 1], bv.exact[h:h + 1],
+                       "bf16", f"hybrid V h={h}")
+
+    # --- the same tokens in 4096-token chunks give identical caches
+    c2 = _new_cache(w, cap, side_cap)
+    for p in range(0, n, 4096):
+        e = min(n, p + 4096)
+        lrkv.compress_hybrid(c2, kd[:, p:e].contiguous(), vd[:, p:e].contiguous(), bkd, bvd, TAU, p)
+    s2 = _snapshot(c2)
+    for h in range(H):
+        a, b_ = _valid_parts(s1, 0, h), _valid_parts(s2, 0, h)
+        for key in a:
+            assert np.array_equal(a[key], b_[key]), f"chunked compress differs in {key} at head {h}"
+
+    # --- decode: sampled rows against the oracle's union attention
+    rows = [(0, hq) for hq in range(w.n_q_heads)] if n <= 8192 else [(0, hq) for hq in (0, 5, 10, 15, 16, 22, 27, 31)]
+    ck_st = {key: O.round_storage(c, "bf16") for key, c in ref["ck"].items()}
+    cv_st = {key: O.round_storage(c, "bf16") for key, c in ref["cv"].items()}
+    o_ref = O.decode_hybrid_rows(q.exact, bk.exact, bv.exact, ck_st, cv_st, ref["k_side"], ref["v_side"], rows)
+    o_ref_arr = np.stack([o_ref[r][0] for r in rows])
+    lse_ref = np.array([o_ref[r][1] for r in rows])
+    qd = to_dev(q, "bf16")
+    # (iii) end to end on the GPU-built cache
+    o, lse = lrkv.decode_attn_hybrid(qd, bkd, bvd, c1)
+    og, lg = to_f64(o), to_f64(lse)
+    check_decode(np.stack([og[r] for r in rows]), np.array([lg[r] for r in rows]), o_ref_arr, lse_ref,
+                 "bf16", f"hybrid e2e n={n}")
+    # (ii) on the oracle's cache contents
+    c3 = _new_cache(w, cap, side_cap)
+    ckb = np.zeros((1, H, cap, w.ranks(0)[0]), np.uint16)
+    cvb = np.zeros((1, H, cap, w.ranks(0)[1]), np.uint16)
+    ksb = np.zeros((1, H, side_cap, d), np.uint16)
+    vsb = np.zeros((1, H, side_cap, d), np.uint16)
+    for h in range(H):
+        nl = len(ck_st[(0, h)])
+        ckb[0, h, :nl] = round_store(ck_st[(0, h)], "bf16")
+        cvb[0, h, :nl] = round_store(cv_st[(0, h)], "bf16")
+        ns = len(ref["k_side"][(0, h)])
+        ksb[0, h, :ns] = round_store(ref["k_side"][(0, h)], "bf16")
+        vsb[0, h, :ns] = round_store(ref["v_side"][(0, h)], "bf16")
+    c3.coeff_k.copy_(to_dev(ckb, "bf16"))
+    c3.coeff_v.copy_(to_dev(synth.to_value_octets(cvb), "bf16"))
+    c3.k_side.copy_(to_dev(ksb, "bf16"))
+    c3.v_side.copy_(to_dev(synth.to_value_octets(vsb), "bf16"))
+    c3.n_lr.copy_(torch.tensor([[len(ck_st[(0, h)]) for h in range(H)]], dtype=torch.int32))
+    c3.n_side.copy_(torch.tensor([[len(ref["k_side"][(0, h)]) for h in range(H)]], dtype=torch.int32))
+    o, lse = lrkv.decode_attn_hybrid(qd, bkd, bvd, c3)
+    og, lg = to_f64(o), to_f64(lse)
+    check_decode(np.stack([og[r] for r in rows]), np.array([lg[r] for r in rows]), o_ref_arr, lse_ref,
+                 "bf16", f"hybrid on oracle cache n={n}")
+
+
+def test_hybrid_side_list_overflow():
+    n = 2048
+    w, inj, k, v, bk, bv, q = _inputs(n)
+    c = _new_cache(w, n, 16)
+    lrkv.compress_hybrid(c, to_dev(k, "bf16"), to_dev(v, "bf16"), to_dev(bk, "bf16"), to_dev(bv, "bf16"), TAU, 0)
+    s = _snapshot(c)
+    assert s["overflow"][0] == 1
+    ref = O.compress_hybrid(k.exact, v.exact, bk.exact, bv.exact, TAU, "bf16")
+    for h in range(w.n_kv_heads):
+        assert s["n_side"][0, h] == 16
+        # the first 16 selected tokens, in order, are the ones kept
+        assert np.array_equal(s["side_idx"][0, h, :16], ref["side_idx"][(0, h)][:16])
+        assert s["n_lr"][0, h] == n - ref["flags"][(0, h)].sum()
+
+
+def test_hybrid_empty_cache_gives_zero_and_minus_inf():
+    w = synth.scaled(synth.HYBRID_128K, n_ctx=(64,))
+    c = _new_cache(w, 64, 8)
+    q = to_dev(synth.query(w, 0), "bf16")
+    o, lse = lrkv.decode_attn_hybrid(q, to_dev(synth.basis(w, 0, "k"), "bf16"), to_dev(synth.basis(w, 0, "v"), "bf16"), c)
+    assert torch.all(o == 0).item()
+    assert torch.all(torch.isneginf(lse)).item()
+
+
+def test_hybrid_tau_inf_matches_plain_decode():
+    """tau = +inf keeps every token low rank: the hybrid decode equals the plain decode."""
+    n = 1000
+    w, inj, k, v, bk, bv, q = _inputs(n)
+    c = _new_cache(w, 1000, 8)
+    kd, vd, bkd, bvd, qd = (to_dev(x, "bf16") for x in (k, v, bk, bv, q))
+    lrkv.compress_hybrid(c, kd, vd, bkd, bvd, math.inf, 0)
+    torch.cuda.synchronize()
+    assert c.n_lr.cpu().eq(n).all() and c.n_side.cpu().eq(0).all()
+    o1, l1 = lrkv.decode_attn_hybrid(qd, bkd, bvd, c)
+    o2, l2 = lrkv.decode_attn(qd, bkd, c.coeff_k, bvd, c.coeff_v, n)
+    assert np.max(np.abs(to_f64(o1) - to_f64(o2))) <= 2 * 2 ** -8 * np.max(np.abs(to_f64(o2)))
+    assert np.max(np.abs(to_f64(l1) - to_f64(l2))) <= 1e-4

@@ -162,3 +162,24 @@ def test_prefill_compress_tiles_and_ragged_tail():
     # rows outside [pos, pos + T) stay zero
     assert not gk[:, :, :pos].any() and not gk[:, :, pos + T:].any()
     assert not gv[:, :, :pos].any() and not gv[:, :, pos + T:].any()
+
+
+@pytest.mark.parametrize("T,pos", [(1, 255), (2, 8), (3, 61), (4, 100), (100, 13)])
+def test_compress_kv_both_caches(T, pos):
+    """The two-cache entry point: a few tokens in one launch, longer chunks per cache."""
+    w = synth.LLAMA_STEP
+    layer, cap, B = 0, 264, 2
+    rk, rv = w.ranks(layer)
+    xk = synth.tokens_major(synth.stack_heads(w, lambda b, h: synth.full_tokens(w, layer, "k", b, h, T, synth.PART_PREFILL), batch=B))
+    xv = synth.tokens_major(synth.stack_heads(w, lambda b, h: synth.full_tokens(w, layer, "v", b, h, T, synth.PART_PREFILL), batch=B))
+    bk, bv = synth.basis(w, layer, "k"), synth.basis(w, layer, "v")
+    ck = torch.zeros((B, 8, cap, rk), dtype=torch.bfloat16, device=DEV)
+    cv = torch.zeros(lrkv.value_cache_shape(B, 8, cap, rv), dtype=torch.bfloat16, device=DEV)
+    lrkv.compress_kv(to_dev(xk, "bf16"), to_dev(xv, "bf16"), to_dev(bk, "bf16"), to_dev(bv, "bf16"), ck, cv, pos)
+    torch.cuda.synchronize()
+    gk = to_f64(ck)
+    gv = synth.from_value_octets(to_f64(cv))
+    check_compress(gk[:, :, pos:pos + T], O.compress(xk.exact, bk.exact), xk.exact, bk.exact, "bf16", "kv K")
+    check_compress(gv[:, :, pos:pos + T], O.compress(xv.exact, bv.exact), xv.exact, bv.exact, "bf16", "kv V")
+    assert not gk[:, :, :pos].any() and not gk[:, :, pos + T:].any()
+    assert not gv[:, :, :pos].any() and not gv[:, :, pos + T:].any()

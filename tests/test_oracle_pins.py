@@ -476,3 +476,24 @@ def test_planted_selection_mistake_is_caught(monkeypatch, mutant):
             test_hybrid_flags_closed_form()
         else:
             test_hybrid_compaction_order_golden()
+
+
+def test_row_sampled_decoders_match_the_full_decoder():
+    """decode_rows (sampled rows) and decode_hybrid_rows with an empty side list
+    equal the pinned full decode."""
+    q, bk, ck, bv, cv = _case(12)
+    n = 30
+    o, lse = O.decode(q, bk, ck, bv, cv, n)
+    g = q.shape[1] // bk.shape[0]
+    rows = [(b, hq) for b in range(q.shape[0]) for hq in range(q.shape[1])]
+    ckd = {(b, h): ck[b, h] for b in range(ck.shape[0]) for h in range(ck.shape[1])}
+    cvd = {(b, h): cv[b, h] for b in range(cv.shape[0]) for h in range(cv.shape[1])}
+    r1 = O.decode_rows(q, bk, ckd, bv, cvd, n, rows)
+    cks = {key: v[:n] for key, v in ckd.items()}
+    cvs = {key: v[:n] for key, v in cvd.items()}
+    empty = {key: np.zeros((0, q.shape[2])) for key in ckd}
+    r2 = O.decode_hybrid_rows(q, bk, bv, cks, cvs, empty, empty, rows)
+    for (b, hq) in rows:
+        for r in (r1, r2):
+            assert np.max(np.abs(r[(b, hq)][0] - o[b, hq])) <= 1e-14
+            assert abs(r[(b, hq)][1] - lse[b, hq]) <= 1e-13
