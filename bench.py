@@ -50,6 +50,7 @@ def parse():
     p.add_argument("--steps", type=int, default=10)
     p.add_argument("--warmup", type=int, default=3)
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-extra", action="store_true", help="skip the hybrid and 32-layer-step figures")
     p.add_argument("--cpu-seconds", type=float, default=15.0,
                    help="approximate CPU time budget of the oracle sample")
     return p.parse_args()
@@ -228,17 +229,129 @@ def main():
                      "bytes_per_launch": round(sum(attn_bytes[l % 2] for l in range(L)) / L)},
     }
 
+    del layers, ws
+    torch.cuda.empty_cache()
+    if not args.no_extra:
+        result["hybrid_128k"] = bench_hybrid(torch, lrkv, bm, synth, dev, threads)
+        result["step_32layer_sweep"] = bench_step_sweep(torch, lrkv, bm, synth, dev, threads)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
     print(json.dumps(result), flush=True)
     return 0
 
 
+def _timed(torch, fn, iters, warm=3):
+    for _ in range(warm):
+        fn(0)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for i in range(iters):
+        fn(i)
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) * 1e3 / iters
+
+
+def bench_hybrid(torch, lrkv, bm, synth, dev, threads):
+    """Hybrid cache at 131072 tokens: selection + compaction of every token, then decode.
+
+    Three caches rotate so that the 256 MB last-level cache cannot hold the
+    working set between decode calls.
+    """
+    w = synth.HYBRID_128K
+    n = w.n_ctx[0]
+    H, d = w.n_kv_heads, w.head_dim
+    rk, rv = w.ranks(0)
+    t0 = time.time()
+    inj = synth.injected_set(w, 0, 0, n)
+    k = synth.tokens_major(synth.stack_heads(w, lambda b, h: synth.hybrid_tokens(w, 0, "k", b, h, n, inj),
+                                             threads=threads)).store
+    v = synth.tokens_major(synth.stack_heads(w, lambda b, h: synth.hybrid_tokens(w, 0, "v", b, h, n, inj),
+                                             threads=threads)).store
+    dv = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
+    kd, vd = dv(k), dv(v)
+    bk, bv, q = dv(synth.basis(w, 0, "k").store), dv(synth.basis(w, 0, "v").store), dv(synth.query(w, 0).store)
+    side_cap = 8192
+    caches = [lrkv.HybridCache(1, w.n_q_heads, H, d, rk, rv, n, side_cap, dev) for _ in range(3)]
+    cws = torch.empty(lrkv.compress_hybrid_workspace_bytes(1, w.n_q_heads, H, d, rk, rv, n, n),
+                      dtype=torch.uint8, device=dev)
+
+    def compress(i):
+        c = caches[i % 3]
+        c.n_lr.zero_()
+        c.n_side.zero_()
+        lrkv.compress_hybrid(c, kd, vd, bk, bv, 0.5, 0, workspace=cws)
+
+    comp_us = _timed(torch, compress, 6)
+    n_side = int(caches[0].n_side[0, 0].item())
+    dws = torch.empty(lrkv.decode_workspace_bytes(1, w.n_q_heads, H, d, rk, rv, n, 0, side_cap),
+                      dtype=torch.uint8, device=dev)
+    out = torch.empty_like(q)
+    lse = torch.empty((1, w.n_q_heads), dtype=torch.float32, device=dev)
+    dec_us = _timed(torch, lambda i: lrkv.decode_attn_hybrid(q, bk, bv, caches[i % 3], out=out, lse=lse,
+                                                             workspace=dws), 30)
+    comp_bytes = (2 * n * H * d * 2 + (n - n_side) * H * (rk + rv) * 2 + n_side * H * (2 * d * 2 + 4)
+                  + H * d * (rk + rv) * 2)
+    dec_bytes = bm.decode_bytes(1, w.n_q_heads, H, d, rk, rv, n, side_tokens=n_side)
+    log(f"hybrid figures in {time.time() - t0:.1f}s")
+    return {"workload": w.name, "context": n, "side_tokens_per_kv_head": n_side,
+            "compress_us": round(comp_us, 1), "compress_GBps": round(comp_bytes / comp_us / 1e3, 1),
+            "decode_us": round(dec_us, 2), "decode_GBps": round(dec_bytes / dec_us / 1e3, 1),
+            "decode_pct_peak": round(100 * dec_bytes / dec_us / 1e3 / HBM_PEAK_GBPS, 2)}
+
+
+def bench_step_sweep(torch, lrkv, bm, synth, dev, threads):
+    """32-layer decode step at batch 1 (append + attention + merge per layer), eager and as a HIP graph."""
+    w = synth.LLAMA_STEP
+    L, Hq, H, d = w.layers, w.n_q_heads, w.n_kv_heads, w.head_dim
+    rk, rv = w.ranks(0)
+    dv = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
+    bk, bv = dv(synth.basis(w, 0, "k").store), dv(synth.basis(w, 0, "v").store)
+    res = {}
+    for n in w.n_ctx:
+        ck0 = synth.stack_heads(w, lambda b, h: synth.direct_coeffs(w, 0, "k", b, h, n, exact=False), threads=threads).store
+        cv0 = synth.stack_heads(w, lambda b, h: synth.direct_coeffs(w, 0, "v", b, h, n, exact=False), threads=threads).store
+        ck0, cv0 = dv(ck0), dv(synth.to_value_octets(cv0))
+        lay = [dict(ck=ck0.clone(), cv=cv0.clone(), q=dv(synth.query(w, l).store),
+                    ak=dv(synth.tokens_major(synth.stack_heads(w, lambda b, h: synth.full_tokens(
+                        w, l, "k", b, h, 1, synth.PART_APPEND))).store),
+                    av=dv(synth.tokens_major(synth.stack_heads(w, lambda b, h: synth.full_tokens(
+                        w, l, "v", b, h, 1, synth.PART_APPEND))).store),
+                    out=torch.empty((1, Hq, d), dtype=torch.bfloat16, device=dev),
+                    lse=torch.empty((1, Hq), dtype=torch.float32, device=dev)) for l in range(L)]
+        ws = torch.empty(lrkv.decode_workspace_bytes(1, Hq, H, d, rk, rv, n, n), dtype=torch.uint8, device=dev)
+
+        def step(_i=0):
+            for x in lay:
+                lrkv.compress_kv(x["ak"], x["av"], bk, bv, x["ck"], x["cv"], n - 1)
+                lrkv.decode_attn(x["q"], bk, x["ck"], bv, x["cv"], n, out=x["out"], lse=x["lse"], workspace=ws)
+
+        eager = _timed(torch, step, 20)
+        s = torch.cuda.Stream()
+        with torch.cuda.stream(s):
+            step()
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=s):
+            step()
+        graph = _timed(torch, lambda i: g.replay(), 50)
+        step_bytes = L * (bm.decode_bytes(1, Hq, H, d, rk, rv, n) + bm.compress_bytes(1, 1, H, d, rk)
+                          + bm.compress_bytes(1, 1, H, d, rv))
+        res[str(n)] = {"eager_us_per_step": round(eager, 1), "graph_us_per_step": round(graph, 1),
+                       "graph_us_per_layer": round(graph / L, 2),
+                       "graph_GBps_effective": round(step_bytes / graph / 1e3, 1)}
+        del lay, g, ws
+        torch.cuda.empty_cache()
+    return {"workload": w.name, "layers": L, "by_context": res,
+            "note": "working set <= 0.6 GB per step; 'effective' bandwidth can include last-level-cache hits"}
+
+
 def measured_traffic():
     """HBM bytes per launch of the attention kernel from the committed counter
     summary, or None when the kernel source changed since it was taken."""
     import hashlib
-    path = os.path.join(ROOT, "profiles", "split_bf16_kernel_llama8b-b16-32k.md")
+    path = os.path.join(ROOT, "profiles", "split_bf16_kernel_llama8b-b16-32k.txt")
     src = os.path.join(ROOT, "decode_attention_lrkv_amd", "csrc", "decode.hip")
     try:
         rec = next(json.loads(l.split("TRAFFIC", 1)[1]) for l in open(path) if l.strip().startswith("TRAFFIC"))

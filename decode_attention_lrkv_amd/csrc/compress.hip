@@ -35,10 +35,6 @@ __global__ __launch_bounds__(256) void compress_bf16_kernel(CompressArgs a) {
   const int b = blockIdx.z;
   const int r = a.rank;
   const int64_t bh = (int64_t)b * a.hkv + h;
-  const int64_t t_base = (int64_t)blockIdx.x * kTile;
-  const int64_t left = a.n_tokens - t_base;
-  const int nt = left < kTile ? (int)left : kTile;
-
   __shared__ __attribute__((aligned(16))) uint16_t s_bt[NB * 16][D + kPad];    // basis, transposed
   // the tile's coefficients: keys as [token][column]; values as [column][slot]
   // with slot = token + (p0 % 8), so each destination octet is 16 aligned bytes
@@ -46,8 +42,6 @@ __global__ __launch_bounds__(256) void compress_bf16_kernel(CompressArgs a) {
   constexpr int kOutCol = kTile + 8 + kPad;
   constexpr int kOutElems = kTile * kOutRow > NB * 16 * kOutCol ? kTile * kOutRow : NB * 16 * kOutCol;
   __shared__ __attribute__((aligned(16))) uint16_t s_out[kOutElems];
-  const int64_t p0 = a.pos + t_base;                       // destination row of the tile's first token
-  const int shift = (int)(p0 & 7);
 
   // basis rows arrive as 16-byte runs of 8 coefficients (all loads issued
   // before the first wait) and are written transposed
@@ -79,76 +73,96 @@ __global__ __launch_bounds__(256) void compress_bf16_kernel(CompressArgs a) {
   }
   __syncthreads();
 
-  // each wave takes two 16-token sub-tiles; both sub-tiles' rows are loaded
-  // before either is multiplied, so each wave keeps 8 KB of loads in flight
+  // The workgroup loops over tiles blockIdx.x, blockIdx.x + gridDim.x, ... of
+  // this (b, h); the basis above is staged once.  Each wave takes two 16-token
+  // sub-tiles per tile, and the next tile's rows are loaded while the current
+  // tile is multiplied and stored.
   constexpr int kSubs = kTile / 16 / 4;
-  u32x4 xa[kSubs][D / 32];
+  const int64_t n_tiles = (a.n_tokens + kTile - 1) / kTile;
+  auto load_tile = [&](u32x4 (&xa)[kSubs][D / 32], int64_t tile) {
 #pragma unroll
-  for (int u = 0; u < kSubs; ++u) {
-    const int tl = 16 * (wave + 4 * u) + n16;
-    const bool valid = tl < nt;
-    const uint16_t* xrow =
-        static_cast<const uint16_t*>(a.x) + ((b * a.n_tokens + t_base + tl) * a.hkv + h) * D;
+    for (int u = 0; u < kSubs; ++u) {
+      const int64_t tok = tile * kTile + 16 * (wave + 4 * u) + n16;
+      const bool valid = tok < a.n_tokens;
+      const uint16_t* xrow = static_cast<const uint16_t*>(a.x) + ((b * a.n_tokens + tok) * a.hkv + h) * D;
 #pragma unroll
-    for (int c = 0; c < D / 32; ++c)
-      xa[u][c] = valid ? *reinterpret_cast<const u32x4*>(xrow + 32 * c + 8 * grp) : u32x4{0u, 0u, 0u, 0u};
-  }
-#pragma unroll
-  for (int u = 0; u < kSubs; ++u) {
-    const int sub = wave + 4 * u;
-    if (16 * sub >= nt) break;
-    f32x4 acc[NB];
-#pragma unroll
-    for (int nb = 0; nb < NB; ++nb) acc[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int c = 0; c < D / 32; ++c) {
-      const int k = 32 * c + 8 * grp;
-#pragma unroll
-      for (int nb = 0; nb < NB; ++nb)
-        acc[nb] = mfma_16x16x32(xa[u][c], *reinterpret_cast<const u32x4*>(&s_bt[16 * nb + n16][k]), acc[nb]);
+      for (int c = 0; c < D / 32; ++c)
+        xa[u][c] = valid ? *reinterpret_cast<const u32x4*>(xrow + 32 * c + 8 * grp) : u32x4{0u, 0u, 0u, 0u};
     }
-    // lane (n16, grp) holds coefficient 16*nb + n16 of tokens 16*sub + 4*grp + i
-#pragma unroll
-    for (int nb = 0; nb < NB; ++nb)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int tl = 16 * sub + 4 * grp + i, col = 16 * nb + n16;
-        const int at = a.values_layout ? col * kOutCol + shift + tl : tl * kOutRow + col;
-        s_out[at] = f32_to_bf16(acc[nb][i]);
-      }
-  }
-  __syncthreads();
-
+  };
   uint16_t* out = static_cast<uint16_t*>(a.coeff);
-  if (!a.values_layout) {
-    // key rows: each destination row is r/8 aligned 16-byte pieces
-    const int per_row = r / 8;
-    uint16_t* dst = out + (bh * a.cap + p0) * r;
-    for (int i = tid; i < nt * per_row; i += 256) {
-      const int tl = i / per_row, c = (i - tl * per_row) * 8;
-      *reinterpret_cast<u32x4*>(dst + (int64_t)tl * r + c) = *reinterpret_cast<const u32x4*>(&s_out[tl * kOutRow + c]);
+  u32x4 xa[kSubs][D / 32], xb[kSubs][D / 32];
+  int64_t tile = blockIdx.x;
+  if (tile < n_tiles) load_tile(xa, tile);
+  for (; tile < n_tiles; tile += gridDim.x) {
+    const int64_t next = tile + gridDim.x;
+    if (next < n_tiles) load_tile(xb, next);
+    const int64_t t_base = tile * kTile;
+    const int64_t left = a.n_tokens - t_base;
+    const int nt = left < kTile ? (int)left : kTile;
+    const int64_t p0 = a.pos + t_base;                   // destination row of the tile's first token
+    const int shift = (int)(p0 & 7);
+#pragma unroll
+    for (int u = 0; u < kSubs; ++u) {
+      const int sub = wave + 4 * u;
+      if (16 * sub < nt) {
+        f32x4 acc[NB];
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) acc[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int c = 0; c < D / 32; ++c) {
+          const int k = 32 * c + 8 * grp;
+#pragma unroll
+          for (int nb = 0; nb < NB; ++nb)
+            acc[nb] = mfma_16x16x32(xa[u][c], *reinterpret_cast<const u32x4*>(&s_bt[16 * nb + n16][k]), acc[nb]);
+        }
+        // lane (n16, grp) holds coefficient 16*nb + n16 of tokens 16*sub + 4*grp + i
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int tl = 16 * sub + 4 * grp + i, col = 16 * nb + n16;
+            const int at = a.values_layout ? col * kOutCol + shift + tl : tl * kOutRow + col;
+            s_out[at] = f32_to_bf16(acc[nb][i]);
+          }
+      }
     }
-  } else {
-    // value octets: a whole octet is one 16-byte LDS read and one 16-byte
-    // store; octets cut by the tile's ends are written element by element
-    const int64_t o_first = p0 >> 3, o_last = (p0 + nt - 1) >> 3;
-    const int n_oct = (int)(o_last - o_first + 1);
-    uint16_t* dst = out + bh * a.cap * r;
-    for (int i = tid; i < n_oct * r; i += 256) {
-      const int oi = i / r, col = i - oi * r;
-      const int64_t o = o_first + oi;
-      const int first = 8 * oi - shift;                    // tile-local token of element 0
-      uint16_t* q = dst + (o * r + col) * 8;
-      const uint16_t* src = &s_out[col * kOutCol + 8 * oi];
-      if (first >= 0 && first + 8 <= nt) {
-        *reinterpret_cast<u32x4*>(q) = *reinterpret_cast<const u32x4*>(src);
-      } else {
-        for (int e = 0; e < 8; ++e) {
-          const int tl = first + e;
-          if (tl >= 0 && tl < nt) q[e] = src[e];
+    __syncthreads();
+    if (!a.values_layout) {
+      // key rows: each destination row is r/8 aligned 16-byte pieces
+      const int per_row = r / 8;
+      uint16_t* dst = out + (bh * a.cap + p0) * r;
+      for (int i = tid; i < nt * per_row; i += 256) {
+        const int tl = i / per_row, c = (i - tl * per_row) * 8;
+        *reinterpret_cast<u32x4*>(dst + (int64_t)tl * r + c) = *reinterpret_cast<const u32x4*>(&s_out[tl * kOutRow + c]);
+      }
+    } else {
+      // value octets: a whole octet is one 16-byte LDS read and one 16-byte
+      // store; octets cut by the tile's ends are written element by element
+      const int64_t o_first = p0 >> 3, o_last = (p0 + nt - 1) >> 3;
+      const int n_oct = (int)(o_last - o_first + 1);
+      uint16_t* dst = out + bh * a.cap * r;
+      for (int i = tid; i < n_oct * r; i += 256) {
+        const int oi = i / r, col = i - oi * r;
+        const int64_t o = o_first + oi;
+        const int first = 8 * oi - shift;                  // tile-local token of element 0
+        uint16_t* q = dst + (o * r + col) * 8;
+        const uint16_t* src = &s_out[col * kOutCol + 8 * oi];
+        if (first >= 0 && first + 8 <= nt) {
+          *reinterpret_cast<u32x4*>(q) = *reinterpret_cast<const u32x4*>(src);
+        } else {
+          for (int e = 0; e < 8; ++e) {
+            const int tl = first + e;
+            if (tl >= 0 && tl < nt) q[e] = src[e];
+          }
         }
       }
     }
+    __syncthreads();   // s_out is rewritten by the next tile
+#pragma unroll
+    for (int u = 0; u < kSubs; ++u)
+#pragma unroll
+      for (int c = 0; c < D / 32; ++c) xa[u][c] = xb[u][c];
   }
 }
 
@@ -238,7 +252,13 @@ __global__ __launch_bounds__(256) void compress_f32_kernel(CompressArgs a) {
     break;
 
 hipError_t launch_compress_bf16(const CompressArgs& a, hipStream_t s) {
-  const dim3 grid((unsigned)((a.n_tokens + kTile - 1) / kTile), a.hkv, a.batch);
+  // about two resident workgroups per compute unit, each looping over tiles
+  const int64_t tiles = (a.n_tokens + kTile - 1) / kTile;
+  const int64_t units = (int64_t)a.hkv * a.batch;
+  int64_t per_unit = (512 + units - 1) / units;
+  if (per_unit > tiles) per_unit = tiles;
+  if (per_unit < 1) per_unit = 1;
+  const dim3 grid((unsigned)per_unit, a.hkv, a.batch);
   const int nb = (a.rank + 15) / 16;
   switch (a.d * 16 + nb) {
     LRKV_COMPRESS_CASE(64, 1) LRKV_COMPRESS_CASE(64, 2) LRKV_COMPRESS_CASE(64, 3)

@@ -71,13 +71,13 @@ struct HybridArgs {
   uint8_t* flags; int32_t* overflow;
   int batch, hkv, d, rk, rv;
   int64_t n_tokens, pos, cap, side_cap;
-  uint8_t* ws_flags;     // [B, Hkv, n_tiles * 64]
-  int32_t* ws_counts;    // [B, Hkv, n_tiles] flagged tokens per tile
-  int32_t* ws_offsets;   // [B, Hkv, n_tiles, 2] (low-rank row, side row) of each tile's first token
+  uint8_t* ws_flags;     // [B, Hkv, n_tiles * kHybridTile]
+  int32_t* ws_counts;    // [B, Hkv, n_tiles] flagged tokens per sub-tile
+  int32_t* ws_offsets;   // [B, Hkv, n_tiles, 2] (low-rank row, side row) of each sub-tile's first token
   int n_tiles;
 };
 
-constexpr int kHybridTile = 64;
+constexpr int kHybridTile = 16;   // tokens per hybrid compaction unit (one wave sub-tile)
 hipError_t launch_hybrid_bf16(const HybridArgs& a, hipStream_t s);
 
 }  // namespace lrkv
