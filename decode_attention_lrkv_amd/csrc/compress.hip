@@ -16,7 +16,6 @@ namespace lrkv {
 namespace {
 
 constexpr int kTile = 128;   // tokens per workgroup (bfloat16 path)
-constexpr int kPad = 8;   // LDS row padding (elements) against bank conflicts
 
 __device__ __forceinline__ int64_t coeff_index(int values_layout, int64_t bh, int64_t cap, int r,
                                                int64_t p, int col) {
@@ -35,11 +34,14 @@ __global__ __launch_bounds__(256) void compress_bf16_kernel(CompressArgs a) {
   const int b = blockIdx.z;
   const int r = a.rank;
   const int64_t bh = (int64_t)b * a.hkv + h;
-  __shared__ __attribute__((aligned(16))) uint16_t s_bt[NB * 16][D + kPad];    // basis, transposed
+  // basis, transposed; a pitch of 8 x odd dwords keeps the 16-byte operand reads conflict-free
+  __shared__ __attribute__((aligned(16))) uint16_t s_bt[NB * 16][D + 16];
   // the tile's coefficients: keys as [token][column]; values as [column][slot]
-  // with slot = token + (p0 % 8), so each destination octet is 16 aligned bytes
-  constexpr int kOutRow = NB * 16 + kPad;
-  constexpr int kOutCol = kTile + 8 + kPad;
+  // with slot = token + (p0 % 8), so each destination octet is 16 aligned
+  // bytes.  Both row pitches are 2 x odd dwords, which keeps the 2-byte writes
+  // from the matrix-core layout and the 8-byte reads free of bank conflicts.
+  constexpr int kOutRow = NB * 16 + 4;
+  constexpr int kOutCol = kTile + 12;
   constexpr int kOutElems = kTile * kOutRow > NB * 16 * kOutCol ? kTile * kOutRow : NB * 16 * kOutCol;
   __shared__ __attribute__((aligned(16))) uint16_t s_out[kOutElems];
 
@@ -73,10 +75,12 @@ __global__ __launch_bounds__(256) void compress_bf16_kernel(CompressArgs a) {
   }
   __syncthreads();
 
-  // The workgroup loops over tiles blockIdx.x, blockIdx.x + gridDim.x, ... of
-  // this (b, h); the basis above is staged once.  Each wave takes two 16-token
-  // sub-tiles per tile, and the next tile's rows are loaded while the current
-  // tile is multiplied and stored.
+  // The workgroup walks a contiguous run of tiles of this (b, h); the basis
+  // above is staged once.  Contiguous runs keep a value octet cut by a tile
+  // boundary in one workgroup (one L2), so its two partial writes merge
+  // before they reach memory.  Each wave takes two 16-token sub-tiles per
+  // tile, and the next tile's rows are loaded while the current tile is
+  // multiplied and stored.
   constexpr int kSubs = kTile / 16 / 4;
   const int64_t n_tiles = (a.n_tokens + kTile - 1) / kTile;
   auto load_tile = [&](u32x4 (&xa)[kSubs][D / 32], int64_t tile) {
@@ -92,11 +96,13 @@ __global__ __launch_bounds__(256) void compress_bf16_kernel(CompressArgs a) {
   };
   uint16_t* out = static_cast<uint16_t*>(a.coeff);
   u32x4 xa[kSubs][D / 32], xb[kSubs][D / 32];
-  int64_t tile = blockIdx.x;
-  if (tile < n_tiles) load_tile(xa, tile);
-  for (; tile < n_tiles; tile += gridDim.x) {
-    const int64_t next = tile + gridDim.x;
-    if (next < n_tiles) load_tile(xb, next);
+  const int64_t per_wg = (n_tiles + gridDim.x - 1) / gridDim.x;
+  int64_t tile = blockIdx.x * per_wg;
+  const int64_t tile_end = tile + per_wg < n_tiles ? tile + per_wg : n_tiles;
+  if (tile < tile_end) load_tile(xa, tile);
+  for (; tile < tile_end; ++tile) {
+    const int64_t next = tile + 1;
+    if (next < tile_end) load_tile(xb, next);
     const int64_t t_base = tile * kTile;
     const int64_t left = a.n_tokens - t_base;
     const int nt = left < kTile ? (int)left : kTile;
@@ -134,7 +140,9 @@ __global__ __launch_bounds__(256) void compress_bf16_kernel(CompressArgs a) {
       uint16_t* dst = out + (bh * a.cap + p0) * r;
       for (int i = tid; i < nt * per_row; i += 256) {
         const int tl = i / per_row, c = (i - tl * per_row) * 8;
-        *reinterpret_cast<u32x4*>(dst + (int64_t)tl * r + c) = *reinterpret_cast<const u32x4*>(&s_out[tl * kOutRow + c]);
+        const uint2* src = reinterpret_cast<const uint2*>(&s_out[tl * kOutRow + c]);
+        const uint2 lo = src[0], hi = src[1];
+        *reinterpret_cast<u32x4*>(dst + (int64_t)tl * r + c) = u32x4{lo.x, lo.y, hi.x, hi.y};
       }
     } else {
       // value octets: a whole octet is one 16-byte LDS read and one 16-byte
@@ -149,7 +157,8 @@ __global__ __launch_bounds__(256) void compress_bf16_kernel(CompressArgs a) {
         uint16_t* q = dst + (o * r + col) * 8;
         const uint16_t* src = &s_out[col * kOutCol + 8 * oi];
         if (first >= 0 && first + 8 <= nt) {
-          *reinterpret_cast<u32x4*>(q) = *reinterpret_cast<const u32x4*>(src);
+          const uint2 lo = reinterpret_cast<const uint2*>(src)[0], hi = reinterpret_cast<const uint2*>(src)[1];
+          *reinterpret_cast<u32x4*>(q) = u32x4{lo.x, lo.y, hi.x, hi.y};
         } else {
           for (int e = 0; e < 8; ++e) {
             const int tl = first + e;

@@ -27,15 +27,6 @@ namespace lrkv {
 namespace {
 
 constexpr int kWaves = 4;
-constexpr uint32_t kOob = 0x80000000u;   // a buffer offset past any valid range
-
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
-}
-
-__device__ __forceinline__ u32x4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t voff) {
-  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, 0, 0));
-}
 
 template <typename T>
 __device__ __forceinline__ float load_f(const T* p, int64_t i);
@@ -62,7 +53,7 @@ __device__ __forceinline__ void store_f<float>(float* p, int64_t i, float v) { p
 // and written as this workgroup's partial.
 // For bfloat16, s_stage must hold d x (rv + 8) elements; it may alias s_acc.
 template <typename T>
-__device__ void workgroup_partial(const SplitArgs& a, int b, int h, const float* s_acc, int acc_ld,
+__device__ void workgroup_partial(const SplitArgs& a, int b, int h, int part, const float* s_acc, int acc_ld,
                                   const float (*s_ml)[8][2], T* s_stage, float* s_merged) {
   const int tid = threadIdx.x;
   const int g = a.g, rv = a.rv, d = a.d;
@@ -109,7 +100,6 @@ __device__ void workgroup_partial(const SplitArgs& a, int b, int h, const float*
   }
   __syncthreads();   // s_acc may share memory with s_stage
   const int64_t row0 = (int64_t)b * a.hq + (int64_t)h * g;
-  const int part = blockIdx.x;
   float* po = a.part_o;
   if (lift) {
     if (kStage) {
@@ -145,6 +135,8 @@ __device__ void workgroup_partial(const SplitArgs& a, int b, int h, const float*
 // ----------------------------------------------------------------------------
 // KC: 32-wide k chunks covering r_K;  VB: 16-wide column blocks covering r_V.
 // FOLD false: keys are full-rank rows (hybrid side list), q' = q * scale.
+// DB: double-buffer the chunks in registers (false where the operands are too
+// wide for two waves per SIMD).
 //
 // Each chunk is read through buffer resources based at the chunk and sized to
 // its valid tokens: rows past the context, and lanes pointed past the end on
@@ -157,8 +149,18 @@ struct Chunk {
   u32x4 v[VB];
 };
 
-template <int KC, int VB, bool FOLD>
-__device__ __forceinline__ void split_bf16_body(const SplitArgs& a) {
+// LDS of one attention workgroup: the prologue's B_K, the waves' accumulator
+// rows and the epilogue's B_V share `raw`.
+struct SplitSmem {
+  static constexpr int kRawBytes = 128 * (128 + 8) * 2;   // >= kWaves * 16 * 128 * 4
+  __attribute__((aligned(16))) unsigned char raw[kRawBytes];
+  float q[8 * 128];
+  float qf[8 * 128];
+  float ml[kWaves][8][2];
+};
+
+template <int KC, int VB, bool FOLD, bool DB>
+__device__ __forceinline__ void split_bf16_body(const SplitArgs& a, int wg, SplitSmem& sm) {
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
   const int lane = tid & 63;
@@ -166,20 +168,17 @@ __device__ __forceinline__ void split_bf16_body(const SplitArgs& a) {
   const int grp = lane >> 4;     // k-slot group
   const int h = blockIdx.y;
   const int b = blockIdx.z;
-  const int split = blockIdx.x * kWaves + wave;
+  const int split = wg * kWaves + wave;
   const int g = a.g;
   const int rk = a.rk, rv = a.rv, d = a.d;
   const int64_t bh = (int64_t)b * a.hkv + h;
 
-  // the prologue's B_K, the waves' accumulator rows and the epilogue's B_V share LDS
-  constexpr int kStageBytes = 128 * (128 + 8) * 2;
-  constexpr int kAccBytes = kWaves * 16 * VB * 16 * 4;
-  __shared__ __attribute__((aligned(16))) unsigned char s_raw[kStageBytes > kAccBytes ? kStageBytes : kAccBytes];
-  __shared__ float s_q[8 * 128];
-  __shared__ float s_qf[8 * 128];
-  __shared__ float s_ml[kWaves][8][2];
-  uint16_t* s_bk = reinterpret_cast<uint16_t*>(s_raw);
-  float (*s_acc)[16][VB * 16] = reinterpret_cast<float (*)[16][VB * 16]>(s_raw);
+  static_assert(kWaves * 16 * VB * 16 * 4 <= SplitSmem::kRawBytes, "accumulator rows exceed LDS");
+  float* s_q = sm.q;
+  float* s_qf = sm.qf;
+  float (*s_ml)[8][2] = sm.ml;
+  uint16_t* s_bk = reinterpret_cast<uint16_t*>(sm.raw);
+  float (*s_acc)[16][VB * 16] = reinterpret_cast<float (*)[16][VB * 16]>(sm.raw);
 
   int64_t n_end = a.n_static;
   if (a.n_dev) {
@@ -369,14 +368,22 @@ __device__ __forceinline__ void split_bf16_body(const SplitArgs& a) {
     }
   };
 
-  Chunk<KC, VB> ca, cb;
-  if (c_begin < c_end) load(ca, c_begin);
-  for (int64_t chunk = c_begin; chunk < c_end; chunk += 2) {
-    if (chunk + 1 < c_end) load(cb, chunk + 1);
-    process(ca, chunk);
-    if (chunk + 1 >= c_end) break;
-    if (chunk + 2 < c_end) load(ca, chunk + 2);
-    process(cb, chunk + 1);
+  if (DB) {
+    Chunk<KC, VB> ca, cb;
+    if (c_begin < c_end) load(ca, c_begin);
+    for (int64_t chunk = c_begin; chunk < c_end; chunk += 2) {
+      if (chunk + 1 < c_end) load(cb, chunk + 1);
+      process(ca, chunk);
+      if (chunk + 1 >= c_end) break;
+      if (chunk + 2 < c_end) load(ca, chunk + 2);
+      process(cb, chunk + 1);
+    }
+  } else {
+    Chunk<KC, VB> ca;
+    for (int64_t chunk = c_begin; chunk < c_end; ++chunk) {
+      load(ca, chunk);
+      process(ca, chunk);
+    }
   }
 
   // --- epilogue: rows j (high part) + rows g + j (low part) are head j
@@ -397,20 +404,31 @@ __device__ __forceinline__ void split_bf16_body(const SplitArgs& a) {
     s_acc[w][j][c] += s_acc[w][g + j][c];
   }
   __syncthreads();
-  workgroup_partial<uint16_t>(a, b, h, &s_acc[0][0][0], VB * 16, s_ml, reinterpret_cast<uint16_t*>(s_raw), s_qf);
+  workgroup_partial<uint16_t>(a, b, h, wg, &s_acc[0][0][0], VB * 16, s_ml, reinterpret_cast<uint16_t*>(sm.raw), s_qf);
 }
+
+// Chunks are double-buffered unless that no longer fits two waves per SIMD.
+template <int KC, int VB>
+constexpr bool kDoubleBuffer = 2 * KC + VB < 16;
 
 // Low-rank keys: two waves per SIMD (one round of workgroups fills the chip).
 template <int KC, int VB>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void split_bf16_kernel(SplitArgs a) {
-  split_bf16_body<KC, VB, true>(a);
+  __shared__ SplitSmem sm;
+  split_bf16_body<KC, VB, true, kDoubleBuffer<KC, VB>>(a, blockIdx.x, sm);
 }
 
-// Full-rank side-list keys (r = d): the wider operands need one wave per SIMD.
-template <int KC, int VB>
-__global__ __launch_bounds__(256) void split_bf16_side_kernel(SplitArgs a) {
-  split_bf16_body<KC, VB, false>(a);
+// Hybrid cache in one launch: the first wg_lr workgroups of each (b, kv head)
+// attend the low-rank rows, the others the full-rank side list (r = d, no
+// fold and no lift, single-buffered so that both fit two waves per SIMD).
+// Both kinds write partials that the merge kernel combines.
+template <int KC, int VB, int SKC, int SVB>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void split_bf16_hybrid_kernel(SplitArgs lr, SplitArgs side, int wg_lr) {
+  __shared__ SplitSmem sm;
+  if ((int)blockIdx.x < wg_lr) split_bf16_body<KC, VB, true, kDoubleBuffer<KC, VB>>(lr, blockIdx.x, sm);
+  else split_bf16_body<SKC, SVB, false, false>(side, blockIdx.x - wg_lr, sm);
 }
 
 // ----------------------------------------------------------------------------
@@ -537,66 +555,76 @@ __global__ __launch_bounds__(256) void split_f32_kernel(SplitArgs a) {
     }
   }
   __syncthreads();
-  workgroup_partial<float>(a, b, h, &s_acc[0][0][0], 128, s_ml, nullptr, s_qf);
+  workgroup_partial<float>(a, b, h, blockIdx.x, &s_acc[0][0][0], 128, s_ml, nullptr, s_qf);
 }
 
 // ----------------------------------------------------------------------------
-// merge: one wave per (batch, query head), four rows per workgroup
+// merge: one workgroup per (batch, query head)
 // ----------------------------------------------------------------------------
 //   M = max_s m_s,  w_s = 2^(m_s - M),  L = sum_s w_s l_s,
 //   out = sum_s w_s o_s / L,  lse = (M + log2 L) ln 2
 // over the low-rank partials and, for a hybrid cache, the side-list partials.
+// The partials are spread over the workgroup: thread t adds the float4 column
+// t % (d/4) of partials t / (d/4), t / (d/4) + 256 / (d/4), ...; the column
+// groups are then summed in LDS.
 template <typename T>
 __global__ __launch_bounds__(256) void merge_kernel(MergeArgs a) {
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int64_t row = (int64_t)blockIdx.x * 4 + wave;
-  if (row >= (int64_t)a.batch * a.hq) return;
-  const int S = a.n_parts, SS = a.n_side_parts, d = a.d;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int64_t row = blockIdx.x;
+  const int S = a.n_parts, SS = a.n_side_parts, n = S + SS, d = a.d;
   const float* ml = a.part_ml + row * S * 2;
   const float* sml = SS ? a.side_ml + row * SS * 2 : nullptr;
+  auto mls = [&](int s) { return s < S ? ml + 2 * s : sml + 2 * (s - S); };
+  __shared__ float s_red[kWaves][2];
+  __shared__ __attribute__((aligned(16))) float s_o[256 * 4];
 
   float m = -INFINITY;
-  for (int s = lane; s < S; s += 64) m = fmaxf(m, ml[2 * s]);
-  for (int s = lane; s < SS; s += 64) m = fmaxf(m, sml[2 * s]);
-  const float M = wave_max(m);
+  for (int s = tid; s < n; s += 256) m = fmaxf(m, mls(s)[0]);
+  m = wave_max(m);
+  if (lane == 0) s_red[wave][0] = m;
+  __syncthreads();
+  const float M = fmaxf(fmaxf(s_red[0][0], s_red[1][0]), fmaxf(s_red[2][0], s_red[3][0]));
   float l = 0.f;
-  for (int s = lane; s < S; s += 64) l += ml[2 * s] == -INFINITY ? 0.f : exp2_fast(ml[2 * s] - M) * ml[2 * s + 1];
-  for (int s = lane; s < SS; s += 64)
-    l += sml[2 * s] == -INFINITY ? 0.f : exp2_fast(sml[2 * s] - M) * sml[2 * s + 1];
-  const float L = wave_sum(l);
-  const float inv = L > 0.f ? 1.f / L : 0.f;
+  for (int s = tid; s < n; s += 256) {
+    const float* p = mls(s);
+    l += p[0] == -INFINITY ? 0.f : exp2_fast(p[0] - M) * p[1];
+  }
+  l = wave_sum(l);
+  if (lane == 0) s_red[wave][1] = l;
 
-  // each lane owns head_dim elements lane and lane + 64; eight partials in flight
-  float o[2] = {0.f, 0.f};
-  for (int pass = 0; pass < 2; ++pass) {
-    const int n = pass ? SS : S;
-    const float* pm = pass ? sml : ml;
-    const float* po = pass ? a.side_o + row * (int64_t)SS * d : a.part_o + row * (int64_t)S * d;
-    for (int s0 = 0; s0 < n; s0 += 8) {
-      float v[8][2], wt[8];
+  const int cols = d / 4, groups = 256 / cols;
+  const int col = tid % cols, grp = tid / cols;
+  f32x4 o = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int s0 = grp; s0 < n; s0 += 4 * groups) {
+    f32x4 v[4];
+    float wt[4];
 #pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const bool ok = s0 + u < n;
-        const float ms = ok ? pm[2 * (s0 + u)] : -INFINITY;
+    for (int u = 0; u < 4; ++u) {
+      const int s = s0 + u * groups;
+      wt[u] = 0.f;
+      v[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+      if (s < n) {
+        const float ms = mls(s)[0];
         wt[u] = ms == -INFINITY ? 0.f : exp2_fast(ms - M);
-#pragma unroll
-        for (int e = 0; e < 2; ++e) {
-          const int dd = lane + 64 * e;
-          v[u][e] = (ok && dd < d) ? po[(int64_t)(s0 + u) * d + dd] : 0.f;
-        }
+        const float* po = s < S ? a.part_o + (row * S + s) * d : a.side_o + (row * SS + (s - S)) * d;
+        v[u] = *reinterpret_cast<const f32x4*>(po + 4 * col);
       }
-#pragma unroll
-      for (int u = 0; u < 8; ++u)
-#pragma unroll
-        for (int e = 0; e < 2; ++e) o[e] = fmaf(wt[u], v[u][e], o[e]);
     }
-  }
 #pragma unroll
-  for (int e = 0; e < 2; ++e) {
-    const int dd = lane + 64 * e;
-    if (dd < d) store_f(static_cast<T*>(a.out), row * d + dd, o[e] * inv);
+    for (int u = 0; u < 4; ++u)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) o[e] = fmaf(wt[u], v[u][e], o[e]);
   }
-  if (lane == 0 && a.lse) a.lse[row] = L > 0.f ? (M + __log2f(L)) * kLn2 : -INFINITY;
+  *reinterpret_cast<f32x4*>(&s_o[4 * tid]) = o;
+  __syncthreads();
+  const float L = s_red[0][1] + s_red[1][1] + s_red[2][1] + s_red[3][1];
+  const float inv = L > 0.f ? 1.f / L : 0.f;
+  if (tid < d) {
+    float acc = 0.f;
+    for (int gi = 0; gi < groups; ++gi) acc += s_o[4 * (gi * cols) + tid];
+    store_f(static_cast<T*>(a.out), row * d + tid, acc * inv);
+  }
+  if (tid == 0 && a.lse) a.lse[row] = L > 0.f ? (M + __log2f(L)) * kLn2 : -INFINITY;
 }
 
 }  // namespace
@@ -609,11 +637,7 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeArgs a) {
 hipError_t launch_split_bf16(const SplitArgs& a, hipStream_t s) {
   const dim3 grid((a.n_splits + kWaves - 1) / kWaves, a.hkv, a.batch);
   const int kc = (a.rk + 31) / 32, vb = (a.rv + 15) / 16;
-  if (a.basis_k == nullptr) {
-    if (a.d == 128) hipLaunchKernelGGL((split_bf16_side_kernel<4, 8>), grid, dim3(256), 0, s, a);
-    else hipLaunchKernelGGL((split_bf16_side_kernel<2, 4>), grid, dim3(256), 0, s, a);
-    return hipGetLastError();
-  }
+  if (a.basis_k == nullptr || a.basis_v == nullptr) return hipErrorInvalidValue;
   switch (kc * 16 + vb) {
     LRKV_SPLIT_CASE(1, 1) LRKV_SPLIT_CASE(1, 2) LRKV_SPLIT_CASE(1, 3) LRKV_SPLIT_CASE(1, 4)
     LRKV_SPLIT_CASE(1, 5) LRKV_SPLIT_CASE(1, 6) LRKV_SPLIT_CASE(1, 7) LRKV_SPLIT_CASE(1, 8)
@@ -629,6 +653,43 @@ hipError_t launch_split_bf16(const SplitArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
+#define LRKV_HYB_CASE(KC, VB, SKC, SVB)                                                              \
+  case (KC * 16 + VB):                                                                               \
+    hipLaunchKernelGGL((split_bf16_hybrid_kernel<KC, VB, SKC, SVB>), grid, dim3(256), 0, s, lr, side, wg_lr); \
+    break;
+
+hipError_t launch_split_bf16_hybrid(const SplitArgs& lr, const SplitArgs& side, hipStream_t s) {
+  const int wg_lr = (lr.n_splits + kWaves - 1) / kWaves;
+  const int wg_side = (side.n_splits + kWaves - 1) / kWaves;
+  const dim3 grid(wg_lr + wg_side, lr.hkv, lr.batch);
+  const int kc = (lr.rk + 31) / 32, vb = (lr.rv + 15) / 16;
+  if (lr.basis_k == nullptr || lr.basis_v == nullptr || side.basis_k != nullptr || side.basis_v != nullptr ||
+      side.rk != lr.d || side.rv != lr.d)
+    return hipErrorInvalidValue;
+  if (lr.d == 64) {
+    switch (kc * 16 + vb) {
+      LRKV_HYB_CASE(1, 1, 2, 4) LRKV_HYB_CASE(1, 2, 2, 4) LRKV_HYB_CASE(1, 3, 2, 4) LRKV_HYB_CASE(1, 4, 2, 4)
+      LRKV_HYB_CASE(2, 1, 2, 4) LRKV_HYB_CASE(2, 2, 2, 4) LRKV_HYB_CASE(2, 3, 2, 4) LRKV_HYB_CASE(2, 4, 2, 4)
+      default:
+        return hipErrorInvalidValue;
+    }
+  } else {
+    switch (kc * 16 + vb) {
+      LRKV_HYB_CASE(1, 1, 4, 8) LRKV_HYB_CASE(1, 2, 4, 8) LRKV_HYB_CASE(1, 3, 4, 8) LRKV_HYB_CASE(1, 4, 4, 8)
+      LRKV_HYB_CASE(1, 5, 4, 8) LRKV_HYB_CASE(1, 6, 4, 8) LRKV_HYB_CASE(1, 7, 4, 8) LRKV_HYB_CASE(1, 8, 4, 8)
+      LRKV_HYB_CASE(2, 1, 4, 8) LRKV_HYB_CASE(2, 2, 4, 8) LRKV_HYB_CASE(2, 3, 4, 8) LRKV_HYB_CASE(2, 4, 4, 8)
+      LRKV_HYB_CASE(2, 5, 4, 8) LRKV_HYB_CASE(2, 6, 4, 8) LRKV_HYB_CASE(2, 7, 4, 8) LRKV_HYB_CASE(2, 8, 4, 8)
+      LRKV_HYB_CASE(3, 1, 4, 8) LRKV_HYB_CASE(3, 2, 4, 8) LRKV_HYB_CASE(3, 3, 4, 8) LRKV_HYB_CASE(3, 4, 4, 8)
+      LRKV_HYB_CASE(3, 5, 4, 8) LRKV_HYB_CASE(3, 6, 4, 8) LRKV_HYB_CASE(3, 7, 4, 8) LRKV_HYB_CASE(3, 8, 4, 8)
+      LRKV_HYB_CASE(4, 1, 4, 8) LRKV_HYB_CASE(4, 2, 4, 8) LRKV_HYB_CASE(4, 3, 4, 8) LRKV_HYB_CASE(4, 4, 4, 8)
+      LRKV_HYB_CASE(4, 5, 4, 8) LRKV_HYB_CASE(4, 6, 4, 8) LRKV_HYB_CASE(4, 7, 4, 8) LRKV_HYB_CASE(4, 8, 4, 8)
+      default:
+        return hipErrorInvalidValue;
+    }
+  }
+  return hipGetLastError();
+}
+
 hipError_t launch_split_f32(const SplitArgs& a, hipStream_t s) {
   const dim3 grid((a.n_splits + kWaves - 1) / kWaves, a.hkv, a.batch);
   hipLaunchKernelGGL(split_f32_kernel, grid, dim3(256), 0, s, a);
@@ -636,7 +697,7 @@ hipError_t launch_split_f32(const SplitArgs& a, hipStream_t s) {
 }
 
 hipError_t launch_merge(const MergeArgs& a, bool bf16, hipStream_t s) {
-  const dim3 grid((unsigned)(((int64_t)a.batch * a.hq + 3) / 4));
+  const dim3 grid((unsigned)((int64_t)a.batch * a.hq));
   if (bf16) hipLaunchKernelGGL(merge_kernel<uint16_t>, grid, dim3(256), 0, s, a);
   else hipLaunchKernelGGL(merge_kernel<float>, grid, dim3(256), 0, s, a);
   return hipGetLastError();

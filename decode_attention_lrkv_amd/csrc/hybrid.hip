@@ -3,17 +3,25 @@
 // are appended to the low-rank caches (gfx950).
 //
 // Three launches, all deterministic (no order-dependent atomics):
-//   select  c = round(x B) and x_hat = c B^T on the matrix cores, then
+//   select  c = x B and x_hat = round(c) B^T on the matrix cores, then
 //           ||x - x_hat||^2 > tau^2 ||x||^2 in float32, for K and for V; a token
 //           is flagged when either is.  Per 16-token sub-tile: flags and count.
+//           The squared residual is evaluated as ||x||^2 - 2 <c, round(c)> +
+//           ||x_hat||^2 (equal to it in exact arithmetic, since <x, x_hat> =
+//           <x B, round(c)>), which keeps every operand in registers.
 //   scan    per (b, kv head): exclusive prefix of the sub-tile counts gives every
 //           sub-tile's first low-rank row and first side-list row; the counters
 //           advance (clamped at the capacities, with an overflow flag).
 //   write   recompute c; each token goes to its sub-tile's offset plus its rank
 //           among the sub-tile's tokens of the same kind (a wave ballot).
-// Select and write are persistent: a workgroup stages both bases in LDS once
-// and its waves walk 16-token sub-tiles of one (b, kv head), each wave
-// loading the next sub-tile's rows while it works on the current one.
+// Select and write are persistent: a workgroup stages the bases in LDS once
+// (sized to the ranks) and each of its waves walks a contiguous run of
+// 16-token sub-tiles of one (b, kv head), loading the next sub-tile's key and
+// value rows (and, in write, its flags and offsets) while it works on the
+// current one.  Contiguous runs keep the partial writes of a value octet or a
+// flag line that straddles two sub-tiles inside one L2.
+#include <type_traits>
+
 #include "lrkv_device.h"
 #include "lrkv_internal.h"
 
@@ -21,18 +29,44 @@ namespace lrkv {
 
 namespace {
 
-constexpr int kPad = 8;
-constexpr int kMaxRank = 128;
-constexpr int kWavesH = 8;                 // waves per hybrid workgroup
+constexpr int kWavesH = 4;                 // waves per hybrid workgroup
 constexpr int kThreadsH = 64 * kWavesH;
 
-// Both bases of kv head h, transposed ([coefficient][dim]); rows >= rank are zero.
+// LDS layout of one workgroup, in bfloat16 elements: both bases transposed
+// ([coefficient][dim], 16 NB rows each) and, for select, as stored ([dim]
+// [coefficient], 32 ceil(NB/2) columns each); rows and columns past a rank
+// are zero.  Row pitches are chosen so that the per-item reads are free of
+// bank conflicts on gfx950: the transposed basis is read 16 bytes per lane
+// from 16 consecutive rows (pitch of 8 x odd dwords), the natural one 8 bytes
+// per lane (pitch of 2 x odd dwords).
+struct HybridLds {
+  int rows, pitch_t, cols_n, pitch_n;
+  int off_t[2], off_n[2];
+  int elems_write, elems_select;
+};
+
+__host__ __device__ inline HybridLds hybrid_lds(int d, int nb) {
+  HybridLds L;
+  L.rows = 16 * nb;
+  L.pitch_t = d + 16;
+  L.cols_n = 32 * ((nb + 1) / 2);
+  L.pitch_n = L.cols_n + 4;
+  L.off_t[0] = 0;
+  L.off_t[1] = L.rows * L.pitch_t;
+  L.elems_write = 2 * L.rows * L.pitch_t;
+  L.off_n[0] = L.elems_write;
+  L.off_n[1] = L.elems_write + d * L.pitch_n;
+  L.elems_select = L.elems_write + 2 * d * L.pitch_n;
+  return L;
+}
+
 template <int D>
-__device__ void stage_bases(const HybridArgs& a, int h, uint16_t (*s_bt)[kMaxRank][D + kPad]) {
+__device__ void stage_transposed(const HybridArgs& a, const HybridLds& L, int h, uint16_t* smem) {
   const int tid = threadIdx.x;
   for (int kind = 0; kind < 2; ++kind) {
     const int r = kind ? a.rv : a.rk;
     const uint16_t* bs = static_cast<const uint16_t*>(kind ? a.bv : a.bk) + (int64_t)h * D * r;
+    uint16_t* st = smem + L.off_t[kind];
     const int n = D * (r / 8);
     // piece i = (8-column group, head_dim row): consecutive lanes take consecutive
     // rows, so the transposed 2-byte LDS writes land in distinct banks
@@ -50,216 +84,390 @@ __device__ void stage_bases(const HybridArgs& a, int h, uint16_t (*s_bt)[kMaxRan
           const int dd = i % D, c = (i / D) * 8;
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
-            s_bt[kind][c + 2 * e][dd] = (uint16_t)(w[u][e] & 0xFFFFu);
-            s_bt[kind][c + 2 * e + 1][dd] = (uint16_t)(w[u][e] >> 16);
+            st[(c + 2 * e) * L.pitch_t + dd] = (uint16_t)(w[u][e] & 0xFFFFu);
+            st[(c + 2 * e + 1) * L.pitch_t + dd] = (uint16_t)(w[u][e] >> 16);
           }
         }
       }
     }
-    for (int i = tid; i < (kMaxRank - r) * D; i += kThreadsH) s_bt[kind][r + i / D][i % D] = 0;
+    for (int i = tid; i < (L.rows - r) * D; i += kThreadsH) st[(r + i / D) * L.pitch_t + i % D] = 0;
   }
 }
 
-// Rows of one 16-token sub-tile as matrix-core A operands: lane (n16, grp)
-// holds token n16's elements 32c + 8 grp .. +7.
 template <int D>
-__device__ __forceinline__ void load_rows(const HybridArgs& a, int b, int h, int kind, int64_t sub, int n16,
-                                          int grp, u32x4 (&xa)[D / 32]) {
-  const int64_t tok = sub * kHybridTile + n16;
-  const bool valid = tok < a.n_tokens;
-  const uint16_t* x = static_cast<const uint16_t*>(kind ? a.v : a.k) + ((b * a.n_tokens + tok) * a.hkv + h) * D;
-#pragma unroll
-  for (int c = 0; c < D / 32; ++c)
-    xa[c] = valid ? *reinterpret_cast<const u32x4*>(x + 32 * c + 8 * grp) : u32x4{0u, 0u, 0u, 0u};
+__device__ void stage_natural(const HybridArgs& a, const HybridLds& L, int h, uint16_t* smem) {
+  const int tid = threadIdx.x;
+  for (int kind = 0; kind < 2; ++kind) {
+    const int r = kind ? a.rv : a.rk;
+    const uint16_t* bs = static_cast<const uint16_t*>(kind ? a.bv : a.bk) + (int64_t)h * D * r;
+    uint16_t* sn = smem + L.off_n[kind];
+    const int pieces = L.cols_n / 8;   // 8-coefficient pieces per row
+    for (int i = tid; i < D * pieces; i += kThreadsH) {
+      const int row = i / pieces, c = (i % pieces) * 8;
+      const u32x4 w = c < r ? *reinterpret_cast<const u32x4*>(bs + row * r + c) : u32x4{0u, 0u, 0u, 0u};
+      uint32_t* dst = reinterpret_cast<uint32_t*>(sn + row * L.pitch_n + c);   // 8-byte aligned
+      *reinterpret_cast<uint2*>(dst) = uint2{w[0], w[1]};
+      *reinterpret_cast<uint2*>(dst + 2) = uint2{w[2], w[3]};
+    }
+  }
 }
 
-// c = x B for the sub-tile: acc[nb] lane (n16, grp) register i is coefficient
-// 16 nb + n16 of token 4 grp + i.
+// Rows of one 16-token sub-tile as matrix-core operands: lane (n16, grp)
+// holds token n16's elements 32c + 8 grp .. +7.  Tokens past the end, and
+// every lane when `live` is false, read zero (buffer range), so the number
+// of loads never depends on the data.
 template <int D>
-__device__ __forceinline__ void coeffs(const u32x4 (&xa)[D / 32], const uint16_t (*bt)[D + kPad], int nbr, int n16,
-                                       int grp, f32x4 (&acc)[8]) {
+__device__ __forceinline__ void load_rows(const HybridArgs& a, int b, int h, int kind, int64_t sub, bool live,
+                                          int n16, int grp, u32x4 (&xa)[D / 32]) {
+  const int64_t t0 = sub * kHybridTile;
+  const int64_t left = a.n_tokens - t0;
+  const int nt = left < kHybridTile ? (int)left : kHybridTile;
+  const uint16_t* x = static_cast<const uint16_t*>(kind ? a.v : a.k) + ((b * a.n_tokens + t0) * a.hkv + h) * D;
+  const uint32_t bytes = live && nt > 0 ? (uint32_t)(((nt - 1) * a.hkv + 1) * D * 2) : 0u;
+  const __amdgpu_buffer_rsrc_t rs = make_rsrc(x, bytes);
+  const uint32_t voff = (uint32_t)((n16 * a.hkv * D + 8 * grp) * 2);
 #pragma unroll
-  for (int nb = 0; nb < 8; ++nb) acc[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int c = 0; c < D / 32; ++c) xa[c] = buf_load16(rs, voff + 64 * c);
+}
+
+// c^T = B^T x^T for the sub-tile (transposed basis as the row operand, the
+// token rows as loaded as the column operand): acc[nb] lane (n16, grp)
+// register i is coefficient 16 nb + 4 grp + i of token n16.
+template <int D, int NB>
+__device__ __forceinline__ void coeffs_t(const u32x4 (&xa)[D / 32], const uint16_t* bt, int pitch, int n16, int grp,
+                                         f32x4 (&acc)[NB]) {
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) acc[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int c = 0; c < D / 32; ++c) {
     const int k = 32 * c + 8 * grp;
 #pragma unroll
-    for (int nb = 0; nb < 8; ++nb)
-      if (nb < nbr) acc[nb] = mfma_16x16x32(xa[c], *reinterpret_cast<const u32x4*>(&bt[16 * nb + n16][k]), acc[nb]);
+    for (int nb = 0; nb < NB; ++nb)
+      acc[nb] = mfma_16x16x32(*reinterpret_cast<const u32x4*>(bt + (16 * nb + n16) * pitch + k), xa[c], acc[nb]);
   }
 }
 
-template <int D>
-__global__ __launch_bounds__(kThreadsH) void hybrid_select_kernel(HybridArgs a) {
+// Two waves per SIMD: the LDS of two workgroups (both bases twice) fills a compute unit.
+template <int D, int NB>
+__global__ __launch_bounds__(kThreadsH) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void hybrid_select_kernel(HybridArgs a) {
+  extern __shared__ __attribute__((aligned(16))) uint16_t smem[];
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int n16 = lane & 15, grp = lane >> 4;
   const int h = blockIdx.y, b = blockIdx.z;
   const int64_t bh = (int64_t)b * a.hkv + h;
   const int64_t n_slots = (int64_t)a.n_tiles * kHybridTile;
+  const HybridLds L = hybrid_lds(D, NB);
+  constexpr int KK = (NB + 1) / 2;
 
-  __shared__ __attribute__((aligned(16))) uint16_t s_bt[2][kMaxRank][D + kPad];
-  __shared__ __attribute__((aligned(16))) uint16_t s_x[kWavesH][kHybridTile][D + kPad];
-  __shared__ __attribute__((aligned(16))) uint16_t s_c[kWavesH][kHybridTile][kMaxRank + kPad];
-  stage_bases<D>(a, h, s_bt);
+  stage_transposed<D>(a, L, h, smem);
+  stage_natural<D>(a, L, h, smem);
   __syncthreads();
 
-  const int64_t stride = (int64_t)gridDim.x * kWavesH;
-  int64_t sub = (int64_t)blockIdx.x * kWavesH + wave;
-  u32x4 xa[D / 32], xn[D / 32];
-  if (sub < a.n_tiles) load_rows<D>(a, b, h, 0, sub, n16, grp, xa);
-  for (; sub < a.n_tiles; sub += stride) {
-    bool sel[4] = {false, false, false, false};
-    for (int kind = 0; kind < 2; ++kind) {
-      // rows of the next item: this sub-tile's values, or the next sub-tile's keys
-      if (kind == 0) load_rows<D>(a, b, h, 1, sub, n16, grp, xn);
-      else if (sub + stride < a.n_tiles) load_rows<D>(a, b, h, 0, sub + stride, n16, grp, xn);
-      const int r = kind ? a.rv : a.rk;
-      const int nbr = (r + 15) / 16, kc2 = (r + 31) / 32;
-      const uint16_t (*bt)[D + kPad] = s_bt[kind];
+  const int64_t n_waves = (int64_t)gridDim.x * kWavesH;
+  const int64_t per_wave = (a.n_tiles + n_waves - 1) / n_waves;
+  int64_t sub = ((int64_t)blockIdx.x * kWavesH + wave) * per_wave;
+  const int64_t sub_end = sub + per_wave < a.n_tiles ? sub + per_wave : a.n_tiles;
+  const __amdgpu_buffer_rsrc_t rs_wsf = make_rsrc(a.ws_flags + bh * n_slots, (uint32_t)n_slots);
+  const __amdgpu_buffer_rsrc_t rs_flags =
+      make_rsrc(a.flags ? a.flags + bh * a.n_tokens : a.ws_flags, a.flags ? (uint32_t)a.n_tokens : 0u);
+  const __amdgpu_buffer_rsrc_t rs_cnt = make_rsrc(a.ws_counts + bh * a.n_tiles, (uint32_t)(a.n_tiles * 4));
+
+  // ||x - x_hat||^2 > tau^2 ||x||^2 for token n16 of the sub-tile, one kind
+  auto flagged = [&](const u32x4 (&xa)[D / 32], int kind) -> bool {
+    f32x4 acc1[NB];
+    coeffs_t<D, NB>(xa, smem + L.off_t[kind], L.pitch_t, n16, grp, acc1);
+    // stored coefficients round(c), packed as the column operand of x_hat^T = B round(c)^T:
+    // k-slots 0..3 of block kk are coefficients 32 kk + 4 grp + 0..3, slots 4..7 are 32 kk + 16 + 4 grp + 0..3
+    float cc = 0.f;
+    uint32_t cw[2 * KK][2];
 #pragma unroll
-      for (int c = 0; c < D / 32; ++c) *reinterpret_cast<u32x4*>(&s_x[wave][n16][32 * c + 8 * grp]) = xa[c];
-      f32x4 acc1[8];
-      coeffs<D>(xa, bt, nbr, n16, grp, acc1);
-      // the stored coefficients, zero past the rank up to the reconstruction's k range
-#pragma unroll
-      for (int nb = 0; nb < 8; ++nb)
-        if (nb < 2 * kc2)
-#pragma unroll
-          for (int i = 0; i < 4; ++i)
-            s_c[wave][4 * grp + i][16 * nb + n16] = nb < nbr ? f32_to_bf16(acc1[nb][i]) : (uint16_t)0;
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-      __builtin_amdgcn_wave_barrier();
-      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-      // x_hat = c B^T one 16-dim block at a time; residual and norm per token
-      float e2[4] = {0.f, 0.f, 0.f, 0.f}, n2[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int db = 0; db < D / 16; ++db) {
-        f32x4 acc2 = f32x4{0.f, 0.f, 0.f, 0.f};
-        for (int c = 0; c < kc2; ++c) {
-          const int k = 32 * c + 8 * grp;
-          const u32x4 ca = *reinterpret_cast<const u32x4*>(&s_c[wave][n16][k]);
-          uint32_t w[4];
-#pragma unroll
-          for (int e = 0; e < 4; ++e)
-            w[e] = (uint32_t)bt[k + 2 * e][16 * db + n16] | ((uint32_t)bt[k + 2 * e + 1][16 * db + n16] << 16);
-          acc2 = mfma_16x16x32(ca, u32x4{w[0], w[1], w[2], w[3]}, acc2);
-        }
+    for (int nb = 0; nb < 2 * KK; ++nb) {
+      uint16_t t[4] = {0, 0, 0, 0};
+      if (nb < NB) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const float xv = bf16_to_f32(s_x[wave][4 * grp + i][16 * db + n16]);
-          const float res = xv - acc2[i];
-          e2[i] = fmaf(res, res, e2[i]);
-          n2[i] = fmaf(xv, xv, n2[i]);
+          t[i] = f32_to_bf16(acc1[nb < NB ? nb : 0][i]);
+          cc = fmaf(acc1[nb < NB ? nb : 0][i], bf16_to_f32(t[i]), cc);
         }
       }
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-#pragma unroll
-        for (int o = 1; o < 16; o <<= 1) {
-          e2[i] += __shfl_xor(e2[i], o);
-          n2[i] += __shfl_xor(n2[i], o);
-        }
-        sel[i] = sel[i] || (e2[i] > a.tau2 * n2[i]);
-      }
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-      __builtin_amdgcn_wave_barrier();   // s_x and s_c are rewritten by the next item
-      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-#pragma unroll
-      for (int c = 0; c < D / 32; ++c) xa[c] = xn[c];
+      cw[nb][0] = (uint32_t)t[0] | ((uint32_t)t[1] << 16);
+      cw[nb][1] = (uint32_t)t[2] | ((uint32_t)t[3] << 16);
     }
-    // lanes (n16 = 0, grp) hold the flags of tokens 4 grp + i
-    int count = 0;
+    __builtin_amdgcn_sched_barrier(0);
+    const uint16_t* bn = smem + L.off_n[kind];
+    float xh2 = 0.f;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int64_t tok = sub * kHybridTile + 4 * grp + i;
-      const bool f = sel[i] && tok < a.n_tokens;
-      if (n16 == 0 && tok < a.n_tokens) {
-        a.ws_flags[bh * n_slots + tok] = (uint8_t)f;
-        if (a.flags) a.flags[bh * a.n_tokens + tok] = (uint8_t)f;
+    for (int db = 0; db < D / 16; ++db) {
+      f32x4 acc2 = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kk = 0; kk < KK; ++kk) {
+        const uint16_t* row = bn + (16 * db + n16) * L.pitch_n + 32 * kk + 4 * grp;
+        const uint2 lo = *reinterpret_cast<const uint2*>(row);
+        const uint2 hi = *reinterpret_cast<const uint2*>(row + 16);
+        acc2 = mfma_16x16x32(u32x4{lo.x, lo.y, hi.x, hi.y},
+                             u32x4{cw[2 * kk][0], cw[2 * kk][1], cw[2 * kk + 1][0], cw[2 * kk + 1][1]}, acc2);
       }
-      count += __popcll(__ballot(n16 == 0 && f));
+      // lane (n16, grp) register i: x_hat of token n16 at dim 16 db + 4 grp + i
+#pragma unroll
+      for (int i = 0; i < 4; ++i) xh2 = fmaf(acc2[i], acc2[i], xh2);
     }
-    if (lane == 0) a.ws_counts[bh * a.n_tiles + sub] = count;
+    float n2 = 0.f;
+#pragma unroll
+    for (int c = 0; c < D / 32; ++c)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float lo = bf16_lo(xa[c][e]), hi = bf16_hi(xa[c][e]);
+        n2 = fmaf(lo, lo, n2);
+        n2 = fmaf(hi, hi, n2);
+      }
+#pragma unroll
+    for (int o = 16; o < 64; o <<= 1) {
+      cc += __shfl_xor(cc, o);
+      xh2 += __shfl_xor(xh2, o);
+      n2 += __shfl_xor(n2, o);
+    }
+    const float e2 = n2 - 2.f * cc + xh2;
+    return e2 > a.tau2 * n2;
+  };
+
+  // keys and values of the current sub-tile; those of the next are in flight meanwhile
+  u32x4 xk[D / 32], xv[D / 32], nk[D / 32], nv[D / 32];
+  if (sub < sub_end) {
+    load_rows<D>(a, b, h, 0, sub, true, n16, grp, xk);
+    load_rows<D>(a, b, h, 1, sub, true, n16, grp, xv);
+  }
+  for (; sub < sub_end; ++sub) {
+    const bool more = sub + 1 < sub_end;
+    load_rows<D>(a, b, h, 0, more ? sub + 1 : sub, more, n16, grp, nk);
+    load_rows<D>(a, b, h, 1, more ? sub + 1 : sub, more, n16, grp, nv);
+    __builtin_amdgcn_sched_barrier(0);   // keep the prefetch ahead and the two kinds apart
+    const bool fk = flagged(xk, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    const bool fv = flagged(xv, 1);
+    __builtin_amdgcn_sched_barrier(0);
+    const int64_t tok = sub * kHybridTile + n16;
+    const bool f = (fk || fv) && tok < a.n_tokens;
+    const uint32_t slot = grp == 0 ? (uint32_t)tok : kOob;
+    buf_store1(rs_wsf, slot, (uint8_t)f);
+    buf_store1(rs_flags, slot, (uint8_t)f);
+    const int count = __popcll(__ballot(grp == 0 && f));
+    buf_store4(rs_cnt, lane == 0 ? (uint32_t)(sub * 4) : kOob, (uint32_t)count);
+#pragma unroll
+    for (int c = 0; c < D / 32; ++c) {
+      xk[c] = nk[c];
+      xv[c] = nv[c];
+    }
   }
 }
 
-template <int D>
-__global__ __launch_bounds__(kThreadsH) void hybrid_write_kernel(HybridArgs a) {
+// Per-wave LDS rings of the write kernel: value octet rows (8 consecutive
+// cache rows x all columns) being assembled, for the low-rank cache and for
+// the side list.  Slots 0..2 hold rows o % 3 (at most three rows are open at
+// once, since a sub-tile adds at most 16 rows); slot 3 holds the wave's first
+// row when the wave's run starts inside it (that row is shared with the
+// previous wave and is written slot by slot at the end).
+template <int D, int NB>
+struct WriteRings {
+  static constexpr int kLrRow = 16 * NB * 8 + 8;   // elements per ring row, padded
+  static constexpr int kSideRow = D * 8 + 8;
+  static constexpr int kPerWave = 4 * kLrRow + 4 * kSideRow;
+};
+
+template <int D, int NB>
+size_t write_lds_bytes(const HybridLds& L) {
+  return 2 * ((size_t)L.elems_write + (size_t)kWavesH * WriteRings<D, NB>::kPerWave);
+}
+
+// Octet row o of a ring: flush its columns col0 + 64 j with 16-byte stores
+// (offset kOob when the row is not to be written).
+template <int COLS>
+__device__ __forceinline__ void flush_row(__amdgpu_buffer_rsrc_t rs, const uint16_t* ring_row, int64_t o, bool ok,
+                                          int cols, int lane) {
+#pragma unroll
+  for (int j = 0; j < (COLS + 63) / 64; ++j) {
+    const int col = lane + 64 * j;
+    const int cc = col < COLS ? col : 0;
+    const u32x4 v = *reinterpret_cast<const u32x4*>(ring_row + cc * 8);
+    buf_store16(rs, ok && col < cols ? (uint32_t)((o * cols + col) * 16) : kOob, v);
+  }
+}
+
+// Slots [s0, s1) of octet row o, 2 bytes at a time (rows shared with another wave).
+template <int COLS>
+__device__ void flush_row_part(__amdgpu_buffer_rsrc_t rs, const uint16_t* ring_row, int64_t o, int s0, int s1,
+                               int cols, int lane) {
+  for (int j = 0; j < (COLS + 63) / 64; ++j) {
+    const int col = lane + 64 * j;
+    if (col >= cols) continue;
+    for (int sl = s0; sl < s1; ++sl)
+      buf_store2(rs, (uint32_t)(((o * cols + col) * 8 + sl) * 2), ring_row[col * 8 + sl]);
+  }
+}
+
+// Two waves per SIMD: the bases and the rings of two workgroups fill a compute unit's LDS.
+template <int D, int NB>
+__global__ __launch_bounds__(kThreadsH) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void hybrid_write_kernel(HybridArgs a) {
+  extern __shared__ __attribute__((aligned(16))) uint16_t smem[];
+  using R = WriteRings<D, NB>;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int n16 = lane & 15, grp = lane >> 4;
   const int h = blockIdx.y, b = blockIdx.z;
   const int64_t bh = (int64_t)b * a.hkv + h;
   const int64_t n_slots = (int64_t)a.n_tiles * kHybridTile;
+  const HybridLds L = hybrid_lds(D, NB);
+  const int rk = a.rk, rv = a.rv;
+  uint16_t* ring_lr = smem + L.elems_write + wave * R::kPerWave;
+  uint16_t* ring_side = ring_lr + 4 * R::kLrRow;
 
-  __shared__ __attribute__((aligned(16))) uint16_t s_bt[2][kMaxRank][D + kPad];
-  stage_bases<D>(a, h, s_bt);
+  stage_transposed<D>(a, L, h, smem);
   __syncthreads();
 
-  const int64_t stride = (int64_t)gridDim.x * kWavesH;
-  int64_t sub = (int64_t)blockIdx.x * kWavesH + wave;
-  u32x4 xa[D / 32], xn[D / 32];
-  if (sub < a.n_tiles) load_rows<D>(a, b, h, 0, sub, n16, grp, xa);
-  for (; sub < a.n_tiles; sub += stride) {
-    // flags of this sub-tile's tokens and each token's rank within its kind
-    const int64_t tok_lane = sub * kHybridTile + n16;
-    const bool f_lane = tok_lane < a.n_tokens && a.ws_flags[bh * n_slots + tok_lane];
+  const int64_t n_waves = (int64_t)gridDim.x * kWavesH;
+  const int64_t per_wave = (a.n_tiles + n_waves - 1) / n_waves;
+  const int64_t sub_begin = ((int64_t)blockIdx.x * kWavesH + wave) * per_wave;
+  const int64_t sub_end = sub_begin + per_wave < a.n_tiles ? sub_begin + per_wave : a.n_tiles;
+  if (sub_begin >= sub_end) return;   // no barrier follows
+  const __amdgpu_buffer_rsrc_t rs_wsf = make_rsrc(a.ws_flags + bh * n_slots, (uint32_t)n_slots);
+  const __amdgpu_buffer_rsrc_t rs_off = make_rsrc(a.ws_offsets + bh * a.n_tiles * 2, (uint32_t)(a.n_tiles * 8));
+  const __amdgpu_buffer_rsrc_t rs_ck =
+      make_rsrc(static_cast<uint16_t*>(a.ck) + bh * a.cap * rk, (uint32_t)(a.cap * rk * 2));
+  const __amdgpu_buffer_rsrc_t rs_cv =
+      make_rsrc(static_cast<uint16_t*>(a.cv) + bh * a.cap * rv, (uint32_t)(a.cap * rv * 2));
+  const __amdgpu_buffer_rsrc_t rs_ks =
+      make_rsrc(static_cast<uint16_t*>(a.k_side) + bh * a.side_cap * D, (uint32_t)(a.side_cap * D * 2));
+  const __amdgpu_buffer_rsrc_t rs_vs =
+      make_rsrc(static_cast<uint16_t*>(a.v_side) + bh * a.side_cap * D, (uint32_t)(a.side_cap * D * 2));
+  const __amdgpu_buffer_rsrc_t rs_idx = make_rsrc(a.side_idx + bh * a.side_cap, (uint32_t)(a.side_cap * 4));
+
+  // keys, values, token n16's flag and the sub-tile's (low-rank row, side row)
+  // for the current sub-tile; those of the next are in flight meanwhile
+  u32x4 xk[D / 32], xv[D / 32], nk[D / 32], nv[D / 32];
+  int64_t sub = sub_begin;
+  load_rows<D>(a, b, h, 0, sub, true, n16, grp, xk);
+  load_rows<D>(a, b, h, 1, sub, true, n16, grp, xv);
+  uint32_t fl = buf_load1(rs_wsf, (uint32_t)(sub * kHybridTile + n16)), fl_next = 0;
+  u32x2 off = buf_load8(rs_off, (uint32_t)(sub * 8)), off_next = u32x2{0u, 0u};
+
+  // the run's first rows; when they start inside an octet row, that row is shared
+  const int64_t p0_lr = (int32_t)off[0], p0_side = (int32_t)off[1];
+  const int64_t first_lr = (p0_lr & 7) ? (p0_lr >> 3) : -1;
+  const int64_t first_side = (p0_side & 7) ? (p0_side >> 3) : -1;
+  auto lr_row = [&](int64_t o) { return ring_lr + (o == first_lr ? 3 : (int)(o % 3)) * R::kLrRow; };
+  auto side_row = [&](int64_t o) { return ring_side + (o == first_side ? 3 : (int)(o % 3)) * R::kSideRow; };
+  int64_t lr_end = p0_lr, side_end = p0_side;
+
+  for (; sub < sub_end; ++sub) {
+    const bool more = sub + 1 < sub_end;
+    const int64_t nsub = more ? sub + 1 : sub;
+    load_rows<D>(a, b, h, 0, nsub, more, n16, grp, nk);
+    load_rows<D>(a, b, h, 1, nsub, more, n16, grp, nv);
+    fl_next = buf_load1(rs_wsf, more ? (uint32_t)(nsub * kHybridTile + n16) : kOob);
+    off_next = buf_load8(rs_off, more ? (uint32_t)(nsub * 8) : kOob);
+    __builtin_amdgcn_sched_barrier(0);   // keep the prefetch ahead of the phases below
+
+    const int64_t tok = sub * kHybridTile + n16;
+    const int64_t left = a.n_tokens - sub * kHybridTile;
+    const int nt = left < kHybridTile ? (int)left : kHybridTile;
+    const bool f_lane = fl != 0u;
     const uint32_t side_mask = (uint32_t)(__ballot(grp == 0 && f_lane) & 0xFFFFu);
-    const int nt = (int)((a.n_tokens - sub * kHybridTile) < kHybridTile ? (a.n_tokens - sub * kHybridTile) : kHybridTile);
-    const int64_t lr_off = a.ws_offsets[(bh * a.n_tiles + sub) * 2 + 0];
-    const int64_t side_off = a.ws_offsets[(bh * a.n_tiles + sub) * 2 + 1];
-    for (int kind = 0; kind < 2; ++kind) {
-      if (kind == 0) load_rows<D>(a, b, h, 1, sub, n16, grp, xn);
-      else if (sub + stride < a.n_tiles) load_rows<D>(a, b, h, 0, sub + stride, n16, grp, xn);
-      const int r = kind ? a.rv : a.rk;
-      const int nbr = (r + 15) / 16;
-      f32x4 acc1[8];
-      coeffs<D>(xa, s_bt[kind], nbr, n16, grp, acc1);
-      // low-rank tokens: coefficients to the row (keys) or octet (values) layout
-      uint16_t* out = static_cast<uint16_t*>(kind ? a.cv : a.ck);
+    const uint32_t below = side_mask & ((1u << n16) - 1u);
+    const int64_t lr_off = (int32_t)off[0], side_off = (int32_t)off[1];
+    const int64_t p_lr = lr_off + n16 - __popc(below);
+    const int64_t p_side = side_off + __popc(below);
+    const bool lr_ok = n16 < nt && !f_lane && p_lr < a.cap;
+    const bool side_ok = f_lane && p_side < a.side_cap;
+    const int n_side_sub = __popc(side_mask);
+    const int64_t lr_next = lr_off + nt - n_side_sub, side_next = side_off + n_side_sub;
+
+    f32x4 acc[NB];
+    // keys: coefficients 16 nb + 4 grp + 0..3 of token n16, one 8-byte store per block
+    coeffs_t<D, NB>(xk, smem + L.off_t[0], L.pitch_t, n16, grp, acc);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int tl = 4 * grp + i;
-        if (tl < nt && !((side_mask >> tl) & 1u)) {
-          const int64_t p = lr_off + tl - __popc(side_mask & ((1u << tl) - 1u));
-          if (p < a.cap) {
-#pragma unroll
-            for (int nb = 0; nb < 8; ++nb) {
-              const int col = 16 * nb + n16;
-              if (nb < nbr && col < r) {
-                const int64_t idx = kind ? bh * a.cap * r + ((p >> 3) * r + col) * 8 + (p & 7)
-                                         : (bh * a.cap + p) * r + col;
-                out[idx] = f32_to_bf16(acc1[nb][i]);
-              }
-            }
-          }
-        }
-      }
-      // full-rank tokens: their rows, bit for bit, into the side list
-      if (f_lane && n16 < nt) {
-        const int64_t p = side_off + __popc(side_mask & ((1u << n16) - 1u));
-        if (p < a.side_cap) {
-          uint16_t* side = static_cast<uint16_t*>(kind ? a.v_side : a.k_side);
-#pragma unroll
-          for (int c = 0; c < D / 32; ++c) {
-            const int col = 32 * c + 8 * grp;
-            if (!kind) {
-              *reinterpret_cast<u32x4*>(side + (bh * a.side_cap + p) * D + col) = xa[c];
-            } else {
-              uint16_t* q = side + bh * a.side_cap * D + (p & 7);
-#pragma unroll
-              for (int e = 0; e < 4; ++e) {
-                q[((p >> 3) * D + col + 2 * e) * 8] = (uint16_t)(xa[c][e] & 0xFFFFu);
-                q[((p >> 3) * D + col + 2 * e + 1) * 8] = (uint16_t)(xa[c][e] >> 16);
-              }
-            }
-          }
-          if (kind == 0 && grp == 0) a.side_idx[bh * a.side_cap + p] = (int32_t)(a.pos + tok_lane);
-        }
-      }
-#pragma unroll
-      for (int c = 0; c < D / 32; ++c) xa[c] = xn[c];
+    for (int nb = 0; nb < NB; ++nb) {
+      const int col = 16 * nb + 4 * grp;
+      const uint32_t voff = lr_ok && col < rk ? (uint32_t)((p_lr * rk + col) * 2) : kOob;
+      buf_store8(rs_ck, voff, u32x2{pack_bf16(acc[nb][0], acc[nb][1]), pack_bf16(acc[nb][2], acc[nb][3])});
     }
+    __builtin_amdgcn_sched_barrier(0);
+    // values: into the octet rows being assembled
+    coeffs_t<D, NB>(xv, smem + L.off_t[1], L.pitch_t, n16, grp, acc);
+    if (lr_ok) {
+      uint16_t* rr = lr_row(p_lr >> 3) + (p_lr & 7);
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int col = 16 * nb + 4 * grp + i;
+          if (col < rv) rr[col * 8] = f32_to_bf16(acc[nb][i]);
+        }
+    }
+    // selected tokens: value elements into the side list's octet rows
+    if (side_mask) {
+      if (side_ok) {
+        uint16_t* rr = side_row(p_side >> 3) + (p_side & 7);
+#pragma unroll
+        for (int c = 0; c < D / 32; ++c)
+#pragma unroll
+          for (int e = 0; e < 8; ++e)
+            rr[(32 * c + 8 * grp + e) * 8] = (uint16_t)(e & 1 ? xv[c][e >> 1] >> 16 : xv[c][e >> 1] & 0xFFFFu);
+      }
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    __builtin_amdgcn_sched_barrier(0);
+    // rows completed by this sub-tile (at most two of each list), whole rows only
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      const int64_t o = (lr_off >> 3) + k;
+      flush_row<16 * NB>(rs_cv, lr_row(o), o, o < (lr_next >> 3) && o != first_lr, rv, lane);
+    }
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      const int64_t o = (side_off >> 3) + k;
+      flush_row<D>(rs_vs, side_row(o), o, o < (side_next >> 3) && o != first_side, D, lane);
+    }
+    // selected tokens: key rows (bit for bit) and indices
+#pragma unroll
+    for (int c = 0; c < D / 32; ++c)
+      buf_store16(rs_ks, side_ok ? (uint32_t)((p_side * D + 32 * c + 8 * grp) * 2) : kOob, xk[c]);
+    buf_store4(rs_idx, side_ok && grp == 0 ? (uint32_t)(p_side * 4) : kOob, (uint32_t)(a.pos + tok));
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");   // ring reads before the next sub-tile's writes
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+
+#pragma unroll
+    for (int c = 0; c < D / 32; ++c) {
+      xk[c] = nk[c];
+      xv[c] = nv[c];
+    }
+    fl = fl_next;
+    off = off_next;
+    lr_end = lr_next;
+    side_end = side_next;
   }
+
+  // the run's shared rows: its first row (when it started inside one) and its
+  // last, unfinished row, written slot by slot
+  auto finish = [&](const uint16_t* first_ring, int64_t first, int64_t p0, int64_t end, __amdgpu_buffer_rsrc_t rs,
+                    int cols, auto row_of, auto cols_tag) {
+    constexpr int COLS = decltype(cols_tag)::value;
+    if (first >= 0) {
+      const int64_t stop = end < 8 * (first + 1) ? end : 8 * (first + 1);
+      if (stop > p0) flush_row_part<COLS>(rs, first_ring, first, (int)(p0 & 7), (int)(stop - 8 * first), cols, lane);
+    }
+    const int64_t last = end >> 3;
+    if ((end & 7) && last != first) flush_row_part<COLS>(rs, row_of(last), last, 0, (int)(end & 7), cols, lane);
+  };
+  const int64_t lr_stop = lr_end < a.cap ? lr_end : a.cap;
+  const int64_t side_stop = side_end < a.side_cap ? side_end : a.side_cap;
+  finish(ring_lr + 3 * R::kLrRow, first_lr, p0_lr, lr_stop, rs_cv, rv, lr_row,
+         std::integral_constant<int, 16 * NB>{});
+  finish(ring_side + 3 * R::kSideRow, first_side, p0_side, side_stop, rs_vs, D, side_row,
+         std::integral_constant<int, D>{});
 }
 
 // Exclusive scan of the per-sub-tile counts of one (b, kv head); advances the counters.
@@ -304,30 +512,62 @@ __global__ __launch_bounds__(256) void hybrid_scan_kernel(HybridArgs a) {
   }
 }
 
-// Persistent grid: about `target` workgroups in all, none without work.
-dim3 persistent_grid(const HybridArgs& a, int target) {
+// Persistent grid: one round of resident workgroups, none without work.
+template <typename K>
+hipError_t launch_persistent(K kernel, const HybridArgs& a, size_t lds_bytes, hipStream_t s) {
+  const void* fn = reinterpret_cast<const void*>(kernel);
+  hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_bytes);
+  if (e != hipSuccess) return e;
+  int per_cu = 0;
+  e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, kThreadsH, lds_bytes);
+  if (e != hipSuccess) return e;
+  if (per_cu < 1) return hipErrorInvalidConfiguration;
   const int64_t units = (int64_t)a.hkv * a.batch;
+  const int64_t target = (int64_t)(a.cus > 0 ? a.cus : 256) * per_cu;
   int64_t per_unit = (target + units - 1) / units;
   const int64_t max_per_unit = (a.n_tiles + kWavesH - 1) / kWavesH;
   if (per_unit > max_per_unit) per_unit = max_per_unit;
   if (per_unit < 1) per_unit = 1;
-  return dim3((unsigned)per_unit, a.hkv, a.batch);
+  hipLaunchKernelGGL(kernel, dim3((unsigned)per_unit, a.hkv, a.batch), dim3(kThreadsH), lds_bytes, s, a);
+  return hipGetLastError();
+}
+
+template <int D, int NB>
+hipError_t launch_hybrid_nb(const HybridArgs& a, hipStream_t s) {
+  const HybridLds L = hybrid_lds(D, NB);
+  hipError_t e = launch_persistent(hybrid_select_kernel<D, NB>, a, 2 * (size_t)L.elems_select, s);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(hybrid_scan_kernel, dim3(a.hkv, a.batch), dim3(256), 0, s, a);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  return launch_persistent(hybrid_write_kernel<D, NB>, a, write_lds_bytes<D, NB>(L), s);
 }
 
 }  // namespace
 
 hipError_t launch_hybrid_bf16(const HybridArgs& a, hipStream_t s) {
-  const dim3 gs = persistent_grid(a, 256), gw = persistent_grid(a, 512);
-  if (a.d == 128) hipLaunchKernelGGL(hybrid_select_kernel<128>, gs, dim3(kThreadsH), 0, s, a);
-  else hipLaunchKernelGGL(hybrid_select_kernel<64>, gs, dim3(kThreadsH), 0, s, a);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(hybrid_scan_kernel, dim3(a.hkv, a.batch), dim3(256), 0, s, a);
-  e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  if (a.d == 128) hipLaunchKernelGGL(hybrid_write_kernel<128>, gw, dim3(kThreadsH), 0, s, a);
-  else hipLaunchKernelGGL(hybrid_write_kernel<64>, gw, dim3(kThreadsH), 0, s, a);
-  return hipGetLastError();
+  const int nb = ((a.rk > a.rv ? a.rk : a.rv) + 15) / 16;
+  if (a.d == 64) {
+    switch (nb) {
+      case 1: return launch_hybrid_nb<64, 1>(a, s);
+      case 2: return launch_hybrid_nb<64, 2>(a, s);
+      case 3: return launch_hybrid_nb<64, 3>(a, s);
+      case 4: return launch_hybrid_nb<64, 4>(a, s);
+      default: return hipErrorInvalidValue;
+    }
+  }
+  if (a.d != 128) return hipErrorInvalidValue;
+  switch (nb) {
+    case 1: return launch_hybrid_nb<128, 1>(a, s);
+    case 2: return launch_hybrid_nb<128, 2>(a, s);
+    case 3: return launch_hybrid_nb<128, 3>(a, s);
+    case 4: return launch_hybrid_nb<128, 4>(a, s);
+    case 5: return launch_hybrid_nb<128, 5>(a, s);
+    case 6: return launch_hybrid_nb<128, 6>(a, s);
+    case 7: return launch_hybrid_nb<128, 7>(a, s);
+    case 8: return launch_hybrid_nb<128, 8>(a, s);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 }  // namespace lrkv

@@ -90,12 +90,20 @@ DecodeLayout decode_layout(const lrkv_dims& d, int64_t n_lr_tokens, int64_t side
   const int cus = device_cu_count();
   const int64_t units = (int64_t)d.batch * d.n_kv_heads;
   const int64_t rows = (int64_t)d.batch * d.n_q_heads;
-  L.lr = plan_splits(units, n_lr_tokens, cus, kMaxSplits);
-  L.parts_lr = (int)cdiv(L.lr.n_splits, kSplitsPerPart);
   if (side_cap > 0) {
-    L.side = plan_splits(units, side_cap, cus, kMaxSplits);
+    // one launch attends both lists: its round of workgroups is shared in
+    // proportion to the bytes each list can hold per (b, kv head)
+    const double lr_w = (double)n_lr_tokens * (d.rank_k + d.rank_v);
+    const double side_w = (double)side_cap * 2.0 * d.head_dim;
+    int cus_side = (int)std::lround(cus * side_w / (lr_w + side_w));
+    cus_side = std::max(1, std::min(cus - 1, cus_side));
+    L.lr = plan_splits(units, n_lr_tokens, std::max(1, cus - cus_side), kMaxSplits);
+    L.side = plan_splits(units, side_cap, cus_side, kMaxSplits);
     L.parts_side = (int)cdiv(L.side.n_splits, kSplitsPerPart);
+  } else {
+    L.lr = plan_splits(units, n_lr_tokens, cus, kMaxSplits);
   }
+  L.parts_lr = (int)cdiv(L.lr.n_splits, kSplitsPerPart);
   size_t off = 0;
   L.o_lr = off;  off = align256(off + sizeof(float) * rows * L.parts_lr * d.head_dim);
   L.ml_lr = off; off = align256(off + sizeof(float) * rows * L.parts_lr * 2);
@@ -408,6 +416,7 @@ lrkv_status lrkv_compress_hybrid(const void* k, const void* v, const void* basis
   a.ws_counts = reinterpret_cast<int32_t*>(ws + off); off = align256(off + sizeof(int32_t) * units * tiles);
   a.ws_offsets = reinterpret_cast<int32_t*>(ws + off);
   a.n_tiles = (int)tiles;
+  a.cus = device_cu_count();
   const hipError_t e = launch_hybrid_bf16(a, stream);
   return e == hipSuccess ? LRKV_OK : device_fail(fn, e);
 }
@@ -454,16 +463,19 @@ lrkv_status lrkv_decode_attn_hybrid(const void* q, const void* basis_k, const vo
   sa.qscale = qscale;
   sa.part_o = reinterpret_cast<float*>(ws + L.o_lr);
   sa.part_ml = reinterpret_cast<float*>(ws + L.ml_lr);
-  hipError_t e = bf16 ? launch_split_bf16(sa, stream) : launch_split_f32(sa, stream);
-  if (e != hipSuccess) return device_fail(fn, e);
-
   SplitArgs ss = sa;   // side list: full-rank rows, no fold and no lift
   ss.basis_k = nullptr; ss.basis_v = nullptr; ss.ck = k_side; ss.cv = v_side; ss.cap = side_cap;
   ss.rk = dims->head_dim; ss.rv = dims->head_dim; ss.n_dev = n_side;
   ss.chunks_per_split = L.side.chunks_per_split; ss.n_splits = L.side.n_splits; ss.n_parts = L.parts_side;
   ss.part_o = reinterpret_cast<float*>(ws + L.o_side);
   ss.part_ml = reinterpret_cast<float*>(ws + L.ml_side);
-  e = bf16 ? launch_split_bf16(ss, stream) : launch_split_f32(ss, stream);
+  hipError_t e;
+  if (bf16) {
+    e = launch_split_bf16_hybrid(sa, ss, stream);
+  } else {
+    e = launch_split_f32(sa, stream);
+    if (e == hipSuccess) e = launch_split_f32(ss, stream);
+  }
   if (e != hipSuccess) return device_fail(fn, e);
 
   MergeArgs ma{};

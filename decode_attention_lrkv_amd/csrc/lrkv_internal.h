@@ -57,6 +57,8 @@ struct CompressKvArgs {
 };
 
 hipError_t launch_split_bf16(const SplitArgs& a, hipStream_t s);
+// Hybrid cache: low-rank rows (lr) and full-rank side list (side) in one launch.
+hipError_t launch_split_bf16_hybrid(const SplitArgs& lr, const SplitArgs& side, hipStream_t s);
 hipError_t launch_compress_kv_small_bf16(const CompressKvArgs& a, hipStream_t s);
 hipError_t launch_split_f32(const SplitArgs& a, hipStream_t s);
 hipError_t launch_merge(const MergeArgs& a, bool bf16, hipStream_t s);
@@ -75,6 +77,7 @@ struct HybridArgs {
   int32_t* ws_counts;    // [B, Hkv, n_tiles] flagged tokens per sub-tile
   int32_t* ws_offsets;   // [B, Hkv, n_tiles, 2] (low-rank row, side row) of each sub-tile's first token
   int n_tiles;
+  int cus;               // compute units of the device (sizes the persistent grids)
 };
 
 constexpr int kHybridTile = 16;   // tokens per hybrid compaction unit (one wave sub-tile)

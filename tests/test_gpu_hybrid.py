@@ -173,3 +173,56 @@ def test_hybrid_tau_inf_matches_plain_decode():
     o2, l2 = lrkv.decode_attn(qd, bkd, c.coeff_k, bvd, c.coeff_v, n)
     assert np.max(np.abs(to_f64(o1) - to_f64(o2))) <= 2 * 2 ** -8 * np.max(np.abs(to_f64(o2)))
     assert np.max(np.abs(to_f64(l1) - to_f64(l2))) <= 1e-4
+
+
+@pytest.mark.parametrize("batch,hq,hkv,d,rk,rv,n", [
+    (2, 8, 2, 64, 16, 40, 3001),       # head_dim 64, unequal ranks, ragged sub-tile
+    (1, 8, 2, 128, 56, 72, 5000),      # the step workload's ranks
+    (1, 4, 1, 128, 128, 32, 777),      # full-rank keys, narrow values
+])
+def test_hybrid_other_shapes(batch, hq, hkv, d, rk, rv, n):
+    """Selection, compaction and union decode at shapes other than the 128K workload's."""
+    w = synth.scaled(synth.HYBRID_128K, batch=batch, n_q_heads=hq, n_kv_heads=hkv, head_dim=d,
+                     ranks_even=(rk, rv), ranks_odd=(rk, rv), n_ctx=(n,))
+    inj = synth.injected_set(w, 0, 0, n)
+    k = synth.tokens_major(synth.stack_heads(w, lambda b, h: synth.hybrid_tokens(w, 0, "k", b, h, n, inj)))
+    v = synth.tokens_major(synth.stack_heads(w, lambda b, h: synth.hybrid_tokens(w, 0, "v", b, h, n, inj)))
+    bk, bv, q = synth.basis(w, 0, "k"), synth.basis(w, 0, "v"), synth.query(w, 0)
+    ref = O.compress_hybrid(k.exact, v.exact, bk.exact, bv.exact, TAU, "bf16")
+    # the decision is unique: every token's residual is far from the threshold
+    for b in range(batch):
+        for h in range(hkv):
+            for x, bs in ((k.exact[b, :, h], bk.exact[h]), (v.exact[b, :, h], bv.exact[h])):
+                e = O.relative_residual(x, bs)
+                assert not np.any((e > 0.25) & (e < 0.75))
+    cap = _round8(n)
+    side_cap = _round8(len(inj) + 8)
+    c = lrkv.HybridCache(batch, hq, hkv, d, rk, rv, cap, side_cap, DEV)
+    flags = torch.zeros((batch, hkv, n), dtype=torch.uint8, device=DEV)
+    kd, vd, bkd, bvd, qd = (to_dev(x, "bf16") for x in (k, v, bk, bv, q))
+    lrkv.compress_hybrid(c, kd, vd, bkd, bvd, TAU, 0, flags=flags)
+    s = _snapshot(c)
+    fl = flags.cpu().numpy()
+    assert s["overflow"][0] == 0
+    for b in range(batch):
+        for h in range(hkv):
+            f_ref = ref["flags"][(b, h)]
+            assert np.array_equal(fl[b, h].astype(bool), f_ref), f"flags differ at ({b}, {h})"
+            part = _valid_parts(s, b, h)
+            assert np.array_equal(part["idx"], ref["side_idx"][(b, h)])
+            side, lr = np.nonzero(f_ref)[0], np.nonzero(~f_ref)[0]
+            assert np.array_equal(part["ks"], k.store[b, side, h])
+            assert np.array_equal(part["vs"], v.store[b, side, h])
+            check_compress(synth.bf16_bits_to_f64(part["ck"])[None, None], ref["ck"][(b, h)][None, None],
+                           k.exact[b:b + 1, lr, h:h + 1], bk.exact[h:h + 1], "bf16", f"K ({b}, {h})")
+            check_compress(synth.bf16_bits_to_f64(part["cv"])[None, None], ref["cv"][(b, h)][None, None],
+                           v.exact[b:b + 1, lr, h:h + 1], bv.exact[h:h + 1], "bf16", f"V ({b}, {h})")
+    rows = [(b, hq_) for b in range(batch) for hq_ in range(hq)]
+    ck_st = {key: O.round_storage(x, "bf16") for key, x in ref["ck"].items()}
+    cv_st = {key: O.round_storage(x, "bf16") for key, x in ref["cv"].items()}
+    o_ref = O.decode_hybrid_rows(q.exact, bk.exact, bv.exact, ck_st, cv_st, ref["k_side"], ref["v_side"], rows)
+    o, lse = lrkv.decode_attn_hybrid(qd, bkd, bvd, c)
+    og, lg = to_f64(o), to_f64(lse)
+    check_decode(np.stack([og[r] for r in rows]), np.array([lg[r] for r in rows]),
+                 np.stack([o_ref[r][0] for r in rows]), np.array([o_ref[r][1] for r in rows]),
+                 "bf16", f"hybrid shape {(batch, hq, hkv, d, rk, rv, n)}")
