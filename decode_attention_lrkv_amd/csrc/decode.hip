@@ -35,6 +35,14 @@ __device__ __forceinline__ float load_f<uint16_t>(const uint16_t* p, int64_t i) 
 template <>
 __device__ __forceinline__ float load_f<float>(const float* p, int64_t i) { return p[i]; }
 
+// Partials are stored and, by the workgroup that merges them inside the same
+// launch, loaded at device scope: these accesses go to the coherence point
+// shared by all XCDs instead of staying in one XCD's L2, so no cache has to
+// be written back or invalidated for the merging workgroup to see them.
+__device__ __forceinline__ void store_partial(float* p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 template <typename T>
 __device__ __forceinline__ void store_f(T* p, int64_t i, float v);
 template <>
@@ -51,10 +59,11 @@ __device__ __forceinline__ void store_f<float>(float* p, int64_t i, float v) { p
 // acc = sum_w 2^(m_w - M) acc_w, likewise the sum), the result is lifted
 // through B_V^T (or taken as is when the values are full rank, basis_v null)
 // and written as this workgroup's partial.
-// For bfloat16, s_stage must hold d x (rv + 8) elements; it may alias s_acc.
+// s_bv: B_V already staged in LDS with row pitch rv + 16 / sizeof(T), or
+// null to read it from memory.
 template <typename T>
 __device__ void workgroup_partial(const SplitArgs& a, int b, int h, int part, const float* s_acc, int acc_ld,
-                                  const float (*s_ml)[8][2], T* s_stage, float* s_merged) {
+                                  const float (*s_ml)[8][2], const T* s_bv, float* s_merged) {
   const int tid = threadIdx.x;
   const int g = a.g, rv = a.rv, d = a.d;
   constexpr int kVec = 16 / sizeof(T);
@@ -62,19 +71,8 @@ __device__ void workgroup_partial(const SplitArgs& a, int b, int h, int part, co
   const bool lift = a.basis_v != nullptr;
   __shared__ float s_w[kWaves][8];
   __shared__ float s_mm[8][2];
-
-  // issue the B_V loads first; they land while the waves are merged
-  // (bfloat16 bases are staged in LDS; float32 ones are read from memory)
-  constexpr bool kStage = sizeof(T) == 2;
-  constexpr int kIter = kStage ? 128 * 128 / kVec / 256 : 1;
-  u32x4 wb[kIter];
-  const int per_row = rv / kVec, nb = (lift && kStage) ? d * per_row : 0;
   const T* bv = lift ? static_cast<const T*>(a.basis_v) + (int64_t)h * d * rv : nullptr;
-#pragma unroll
-  for (int it = 0; it < kIter; ++it) {
-    const int i = tid + 256 * it;
-    if (i < nb) wb[it] = *reinterpret_cast<const u32x4*>(bv + (i / per_row) * rv + (i % per_row) * kVec);
-  }
+
   if (tid < g) {
     float M = -INFINITY;
 #pragma unroll
@@ -98,36 +96,141 @@ __device__ void workgroup_partial(const SplitArgs& a, int b, int h, int part, co
     for (int w = 0; w < kWaves; ++w) acc = fmaf(s_w[w][j], s_acc[(w * 16 + j) * acc_ld + c], acc);
     s_merged[j * 128 + c] = acc;
   }
-  __syncthreads();   // s_acc may share memory with s_stage
+  __syncthreads();
   const int64_t row0 = (int64_t)b * a.hq + (int64_t)h * g;
   float* po = a.part_o;
   if (lift) {
-    if (kStage) {
-#pragma unroll
-      for (int it = 0; it < kIter; ++it) {
-        const int i = tid + 256 * it;
-        if (i < nb) *reinterpret_cast<u32x4*>(s_stage + (i / per_row) * ldb + (i % per_row) * kVec) = wb[it];
-      }
-      __syncthreads();
-    }
     for (int i = tid; i < g * d; i += 256) {
       const int j = i / d, dd = i - j * d;
-      const T* br = kStage ? s_stage + dd * ldb : bv + (int64_t)dd * rv;
+      const T* br = s_bv ? s_bv + dd * ldb : bv + (int64_t)dd * rv;
       const float* ac = s_merged + j * 128;
       float o = 0.f;
       for (int c = 0; c < rv; ++c) o = fmaf(load_f(br, c), ac[c], o);
-      po[((row0 + j) * a.n_parts + part) * d + dd] = o;
+      store_partial(po + ((row0 + j) * a.n_parts + part) * d + dd, o);
     }
   } else {
     for (int i = tid; i < g * d; i += 256) {
       const int j = i / d, dd = i - j * d;
-      po[((row0 + j) * a.n_parts + part) * d + dd] = s_merged[j * 128 + dd];
+      store_partial(po + ((row0 + j) * a.n_parts + part) * d + dd, s_merged[j * 128 + dd]);
     }
   }
   if (tid < g) {
-    a.part_ml[((row0 + tid) * a.n_parts + part) * 2 + 0] = s_mm[tid][0];
-    a.part_ml[((row0 + tid) * a.n_parts + part) * 2 + 1] = s_mm[tid][1];
+    store_partial(a.part_ml + ((row0 + tid) * a.n_parts + part) * 2 + 0, s_mm[tid][0]);
+    store_partial(a.part_ml + ((row0 + tid) * a.n_parts + part) * 2 + 1, s_mm[tid][1]);
   }
+}
+
+// ----------------------------------------------------------------------------
+// log-sum-exp merge of the partials of one (batch, kv head)
+// ----------------------------------------------------------------------------
+//   M = max_s m_s,  L = sum_s 2^(m_s - M) l_s,
+//   out = sum_s 2^(m_s - M) o_s / L,  lse = (M + log2 L) ln 2
+// over the n_parts partials of each of the unit's g query heads; partials of
+// workgroups that saw no token have m_s = -inf and weigh nothing.  Wave w
+// takes heads w, w + 4.  Lane (grp, col) of a wave folds float4 column col of
+// partials grp, grp + 64 / (d / 4), ... into a running (max, sum, output)
+// in ascending order, issuing the loads of sixteen partials at a time, and the
+// lane groups are then combined pairwise (the lower lane's state first, so
+// that both lanes of a pair compute the same bits).  The same code serves the
+// merge kernel and the workgroup that finishes a fused decode, so both give
+// the same bits; kCoherent makes the loads device-scope (the partials were
+// written by workgroups of the same launch, possibly on another XCD).
+struct MergeState {
+  float m, l;
+  f32x4 o;
+};
+
+__device__ __forceinline__ MergeState merge_two(const MergeState& a, const MergeState& b) {
+  const float M = fmaxf(a.m, b.m);
+  const float wa = a.m == -INFINITY ? 0.f : exp2_fast(a.m - M);
+  const float wb = b.m == -INFINITY ? 0.f : exp2_fast(b.m - M);
+  MergeState r;
+  r.m = M;
+  r.l = fmaf(b.l, wb, a.l * wa);
+#pragma unroll
+  for (int e = 0; e < 4; ++e) r.o[e] = fmaf(b.o[e], wb, a.o[e] * wa);
+  return r;
+}
+
+template <typename T, bool kCoherent>
+__device__ void merge_unit(const MergeArgs& a, int64_t unit) {
+  constexpr int kU = 16;
+  constexpr int kAux = kCoherent ? 16 : 0;   // cache policy: sc1, device-scope coherent
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int S = a.n_parts, d = a.d, g = a.g;
+  const int cols = d / 4, groups = 64 / cols;
+  const int col = lane % cols, grp = lane / cols;
+  for (int j = wave; j < g; j += kWaves) {
+    const int64_t row = unit * g + j;
+    const __amdgpu_buffer_rsrc_t rs_ml = make_rsrc(a.part_ml + row * S * 2, (uint32_t)(S * 8));
+    const __amdgpu_buffer_rsrc_t rs_o = make_rsrc(a.part_o + row * S * d, (uint32_t)(S * d * 4));
+    MergeState st{-INFINITY, 0.f, f32x4{0.f, 0.f, 0.f, 0.f}};
+    for (int s0 = grp; s0 < S; s0 += groups * kU) {
+      u32x2 ml[kU];
+      u32x4 ov[kU];
+#pragma unroll
+      for (int u = 0; u < kU; ++u) {
+        const uint32_t s = (uint32_t)(s0 + u * groups);
+        ml[u] = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rs_ml, (int)(s * 8), 0, kAux));
+        ov[u] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                  rs_o, (int)((s * d + 4 * col) * 4), 0, kAux));
+      }
+#pragma unroll
+      for (int u = 0; u < kU; ++u) {
+        const float ms = __uint_as_float(ml[u][0]);
+        if (s0 + u * groups < S && ms != -INFINITY) {
+          MergeState p;
+          p.m = ms;
+          p.l = __uint_as_float(ml[u][1]);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) p.o[e] = __uint_as_float(ov[u][e]);
+          st = merge_two(st, p);
+        }
+      }
+    }
+    for (int off = cols; off < 64; off <<= 1) {
+      MergeState other;
+      other.m = __shfl_xor(st.m, off);
+      other.l = __shfl_xor(st.l, off);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) other.o[e] = __shfl_xor(st.o[e], off);
+      st = (lane & off) ? merge_two(other, st) : merge_two(st, other);
+    }
+    const float inv = st.l > 0.f ? 1.f / st.l : 0.f;
+    if (grp == 0) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) store_f(static_cast<T*>(a.out), row * d + 4 * col + e, st.o[e] * inv);
+    }
+    if (lane == 0 && a.lse) a.lse[row] = st.l > 0.f ? (st.m + __log2f(st.l)) * kLn2 : -INFINITY;
+  }
+}
+
+// Fused merge: every workgroup of a (b, kv head) takes a ticket once its
+// partial is written; the one that draws the last ticket merges the unit and
+// puts the counter back to zero.  The partials were stored at device scope;
+// each wave waits until its stores are acknowledged before the workgroup
+// takes its ticket, and the merging workgroup loads them at device scope, so
+// partials written on other XCDs are seen without cache maintenance.
+// No workgroup waits for another.
+template <typename T>
+__device__ void finish_unit(const SplitArgs& a, int b, int h) {
+  if (a.counters == nullptr) return;
+  __shared__ int s_last;
+  const int64_t bh = (int64_t)b * a.hkv + h;
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const int t = __hip_atomic_fetch_add(a.counters + bh, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    s_last = t == a.n_parts - 1;
+  }
+  __syncthreads();
+  if (!s_last) return;
+  MergeArgs m;
+  m.part_o = a.part_o; m.part_ml = a.part_ml; m.n_parts = a.n_parts;
+  m.d = a.d; m.g = a.g; m.hq = a.hq; m.hkv = a.hkv; m.batch = a.batch;
+  m.out = a.out; m.lse = a.lse;
+  merge_unit<T, true>(m, bh);
+  if (threadIdx.x == 0) __hip_atomic_store(a.counters + bh, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // ----------------------------------------------------------------------------
@@ -135,8 +238,8 @@ __device__ void workgroup_partial(const SplitArgs& a, int b, int h, int part, co
 // ----------------------------------------------------------------------------
 // KC: 32-wide k chunks covering r_K;  VB: 16-wide column blocks covering r_V.
 // FOLD false: keys are full-rank rows (hybrid side list), q' = q * scale.
-// DB: double-buffer the chunks in registers (false where the operands are too
-// wide for two waves per SIMD).
+// STAGES: chunks in flight per wave, held in registers (2, or 1 where the
+// operands are too wide for two waves per SIMD).
 //
 // Each chunk is read through buffer resources based at the chunk and sized to
 // its valid tokens: rows past the context, and lanes pointed past the end on
@@ -149,18 +252,22 @@ struct Chunk {
   u32x4 v[VB];
 };
 
-// LDS of one attention workgroup: the prologue's B_K, the waves' accumulator
-// rows and the epilogue's B_V share `raw`.
+// LDS of one attention workgroup: the prologue's B_K and the waves'
+// accumulator rows share `raw`; B_V is staged in the prologue, so that its
+// load overlaps the fold and the stream instead of delaying the epilogue.
 struct SplitSmem {
   static constexpr int kRawBytes = 128 * (128 + 8) * 2;   // >= kWaves * 16 * 128 * 4
   __attribute__((aligned(16))) unsigned char raw[kRawBytes];
+  __attribute__((aligned(16))) uint16_t bv[128 * (128 + 8)];   // B_V for the lift, pitch rv + 8
   float q[8 * 128];
   float qf[8 * 128];
   float ml[kWaves][8][2];
 };
 
-template <int KC, int VB, bool FOLD, bool DB>
-__device__ __forceinline__ void split_bf16_body(const SplitArgs& a, int wg, SplitSmem& sm) {
+// wg: this workgroup's index among the workgroups attending this list of
+// this (b, kv head); part: the partial it writes.
+template <int KC, int VB, bool FOLD, int STAGES>
+__device__ __forceinline__ void split_bf16_body(const SplitArgs& a, int wg, int part, SplitSmem& sm) {
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
   const int lane = tid & 63;
@@ -223,8 +330,9 @@ __device__ __forceinline__ void split_bf16_body(const SplitArgs& a, int wg, Spli
   };
 
   // --- fold q' = q B_K * scale * log2(e) for the g query heads of this kv head
+  Chunk<KC, VB> ca, cb;
   {
-    // every load of the prologue is issued before the first wait
+    // every load of the prologue, and the first chunk's, is issued before the first wait
     const uint16_t* q = static_cast<const uint16_t*>(a.q) + ((int64_t)b * a.hq + (int64_t)h * g) * d;
     const int nq = g * d / 8;                       // <= 128 sixteen-byte pieces
     const u32x4 wq = tid < nq ? *reinterpret_cast<const u32x4*>(q + 8 * tid) : u32x4{0u, 0u, 0u, 0u};
@@ -237,6 +345,17 @@ __device__ __forceinline__ void split_bf16_body(const SplitArgs& a, int wg, Spli
       const int i = tid + 256 * it;
       if (i < nb) wb[it] = *reinterpret_cast<const u32x4*>(bk + 8 * i);
     }
+    // B_V of the epilogue's lift
+    const int bv_row = a.rv / 8, nbv = a.basis_v ? d * bv_row : 0;
+    const uint16_t* bvs = a.basis_v ? static_cast<const uint16_t*>(a.basis_v) + (int64_t)h * d * a.rv : nullptr;
+    u32x4 wv[kBkIter];
+#pragma unroll
+    for (int it = 0; it < kBkIter; ++it) {
+      const int i = tid + 256 * it;
+      if (i < nbv) wv[it] = *reinterpret_cast<const u32x4*>(bvs + 8 * i);
+    }
+    // the first chunk streams in while the query is folded
+    if (c_begin < c_end) load(ca, c_begin);
     if (tid < nq) {
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
@@ -248,6 +367,11 @@ __device__ __forceinline__ void split_bf16_body(const SplitArgs& a, int wg, Spli
     for (int it = 0; it < kBkIter; ++it) {
       const int i = tid + 256 * it;
       if (i < nb) *reinterpret_cast<u32x4*>(s_bk + 8 * i) = wb[it];
+    }
+#pragma unroll
+    for (int it = 0; it < kBkIter; ++it) {
+      const int i = tid + 256 * it;
+      if (i < nbv) *reinterpret_cast<u32x4*>(sm.bv + (i / bv_row) * (a.rv + 8) + (i % bv_row) * 8) = wv[it];
     }
     __syncthreads();
     if (FOLD) {
@@ -368,9 +492,7 @@ __device__ __forceinline__ void split_bf16_body(const SplitArgs& a, int wg, Spli
     }
   };
 
-  if (DB) {
-    Chunk<KC, VB> ca, cb;
-    if (c_begin < c_end) load(ca, c_begin);
+  if (STAGES == 2) {
     for (int64_t chunk = c_begin; chunk < c_end; chunk += 2) {
       if (chunk + 1 < c_end) load(cb, chunk + 1);
       process(ca, chunk);
@@ -379,10 +501,9 @@ __device__ __forceinline__ void split_bf16_body(const SplitArgs& a, int wg, Spli
       process(cb, chunk + 1);
     }
   } else {
-    Chunk<KC, VB> ca;
     for (int64_t chunk = c_begin; chunk < c_end; ++chunk) {
-      load(ca, chunk);
       process(ca, chunk);
+      if (chunk + 1 < c_end) load(ca, chunk + 1);
     }
   }
 
@@ -404,31 +525,63 @@ __device__ __forceinline__ void split_bf16_body(const SplitArgs& a, int wg, Spli
     s_acc[w][j][c] += s_acc[w][g + j][c];
   }
   __syncthreads();
-  workgroup_partial<uint16_t>(a, b, h, wg, &s_acc[0][0][0], VB * 16, s_ml, reinterpret_cast<uint16_t*>(sm.raw), s_qf);
+  workgroup_partial<uint16_t>(a, b, h, part, &s_acc[0][0][0], VB * 16, s_ml, sm.bv, s_qf);
 }
 
-// Chunks are double-buffered unless that no longer fits two waves per SIMD.
+// Chunks in flight per wave: two unless that no longer fits two waves per
+// SIMD (a chunk takes 4 (2 KC + VB) registers per lane).
 template <int KC, int VB>
-constexpr bool kDoubleBuffer = 2 * KC + VB < 16;
+constexpr int kStages = 2 * KC + VB < 16 ? 2 : 1;
 
 // Low-rank keys: two waves per SIMD (one round of workgroups fills the chip).
 template <int KC, int VB>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void split_bf16_kernel(SplitArgs a) {
   __shared__ SplitSmem sm;
-  split_bf16_body<KC, VB, true, kDoubleBuffer<KC, VB>>(a, blockIdx.x, sm);
+  split_bf16_body<KC, VB, true, kStages<KC, VB>>(a, blockIdx.x, blockIdx.x, sm);
+  finish_unit<uint16_t>(a, blockIdx.z, blockIdx.y);
 }
 
-// Hybrid cache in one launch: the first wg_lr workgroups of each (b, kv head)
-// attend the low-rank rows, the others the full-rank side list (r = d, no
-// fold and no lift, single-buffered so that both fit two waves per SIMD).
-// Both kinds write partials that the merge kernel combines.
+// Hybrid cache in one launch: the gridDim.x workgroups of each (b, kv head)
+// are divided between the low-rank rows and the full-rank side list (r = d,
+// no fold and no lift, single-buffered so that both fit two waves per SIMD)
+// in proportion to the bytes each list holds, from the counts on the device;
+// within a list, each wave takes an equal run of chunks.  Every workgroup
+// writes partial blockIdx.x; the last one to finish merges them.
 template <int KC, int VB, int SKC, int SVB>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
-void split_bf16_hybrid_kernel(SplitArgs lr, SplitArgs side, int wg_lr) {
+void split_bf16_hybrid_kernel(SplitArgs lr, SplitArgs side) {
   __shared__ SplitSmem sm;
-  if ((int)blockIdx.x < wg_lr) split_bf16_body<KC, VB, true, kDoubleBuffer<KC, VB>>(lr, blockIdx.x, sm);
-  else split_bf16_body<SKC, SVB, false, false>(side, blockIdx.x - wg_lr, sm);
+  const int64_t bh = (int64_t)blockIdx.z * lr.hkv + blockIdx.y;
+  auto count = [](const SplitArgs& a, int64_t bh) {
+    int64_t n = a.n_dev[bh];
+    return n < 0 ? (int64_t)0 : (n > a.cap ? a.cap : n);
+  };
+  const int64_t ch_lr = (count(lr, bh) + kChunk - 1) / kChunk;
+  const int64_t ch_side = (count(side, bh) + kChunk - 1) / kChunk;
+  const int64_t P = gridDim.x;
+  int64_t p_side = 0;
+  if (ch_side > 0) {
+    if (ch_lr == 0) {
+      p_side = P;
+    } else {
+      const int64_t w_lr = ch_lr * (lr.rk + lr.rv), w_side = ch_side * 2 * lr.d;
+      p_side = (P * w_side + (w_lr + w_side) / 2) / (w_lr + w_side);
+      p_side = p_side < 1 ? 1 : (p_side > P - 1 ? P - 1 : p_side);
+    }
+  }
+  const int64_t p_lr = P - p_side;
+  const int x = blockIdx.x;
+  if (x < p_lr) {
+    SplitArgs a = lr;
+    a.chunks_per_split = (int)((ch_lr + p_lr * kWaves - 1) / (p_lr * kWaves));
+    split_bf16_body<KC, VB, true, kStages<KC, VB>>(a, x, x, sm);
+  } else {
+    SplitArgs a = side;
+    a.chunks_per_split = (int)((ch_side + p_side * kWaves - 1) / (p_side * kWaves));
+    split_bf16_body<SKC, SVB, false, 1>(a, x - (int)p_lr, x, sm);
+  }
+  finish_unit<uint16_t>(lr, blockIdx.z, blockIdx.y);
 }
 
 // ----------------------------------------------------------------------------
@@ -556,75 +709,15 @@ __global__ __launch_bounds__(256) void split_f32_kernel(SplitArgs a) {
   }
   __syncthreads();
   workgroup_partial<float>(a, b, h, blockIdx.x, &s_acc[0][0][0], 128, s_ml, nullptr, s_qf);
+  finish_unit<float>(a, b, h);
 }
 
 // ----------------------------------------------------------------------------
-// merge: one workgroup per (batch, query head)
+// merge kernel of the two-phase interface: one workgroup per (batch, kv head)
 // ----------------------------------------------------------------------------
-//   M = max_s m_s,  w_s = 2^(m_s - M),  L = sum_s w_s l_s,
-//   out = sum_s w_s o_s / L,  lse = (M + log2 L) ln 2
-// over the low-rank partials and, for a hybrid cache, the side-list partials.
-// The partials are spread over the workgroup: thread t adds the float4 column
-// t % (d/4) of partials t / (d/4), t / (d/4) + 256 / (d/4), ...; the column
-// groups are then summed in LDS.
 template <typename T>
 __global__ __launch_bounds__(256) void merge_kernel(MergeArgs a) {
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const int64_t row = blockIdx.x;
-  const int S = a.n_parts, SS = a.n_side_parts, n = S + SS, d = a.d;
-  const float* ml = a.part_ml + row * S * 2;
-  const float* sml = SS ? a.side_ml + row * SS * 2 : nullptr;
-  auto mls = [&](int s) { return s < S ? ml + 2 * s : sml + 2 * (s - S); };
-  __shared__ float s_red[kWaves][2];
-  __shared__ __attribute__((aligned(16))) float s_o[256 * 4];
-
-  float m = -INFINITY;
-  for (int s = tid; s < n; s += 256) m = fmaxf(m, mls(s)[0]);
-  m = wave_max(m);
-  if (lane == 0) s_red[wave][0] = m;
-  __syncthreads();
-  const float M = fmaxf(fmaxf(s_red[0][0], s_red[1][0]), fmaxf(s_red[2][0], s_red[3][0]));
-  float l = 0.f;
-  for (int s = tid; s < n; s += 256) {
-    const float* p = mls(s);
-    l += p[0] == -INFINITY ? 0.f : exp2_fast(p[0] - M) * p[1];
-  }
-  l = wave_sum(l);
-  if (lane == 0) s_red[wave][1] = l;
-
-  const int cols = d / 4, groups = 256 / cols;
-  const int col = tid % cols, grp = tid / cols;
-  f32x4 o = f32x4{0.f, 0.f, 0.f, 0.f};
-  for (int s0 = grp; s0 < n; s0 += 4 * groups) {
-    f32x4 v[4];
-    float wt[4];
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int s = s0 + u * groups;
-      wt[u] = 0.f;
-      v[u] = f32x4{0.f, 0.f, 0.f, 0.f};
-      if (s < n) {
-        const float ms = mls(s)[0];
-        wt[u] = ms == -INFINITY ? 0.f : exp2_fast(ms - M);
-        const float* po = s < S ? a.part_o + (row * S + s) * d : a.side_o + (row * SS + (s - S)) * d;
-        v[u] = *reinterpret_cast<const f32x4*>(po + 4 * col);
-      }
-    }
-#pragma unroll
-    for (int u = 0; u < 4; ++u)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) o[e] = fmaf(wt[u], v[u][e], o[e]);
-  }
-  *reinterpret_cast<f32x4*>(&s_o[4 * tid]) = o;
-  __syncthreads();
-  const float L = s_red[0][1] + s_red[1][1] + s_red[2][1] + s_red[3][1];
-  const float inv = L > 0.f ? 1.f / L : 0.f;
-  if (tid < d) {
-    float acc = 0.f;
-    for (int gi = 0; gi < groups; ++gi) acc += s_o[4 * (gi * cols) + tid];
-    store_f(static_cast<T*>(a.out), row * d + tid, acc * inv);
-  }
-  if (tid == 0 && a.lse) a.lse[row] = L > 0.f ? (M + __log2f(L)) * kLn2 : -INFINITY;
+  merge_unit<T, false>(a, blockIdx.x);
 }
 
 }  // namespace
@@ -655,13 +748,13 @@ hipError_t launch_split_bf16(const SplitArgs& a, hipStream_t s) {
 
 #define LRKV_HYB_CASE(KC, VB, SKC, SVB)                                                              \
   case (KC * 16 + VB):                                                                               \
-    hipLaunchKernelGGL((split_bf16_hybrid_kernel<KC, VB, SKC, SVB>), grid, dim3(256), 0, s, lr, side, wg_lr); \
+    hipLaunchKernelGGL((split_bf16_hybrid_kernel<KC, VB, SKC, SVB>), grid, dim3(256), 0, s, lr, side); \
     break;
 
-hipError_t launch_split_bf16_hybrid(const SplitArgs& lr, const SplitArgs& side, hipStream_t s) {
-  const int wg_lr = (lr.n_splits + kWaves - 1) / kWaves;
-  const int wg_side = (side.n_splits + kWaves - 1) / kWaves;
-  const dim3 grid(wg_lr + wg_side, lr.hkv, lr.batch);
+hipError_t launch_split_bf16_hybrid(const SplitArgs& lr, const SplitArgs& side, int wgs_per_unit, hipStream_t s) {
+  const dim3 grid(wgs_per_unit, lr.hkv, lr.batch);
+  if (wgs_per_unit < 1 || lr.n_parts != wgs_per_unit || lr.n_dev == nullptr || side.n_dev == nullptr)
+    return hipErrorInvalidValue;
   const int kc = (lr.rk + 31) / 32, vb = (lr.rv + 15) / 16;
   if (lr.basis_k == nullptr || lr.basis_v == nullptr || side.basis_k != nullptr || side.basis_v != nullptr ||
       side.rk != lr.d || side.rv != lr.d)
@@ -697,7 +790,7 @@ hipError_t launch_split_f32(const SplitArgs& a, hipStream_t s) {
 }
 
 hipError_t launch_merge(const MergeArgs& a, bool bf16, hipStream_t s) {
-  const dim3 grid((unsigned)((int64_t)a.batch * a.hq));
+  const dim3 grid((unsigned)((int64_t)a.batch * a.hkv));
   if (bf16) hipLaunchKernelGGL(merge_kernel<uint16_t>, grid, dim3(256), 0, s, a);
   else hipLaunchKernelGGL(merge_kernel<float>, grid, dim3(256), 0, s, a);
   return hipGetLastError();

@@ -79,10 +79,12 @@ Plan plan_splits(int64_t units, int64_t n_tokens, int cus, int max_splits) {
   return p;
 }
 
+// Decode workspace: fused-merge counters [B, Hkv] int32 first, then the
+// partials [B, Hq, parts, d] and their (max, sum) [B, Hq, parts, 2].
 struct DecodeLayout {
-  Plan lr, side;
-  int parts_lr = 0, parts_side = 0;   // partials per (b, h): one per attention workgroup
-  size_t o_lr = 0, ml_lr = 0, o_side = 0, ml_side = 0, total = 0;
+  Plan lr;             // plain decode: splits of the context
+  int parts = 0;       // partials per (b, q head): one per attention workgroup
+  size_t counters = 0, o = 0, ml = 0, total = 0;
 };
 
 DecodeLayout decode_layout(const lrkv_dims& d, int64_t n_lr_tokens, int64_t side_cap) {
@@ -91,26 +93,26 @@ DecodeLayout decode_layout(const lrkv_dims& d, int64_t n_lr_tokens, int64_t side
   const int64_t units = (int64_t)d.batch * d.n_kv_heads;
   const int64_t rows = (int64_t)d.batch * d.n_q_heads;
   if (side_cap > 0) {
-    // one launch attends both lists: its round of workgroups is shared in
-    // proportion to the bytes each list can hold per (b, kv head)
-    const double lr_w = (double)n_lr_tokens * (d.rank_k + d.rank_v);
-    const double side_w = (double)side_cap * 2.0 * d.head_dim;
-    int cus_side = (int)std::lround(cus * side_w / (lr_w + side_w));
-    cus_side = std::max(1, std::min(cus - 1, cus_side));
-    L.lr = plan_splits(units, n_lr_tokens, std::max(1, cus - cus_side), kMaxSplits);
-    L.side = plan_splits(units, side_cap, cus_side, kMaxSplits);
-    L.parts_side = (int)cdiv(L.side.n_splits, kSplitsPerPart);
+    // hybrid: one round of workgroups (two per compute unit), divided between
+    // the two lists on the device; at least one per list, and no more than
+    // one chunk per wave of the largest possible lists
+    const int64_t chunks = cdiv(n_lr_tokens, kChunk) + cdiv(side_cap, kChunk);
+    int64_t p = (2 * (int64_t)cus) / units;
+    p = std::min<int64_t>(p, cdiv(chunks, kSplitsPerPart));
+    p = std::min<int64_t>(p, kMaxSplits / kSplitsPerPart);
+    if (const char* env = std::getenv("LRKV_HYBRID_WGS")) {   // forced workgroups per (b, kv head)
+      const long v = std::strtol(env, nullptr, 10);
+      if (v > 0) p = std::min<long>(v, kMaxSplits / kSplitsPerPart);
+    }
+    L.parts = (int)std::max<int64_t>(2, p);
   } else {
     L.lr = plan_splits(units, n_lr_tokens, cus, kMaxSplits);
+    L.parts = (int)cdiv(L.lr.n_splits, kSplitsPerPart);
   }
-  L.parts_lr = (int)cdiv(L.lr.n_splits, kSplitsPerPart);
   size_t off = 0;
-  L.o_lr = off;  off = align256(off + sizeof(float) * rows * L.parts_lr * d.head_dim);
-  L.ml_lr = off; off = align256(off + sizeof(float) * rows * L.parts_lr * 2);
-  if (side_cap > 0) {
-    L.o_side = off;  off = align256(off + sizeof(float) * rows * L.parts_side * d.head_dim);
-    L.ml_side = off; off = align256(off + sizeof(float) * rows * L.parts_side * 2);
-  }
+  L.counters = off; off = align256(off + sizeof(int32_t) * units);
+  L.o = off;        off = align256(off + sizeof(float) * rows * L.parts * d.head_dim);
+  L.ml = off;       off = align256(off + sizeof(float) * rows * L.parts * 2);
   L.total = off;
   return L;
 }
@@ -272,7 +274,7 @@ lrkv_status check_decode_common(const lrkv_dims* dims, int64_t n_ctx, lrkv_dtype
 lrkv_status decode_partial(const void* q, const void* basis_k, const void* coeff_k, const void* basis_v,
                            const void* coeff_v, const lrkv_dims* dims, int64_t n_ctx, float scale,
                            lrkv_dtype dtype, void* workspace, const DecodeLayout& L, hipStream_t stream,
-                           const char* fn) {
+                           const char* fn, void* fused_out = nullptr, float* fused_lse = nullptr) {
   char* ws = static_cast<char*>(workspace);
   SplitArgs sa{};
   sa.q = q; sa.basis_k = basis_k; sa.ck = coeff_k; sa.cv = coeff_v; sa.basis_v = basis_v;
@@ -280,10 +282,15 @@ lrkv_status decode_partial(const void* q, const void* basis_k, const void* coeff
   sa.g = dims->n_q_heads / dims->n_kv_heads; sa.hq = dims->n_q_heads; sa.hkv = dims->n_kv_heads;
   sa.batch = dims->batch;
   sa.n_static = n_ctx; sa.n_dev = nullptr;
-  sa.chunks_per_split = L.lr.chunks_per_split; sa.n_splits = L.lr.n_splits; sa.n_parts = L.parts_lr;
+  sa.chunks_per_split = L.lr.chunks_per_split; sa.n_splits = L.lr.n_splits; sa.n_parts = L.parts;
   sa.qscale = resolve_scale(scale, dims->head_dim) * kLog2eHost;
-  sa.part_o = reinterpret_cast<float*>(ws + L.o_lr);
-  sa.part_ml = reinterpret_cast<float*>(ws + L.ml_lr);
+  sa.part_o = reinterpret_cast<float*>(ws + L.o);
+  sa.part_ml = reinterpret_cast<float*>(ws + L.ml);
+  if (fused_out) {
+    sa.counters = reinterpret_cast<int32_t*>(ws + L.counters);
+    sa.out = fused_out;
+    sa.lse = fused_lse;
+  }
   const hipError_t e = dtype == LRKV_BF16 ? launch_split_bf16(sa, stream) : launch_split_f32(sa, stream);
   return e == hipSuccess ? LRKV_OK : device_fail(fn, e);
 }
@@ -292,11 +299,11 @@ lrkv_status decode_merge(void* out, float* lse, const lrkv_dims* dims, lrkv_dtyp
                          const DecodeLayout& L, hipStream_t stream, const char* fn) {
   char* ws = static_cast<char*>(workspace);
   MergeArgs ma{};
-  ma.part_o = reinterpret_cast<const float*>(ws + L.o_lr);
-  ma.part_ml = reinterpret_cast<const float*>(ws + L.ml_lr);
-  ma.n_parts = L.parts_lr;
-  ma.side_o = nullptr; ma.side_ml = nullptr; ma.n_side_parts = 0;
-  ma.d = dims->head_dim; ma.hq = dims->n_q_heads; ma.batch = dims->batch;
+  ma.part_o = reinterpret_cast<const float*>(ws + L.o);
+  ma.part_ml = reinterpret_cast<const float*>(ws + L.ml);
+  ma.n_parts = L.parts;
+  ma.d = dims->head_dim; ma.g = dims->n_q_heads / dims->n_kv_heads; ma.hq = dims->n_q_heads;
+  ma.hkv = dims->n_kv_heads; ma.batch = dims->batch;
   ma.out = out; ma.lse = lse;
   const hipError_t e = launch_merge(ma, dtype == LRKV_BF16, stream);
   return e == hipSuccess ? LRKV_OK : device_fail(fn, e);
@@ -322,9 +329,9 @@ lrkv_status lrkv_decode_attn(const void* q, const void* basis_k, const void* coe
   LRKV_CHECK_PTR(coeff_v, fn);
   LRKV_CHECK_PTR(out, fn);
   if (lse && !aligned16(lse)) return fail(LRKV_ERR_INVALID_ARGUMENT, "%s: lse is not 16-byte aligned", fn);
-  st = decode_partial(q, basis_k, coeff_k, basis_v, coeff_v, dims, n_ctx, scale, dtype, workspace, L, stream, fn);
-  if (st != LRKV_OK) return st;
-  return decode_merge(out, lse, dims, dtype, workspace, L, stream, fn);
+  // one launch: the last workgroup of each (b, kv head) merges
+  return decode_partial(q, basis_k, coeff_k, basis_v, coeff_v, dims, n_ctx, scale, dtype, workspace, L, stream,
+                        fn, out, lse);
 }
 
 lrkv_status lrkv_decode_attn_partial(const void* q, const void* basis_k, const void* coeff_k,
@@ -446,44 +453,29 @@ lrkv_status lrkv_decode_attn_hybrid(const void* q, const void* basis_k, const vo
   LRKV_CHECK_PTR(workspace, fn);
   if (!n_lr || !n_side) return fail(LRKV_ERR_INVALID_ARGUMENT, "%s: n_lr and n_side must not be NULL", fn);
   if (lse && !aligned16(lse)) return fail(LRKV_ERR_INVALID_ARGUMENT, "%s: lse is not 16-byte aligned", fn);
+  if (dtype != LRKV_BF16) return fail(LRKV_ERR_UNSUPPORTED, "%s: only bfloat16 caches are supported", fn);
   const DecodeLayout L = decode_layout(*dims, dims->capacity, side_cap);
   if (workspace_bytes < L.total)
     return fail(LRKV_ERR_WORKSPACE_TOO_SMALL, "%s: workspace of %zu bytes, %zu needed", fn, workspace_bytes, L.total);
   char* ws = static_cast<char*>(workspace);
   const int g = dims->n_q_heads / dims->n_kv_heads;
-  const bool bf16 = dtype == LRKV_BF16;
-  const float qscale = resolve_scale(scale, dims->head_dim) * kLog2eHost;
 
   SplitArgs sa{};
   sa.q = q; sa.basis_k = basis_k; sa.ck = coeff_k; sa.cv = coeff_v; sa.basis_v = basis_v;
   sa.cap = dims->capacity; sa.rk = dims->rank_k; sa.rv = dims->rank_v; sa.d = dims->head_dim;
   sa.g = g; sa.hq = dims->n_q_heads; sa.hkv = dims->n_kv_heads; sa.batch = dims->batch;
   sa.n_static = 0; sa.n_dev = n_lr;
-  sa.chunks_per_split = L.lr.chunks_per_split; sa.n_splits = L.lr.n_splits; sa.n_parts = L.parts_lr;
-  sa.qscale = qscale;
-  sa.part_o = reinterpret_cast<float*>(ws + L.o_lr);
-  sa.part_ml = reinterpret_cast<float*>(ws + L.ml_lr);
+  sa.n_parts = L.parts;   // chunks per split are planned on the device
+  sa.qscale = resolve_scale(scale, dims->head_dim) * kLog2eHost;
+  sa.part_o = reinterpret_cast<float*>(ws + L.o);
+  sa.part_ml = reinterpret_cast<float*>(ws + L.ml);
+  sa.counters = reinterpret_cast<int32_t*>(ws + L.counters);
+  sa.out = out;
+  sa.lse = lse;
   SplitArgs ss = sa;   // side list: full-rank rows, no fold and no lift
   ss.basis_k = nullptr; ss.basis_v = nullptr; ss.ck = k_side; ss.cv = v_side; ss.cap = side_cap;
   ss.rk = dims->head_dim; ss.rv = dims->head_dim; ss.n_dev = n_side;
-  ss.chunks_per_split = L.side.chunks_per_split; ss.n_splits = L.side.n_splits; ss.n_parts = L.parts_side;
-  ss.part_o = reinterpret_cast<float*>(ws + L.o_side);
-  ss.part_ml = reinterpret_cast<float*>(ws + L.ml_side);
-  hipError_t e;
-  if (bf16) {
-    e = launch_split_bf16_hybrid(sa, ss, stream);
-  } else {
-    e = launch_split_f32(sa, stream);
-    if (e == hipSuccess) e = launch_split_f32(ss, stream);
-  }
-  if (e != hipSuccess) return device_fail(fn, e);
-
-  MergeArgs ma{};
-  ma.part_o = sa.part_o; ma.part_ml = sa.part_ml; ma.n_parts = L.parts_lr;
-  ma.side_o = ss.part_o; ma.side_ml = ss.part_ml; ma.n_side_parts = L.parts_side;
-  ma.d = dims->head_dim; ma.hq = dims->n_q_heads; ma.batch = dims->batch;
-  ma.out = out; ma.lse = lse;
-  e = launch_merge(ma, bf16, stream);
+  const hipError_t e = launch_split_bf16_hybrid(sa, ss, L.parts, stream);
   return e == hipSuccess ? LRKV_OK : device_fail(fn, e);
 }
 

@@ -27,16 +27,22 @@ struct SplitArgs {
   const int32_t* n_dev;  // per-(b, h) token counts on the device, or null
   int chunks_per_split;
   int n_splits;
-  int n_parts;           // workgroups per (b, h) = ceil(n_splits / kSplitsPerPart)
+  int n_parts;           // partials per (b, q head): one per attention workgroup
   float qscale;          // softmax scale * log2(e)
   float* part_o;         // [B, Hq, n_parts, d]  unnormalised outputs
   float* part_ml;        // [B, Hq, n_parts, 2]  running max (log2 units), softmax sum
+  // Fused merge: when counters is non-null, the last workgroup of each
+  // (b, kv head) to finish (counted on counters[b * Hkv + h], which must be
+  // zero on entry and is left zero) merges the partials into out and lse.
+  int32_t* counters;     // [B, Hkv] or null
+  void* out;             // [B, Hq, d] storage dtype
+  float* lse;            // [B, Hq] or null
 };
 
+// Log-sum-exp merge of n_parts partials per (b, q head).
 struct MergeArgs {
   const float* part_o; const float* part_ml; int n_parts;
-  const float* side_o; const float* side_ml; int n_side_parts;   // hybrid only
-  int d, hq, batch;
+  int d, g, hq, hkv, batch;
   void* out;             // [B, Hq, d]
   float* lse;            // [B, Hq] or null
 };
@@ -57,8 +63,11 @@ struct CompressKvArgs {
 };
 
 hipError_t launch_split_bf16(const SplitArgs& a, hipStream_t s);
-// Hybrid cache: low-rank rows (lr) and full-rank side list (side) in one launch.
-hipError_t launch_split_bf16_hybrid(const SplitArgs& lr, const SplitArgs& side, hipStream_t s);
+// Hybrid cache: low-rank rows (lr) and full-rank side list (side) in one
+// launch of wgs_per_unit workgroups per (b, kv head), divided between the two
+// lists on the device from the counts there.  Partials go to lr.part_o /
+// lr.part_ml with lr.n_parts = wgs_per_unit.
+hipError_t launch_split_bf16_hybrid(const SplitArgs& lr, const SplitArgs& side, int wgs_per_unit, hipStream_t s);
 hipError_t launch_compress_kv_small_bf16(const CompressKvArgs& a, hipStream_t s);
 hipError_t launch_split_f32(const SplitArgs& a, hipStream_t s);
 hipError_t launch_merge(const MergeArgs& a, bool bf16, hipStream_t s);

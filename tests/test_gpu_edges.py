@@ -141,13 +141,15 @@ def test_graph_replay_matches_eager():
 
 
 def test_partial_then_merge_equals_one_call():
-    """The two-phase API runs the same two kernels as the one-call decode."""
+    """The two-phase API (attention kernel, then the merge kernel) gives the
+    same bits as the one-launch decode, whose last workgroup per (b, kv head)
+    runs the same merge code."""
     dev, (o_ref, lse_ref), n = _case(7, n=2222)
     B, Hq, d = dev["q"].shape
     H, _, rk = dev["bk"].shape
     rv = dev["bv"].shape[2]
     cap = dev["ck"].shape[2]
-    ws = torch.empty(lrkv.decode_workspace_bytes(B, Hq, H, d, rk, rv, cap, n), dtype=torch.uint8, device=DEV)
+    ws = torch.zeros(lrkv.decode_workspace_bytes(B, Hq, H, d, rk, rv, cap, n), dtype=torch.uint8, device=DEV)
     o1, l1 = _run(dev, n)
     out = torch.empty_like(dev["q"])
     lse = torch.empty((B, Hq), dtype=torch.float32, device=DEV)
@@ -166,7 +168,7 @@ def test_workspace_reuse_across_calls():
     H, _, rk = dev["bk"].shape
     rv = dev["bv"].shape[2]
     cap = dev["ck"].shape[2]
-    ws = torch.empty(max(lrkv.decode_workspace_bytes(B, Hq, H, d, rk, rv, cap, m) for m in (n, 777, 64)),
+    ws = torch.zeros(max(lrkv.decode_workspace_bytes(B, Hq, H, d, rk, rv, cap, m) for m in (n, 777, 64)),
                      dtype=torch.uint8, device=DEV)
     first = None
     for i, m in enumerate([n, 777, n, 64, n]):
@@ -179,6 +181,8 @@ def test_workspace_reuse_across_calls():
             else:
                 assert torch.equal(o.view(torch.int16), first[0].view(torch.int16)), f"call {i}"
                 assert torch.equal(lse, first[1]), f"call {i}"
+        # the fused merge's per-(b, kv head) counters are left zero by every call
+        assert not torch.any(ws[:4 * B * H]), f"counters not reset after call {i}"
 
 
 def test_explicit_scale():

@@ -226,3 +226,74 @@ def test_hybrid_other_shapes(batch, hq, hkv, d, rk, rv, n):
     check_decode(np.stack([og[r] for r in rows]), np.array([lg[r] for r in rows]),
                  np.stack([o_ref[r][0] for r in rows]), np.array([o_ref[r][1] for r in rows]),
                  "bf16", f"hybrid shape {(batch, hq, hkv, d, rk, rv, n)}")
+
+
+def test_hybrid_decode_uneven_counts_per_unit():
+    """Each (b, kv head) divides its workgroups between the two lists from its
+    own counts on the device: counts that differ per unit, lists that are
+    empty on one side or on both, and a side list much shorter than its
+    capacity all give the oracle's union softmax."""
+    w = synth.scaled(synth.HYBRID_128K, batch=2, n_q_heads=16, n_kv_heads=4, n_ctx=(8192,))
+    B, Hq, H, d = w.batch, w.n_q_heads, w.n_kv_heads, w.head_dim
+    rk, rv = w.ranks(0)
+    cap, side_cap = 8192, 2048
+    n_lr = np.array([[0, 8192, 33, 4096], [1, 0, 7001, 100]], np.int32)
+    n_side = np.array([[64, 0, 1000, 9], [0, 0, 300, 2048]], np.int32)
+    ck = synth.stack_heads(w, lambda b, h: synth.direct_coeffs(w, 0, "k", b, h, cap))
+    cv = synth.stack_heads(w, lambda b, h: synth.direct_coeffs(w, 0, "v", b, h, cap))
+    ks = synth.stack_heads(w, lambda b, h: synth.full_tokens(w, 0, "k", b, h, side_cap, synth.PART_PREFILL))
+    vs = synth.stack_heads(w, lambda b, h: synth.full_tokens(w, 0, "v", b, h, side_cap, synth.PART_PREFILL))
+    bk, bv, q = synth.basis(w, 0, "k"), synth.basis(w, 0, "v"), synth.query(w, 0)
+    c = lrkv.HybridCache(B, Hq, H, d, rk, rv, cap, side_cap, DEV)
+    c.coeff_k.copy_(to_dev(ck, "bf16"))
+    c.coeff_v.copy_(to_dev(synth.to_value_octets(cv.store), "bf16").view(c.coeff_v.shape))
+    c.k_side.copy_(to_dev(ks, "bf16"))
+    c.v_side.copy_(to_dev(synth.to_value_octets(vs.store), "bf16").view(c.v_side.shape))
+    c.n_lr.copy_(torch.from_numpy(n_lr))
+    c.n_side.copy_(torch.from_numpy(n_side))
+    bkd, bvd, qd = (to_dev(x, "bf16") for x in (bk, bv, q))
+    o, lse = lrkv.decode_attn_hybrid(qd, bkd, bvd, c)
+    og, lg = to_f64(o), to_f64(lse)
+    g = Hq // H
+    rows = [(b, hq) for b in range(B) for hq in range(Hq) if n_lr[b, hq // g] + n_side[b, hq // g] > 0]
+    empty = [(b, hq) for b in range(B) for hq in range(Hq) if n_lr[b, hq // g] + n_side[b, hq // g] == 0]
+    keys = [(b, h) for b in range(B) for h in range(H)]
+    o_ref = O.decode_hybrid_rows(q.exact, bk.exact, bv.exact,
+                                 {k: ck.exact[k][:n_lr[k]] for k in keys}, {k: cv.exact[k][:n_lr[k]] for k in keys},
+                                 {k: ks.exact[k][:n_side[k]] for k in keys}, {k: vs.exact[k][:n_side[k]] for k in keys},
+                                 rows)
+    check_decode(np.stack([og[r] for r in rows]), np.array([lg[r] for r in rows]),
+                 np.stack([o_ref[r][0] for r in rows]), np.array([o_ref[r][1] for r in rows]),
+                 "bf16", "hybrid uneven counts")
+    assert empty and all(np.all(og[r] == 0) and np.isneginf(lg[r]) for r in empty)
+
+
+def test_hybrid_tau_zero_keeps_every_token_full_rank():
+    """tau = 0 flags every token with a residual off the basis span (here all
+    of them: full-spectrum tokens leave about 2% of their energy off a rank-64
+    span): nothing is low rank and the hybrid decode is dense attention over
+    the bfloat16 keys and values."""
+    n = 1500
+    w = synth.scaled(synth.HYBRID_128K, n_ctx=(n,))
+    k = synth.tokens_major(synth.stack_heads(w, lambda b, h: synth.full_tokens(w, 0, "k", b, h, n, synth.PART_PREFILL)))
+    v = synth.tokens_major(synth.stack_heads(w, lambda b, h: synth.full_tokens(w, 0, "v", b, h, n, synth.PART_PREFILL)))
+    bk, bv, q = synth.basis(w, 0, "k"), synth.basis(w, 0, "v"), synth.query(w, 0)
+    assert min(O.relative_residual(x[0, :, h], b_.exact[h]).min() for x, b_ in ((k.exact, bk), (v.exact, bv))
+               for h in range(w.n_kv_heads)) > 0.05
+    c = _new_cache(w, n + 4, _round8(n))
+    kd, vd, bkd, bvd, qd = (to_dev(x, "bf16") for x in (k, v, bk, bv, q))
+    lrkv.compress_hybrid(c, kd, vd, bkd, bvd, 0.0, 0)
+    torch.cuda.synchronize()
+    assert c.n_lr.cpu().eq(0).all() and c.n_side.cpu().eq(n).all()
+    o, lse = lrkv.decode_attn_hybrid(qd, bkd, bvd, c)
+    H, g = w.n_kv_heads, w.n_q_heads // w.n_kv_heads
+    rows = [(0, hq) for hq in range(w.n_q_heads)]
+    empty = np.zeros((0, bk.exact.shape[2]))
+    o_ref = O.decode_hybrid_rows(q.exact, bk.exact, bv.exact, {(0, h): empty for h in range(H)},
+                                 {(0, h): np.zeros((0, bv.exact.shape[2])) for h in range(H)},
+                                 {(0, h): k.exact[0, :, h] for h in range(H)},
+                                 {(0, h): v.exact[0, :, h] for h in range(H)}, rows)
+    og, lg = to_f64(o), to_f64(lse)
+    check_decode(np.stack([og[r] for r in rows]), np.array([lg[r] for r in rows]),
+                 np.stack([o_ref[r][0] for r in rows]), np.array([o_ref[r][1] for r in rows]),
+                 "bf16", "hybrid tau = 0")
