@@ -11,12 +11,11 @@ head over all N tokens.
 All inputs are synthetic, seeded, and resident in HBM before timing.
 
 Reported `value`: decode microseconds per layer-step (appended-token
-compress of K and V in one launch + the attention launch, whose last
-workgroup per (batch, kv head) merges the partial results), averaged over the
-32 layers and the timed steps, measured with HIP events on the launch stream.
-The roofline entry is for the attention kernel (split_bf16_kernel, the
-dominant one): its algorithmic bytes per launch (key and value coefficient
-rows, both bases, the queries in and the outputs out) over its average launch
+compress of K and V in one launch + the attention kernel + the merge kernel),
+averaged over the 32 layers and the timed steps, measured with HIP events on
+the launch stream.  The roofline entry is for the attention kernel
+(split_bf16_kernel, the dominant one): its algorithmic bytes per launch (key
+and value coefficient rows, both bases, the queries) over its average launch
 time.  `cpu_baseline` times the float64 CPU oracle on a
 bounded sample of the same decode and scales it to a layer-step.
 
@@ -136,10 +135,11 @@ def main():
             if ev: ev["dec"][l][0].record()
             lrkv.compress_kv(lay["ak"], lay["av"], lay["bk"], lay["bv"], lay["ck"], lay["cv"], N - 1)
             if ev: ev["dec"][l][1].record()
-            # one launch: attention, and the merge in the last workgroup of each (b, kv head)
-            lrkv.decode_attn(lay["q"], lay["bk"], lay["ck"], lay["bv"], lay["cv"], N, out=lay["out"],
-                             lse=lay["lse"], workspace=ws)
+            # lrkv_decode_attn as its two launches, so that the attention kernel is timed alone
+            lrkv.decode_attn_partial(lay["q"], lay["bk"], lay["ck"], lay["bv"], lay["cv"], N, ws)
             if ev: ev["dec"][l][2].record()
+            lrkv.decode_attn_merge(lay["out"], lay["lse"], N, ws, H, lay["rk"], lay["rv"], cap)
+            if ev: ev["dec"][l][3].record()
 
     for _ in range(args.warmup):
         step()
@@ -147,7 +147,7 @@ def main():
 
     K = args.steps
     mk = lambda n: [torch.cuda.Event(enable_timing=True) for _ in range(n)]
-    events = [{"pre": [mk(2) for _ in range(L)], "dec": [mk(3) for _ in range(L)]} for _ in range(K)]
+    events = [{"pre": [mk(2) for _ in range(L)], "dec": [mk(4) for _ in range(L)]} for _ in range(K)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for k in range(K):
@@ -156,7 +156,7 @@ def main():
     wall = time.perf_counter() - t0
     log(f"timed {K} steps in {wall:.3f}s")
 
-    prefill_us, decode_us, attn_us, append_us = [], [], [], []
+    prefill_us, decode_us, attn_us, merge_us, append_us = [], [], [], [], []
     attn_by_par = {0: [], 1: []}
     for k in range(K):
         for l in range(L):
@@ -164,7 +164,8 @@ def main():
             prefill_us.append(ep[0].elapsed_time(ep[1]) * 1e3)
             append_us.append(ed[0].elapsed_time(ed[1]) * 1e3)
             attn_us.append(ed[1].elapsed_time(ed[2]) * 1e3)
-            decode_us.append(ed[0].elapsed_time(ed[2]) * 1e3)
+            merge_us.append(ed[2].elapsed_time(ed[3]) * 1e3)
+            decode_us.append(ed[0].elapsed_time(ed[3]) * 1e3)
             attn_by_par[l % 2].append(attn_us[-1])
 
     # ---------------- bytes and rates
@@ -217,6 +218,7 @@ def main():
         "attn_tokens_per_s": round(tok_s, 1),
         "decode_us_per_step_32_layers": round(step_decode_us, 1),
         "attn_kernel_us": {"even": round(attn_mean[0], 3), "odd": round(attn_mean[1], 3)},
+        "merge_us": round(mean(merge_us), 3),
         "append_compress_us": round(mean(append_us), 3),
         "prefill_compress_us_per_layer": round(mean(prefill_us), 3),
         "prefill_compress_GBps": round(pre_gbps, 1),

@@ -153,11 +153,10 @@ def decode_workspace_bytes(batch, n_q_heads, n_kv_heads, head_dim, rank_k, rank_
 
 
 def _workspace(nbytes: int, device, workspace: Optional[torch.Tensor]) -> torch.Tensor:
-    """The caller's workspace, or a new zero-filled one (decode calls need
-    their counter words zero on entry and leave them zero)."""
+    """The caller's workspace, or a new one."""
     if workspace is not None:
         return workspace
-    return torch.zeros(max(nbytes, 16), dtype=torch.uint8, device=device)
+    return torch.empty(max(nbytes, 16), dtype=torch.uint8, device=device)
 
 
 def decode_attn(q, basis_k, coeff_k, basis_v, coeff_v, n_ctx: int, out=None, lse=None,

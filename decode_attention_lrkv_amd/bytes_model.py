@@ -43,11 +43,12 @@ def decode_bytes(batch, n_q_heads, n_kv_heads, head_dim, rank_k, rank_v, n_ctx, 
 
 
 def split_kernel_bytes(batch, n_q_heads, n_kv_heads, head_dim, rank_k, rank_v, n_ctx, elem_bytes=2):
-    """The attention kernel (one launch; its last workgroup per (b, kv head)
-    merges): C_K and C_V rows, both bases (B_K folds the query, B_V lifts each
-    workgroup's partial), the queries in and the outputs out.  Its float32
+    """The attention kernel alone: C_K and C_V rows, both bases (B_K folds the
+    query, B_V lifts each workgroup's partial) and the queries.  Its float32
     partials (a few KB per workgroup) are workspace traffic, not counted."""
-    return decode_bytes(batch, n_q_heads, n_kv_heads, head_dim, rank_k, rank_v, n_ctx, elem_bytes)
+    s = elem_bytes
+    return (s * batch * n_kv_heads * n_ctx * (rank_k + rank_v) + s * n_kv_heads * head_dim * (rank_k + rank_v)
+            + s * batch * n_q_heads * head_dim)
 
 
 def compress_bytes(batch, n_tokens, n_kv_heads, head_dim, rank, elem_bytes=2):

@@ -35,13 +35,7 @@ __device__ __forceinline__ float load_f<uint16_t>(const uint16_t* p, int64_t i) 
 template <>
 __device__ __forceinline__ float load_f<float>(const float* p, int64_t i) { return p[i]; }
 
-// Partials are stored and, by the workgroup that merges them inside the same
-// launch, loaded at device scope: these accesses go to the coherence point
-// shared by all XCDs instead of staying in one XCD's L2, so no cache has to
-// be written back or invalidated for the merging workgroup to see them.
-__device__ __forceinline__ void store_partial(float* p, float v) {
-  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
+__device__ __forceinline__ void store_partial(float* p, float v) { *p = v; }
 
 template <typename T>
 __device__ __forceinline__ void store_f(T* p, int64_t i, float v);
@@ -131,10 +125,7 @@ __device__ void workgroup_partial(const SplitArgs& a, int b, int h, int part, co
 // partials grp, grp + 64 / (d / 4), ... into a running (max, sum, output)
 // in ascending order, issuing the loads of sixteen partials at a time, and the
 // lane groups are then combined pairwise (the lower lane's state first, so
-// that both lanes of a pair compute the same bits).  The same code serves the
-// merge kernel and the workgroup that finishes a fused decode, so both give
-// the same bits; kCoherent makes the loads device-scope (the partials were
-// written by workgroups of the same launch, possibly on another XCD).
+// that both lanes of a pair compute the same bits).
 struct MergeState {
   float m, l;
   f32x4 o;
@@ -152,10 +143,9 @@ __device__ __forceinline__ MergeState merge_two(const MergeState& a, const Merge
   return r;
 }
 
-template <typename T, bool kCoherent>
+template <typename T>
 __device__ void merge_unit(const MergeArgs& a, int64_t unit) {
   constexpr int kU = 16;
-  constexpr int kAux = kCoherent ? 16 : 0;   // cache policy: sc1, device-scope coherent
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int S = a.n_parts, d = a.d, g = a.g;
   const int cols = d / 4, groups = 64 / cols;
@@ -171,9 +161,8 @@ __device__ void merge_unit(const MergeArgs& a, int64_t unit) {
 #pragma unroll
       for (int u = 0; u < kU; ++u) {
         const uint32_t s = (uint32_t)(s0 + u * groups);
-        ml[u] = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rs_ml, (int)(s * 8), 0, kAux));
-        ov[u] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
-                                                  rs_o, (int)((s * d + 4 * col) * 4), 0, kAux));
+        ml[u] = buf_load8(rs_ml, s * 8);
+        ov[u] = buf_load16(rs_o, (s * d + 4 * col) * 4);
       }
 #pragma unroll
       for (int u = 0; u < kU; ++u) {
@@ -203,34 +192,6 @@ __device__ void merge_unit(const MergeArgs& a, int64_t unit) {
     }
     if (lane == 0 && a.lse) a.lse[row] = st.l > 0.f ? (st.m + __log2f(st.l)) * kLn2 : -INFINITY;
   }
-}
-
-// Fused merge: every workgroup of a (b, kv head) takes a ticket once its
-// partial is written; the one that draws the last ticket merges the unit and
-// puts the counter back to zero.  The partials were stored at device scope;
-// each wave waits until its stores are acknowledged before the workgroup
-// takes its ticket, and the merging workgroup loads them at device scope, so
-// partials written on other XCDs are seen without cache maintenance.
-// No workgroup waits for another.
-template <typename T>
-__device__ void finish_unit(const SplitArgs& a, int b, int h) {
-  if (a.counters == nullptr) return;
-  __shared__ int s_last;
-  const int64_t bh = (int64_t)b * a.hkv + h;
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    const int t = __hip_atomic_fetch_add(a.counters + bh, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    s_last = t == a.n_parts - 1;
-  }
-  __syncthreads();
-  if (!s_last) return;
-  MergeArgs m;
-  m.part_o = a.part_o; m.part_ml = a.part_ml; m.n_parts = a.n_parts;
-  m.d = a.d; m.g = a.g; m.hq = a.hq; m.hkv = a.hkv; m.batch = a.batch;
-  m.out = a.out; m.lse = a.lse;
-  merge_unit<T, true>(m, bh);
-  if (threadIdx.x == 0) __hip_atomic_store(a.counters + bh, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // ----------------------------------------------------------------------------
@@ -334,8 +295,14 @@ __device__ __forceinline__ void split_bf16_body(const SplitArgs& a, int wg, int 
   {
     // every load of the prologue, and the first chunk's, is issued before the first wait
     const uint16_t* q = static_cast<const uint16_t*>(a.q) + ((int64_t)b * a.hq + (int64_t)h * g) * d;
-    const int nq = g * d / 8;                       // <= 128 sixteen-byte pieces
+    const int nq = FOLD ? 0 : g * d / 8;            // <= 128 sixteen-byte pieces
     const u32x4 wq = tid < nq ? *reinterpret_cast<const u32x4*>(q + 8 * tid) : u32x4{0u, 0u, 0u, 0u};
+    // the fold's row operand: lane (n16, grp) holds q[head n16][32 c + 8 grp .. + 7]
+    u32x4 qa[4];
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+      qa[c] = (FOLD && n16 < g && 32 * c < d) ? *reinterpret_cast<const u32x4*>(q + n16 * d + 32 * c + 8 * grp)
+                                              : u32x4{0u, 0u, 0u, 0u};
     constexpr int kBkIter = 8;                      // d * rk / 8 <= 2048 = 8 * 256
     u32x4 wb[kBkIter];
     const uint16_t* bk = FOLD ? static_cast<const uint16_t*>(a.basis_k) + (int64_t)h * d * rk : nullptr;
@@ -375,12 +342,29 @@ __device__ __forceinline__ void split_bf16_body(const SplitArgs& a, int wg, int 
     }
     __syncthreads();
     if (FOLD) {
-      for (int i = tid; i < g * rk; i += 256) {
-        const int j = i / rk, k = i - j * rk;
-        float acc = 0.f;
-#pragma unroll 8
-        for (int e = 0; e < d; ++e) acc = fmaf(s_q[j * d + e], bf16_to_f32(s_bk[e * rk + k]), acc);
-        s_qf[i] = acc * a.qscale;
+      // on the matrix cores: wave w takes the 16-column blocks w, w + 4, ... of q' = q B_K;
+      // the column operand, lane (n16, grp): B_K[32 c + 8 grp + e][16 nb + n16], e < 8
+      for (int nb = wave; nb * 16 < rk; nb += kWaves) {
+        const int col = 16 * nb + n16;
+        f32x4 f = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          if (32 * c < d) {
+            uint32_t w4[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const int r0 = 32 * c + 8 * grp + 2 * e;
+              const uint32_t lo = col < rk ? s_bk[r0 * rk + col] : 0u;
+              const uint32_t hi = col < rk ? s_bk[(r0 + 1) * rk + col] : 0u;
+              w4[e] = lo | (hi << 16);
+            }
+            f = mfma_16x16x32(qa[c], u32x4{w4[0], w4[1], w4[2], w4[3]}, f);
+          }
+        }
+        // lane (n16, grp) register i: q' of head 4 grp + i, column col
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          if (4 * grp + i < g && col < rk) s_qf[(4 * grp + i) * rk + col] = f[i] * a.qscale;
       }
     } else {
       for (int i = tid; i < g * d; i += 256) s_qf[i] = s_q[i] * a.qscale;
@@ -507,12 +491,26 @@ __device__ __forceinline__ void split_bf16_body(const SplitArgs& a, int wg, int 
     }
   }
 
-  // --- epilogue: rows j (high part) + rows g + j (low part) are head j
-  __syncthreads();   // the prologue's LDS is reused below
+  // --- epilogue
+  // 1. Head j of the wave is accumulator row j (high part of p) plus row g + j
+  //    (low part).  Row r lives in lane group r / 4, register r % 4, so for the
+  //    lane holding row 4 grp + i the partner row sits 16 (g + i) / 4 lanes up,
+  //    in register (g + i) % 4 (the same for every lane of the wave).
+  //    The LDS written here (s_acc over the prologue's B_K, s_ml) was last read
+  //    before the fold's barrier, so no barrier is needed first.
+  {
 #pragma unroll
-  for (int vb = 0; vb < VB; ++vb)
+    for (int i = 0; i < 4; ++i) {
+      const int sr = (g + i) & 3;
+      const int src = lane + 16 * ((g + i) >> 2);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) s_acc[wave][4 * grp + i][16 * vb + n16] = acc[vb][i];
+      for (int vb = 0; vb < VB; ++vb) {
+        const float v = sr == 0 ? acc[vb][0] : (sr == 1 ? acc[vb][1] : (sr == 2 ? acc[vb][2] : acc[vb][3]));
+        const float lo = __shfl(v, src & 63);
+        if (4 * grp + i < g) s_acc[wave][4 * grp + i][16 * vb + n16] = acc[vb][i] + lo;
+      }
+    }
+  }
   float l_tot = l_run + __shfl_xor(l_run, 16);
   l_tot += __shfl_xor(l_tot, 32);
   if (lane < g) {
@@ -520,12 +518,74 @@ __device__ __forceinline__ void split_bf16_body(const SplitArgs& a, int wg, int 
     s_ml[wave][lane][1] = l_tot;
   }
   __syncthreads();
-  for (int i = tid; i < kWaves * g * rv; i += 256) {
-    const int w = i / (g * rv), r = i - w * g * rv, j = r / rv, c = r - j * rv;
-    s_acc[w][j][c] += s_acc[w][g + j][c];
+  // 2. the four waves merged: M = max_w m_w, acc = sum_w 2^(m_w - M) acc_w, likewise the sum
+  float* s_merged = s_qf;   // the query operand was read before the main loop
+  for (int i = tid; i < g * rv; i += 256) {
+    const int j = i / rv, c = i - j * rv;
+    float M = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) M = fmaxf(M, s_ml[w][j][0]);
+    float o = 0.f;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+      const float m = s_ml[w][j][0];
+      o = fmaf(m == -INFINITY ? 0.f : exp2_fast(m - M), s_acc[w][j][c], o);
+    }
+    s_merged[j * 128 + c] = o;
+  }
+  const int64_t row0 = (int64_t)b * a.hq + (int64_t)h * g;
+  if (tid < g) {
+    float M = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) M = fmaxf(M, s_ml[w][tid][0]);
+    float L = 0.f;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+      const float m = s_ml[w][tid][0];
+      L = fmaf(m == -INFINITY ? 0.f : exp2_fast(m - M), s_ml[w][tid][1], L);
+    }
+    store_partial(a.part_ml + ((row0 + tid) * a.n_parts + part) * 2 + 0, M);
+    store_partial(a.part_ml + ((row0 + tid) * a.n_parts + part) * 2 + 1, L);
   }
   __syncthreads();
-  workgroup_partial<uint16_t>(a, b, h, part, &s_acc[0][0][0], VB * 16, s_ml, sm.bv, s_qf);
+  // 3. lift o = acc B_V^T on the matrix cores: wave w takes the 16-dim blocks
+  //    w, w + 4, ...; the row operand is acc (head n16) split into high and
+  //    low bfloat16 parts, the column operand B_V[dim][32 c + 8 grp .. + 7]
+  //    straight from the staged rows.  Full-rank values (side list) are the
+  //    output as they are.
+  float* po = a.part_o;
+  if (FOLD) {
+    const int ldb = rv + 8;
+    for (int nd = wave; nd * 16 < d; nd += kWaves) {
+      const int dim = 16 * nd + n16;
+      f32x4 o = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int c = 0; 32 * c < rv; ++c) {
+        const int k0 = 32 * c + 8 * grp;
+        const bool kv = k0 < rv;   // rv is a multiple of 8: a lane group is all in or all out
+        float v[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[e] = (kv && n16 < g) ? s_merged[n16 * 128 + k0 + e] : 0.f;
+        uint32_t hi[4], lo[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          hi[e] = pack_bf16(v[2 * e], v[2 * e + 1]);
+          lo[e] = pack_bf16(v[2 * e] - bf16_lo(hi[e]), v[2 * e + 1] - bf16_hi(hi[e]));
+        }
+        const u32x4 bvw = kv ? *reinterpret_cast<const u32x4*>(sm.bv + dim * ldb + k0) : u32x4{0u, 0u, 0u, 0u};
+        o = mfma_16x16x32(u32x4{hi[0], hi[1], hi[2], hi[3]}, bvw, o);
+        o = mfma_16x16x32(u32x4{lo[0], lo[1], lo[2], lo[3]}, bvw, o);
+      }
+      // lane (n16, grp) register i: head 4 grp + i, dim
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        if (4 * grp + i < g) store_partial(po + ((row0 + 4 * grp + i) * a.n_parts + part) * d + dim, o[i]);
+    }
+  } else {
+    for (int i = tid; i < g * d; i += 256) {
+      const int j = i / d, dd = i - j * d;
+      store_partial(po + ((row0 + j) * a.n_parts + part) * d + dd, s_merged[j * 128 + dd]);
+    }
+  }
 }
 
 // Chunks in flight per wave: two unless that no longer fits two waves per
@@ -539,7 +599,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void split_bf16_kernel(SplitArgs a) {
   __shared__ SplitSmem sm;
   split_bf16_body<KC, VB, true, kStages<KC, VB>>(a, blockIdx.x, blockIdx.x, sm);
-  finish_unit<uint16_t>(a, blockIdx.z, blockIdx.y);
 }
 
 // Hybrid cache in one launch: the gridDim.x workgroups of each (b, kv head)
@@ -547,7 +606,7 @@ void split_bf16_kernel(SplitArgs a) {
 // no fold and no lift, single-buffered so that both fit two waves per SIMD)
 // in proportion to the bytes each list holds, from the counts on the device;
 // within a list, each wave takes an equal run of chunks.  Every workgroup
-// writes partial blockIdx.x; the last one to finish merges them.
+// writes partial blockIdx.x.
 template <int KC, int VB, int SKC, int SVB>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void split_bf16_hybrid_kernel(SplitArgs lr, SplitArgs side) {
@@ -581,7 +640,6 @@ void split_bf16_hybrid_kernel(SplitArgs lr, SplitArgs side) {
     a.chunks_per_split = (int)((ch_side + p_side * kWaves - 1) / (p_side * kWaves));
     split_bf16_body<SKC, SVB, false, 1>(a, x - (int)p_lr, x, sm);
   }
-  finish_unit<uint16_t>(lr, blockIdx.z, blockIdx.y);
 }
 
 // ----------------------------------------------------------------------------
@@ -709,7 +767,6 @@ __global__ __launch_bounds__(256) void split_f32_kernel(SplitArgs a) {
   }
   __syncthreads();
   workgroup_partial<float>(a, b, h, blockIdx.x, &s_acc[0][0][0], 128, s_ml, nullptr, s_qf);
-  finish_unit<float>(a, b, h);
 }
 
 // ----------------------------------------------------------------------------
@@ -717,7 +774,7 @@ __global__ __launch_bounds__(256) void split_f32_kernel(SplitArgs a) {
 // ----------------------------------------------------------------------------
 template <typename T>
 __global__ __launch_bounds__(256) void merge_kernel(MergeArgs a) {
-  merge_unit<T, false>(a, blockIdx.x);
+  merge_unit<T>(a, blockIdx.x);
 }
 
 }  // namespace

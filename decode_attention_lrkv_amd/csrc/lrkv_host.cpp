@@ -79,12 +79,12 @@ Plan plan_splits(int64_t units, int64_t n_tokens, int cus, int max_splits) {
   return p;
 }
 
-// Decode workspace: fused-merge counters [B, Hkv] int32 first, then the
-// partials [B, Hq, parts, d] and their (max, sum) [B, Hq, parts, 2].
+// Decode workspace: the partials [B, Hq, parts, d] and their (max, sum)
+// [B, Hq, parts, 2].
 struct DecodeLayout {
   Plan lr;             // plain decode: splits of the context
   int parts = 0;       // partials per (b, q head): one per attention workgroup
-  size_t counters = 0, o = 0, ml = 0, total = 0;
+  size_t o = 0, ml = 0, total = 0;
 };
 
 DecodeLayout decode_layout(const lrkv_dims& d, int64_t n_lr_tokens, int64_t side_cap) {
@@ -93,11 +93,12 @@ DecodeLayout decode_layout(const lrkv_dims& d, int64_t n_lr_tokens, int64_t side
   const int64_t units = (int64_t)d.batch * d.n_kv_heads;
   const int64_t rows = (int64_t)d.batch * d.n_q_heads;
   if (side_cap > 0) {
-    // hybrid: one round of workgroups (two per compute unit), divided between
-    // the two lists on the device; at least one per list, and no more than
-    // one chunk per wave of the largest possible lists
+    // hybrid: one workgroup per compute unit (measured faster than two: the
+    // streams stay as long as possible and the merge has half the partials),
+    // divided between the two lists on the device; at least one per list,
+    // and no more than one chunk per wave of the largest possible lists
     const int64_t chunks = cdiv(n_lr_tokens, kChunk) + cdiv(side_cap, kChunk);
-    int64_t p = (2 * (int64_t)cus) / units;
+    int64_t p = (int64_t)cus / units;
     p = std::min<int64_t>(p, cdiv(chunks, kSplitsPerPart));
     p = std::min<int64_t>(p, kMaxSplits / kSplitsPerPart);
     if (const char* env = std::getenv("LRKV_HYBRID_WGS")) {   // forced workgroups per (b, kv head)
@@ -110,7 +111,6 @@ DecodeLayout decode_layout(const lrkv_dims& d, int64_t n_lr_tokens, int64_t side
     L.parts = (int)cdiv(L.lr.n_splits, kSplitsPerPart);
   }
   size_t off = 0;
-  L.counters = off; off = align256(off + sizeof(int32_t) * units);
   L.o = off;        off = align256(off + sizeof(float) * rows * L.parts * d.head_dim);
   L.ml = off;       off = align256(off + sizeof(float) * rows * L.parts * 2);
   L.total = off;
@@ -274,7 +274,7 @@ lrkv_status check_decode_common(const lrkv_dims* dims, int64_t n_ctx, lrkv_dtype
 lrkv_status decode_partial(const void* q, const void* basis_k, const void* coeff_k, const void* basis_v,
                            const void* coeff_v, const lrkv_dims* dims, int64_t n_ctx, float scale,
                            lrkv_dtype dtype, void* workspace, const DecodeLayout& L, hipStream_t stream,
-                           const char* fn, void* fused_out = nullptr, float* fused_lse = nullptr) {
+                           const char* fn) {
   char* ws = static_cast<char*>(workspace);
   SplitArgs sa{};
   sa.q = q; sa.basis_k = basis_k; sa.ck = coeff_k; sa.cv = coeff_v; sa.basis_v = basis_v;
@@ -286,11 +286,6 @@ lrkv_status decode_partial(const void* q, const void* basis_k, const void* coeff
   sa.qscale = resolve_scale(scale, dims->head_dim) * kLog2eHost;
   sa.part_o = reinterpret_cast<float*>(ws + L.o);
   sa.part_ml = reinterpret_cast<float*>(ws + L.ml);
-  if (fused_out) {
-    sa.counters = reinterpret_cast<int32_t*>(ws + L.counters);
-    sa.out = fused_out;
-    sa.lse = fused_lse;
-  }
   const hipError_t e = dtype == LRKV_BF16 ? launch_split_bf16(sa, stream) : launch_split_f32(sa, stream);
   return e == hipSuccess ? LRKV_OK : device_fail(fn, e);
 }
@@ -329,9 +324,9 @@ lrkv_status lrkv_decode_attn(const void* q, const void* basis_k, const void* coe
   LRKV_CHECK_PTR(coeff_v, fn);
   LRKV_CHECK_PTR(out, fn);
   if (lse && !aligned16(lse)) return fail(LRKV_ERR_INVALID_ARGUMENT, "%s: lse is not 16-byte aligned", fn);
-  // one launch: the last workgroup of each (b, kv head) merges
-  return decode_partial(q, basis_k, coeff_k, basis_v, coeff_v, dims, n_ctx, scale, dtype, workspace, L, stream,
-                        fn, out, lse);
+  st = decode_partial(q, basis_k, coeff_k, basis_v, coeff_v, dims, n_ctx, scale, dtype, workspace, L, stream, fn);
+  if (st != LRKV_OK) return st;
+  return decode_merge(out, lse, dims, dtype, workspace, L, stream, fn);
 }
 
 lrkv_status lrkv_decode_attn_partial(const void* q, const void* basis_k, const void* coeff_k,
@@ -469,13 +464,16 @@ lrkv_status lrkv_decode_attn_hybrid(const void* q, const void* basis_k, const vo
   sa.qscale = resolve_scale(scale, dims->head_dim) * kLog2eHost;
   sa.part_o = reinterpret_cast<float*>(ws + L.o);
   sa.part_ml = reinterpret_cast<float*>(ws + L.ml);
-  sa.counters = reinterpret_cast<int32_t*>(ws + L.counters);
-  sa.out = out;
-  sa.lse = lse;
   SplitArgs ss = sa;   // side list: full-rank rows, no fold and no lift
   ss.basis_k = nullptr; ss.basis_v = nullptr; ss.ck = k_side; ss.cv = v_side; ss.cap = side_cap;
   ss.rk = dims->head_dim; ss.rv = dims->head_dim; ss.n_dev = n_side;
-  const hipError_t e = launch_split_bf16_hybrid(sa, ss, L.parts, stream);
+  hipError_t e = launch_split_bf16_hybrid(sa, ss, L.parts, stream);
+  if (e != hipSuccess) return device_fail(fn, e);
+  MergeArgs ma{};
+  ma.part_o = sa.part_o; ma.part_ml = sa.part_ml; ma.n_parts = L.parts;
+  ma.d = dims->head_dim; ma.g = g; ma.hq = dims->n_q_heads; ma.hkv = dims->n_kv_heads; ma.batch = dims->batch;
+  ma.out = out; ma.lse = lse;
+  e = launch_merge(ma, true, stream);
   return e == hipSuccess ? LRKV_OK : device_fail(fn, e);
 }
 

@@ -31,12 +31,6 @@ struct SplitArgs {
   float qscale;          // softmax scale * log2(e)
   float* part_o;         // [B, Hq, n_parts, d]  unnormalised outputs
   float* part_ml;        // [B, Hq, n_parts, 2]  running max (log2 units), softmax sum
-  // Fused merge: when counters is non-null, the last workgroup of each
-  // (b, kv head) to finish (counted on counters[b * Hkv + h], which must be
-  // zero on entry and is left zero) merges the partials into out and lse.
-  int32_t* counters;     // [B, Hkv] or null
-  void* out;             // [B, Hq, d] storage dtype
-  float* lse;            // [B, Hq] or null
 };
 
 // Log-sum-exp merge of n_parts partials per (b, q head).
@@ -66,7 +60,7 @@ hipError_t launch_split_bf16(const SplitArgs& a, hipStream_t s);
 // Hybrid cache: low-rank rows (lr) and full-rank side list (side) in one
 // launch of wgs_per_unit workgroups per (b, kv head), divided between the two
 // lists on the device from the counts there.  Partials go to lr.part_o /
-// lr.part_ml with lr.n_parts = wgs_per_unit.
+// lr.part_ml with lr.n_parts = wgs_per_unit; launch_merge combines them.
 hipError_t launch_split_bf16_hybrid(const SplitArgs& lr, const SplitArgs& side, int wgs_per_unit, hipStream_t s);
 hipError_t launch_compress_kv_small_bf16(const CompressKvArgs& a, hipStream_t s);
 hipError_t launch_split_f32(const SplitArgs& a, hipStream_t s);

@@ -118,13 +118,9 @@ lrkv_status lrkv_compress_kv(const void* xk, const void* xv, const void* basis_k
  * dims->capacity and side_cap instead.  Returns 0 for invalid dims.  The
  * split plan depends on the current device's compute-unit count, so query on
  * the device that will run the call.
- *
- * Decode workspace contract: its first 4 * B * Hkv bytes are per-(b, kv head)
- * int32 counters that must be zero when a decode call starts; every decode
- * call leaves them zero when it completes.  Zero-fill a new workspace once
- * (hipMemsetAsync before capture, or a fill kernel) and again only after a
- * call that failed on the device.  The rest is scratch.  Calls that share a
- * workspace must be ordered on one stream (they must not overlap in time).
+ * The workspace is scratch (no initial contents are needed); calls that
+ * share a workspace must be ordered on one stream (they must not overlap in
+ * time).
  */
 size_t lrkv_decode_workspace_bytes(const lrkv_dims* dims, int64_t n_ctx, int64_t side_cap);
 
@@ -136,16 +132,14 @@ size_t lrkv_decode_workspace_bytes(const lrkv_dims* dims, int64_t n_ctx, int64_t
  * which equals softmax(q K_hat^T * scale) V_hat with K_hat = C_K B_K^T and
  * V_hat = C_V B_V^T ("OjaKV" README, StaticPCA: standard attention over
  * keys and values reconstructed from the low-rank cache).  The context is
- * split into chunks attended in parallel; one kernel launch attends them,
- * and the last workgroup of each (b, kv head) to finish merges the partial
- * results by log-sum-exp (no workgroup waits for another).
+ * split into chunks attended in parallel (one launch) and the partial
+ * results are merged by log-sum-exp (a second launch).
  *   q        [B, Hq, d]
  *   basis_k  [Hkv, d, r_K];   coeff_k  key row layout [B, Hkv, capacity, r_K]
  *   basis_v  [Hkv, d, r_V];   coeff_v  value octet layout [B, Hkv, capacity/8, r_V, 8]
  *   out      [B, Hq, d] (storage dtype);  lse [B, Hq] float32 natural log, or NULL
  *   scale    softmax scale; 0 selects 1/sqrt(head_dim)
- *   workspace at least lrkv_decode_workspace_bytes(dims, n_ctx, 0) bytes, zero-filled
- *            before its first use (see the workspace contract above)
+ *   workspace at least lrkv_decode_workspace_bytes(dims, n_ctx, 0) bytes
  * Requires 1 <= n_ctx <= capacity.
  */
 lrkv_status lrkv_decode_attn(const void* q, const void* basis_k, const void* coeff_k,
@@ -162,9 +156,7 @@ lrkv_status lrkv_decode_attn(const void* q, const void* basis_k, const void* coe
  *             unnormalised head_dim-wide output in the workspace;
  *   _merge    combines those by log-sum-exp into out and lse.
  * The split plan is a function of dims, n_ctx and the device, so both phases
- * must see the same values.  _partial neither reads nor writes the counter
- * words of the workspace.  lrkv_decode_attn gives the same bits as the two
- * phases (the merge code is shared).  Splitting the call lets a caller time the phases
+ * must see the same values.  Splitting the call lets a caller time the phases
  * or combine partial results computed elsewhere (for example on other GPUs,
  * each holding a range of the context) before the merge.
  */
@@ -219,11 +211,10 @@ lrkv_status lrkv_compress_hybrid(const void* k, const void* v, const void* basis
  *   out = (sum_lr p_t C_V[t] B_V^T + sum_side p_j v_j),  p = softmax over both sets
  * with s_t = q' . C_K[t] for low-rank tokens and s_j = scale q . k_j for side tokens.
  * Counts are read on the device; an empty (b, h) gives out = 0, lse = -inf.
- * One launch: each (b, kv head) gets a fixed number of workgroups, divided
- * between the two lists on the device in proportion to the bytes the counts
- * there describe; the last workgroup to finish merges.  bfloat16 only.
- *   workspace at least lrkv_decode_workspace_bytes(dims, 0, side_cap) bytes, zero-filled
- *             before its first use (see the workspace contract above).
+ * Each (b, kv head) gets a fixed number of workgroups, divided between the
+ * two lists on the device in proportion to the bytes the counts there
+ * describe; a second launch merges.  bfloat16 only.
+ *   workspace at least lrkv_decode_workspace_bytes(dims, 0, side_cap) bytes.
  */
 lrkv_status lrkv_decode_attn_hybrid(const void* q, const void* basis_k, const void* coeff_k,
                                     const void* basis_v, const void* coeff_v,

@@ -141,9 +141,7 @@ def test_graph_replay_matches_eager():
 
 
 def test_partial_then_merge_equals_one_call():
-    """The two-phase API (attention kernel, then the merge kernel) gives the
-    same bits as the one-launch decode, whose last workgroup per (b, kv head)
-    runs the same merge code."""
+    """The two-phase API runs the same two kernels as the one-call decode."""
     dev, (o_ref, lse_ref), n = _case(7, n=2222)
     B, Hq, d = dev["q"].shape
     H, _, rk = dev["bk"].shape
@@ -181,8 +179,6 @@ def test_workspace_reuse_across_calls():
             else:
                 assert torch.equal(o.view(torch.int16), first[0].view(torch.int16)), f"call {i}"
                 assert torch.equal(lse, first[1]), f"call {i}"
-        # the fused merge's per-(b, kv head) counters are left zero by every call
-        assert not torch.any(ws[:4 * B * H]), f"counters not reset after call {i}"
 
 
 def test_explicit_scale():
