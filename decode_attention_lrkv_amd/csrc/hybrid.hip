@@ -16,9 +16,9 @@
 //           among the sub-tile's tokens of the same kind (a wave ballot).
 // Select and write are persistent: a workgroup stages the bases in LDS once
 // (sized to the ranks) and each of its waves walks a contiguous run of
-// 16-token sub-tiles of one (b, kv head), loading the next sub-tile's key and
-// value rows (and, in write, its flags and offsets) while it works on the
-// current one.  Contiguous runs keep the partial writes of a value octet or a
+// 16-token sub-tiles of one (b, kv head), loading the next two sub-tiles' key
+// and value rows (and, in write, their flags and offsets) while it works on
+// the current one.  Contiguous runs keep the partial writes of a value octet or a
 // flag line that straddles two sub-tiles inside one L2.
 #include <type_traits>
 
@@ -231,33 +231,45 @@ void hybrid_select_kernel(HybridArgs a) {
     return e2 > a.tau2 * n2;
   };
 
-  // keys and values of the current sub-tile; those of the next are in flight meanwhile
-  u32x4 xk[D / 32], xv[D / 32], nk[D / 32], nv[D / 32];
-  if (sub < sub_end) {
-    load_rows<D>(a, b, h, 0, sub, true, n16, grp, xk);
-    load_rows<D>(a, b, h, 1, sub, true, n16, grp, xv);
-  }
-  for (; sub < sub_end; ++sub) {
-    const bool more = sub + 1 < sub_end;
-    load_rows<D>(a, b, h, 0, more ? sub + 1 : sub, more, n16, grp, nk);
-    load_rows<D>(a, b, h, 1, more ? sub + 1 : sub, more, n16, grp, nv);
+  // keys and values of three consecutive sub-tiles: two stream in while one
+  // is tested.  The buffers rotate statically (the loop is unrolled by three),
+  // so no register copy has to wait for a load in flight.
+  struct Rows {
+    u32x4 k[D / 32], v[D / 32];
+  };
+  auto fetch = [&](Rows& r, int64_t s) {
+    const bool live = s < sub_end;
+    load_rows<D>(a, b, h, 0, live ? s : sub, live, n16, grp, r.k);
+    load_rows<D>(a, b, h, 1, live ? s : sub, live, n16, grp, r.v);
+  };
+  auto test = [&](const Rows& r, int64_t s) {
     __builtin_amdgcn_sched_barrier(0);   // keep the prefetch ahead and the two kinds apart
-    const bool fk = flagged(xk, 0);
+    const bool fk = flagged(r.k, 0);
     __builtin_amdgcn_sched_barrier(0);
-    const bool fv = flagged(xv, 1);
+    const bool fv = flagged(r.v, 1);
     __builtin_amdgcn_sched_barrier(0);
-    const int64_t tok = sub * kHybridTile + n16;
+    const int64_t tok = s * kHybridTile + n16;
     const bool f = (fk || fv) && tok < a.n_tokens;
     const uint32_t slot = grp == 0 ? (uint32_t)tok : kOob;
     buf_store1(rs_wsf, slot, (uint8_t)f);
     buf_store1(rs_flags, slot, (uint8_t)f);
     const int count = __popcll(__ballot(grp == 0 && f));
-    buf_store4(rs_cnt, lane == 0 ? (uint32_t)(sub * 4) : kOob, (uint32_t)count);
-#pragma unroll
-    for (int c = 0; c < D / 32; ++c) {
-      xk[c] = nk[c];
-      xv[c] = nv[c];
-    }
+    buf_store4(rs_cnt, lane == 0 ? (uint32_t)(s * 4) : kOob, (uint32_t)count);
+  };
+  Rows r0, r1, r2;
+  if (sub < sub_end) {
+    fetch(r0, sub);
+    fetch(r1, sub + 1);
+  }
+  for (int64_t s3 = sub; s3 < sub_end; s3 += 3) {
+    fetch(r2, s3 + 2);
+    test(r0, s3);
+    if (s3 + 1 >= sub_end) break;
+    fetch(r0, s3 + 3);
+    test(r1, s3 + 1);
+    if (s3 + 2 >= sub_end) break;
+    fetch(r1, s3 + 4);
+    test(r2, s3 + 2);
   }
 }
 
@@ -342,38 +354,41 @@ void hybrid_write_kernel(HybridArgs a) {
   const __amdgpu_buffer_rsrc_t rs_idx = make_rsrc(a.side_idx + bh * a.side_cap, (uint32_t)(a.side_cap * 4));
 
   // keys, values, token n16's flag and the sub-tile's (low-rank row, side row)
-  // for the current sub-tile; those of the next are in flight meanwhile
-  u32x4 xk[D / 32], xv[D / 32], nk[D / 32], nv[D / 32];
-  int64_t sub = sub_begin;
-  load_rows<D>(a, b, h, 0, sub, true, n16, grp, xk);
-  load_rows<D>(a, b, h, 1, sub, true, n16, grp, xv);
-  uint32_t fl = buf_load1(rs_wsf, (uint32_t)(sub * kHybridTile + n16)), fl_next = 0;
-  u32x2 off = buf_load8(rs_off, (uint32_t)(sub * 8)), off_next = u32x2{0u, 0u};
+  // of three consecutive sub-tiles: two stream in while one is written (a
+  // static rotation, as in the select kernel)
+  struct Rows {
+    u32x4 k[D / 32], v[D / 32];
+    uint32_t fl;
+    u32x2 off;
+  };
+  auto fetch = [&](Rows& r, int64_t s) {
+    const bool live = s < sub_end;
+    load_rows<D>(a, b, h, 0, live ? s : sub_begin, live, n16, grp, r.k);
+    load_rows<D>(a, b, h, 1, live ? s : sub_begin, live, n16, grp, r.v);
+    r.fl = buf_load1(rs_wsf, live ? (uint32_t)(s * kHybridTile + n16) : kOob);
+    r.off = buf_load8(rs_off, live ? (uint32_t)(s * 8) : kOob);
+  };
+  Rows r0, r1, r2;
+  fetch(r0, sub_begin);
+  fetch(r1, sub_begin + 1);
 
   // the run's first rows; when they start inside an octet row, that row is shared
-  const int64_t p0_lr = (int32_t)off[0], p0_side = (int32_t)off[1];
+  const int64_t p0_lr = (int32_t)r0.off[0], p0_side = (int32_t)r0.off[1];
   const int64_t first_lr = (p0_lr & 7) ? (p0_lr >> 3) : -1;
   const int64_t first_side = (p0_side & 7) ? (p0_side >> 3) : -1;
   auto lr_row = [&](int64_t o) { return ring_lr + (o == first_lr ? 3 : (int)(o % 3)) * R::kLrRow; };
   auto side_row = [&](int64_t o) { return ring_side + (o == first_side ? 3 : (int)(o % 3)) * R::kSideRow; };
   int64_t lr_end = p0_lr, side_end = p0_side;
 
-  for (; sub < sub_end; ++sub) {
-    const bool more = sub + 1 < sub_end;
-    const int64_t nsub = more ? sub + 1 : sub;
-    load_rows<D>(a, b, h, 0, nsub, more, n16, grp, nk);
-    load_rows<D>(a, b, h, 1, nsub, more, n16, grp, nv);
-    fl_next = buf_load1(rs_wsf, more ? (uint32_t)(nsub * kHybridTile + n16) : kOob);
-    off_next = buf_load8(rs_off, more ? (uint32_t)(nsub * 8) : kOob);
+  auto place = [&](const Rows& r, int64_t sub) {
     __builtin_amdgcn_sched_barrier(0);   // keep the prefetch ahead of the phases below
-
     const int64_t tok = sub * kHybridTile + n16;
     const int64_t left = a.n_tokens - sub * kHybridTile;
     const int nt = left < kHybridTile ? (int)left : kHybridTile;
-    const bool f_lane = fl != 0u;
+    const bool f_lane = r.fl != 0u;
     const uint32_t side_mask = (uint32_t)(__ballot(grp == 0 && f_lane) & 0xFFFFu);
     const uint32_t below = side_mask & ((1u << n16) - 1u);
-    const int64_t lr_off = (int32_t)off[0], side_off = (int32_t)off[1];
+    const int64_t lr_off = (int32_t)r.off[0], side_off = (int32_t)r.off[1];
     const int64_t p_lr = lr_off + n16 - __popc(below);
     const int64_t p_side = side_off + __popc(below);
     const bool lr_ok = n16 < nt && !f_lane && p_lr < a.cap;
@@ -383,7 +398,7 @@ void hybrid_write_kernel(HybridArgs a) {
 
     f32x4 acc[NB];
     // keys: coefficients 16 nb + 4 grp + 0..3 of token n16, one 8-byte store per block
-    coeffs_t<D, NB>(xk, smem + L.off_t[0], L.pitch_t, n16, grp, acc);
+    coeffs_t<D, NB>(r.k, smem + L.off_t[0], L.pitch_t, n16, grp, acc);
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
       const int col = 16 * nb + 4 * grp;
@@ -392,7 +407,7 @@ void hybrid_write_kernel(HybridArgs a) {
     }
     __builtin_amdgcn_sched_barrier(0);
     // values: into the octet rows being assembled
-    coeffs_t<D, NB>(xv, smem + L.off_t[1], L.pitch_t, n16, grp, acc);
+    coeffs_t<D, NB>(r.v, smem + L.off_t[1], L.pitch_t, n16, grp, acc);
     if (lr_ok) {
       uint16_t* rr = lr_row(p_lr >> 3) + (p_lr & 7);
 #pragma unroll
@@ -411,7 +426,7 @@ void hybrid_write_kernel(HybridArgs a) {
         for (int c = 0; c < D / 32; ++c)
 #pragma unroll
           for (int e = 0; e < 8; ++e)
-            rr[(32 * c + 8 * grp + e) * 8] = (uint16_t)(e & 1 ? xv[c][e >> 1] >> 16 : xv[c][e >> 1] & 0xFFFFu);
+            rr[(32 * c + 8 * grp + e) * 8] = (uint16_t)(e & 1 ? r.v[c][e >> 1] >> 16 : r.v[c][e >> 1] & 0xFFFFu);
       }
     }
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -432,22 +447,25 @@ void hybrid_write_kernel(HybridArgs a) {
     // selected tokens: key rows (bit for bit) and indices
 #pragma unroll
     for (int c = 0; c < D / 32; ++c)
-      buf_store16(rs_ks, side_ok ? (uint32_t)((p_side * D + 32 * c + 8 * grp) * 2) : kOob, xk[c]);
+      buf_store16(rs_ks, side_ok ? (uint32_t)((p_side * D + 32 * c + 8 * grp) * 2) : kOob, r.k[c]);
     buf_store4(rs_idx, side_ok && grp == 0 ? (uint32_t)(p_side * 4) : kOob, (uint32_t)(a.pos + tok));
     __builtin_amdgcn_sched_barrier(0);
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");   // ring reads before the next sub-tile's writes
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-
-#pragma unroll
-    for (int c = 0; c < D / 32; ++c) {
-      xk[c] = nk[c];
-      xv[c] = nv[c];
-    }
-    fl = fl_next;
-    off = off_next;
     lr_end = lr_next;
     side_end = side_next;
+  };
+
+  for (int64_t s3 = sub_begin; s3 < sub_end; s3 += 3) {
+    fetch(r2, s3 + 2);
+    place(r0, s3);
+    if (s3 + 1 >= sub_end) break;
+    fetch(r0, s3 + 3);
+    place(r1, s3 + 1);
+    if (s3 + 2 >= sub_end) break;
+    fetch(r1, s3 + 4);
+    place(r2, s3 + 2);
   }
 
   // the run's shared rows: its first row (when it started inside one) and its
