@@ -10,13 +10,14 @@ compress the appended token (K and V) into row N-1 and attend one query per
 head over all N tokens.
 All inputs are synthetic, seeded, and resident in HBM before timing.
 
-Reported `value`: decode microseconds per layer-step (appended-token
-compress of K and V in one launch + the attention kernel + the merge kernel),
-averaged over the 32 layers and the timed steps, measured with HIP events on
-the launch stream.  The roofline entry is for the attention kernel
+Reported `value`: decode microseconds per layer-step, i.e. one
+lrkv_decode_step per layer (the attention kernel, whose extra workgroup per
+(batch, kv head) compresses and stores the appended token, + the merge
+kernel), averaged over the 32 layers and the timed steps, measured with HIP
+events on the launch stream.  The roofline entry is for the attention kernel
 (split_bf16_kernel, the dominant one): its algorithmic bytes per launch (key
-and value coefficient rows, both bases, the queries) over its average launch
-time.  `cpu_baseline` times the float64 CPU oracle on a
+and value coefficient rows, both bases, the queries, the appended token in and
+its coefficient rows out) over its average launch time.  `cpu_baseline` times the float64 CPU oracle on a
 bounded sample of the same decode and scales it to a layer-step.
 
 Usage: python bench.py [--gpus 1] [--steps 10] [--warmup 3] [--no-cpu-baseline]
@@ -119,7 +120,7 @@ def main():
             out=torch.empty((B, Hq, d), dtype=torch.bfloat16, device=dev),
             lse=torch.empty((B, Hq), dtype=torch.float32, device=dev)))
     del base
-    ws_bytes = max(lrkv.decode_workspace_bytes(B, Hq, H, d, lay["rk"], lay["rv"], cap, N) for lay in layers)
+    ws_bytes = max(lrkv.decode_step_workspace_bytes(B, Hq, H, d, lay["rk"], lay["rv"], cap, N) for lay in layers)
     ws = torch.zeros(ws_bytes, dtype=torch.uint8, device=dev)   # decode workspaces start zero-filled
     torch.cuda.synchronize()
     log(f"inputs ready in {time.time() - t_gen:.1f}s: {torch.cuda.memory_allocated() / 2**30:.1f} GiB on device, "
@@ -132,14 +133,13 @@ def main():
             lrkv.compress_kv(lay["xk"], lay["xv"], lay["bk"], lay["bv"], lay["ck"], lay["cv"], p0)
             if ev: ev["pre"][l][1].record()
         for l, lay in enumerate(layers):
+            # lrkv_decode_step as its two launches, so that the attention kernel
+            # (which also compresses and stores the appended token) is timed alone
             if ev: ev["dec"][l][0].record()
-            lrkv.compress_kv(lay["ak"], lay["av"], lay["bk"], lay["bv"], lay["ck"], lay["cv"], N - 1)
+            lrkv.decode_step_partial(lay["q"], lay["ak"], lay["av"], lay["bk"], lay["ck"], lay["bv"], lay["cv"], N, ws)
             if ev: ev["dec"][l][1].record()
-            # lrkv_decode_attn as its two launches, so that the attention kernel is timed alone
-            lrkv.decode_attn_partial(lay["q"], lay["bk"], lay["ck"], lay["bv"], lay["cv"], N, ws)
+            lrkv.decode_step_merge(lay["out"], lay["lse"], N, ws, H, lay["rk"], lay["rv"], cap)
             if ev: ev["dec"][l][2].record()
-            lrkv.decode_attn_merge(lay["out"], lay["lse"], N, ws, H, lay["rk"], lay["rv"], cap)
-            if ev: ev["dec"][l][3].record()
 
     for _ in range(args.warmup):
         step()
@@ -147,7 +147,7 @@ def main():
 
     K = args.steps
     mk = lambda n: [torch.cuda.Event(enable_timing=True) for _ in range(n)]
-    events = [{"pre": [mk(2) for _ in range(L)], "dec": [mk(4) for _ in range(L)]} for _ in range(K)]
+    events = [{"pre": [mk(2) for _ in range(L)], "dec": [mk(3) for _ in range(L)]} for _ in range(K)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for k in range(K):
@@ -156,23 +156,22 @@ def main():
     wall = time.perf_counter() - t0
     log(f"timed {K} steps in {wall:.3f}s")
 
-    prefill_us, decode_us, attn_us, merge_us, append_us = [], [], [], [], []
+    prefill_us, decode_us, attn_us, merge_us = [], [], [], []
     attn_by_par = {0: [], 1: []}
     for k in range(K):
         for l in range(L):
             ep, ed = events[k]["pre"][l], events[k]["dec"][l]
             prefill_us.append(ep[0].elapsed_time(ep[1]) * 1e3)
-            append_us.append(ed[0].elapsed_time(ed[1]) * 1e3)
-            attn_us.append(ed[1].elapsed_time(ed[2]) * 1e3)
-            merge_us.append(ed[2].elapsed_time(ed[3]) * 1e3)
-            decode_us.append(ed[0].elapsed_time(ed[3]) * 1e3)
+            attn_us.append(ed[0].elapsed_time(ed[1]) * 1e3)
+            merge_us.append(ed[1].elapsed_time(ed[2]) * 1e3)
+            decode_us.append(ed[0].elapsed_time(ed[2]) * 1e3)
             attn_by_par[l % 2].append(attn_us[-1])
 
     # ---------------- bytes and rates
     app_bytes = {p: bm.compress_bytes(B, 1, H, d, w.ranks(p)[0]) + bm.compress_bytes(B, 1, H, d, w.ranks(p)[1])
                  for p in (0, 1)}
     dec_bytes = {p: bm.decode_bytes(B, Hq, H, d, *w.ranks(p), N) for p in (0, 1)}
-    attn_bytes = {p: bm.split_kernel_bytes(B, Hq, H, d, *w.ranks(p), N) for p in (0, 1)}
+    attn_bytes = {p: bm.step_kernel_bytes(B, Hq, H, d, *w.ranks(p), N) for p in (0, 1)}
     pre_bytes = {p: bm.compress_bytes(B, P, H, d, w.ranks(p)[0]) + bm.compress_bytes(B, P, H, d, w.ranks(p)[1])
                  for p in (0, 1)}
     mean = lambda xs: float(np.mean(xs))
@@ -219,7 +218,6 @@ def main():
         "decode_us_per_step_32_layers": round(step_decode_us, 1),
         "attn_kernel_us": {"even": round(attn_mean[0], 3), "odd": round(attn_mean[1], 3)},
         "merge_us": round(mean(merge_us), 3),
-        "append_compress_us": round(mean(append_us), 3),
         "prefill_compress_us_per_layer": round(mean(prefill_us), 3),
         "prefill_compress_GBps": round(pre_gbps, 1),
         "device_copy_GBps": round(copy_gbps, 1),
@@ -302,7 +300,8 @@ def bench_hybrid(torch, lrkv, bm, synth, dev, threads):
 
 
 def bench_step_sweep(torch, lrkv, bm, synth, dev, threads):
-    """32-layer decode step at batch 1 (append + attention + merge per layer), eager and as a HIP graph."""
+    """32-layer decode step at batch 1 (lrkv_decode_step per layer: append + attention, merge), eager and as
+    a HIP graph; and, for comparison, the unfused sequence (compress launch + decode) as a graph."""
     w = synth.LLAMA_STEP
     L, Hq, H, d = w.layers, w.n_q_heads, w.n_kv_heads, w.head_dim
     rk, rv = w.ranks(0)
@@ -320,28 +319,42 @@ def bench_step_sweep(torch, lrkv, bm, synth, dev, threads):
                         w, l, "v", b, h, 1, synth.PART_APPEND))).store),
                     out=torch.empty((1, Hq, d), dtype=torch.bfloat16, device=dev),
                     lse=torch.empty((1, Hq), dtype=torch.float32, device=dev)) for l in range(L)]
-        ws = torch.zeros(lrkv.decode_workspace_bytes(1, Hq, H, d, rk, rv, n, n), dtype=torch.uint8, device=dev)
+        ws = torch.zeros(max(lrkv.decode_workspace_bytes(1, Hq, H, d, rk, rv, n, n),
+                             lrkv.decode_step_workspace_bytes(1, Hq, H, d, rk, rv, n, n)),
+                         dtype=torch.uint8, device=dev)
 
-        def step(_i=0):
+        def step(_i=0):      # one lrkv_decode_step per layer: two launches
+            for x in lay:
+                lrkv.decode_step(x["q"], x["ak"], x["av"], bk, x["ck"], bv, x["cv"], n, out=x["out"], lse=x["lse"],
+                                 workspace=ws)
+
+        def step_unfused(_i=0):   # compress of the token, then the decode: three launches
             for x in lay:
                 lrkv.compress_kv(x["ak"], x["av"], bk, bv, x["ck"], x["cv"], n - 1)
                 lrkv.decode_attn(x["q"], bk, x["ck"], bv, x["cv"], n, out=x["out"], lse=x["lse"], workspace=ws)
 
+        def graph_of(fn):
+            s = torch.cuda.Stream()
+            with torch.cuda.stream(s):
+                fn()
+            torch.cuda.synchronize()
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=s):
+                fn()
+            return g
+
         eager = _timed(torch, step, 20)
-        s = torch.cuda.Stream()
-        with torch.cuda.stream(s):
-            step()
-        torch.cuda.synchronize()
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g, stream=s):
-            step()
+        g = graph_of(step)
         graph = _timed(torch, lambda i: g.replay(), 50)
+        g2 = graph_of(step_unfused)
+        graph_unfused = _timed(torch, lambda i: g2.replay(), 50)
         step_bytes = L * (bm.decode_bytes(1, Hq, H, d, rk, rv, n) + bm.compress_bytes(1, 1, H, d, rk)
                           + bm.compress_bytes(1, 1, H, d, rv))
         res[str(n)] = {"eager_us_per_step": round(eager, 1), "graph_us_per_step": round(graph, 1),
                        "graph_us_per_layer": round(graph / L, 2),
+                       "unfused_graph_us_per_step": round(graph_unfused, 1),
                        "graph_GBps_effective": round(step_bytes / graph / 1e3, 1)}
-        del lay, g, ws
+        del lay, g, g2, ws
         torch.cuda.empty_cache()
     return {"workload": w.name, "layers": L, "by_context": res,
             "note": "working set <= 0.6 GB per step; 'effective' bandwidth can include last-level-cache hits"}

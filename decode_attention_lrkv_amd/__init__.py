@@ -21,6 +21,7 @@ import torch
 
 __all__ = [
     "LrkvError", "library", "compress", "compress_kv", "decode_attn", "decode_workspace_bytes",
+    "decode_step", "decode_step_workspace_bytes", "decode_step_partial", "decode_step_merge",
     "compress_hybrid", "compress_hybrid_workspace_bytes", "decode_attn_hybrid",
     "HybridCache", "value_cache_shape", "LIB_PATH", "decode_attn_partial", "decode_attn_merge",
 ]
@@ -54,6 +55,13 @@ _SIG = {
     "lrkv_decode_workspace_bytes": (ctypes.c_size_t, [ctypes.POINTER(_Dims), _I64, _I64]),
     "lrkv_decode_attn": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, ctypes.POINTER(_Dims), _I64, _F,
                                         ctypes.c_int, _P, ctypes.c_size_t, _P]),
+    "lrkv_decode_step_workspace_bytes": (ctypes.c_size_t, [ctypes.POINTER(_Dims), _I64]),
+    "lrkv_decode_step": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.POINTER(_Dims), _I64, _F,
+                                        ctypes.c_int, _P, ctypes.c_size_t, _P]),
+    "lrkv_decode_step_partial": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, ctypes.POINTER(_Dims), _I64, _F,
+                                                ctypes.c_int, _P, ctypes.c_size_t, _P]),
+    "lrkv_decode_step_merge": (ctypes.c_int, [_P, _P, ctypes.POINTER(_Dims), _I64, ctypes.c_int, _P,
+                                              ctypes.c_size_t, _P]),
     "lrkv_compress_hybrid_workspace_bytes": (ctypes.c_size_t, [ctypes.POINTER(_Dims), _I64]),
     "lrkv_compress_hybrid": (ctypes.c_int, [_P, _P, _P, _P, _F, _P, _P, _P, _P, _P, _P, _P, _P, _P,
                                             ctypes.POINTER(_Dims), _I64, _I64, _I64, ctypes.c_int, _P,
@@ -185,6 +193,37 @@ def decode_attn(q, basis_k, coeff_k, basis_v, coeff_v, n_ctx: int, out=None, lse
     return out, lse
 
 
+def decode_step_workspace_bytes(batch, n_q_heads, n_kv_heads, head_dim, rank_k, rank_v, capacity,
+                                n_ctx: int) -> int:
+    dims = _Dims(batch, n_q_heads, n_kv_heads, head_dim, rank_k, rank_v, capacity)
+    return int(library().lrkv_decode_step_workspace_bytes(ctypes.byref(dims), n_ctx))
+
+
+def decode_step(q, k_new, v_new, basis_k, coeff_k, basis_v, coeff_v, n_ctx: int, out=None, lse=None,
+                scale: float = 0.0, workspace: Optional[torch.Tensor] = None, with_lse: bool = True):
+    """Append the step's token at row n_ctx - 1 of both caches, then attend [0, n_ctx).
+
+    k_new, v_new [B, Hkv, d] (or [B, 1, Hkv, d]); other arguments as decode_attn.
+    Returns (out [B, Hq, d], lse [B, Hq] float32 or None).
+    """
+    B, Hq, d = q.shape
+    H, _, rk = basis_k.shape
+    rv = basis_v.shape[2]
+    cap = coeff_k.shape[2]
+    dims = _Dims(B, Hq, H, d, rk, rv, cap)
+    lib = library()
+    need = int(lib.lrkv_decode_step_workspace_bytes(ctypes.byref(dims), n_ctx))
+    ws = _workspace(need, q.device, workspace)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None and with_lse:
+        lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
+    _check(lib.lrkv_decode_step(_ptr(q), _ptr(k_new), _ptr(v_new), _ptr(basis_k), _ptr(coeff_k), _ptr(basis_v),
+                                _ptr(coeff_v), _ptr(out), _ptr(lse), ctypes.byref(dims), n_ctx, scale,
+                                _dtype_code(q), _ptr(ws), ws.numel(), _stream(q.device)))
+    return out, lse
+
+
 def compress_hybrid_workspace_bytes(batch, n_q_heads, n_kv_heads, head_dim, rank_k, rank_v, capacity,
                                     n_tokens) -> int:
     dims = _Dims(batch, n_q_heads, n_kv_heads, head_dim, rank_k, rank_v, capacity)
@@ -263,4 +302,25 @@ def decode_attn_merge(out, lse, n_ctx: int, workspace: torch.Tensor, n_kv_heads:
     B, Hq, d = out.shape
     dims = _Dims(B, Hq, n_kv_heads, d, rank_k, rank_v, capacity)
     _check(library().lrkv_decode_attn_merge(_ptr(out), _ptr(lse), ctypes.byref(dims), n_ctx, _dtype_code(out),
+                                            _ptr(workspace), workspace.numel(), _stream(out.device)))
+
+
+def decode_step_partial(q, k_new, v_new, basis_k, coeff_k, basis_v, coeff_v, n_ctx: int, workspace: torch.Tensor,
+                        scale: float = 0.0):
+    """First phase of decode_step: append the token, partial results into `workspace`."""
+    B, Hq, d = q.shape
+    H, _, rk = basis_k.shape
+    dims = _Dims(B, Hq, H, d, rk, basis_v.shape[2], coeff_k.shape[2])
+    _check(library().lrkv_decode_step_partial(_ptr(q), _ptr(k_new), _ptr(v_new), _ptr(basis_k), _ptr(coeff_k),
+                                              _ptr(basis_v), _ptr(coeff_v), ctypes.byref(dims), n_ctx, scale,
+                                              _dtype_code(q), _ptr(workspace), workspace.numel(),
+                                              _stream(q.device)))
+
+
+def decode_step_merge(out, lse, n_ctx: int, workspace: torch.Tensor, n_kv_heads: int, rank_k: int, rank_v: int,
+                      capacity: int):
+    """Second phase of decode_step: log-sum-exp merge into out and lse."""
+    B, Hq, d = out.shape
+    dims = _Dims(B, Hq, n_kv_heads, d, rank_k, rank_v, capacity)
+    _check(library().lrkv_decode_step_merge(_ptr(out), _ptr(lse), ctypes.byref(dims), n_ctx, _dtype_code(out),
                                             _ptr(workspace), workspace.numel(), _stream(out.device)))

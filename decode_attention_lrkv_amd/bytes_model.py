@@ -51,6 +51,15 @@ def split_kernel_bytes(batch, n_q_heads, n_kv_heads, head_dim, rank_k, rank_v, n
             + s * batch * n_q_heads * head_dim)
 
 
+def step_kernel_bytes(batch, n_q_heads, n_kv_heads, head_dim, rank_k, rank_v, n_ctx, elem_bytes=2):
+    """The attention kernel of a decode step: the attention of rows
+    [0, n_ctx - 1) (as split_kernel_bytes) plus the appended token, whose key
+    and value come in and whose coefficient rows go out."""
+    s = elem_bytes
+    return (split_kernel_bytes(batch, n_q_heads, n_kv_heads, head_dim, rank_k, rank_v, n_ctx - 1, elem_bytes)
+            + s * batch * n_kv_heads * (2 * head_dim + rank_k + rank_v))
+
+
 def compress_bytes(batch, n_tokens, n_kv_heads, head_dim, rank, elem_bytes=2):
     """One compress call: token rows in, basis in, coefficient rows out."""
     s = elem_bytes

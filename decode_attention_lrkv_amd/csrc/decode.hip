@@ -226,9 +226,13 @@ struct SplitSmem {
 };
 
 // wg: this workgroup's index among the workgroups attending this list of
-// this (b, kv head); part: the partial it writes.
+// this (b, kv head); part: the partial it writes.  append: this workgroup
+// also compresses the appended token (after the fold, while its first chunk
+// streams in), stores its cache rows and writes that token's partial as the
+// last one, a.n_parts - 1.
 template <int KC, int VB, bool FOLD, int STAGES>
-__device__ __forceinline__ void split_bf16_body(const SplitArgs& a, int wg, int part, SplitSmem& sm) {
+__device__ __forceinline__ void split_bf16_body(const SplitArgs& a, int wg, int part, SplitSmem& sm,
+                                                bool append = false) {
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
   const int lane = tid & 63;
@@ -321,8 +325,16 @@ __device__ __forceinline__ void split_bf16_body(const SplitArgs& a, int wg, int 
       const int i = tid + 256 * it;
       if (i < nbv) wv[it] = *reinterpret_cast<const u32x4*>(bvs + 8 * i);
     }
+    // the appended token's key and value (float, into the otherwise unused s_q)
+    const int e_new = tid & 127;
+    float x_new = 0.f;
+    if (append && e_new < d) {
+      if (tid < 128) x_new = bf16_to_f32(static_cast<const uint16_t*>(a.k_new)[bh * d + e_new]);
+      else x_new = bf16_to_f32(static_cast<const uint16_t*>(a.v_new)[bh * d + e_new]);
+    }
     // the first chunk streams in while the query is folded
     if (c_begin < c_end) load(ca, c_begin);
+    if (append && e_new < d) s_q[(tid < 128 ? 0 : 128) + e_new] = x_new;
     if (tid < nq) {
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
@@ -394,6 +406,46 @@ __device__ __forceinline__ void split_bf16_body(const SplitArgs& a, int wg, int 
     bq_hi[c] = u32x4{hi[0], hi[1], hi[2], hi[3]};
     bq_lo[c] = u32x4{lo[0], lo[1], lo[2], lo[3]};
   }
+
+  if (append) {
+    // c = round(x B) for the key (threads < 128, column tid) and the value
+    // (threads >= 128, column tid - 128), stored at the appended row; then the
+    // token's partial: m = q' . c_K (log2 units), l = 1, o = B_V c_V (every head)
+    const int pa = a.n_parts - 1;
+    const int64_t p = a.append_row;
+    float* s_c = s_q + 256;   // past the token's key and value
+    const int col = tid & 127;
+    const bool kind_v = tid >= 128;
+    const int r = kind_v ? rv : rk;
+    if (col < r) {
+      float acc = 0.f;
+      if (kind_v) {
+        for (int e = 0; e < d; ++e) acc = fmaf(s_q[128 + e], bf16_to_f32(sm.bv[e * (rv + 8) + col]), acc);
+      } else {
+        for (int e = 0; e < d; ++e) acc = fmaf(s_q[e], bf16_to_f32(s_bk[e * rk + col]), acc);
+      }
+      const uint16_t c16 = f32_to_bf16(acc);
+      s_c[(kind_v ? 128 : 0) + col] = bf16_to_f32(c16);
+      if (kind_v)
+        static_cast<uint16_t*>(const_cast<void*>(a.cv))[bh * a.cap * rv + ((p >> 3) * rv + col) * 8 + (p & 7)] = c16;
+      else
+        static_cast<uint16_t*>(const_cast<void*>(a.ck))[(bh * a.cap + p) * rk + col] = c16;
+    }
+    __syncthreads();
+    const int64_t row0 = (int64_t)b * a.hq + (int64_t)h * g;
+    if (tid < g) {
+      float s = 0.f;
+      for (int k = 0; k < rk; ++k) s = fmaf(s_qf[tid * rk + k], s_c[k], s);
+      store_partial(a.part_ml + ((row0 + tid) * a.n_parts + pa) * 2 + 0, s);
+      store_partial(a.part_ml + ((row0 + tid) * a.n_parts + pa) * 2 + 1, 1.f);
+    }
+    if (tid < d) {
+      float o = 0.f;
+      for (int c = 0; c < rv; ++c) o = fmaf(bf16_to_f32(sm.bv[tid * (rv + 8) + c]), s_c[128 + c], o);
+      for (int j = 0; j < g; ++j) store_partial(a.part_o + ((row0 + j) * a.n_parts + pa) * d + tid, o);
+    }
+  }
+
 
   f32x4 acc[VB];
 #pragma unroll
@@ -598,7 +650,8 @@ template <int KC, int VB>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void split_bf16_kernel(SplitArgs a) {
   __shared__ SplitSmem sm;
-  split_bf16_body<KC, VB, true, kStages<KC, VB>>(a, blockIdx.x, blockIdx.x, sm);
+  split_bf16_body<KC, VB, true, kStages<KC, VB>>(a, blockIdx.x, blockIdx.x, sm,
+                                                  a.k_new != nullptr && blockIdx.x == gridDim.x - 1);
 }
 
 // Hybrid cache in one launch: the gridDim.x workgroups of each (b, kv head)
@@ -785,7 +838,10 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeArgs a) {
     break;
 
 hipError_t launch_split_bf16(const SplitArgs& a, hipStream_t s) {
-  const dim3 grid((a.n_splits + kWaves - 1) / kWaves, a.hkv, a.batch);
+  // one workgroup per partial; with k_new set, the last workgroup of each
+  // (b, kv head) also appends, and the appended token's partial is the extra
+  // last one
+  const dim3 grid(a.k_new ? a.n_parts - 1 : a.n_parts, a.hkv, a.batch);
   const int kc = (a.rk + 31) / 32, vb = (a.rv + 15) / 16;
   if (a.basis_k == nullptr || a.basis_v == nullptr) return hipErrorInvalidValue;
   switch (kc * 16 + vb) {

@@ -87,7 +87,11 @@ struct DecodeLayout {
   size_t o = 0, ml = 0, total = 0;
 };
 
-DecodeLayout decode_layout(const lrkv_dims& d, int64_t n_lr_tokens, int64_t side_cap) {
+// append (decode step): one more partial, the appended token's.  The token is
+// compressed by one more workgroup per (b, kv head) when the grid still fits
+// one round of two workgroups per compute unit (then it runs beside the
+// attention), else by the last attention workgroup before its own chunks.
+DecodeLayout decode_layout(const lrkv_dims& d, int64_t n_lr_tokens, int64_t side_cap, bool append = false) {
   DecodeLayout L;
   const int cus = device_cu_count();
   const int64_t units = (int64_t)d.batch * d.n_kv_heads;
@@ -109,6 +113,10 @@ DecodeLayout decode_layout(const lrkv_dims& d, int64_t n_lr_tokens, int64_t side
   } else {
     L.lr = plan_splits(units, n_lr_tokens, cus, kMaxSplits);
     L.parts = (int)cdiv(L.lr.n_splits, kSplitsPerPart);
+    if (append) {
+      const bool own_wg = (int64_t)(L.parts + 1) * units <= 2 * (int64_t)cus;
+      L.parts += own_wg ? 2 : 1;   // workgroups (the appending one included) + the token's partial
+    }
   }
   size_t off = 0;
   L.o = off;        off = align256(off + sizeof(float) * rows * L.parts * d.head_dim);
@@ -274,7 +282,7 @@ lrkv_status check_decode_common(const lrkv_dims* dims, int64_t n_ctx, lrkv_dtype
 lrkv_status decode_partial(const void* q, const void* basis_k, const void* coeff_k, const void* basis_v,
                            const void* coeff_v, const lrkv_dims* dims, int64_t n_ctx, float scale,
                            lrkv_dtype dtype, void* workspace, const DecodeLayout& L, hipStream_t stream,
-                           const char* fn) {
+                           const char* fn, const void* k_new = nullptr, const void* v_new = nullptr) {
   char* ws = static_cast<char*>(workspace);
   SplitArgs sa{};
   sa.q = q; sa.basis_k = basis_k; sa.ck = coeff_k; sa.cv = coeff_v; sa.basis_v = basis_v;
@@ -286,6 +294,12 @@ lrkv_status decode_partial(const void* q, const void* basis_k, const void* coeff
   sa.qscale = resolve_scale(scale, dims->head_dim) * kLog2eHost;
   sa.part_o = reinterpret_cast<float*>(ws + L.o);
   sa.part_ml = reinterpret_cast<float*>(ws + L.ml);
+  if (k_new) {   // decode step: rows [0, n_ctx - 1) attended, row n_ctx - 1 appended by the last workgroup
+    sa.n_static = n_ctx - 1;
+    sa.k_new = k_new;
+    sa.v_new = v_new;
+    sa.append_row = n_ctx - 1;
+  }
   const hipError_t e = dtype == LRKV_BF16 ? launch_split_bf16(sa, stream) : launch_split_f32(sa, stream);
   return e == hipSuccess ? LRKV_OK : device_fail(fn, e);
 }
@@ -356,6 +370,114 @@ lrkv_status lrkv_decode_attn_merge(void* out, float* lse, const lrkv_dims* dims,
   LRKV_CHECK_PTR(out, fn);
   if (lse && !aligned16(lse)) return fail(LRKV_ERR_INVALID_ARGUMENT, "%s: lse is not 16-byte aligned", fn);
   return decode_merge(out, lse, dims, dtype, workspace, L, stream, fn);
+}
+
+size_t lrkv_decode_step_workspace_bytes(const lrkv_dims* dims, int64_t n_ctx) {
+  if (check_dims(dims, LRKV_F32, "lrkv_decode_step_workspace_bytes") != LRKV_OK &&
+      check_dims(dims, LRKV_BF16, "lrkv_decode_step_workspace_bytes") != LRKV_OK)
+    return 0;
+  if (n_ctx < 1) return 0;
+  const size_t step = decode_layout(*dims, std::max<int64_t>(n_ctx - 1, 1), 0, true).total;
+  return std::max(step, decode_layout(*dims, n_ctx, 0).total);   // float32 runs compress + decode
+}
+
+}  // extern "C"
+
+namespace {
+
+lrkv_status check_step(const void* q, const void* k_new, const void* v_new, const void* basis_k,
+                       const void* coeff_k, const void* basis_v, const void* coeff_v, const lrkv_dims* dims,
+                       int64_t n_ctx, float scale, lrkv_dtype dtype, void* workspace, size_t workspace_bytes,
+                       const char* fn) {
+  lrkv_status st = check_dims(dims, dtype, fn);
+  if (st != LRKV_OK) return st;
+  if (n_ctx < 1 || n_ctx > dims->capacity)
+    return fail(LRKV_ERR_INVALID_ARGUMENT, "%s: n_ctx = %lld outside [1, capacity = %lld]", fn, (long long)n_ctx,
+                (long long)dims->capacity);
+  if (!std::isfinite(scale)) return fail(LRKV_ERR_INVALID_ARGUMENT, "%s: scale is not finite", fn);
+  LRKV_CHECK_PTR(q, fn);
+  LRKV_CHECK_PTR(k_new, fn);
+  LRKV_CHECK_PTR(v_new, fn);
+  LRKV_CHECK_PTR(basis_k, fn);
+  LRKV_CHECK_PTR(coeff_k, fn);
+  LRKV_CHECK_PTR(basis_v, fn);
+  LRKV_CHECK_PTR(coeff_v, fn);
+  LRKV_CHECK_PTR(workspace, fn);
+  const size_t need = lrkv_decode_step_workspace_bytes(dims, n_ctx);
+  if (workspace_bytes < need)
+    return fail(LRKV_ERR_WORKSPACE_TOO_SMALL, "%s: workspace of %zu bytes, %zu needed", fn, workspace_bytes, need);
+  return LRKV_OK;
+}
+
+// Workspace layout of a decode step: the attention workgroups of rows
+// [0, n_ctx - 1) plus the appended token's partial (bfloat16); float32 runs
+// the plain decode over n_ctx rows after the compress kernel.
+DecodeLayout step_layout(const lrkv_dims& d, int64_t n_ctx, lrkv_dtype dtype) {
+  return dtype == LRKV_BF16 ? decode_layout(d, std::max<int64_t>(n_ctx - 1, 1), 0, true) : decode_layout(d, n_ctx, 0);
+}
+
+lrkv_status step_partial(const void* q, const void* k_new, const void* v_new, const void* basis_k, void* coeff_k,
+                         const void* basis_v, void* coeff_v, const lrkv_dims* dims, int64_t n_ctx, float scale,
+                         lrkv_dtype dtype, void* workspace, const DecodeLayout& L, hipStream_t stream,
+                         const char* fn) {
+  if (dtype != LRKV_BF16) {
+    const lrkv_status st =
+        lrkv_compress_kv(k_new, v_new, basis_k, basis_v, coeff_k, coeff_v, dims, 1, n_ctx - 1, dtype, stream);
+    if (st != LRKV_OK) return st;
+    return decode_partial(q, basis_k, coeff_k, basis_v, coeff_v, dims, n_ctx, scale, dtype, workspace, L, stream, fn);
+  }
+  return decode_partial(q, basis_k, coeff_k, basis_v, coeff_v, dims, n_ctx, scale, dtype, workspace, L, stream, fn,
+                        k_new, v_new);
+}
+
+}  // namespace
+
+extern "C" {
+
+lrkv_status lrkv_decode_step(const void* q, const void* k_new, const void* v_new, const void* basis_k,
+                             void* coeff_k, const void* basis_v, void* coeff_v, void* out, float* lse,
+                             const lrkv_dims* dims, int64_t n_ctx, float scale, lrkv_dtype dtype,
+                             void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  const char* fn = "lrkv_decode_step";
+  lrkv_status st = check_step(q, k_new, v_new, basis_k, coeff_k, basis_v, coeff_v, dims, n_ctx, scale, dtype,
+                              workspace, workspace_bytes, fn);
+  if (st != LRKV_OK) return st;
+  LRKV_CHECK_PTR(out, fn);
+  if (lse && !aligned16(lse)) return fail(LRKV_ERR_INVALID_ARGUMENT, "%s: lse is not 16-byte aligned", fn);
+  const DecodeLayout L = step_layout(*dims, n_ctx, dtype);
+  st = step_partial(q, k_new, v_new, basis_k, coeff_k, basis_v, coeff_v, dims, n_ctx, scale, dtype, workspace, L,
+                    stream, fn);
+  if (st != LRKV_OK) return st;
+  return decode_merge(out, lse, dims, dtype, workspace, L, stream, fn);
+}
+
+lrkv_status lrkv_decode_step_partial(const void* q, const void* k_new, const void* v_new, const void* basis_k,
+                                     void* coeff_k, const void* basis_v, void* coeff_v, const lrkv_dims* dims,
+                                     int64_t n_ctx, float scale, lrkv_dtype dtype, void* workspace,
+                                     size_t workspace_bytes, hipStream_t stream) {
+  const char* fn = "lrkv_decode_step_partial";
+  const lrkv_status st = check_step(q, k_new, v_new, basis_k, coeff_k, basis_v, coeff_v, dims, n_ctx, scale, dtype,
+                                    workspace, workspace_bytes, fn);
+  if (st != LRKV_OK) return st;
+  return step_partial(q, k_new, v_new, basis_k, coeff_k, basis_v, coeff_v, dims, n_ctx, scale, dtype, workspace,
+                      step_layout(*dims, n_ctx, dtype), stream, fn);
+}
+
+lrkv_status lrkv_decode_step_merge(void* out, float* lse, const lrkv_dims* dims, int64_t n_ctx, lrkv_dtype dtype,
+                                   void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  const char* fn = "lrkv_decode_step_merge";
+  lrkv_status st = check_dims(dims, dtype, fn);
+  if (st != LRKV_OK) return st;
+  if (n_ctx < 1 || n_ctx > dims->capacity)
+    return fail(LRKV_ERR_INVALID_ARGUMENT, "%s: n_ctx = %lld outside [1, capacity = %lld]", fn, (long long)n_ctx,
+                (long long)dims->capacity);
+  LRKV_CHECK_PTR(out, fn);
+  LRKV_CHECK_PTR(workspace, fn);
+  if (lse && !aligned16(lse)) return fail(LRKV_ERR_INVALID_ARGUMENT, "%s: lse is not 16-byte aligned", fn);
+  const size_t need = lrkv_decode_step_workspace_bytes(dims, n_ctx);
+  if (workspace_bytes < need)
+    return fail(LRKV_ERR_WORKSPACE_TOO_SMALL, "%s: workspace of %zu bytes, %zu needed", fn, workspace_bytes, need);
+  return decode_merge(out, lse, dims, dtype, workspace, step_layout(*dims, n_ctx, dtype), stream, fn);
 }
 
 size_t lrkv_compress_hybrid_workspace_bytes(const lrkv_dims* dims, int64_t n_tokens) {

@@ -31,6 +31,13 @@ struct SplitArgs {
   float qscale;          // softmax scale * log2(e)
   float* part_o;         // [B, Hq, n_parts, d]  unnormalised outputs
   float* part_ml;        // [B, Hq, n_parts, 2]  running max (log2 units), softmax sum
+  // Append (decode step): when k_new is non-null, the last workgroup of each
+  // (b, kv head) compresses the new token's key and value, stores them at
+  // cache row append_row (through ck / cv) and writes that token's partial;
+  // the other workgroups attend rows [0, n_static).
+  const void* k_new;     // [B, Hkv, d] or null
+  const void* v_new;     // [B, Hkv, d]
+  int64_t append_row;
 };
 
 // Log-sum-exp merge of n_parts partials per (b, q head).

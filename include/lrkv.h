@@ -168,6 +168,40 @@ lrkv_status lrkv_decode_attn_merge(void* out, float* lse, const lrkv_dims* dims,
                                    lrkv_dtype dtype, void* workspace, size_t workspace_bytes,
                                    hipStream_t stream);
 
+/*
+ * Decode step: append the token of this step, then attend.  Equivalent to
+ * lrkv_compress_kv of one token at row n_ctx - 1 followed by
+ * lrkv_decode_attn over [0, n_ctx) (the "Llama-3.1-NovaKV" model card,
+ * results section, times whole decode steps with the cache written and read
+ * inside the step; the cache row is c = round(x B) as in lrkv_compress).
+ * For bfloat16 the append runs inside the attention launch: one extra
+ * workgroup per (b, kv head) compresses the token, stores its rows and
+ * contributes its softmax term, while the others attend rows [0, n_ctx - 1);
+ * a second launch merges.  float32 runs lrkv_compress_kv, then the decode.
+ *   k_new, v_new  [B, Hkv, d] the new token's key and value
+ *   coeff_k, coeff_v  the caches (row n_ctx - 1 is written; rows below are read)
+ *   workspace at least lrkv_decode_step_workspace_bytes(dims, n_ctx) bytes
+ * Other arguments as lrkv_decode_attn.  Requires 1 <= n_ctx <= capacity.
+ */
+size_t lrkv_decode_step_workspace_bytes(const lrkv_dims* dims, int64_t n_ctx);
+lrkv_status lrkv_decode_step(const void* q, const void* k_new, const void* v_new, const void* basis_k,
+                             void* coeff_k, const void* basis_v, void* coeff_v, void* out, float* lse,
+                             const lrkv_dims* dims, int64_t n_ctx, float scale, lrkv_dtype dtype,
+                             void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * The two phases of lrkv_decode_step (same arguments and workspace, same
+ * result back to back on one stream), as for lrkv_decode_attn: _partial
+ * appends the token and leaves the partial results in the workspace, _merge
+ * combines them into out and lse.
+ */
+lrkv_status lrkv_decode_step_partial(const void* q, const void* k_new, const void* v_new, const void* basis_k,
+                                     void* coeff_k, const void* basis_v, void* coeff_v, const lrkv_dims* dims,
+                                     int64_t n_ctx, float scale, lrkv_dtype dtype, void* workspace,
+                                     size_t workspace_bytes, hipStream_t stream);
+lrkv_status lrkv_decode_step_merge(void* out, float* lse, const lrkv_dims* dims, int64_t n_ctx, lrkv_dtype dtype,
+                                   void* workspace, size_t workspace_bytes, hipStream_t stream);
+
 /* Bytes of workspace lrkv_compress_hybrid needs for n_tokens new tokens. */
 size_t lrkv_compress_hybrid_workspace_bytes(const lrkv_dims* dims, int64_t n_tokens);
 

@@ -28,7 +28,9 @@ def test_header_declares_the_entry_points():
     names = _declared()
     for n in ("lrkv_compress", "lrkv_decode_attn", "lrkv_compress_hybrid", "lrkv_decode_attn_hybrid",
               "lrkv_decode_workspace_bytes", "lrkv_status_string", "lrkv_last_error",
-              "lrkv_decode_attn_partial", "lrkv_decode_attn_merge", "lrkv_compress_hybrid_workspace_bytes"):
+              "lrkv_decode_attn_partial", "lrkv_decode_attn_merge", "lrkv_compress_hybrid_workspace_bytes",
+              "lrkv_decode_step", "lrkv_decode_step_workspace_bytes", "lrkv_decode_step_partial",
+              "lrkv_decode_step_merge"):
         assert n in names
 
 

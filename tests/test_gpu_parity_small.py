@@ -141,6 +141,91 @@ def test_llama_step_layer_with_append(N, layer):
     check_decode(to_f64(o3), to_f64(lse3), o_ref, lse_ref, "bf16", f"step e2e N={N} layer={layer}")
 
 
+@pytest.mark.parametrize("N", [1, 2, 33, 256, 2048, 8192])
+@pytest.mark.parametrize("layer", [0, 31])
+def test_decode_step_appends_and_attends(N, layer):
+    """lrkv_decode_step at the 32-layer-step shapes: the appended rows meet the
+    compress gate, the drawn rows are untouched, and the output is the
+    oracle's decode over all N tokens (the new one included)."""
+    w = synth.LLAMA_STEP
+    B, H, d = w.batch, w.n_kv_heads, w.head_dim
+    rk, rv = w.ranks(layer)
+    xk = synth.tokens_major(synth.stack_heads(w, lambda b, h: synth.full_tokens(w, layer, "k", b, h, 1, synth.PART_APPEND)))
+    xv = synth.tokens_major(synth.stack_heads(w, lambda b, h: synth.full_tokens(w, layer, "v", b, h, 1, synth.PART_APPEND)))
+    bk, bv, q = synth.basis(w, layer, "k"), synth.basis(w, layer, "v"), synth.query(w, layer)
+    ak = O.compress(xk.exact, bk.exact)
+    av = O.compress(xv.exact, bv.exact)
+    rows_k = np.zeros((B, H, N, rk))
+    rows_v = np.zeros((B, H, N, rv))
+    if N > 1:
+        rows_k[:, :, :N - 1] = _direct_rows(w, layer, "k", N - 1).exact
+        rows_v[:, :, :N - 1] = _direct_rows(w, layer, "v", N - 1).exact
+    ck_all = rows_k.copy(); ck_all[:, :, N - 1:] = O.round_storage(ak, "bf16")
+    cv_all = rows_v.copy(); cv_all[:, :, N - 1:] = O.round_storage(av, "bf16")
+    o_ref, lse_ref = O.decode(q.exact, bk.exact, ck_all, bv.exact, cv_all, N)
+    cap = max(8, (N + 7) // 8 * 8)
+    ckd, cvd = _cache_from_rows(rows_k, rows_v, "bf16", cap)
+    before_k = bits(ckd)
+    qd, bkd, bvd = to_dev(q, "bf16"), to_dev(bk, "bf16"), to_dev(bv, "bf16")
+    kn, vn = to_dev(xk, "bf16"), to_dev(xv, "bf16")
+    o, lse = lrkv.decode_step(qd, kn, vn, bkd, ckd, bvd, cvd, N)
+    torch.cuda.synchronize()
+    check_compress(to_f64(ckd)[:, :, N - 1:N], ak, xk.exact, bk.exact, "bf16", "step append K")
+    check_compress(synth.from_value_octets(to_f64(cvd))[:, :, N - 1:N], av, xv.exact, bv.exact, "bf16",
+                   "step append V")
+    after_k = bits(ckd)
+    assert np.array_equal(after_k[:, :, :N - 1], before_k[:, :, :N - 1])
+    assert np.array_equal(after_k[:, :, N:], before_k[:, :, N:])
+    check_decode(to_f64(o), to_f64(lse), o_ref, lse_ref, "bf16", f"decode step N={N} layer={layer}")
+
+
+def test_decode_step_two_phase_equals_one_call():
+    """lrkv_decode_step_partial + _merge give the bits of lrkv_decode_step."""
+    w = synth.LLAMA_STEP
+    layer, N = 1, 3000
+    B, H, d = w.batch, w.n_kv_heads, w.head_dim
+    rk, rv = w.ranks(layer)
+    rows_k = np.zeros((B, H, N, rk)); rows_k[:, :, :N - 1] = _direct_rows(w, layer, "k", N - 1).exact
+    rows_v = np.zeros((B, H, N, rv)); rows_v[:, :, :N - 1] = _direct_rows(w, layer, "v", N - 1).exact
+    xk = synth.tokens_major(synth.stack_heads(w, lambda b, h: synth.full_tokens(w, layer, "k", b, h, 1, synth.PART_APPEND)))
+    xv = synth.tokens_major(synth.stack_heads(w, lambda b, h: synth.full_tokens(w, layer, "v", b, h, 1, synth.PART_APPEND)))
+    qd, bkd, bvd = (to_dev(x, "bf16") for x in (synth.query(w, layer), synth.basis(w, layer, "k"), synth.basis(w, layer, "v")))
+    kn, vn = to_dev(xk, "bf16"), to_dev(xv, "bf16")
+    ck1, cv1 = _cache_from_rows(rows_k, rows_v, "bf16", N)
+    ck2, cv2 = ck1.clone(), cv1.clone()
+    o1, l1 = lrkv.decode_step(qd, kn, vn, bkd, ck1, bvd, cv1, N)
+    ws = torch.empty(lrkv.decode_step_workspace_bytes(B, w.n_q_heads, H, d, rk, rv, N, N), dtype=torch.uint8,
+                     device=DEV)
+    o2 = torch.empty_like(o1)
+    l2 = torch.empty_like(l1)
+    lrkv.decode_step_partial(qd, kn, vn, bkd, ck2, bvd, cv2, N, ws)
+    lrkv.decode_step_merge(o2, l2, N, ws, H, rk, rv, N)
+    torch.cuda.synchronize()
+    assert torch.equal(o1.view(torch.int16), o2.view(torch.int16)) and torch.equal(l1, l2)
+    assert torch.equal(ck1.view(torch.int16), ck2.view(torch.int16))
+    assert torch.equal(cv1.view(torch.int16), cv2.view(torch.int16))
+
+
+def test_decode_step_float32():
+    """float32 caches take the compress kernel and the plain decode."""
+    w = synth.TINY_F32
+    rk, rv = w.ranks(0)
+    N = 100
+    rows_k = _direct_rows(w, 0, "k", N - 1).exact
+    rows_v = _direct_rows(w, 0, "v", N - 1).exact
+    xk = synth.tokens_major(synth.stack_heads(w, lambda b, h: synth.full_tokens(w, 0, "k", b, h, 1, synth.PART_APPEND)))
+    xv = synth.tokens_major(synth.stack_heads(w, lambda b, h: synth.full_tokens(w, 0, "v", b, h, 1, synth.PART_APPEND)))
+    bk, bv, q = synth.basis(w, 0, "k"), synth.basis(w, 0, "v"), synth.query(w, 0)
+    ak, av = O.compress(xk.exact, bk.exact), O.compress(xv.exact, bv.exact)
+    ck_all = np.concatenate([rows_k, O.round_storage(ak, "f32")], axis=2)
+    cv_all = np.concatenate([rows_v, O.round_storage(av, "f32")], axis=2)
+    o_ref, lse_ref = O.decode(q.exact, bk.exact, ck_all, bv.exact, cv_all, N)
+    ckd, cvd = _cache_from_rows(rows_k, rows_v, "f32", 104)
+    o, lse = lrkv.decode_step(to_dev(q, "f32"), to_dev(xk, "f32"), to_dev(xv, "f32"), to_dev(bk, "f32"), ckd,
+                              to_dev(bv, "f32"), cvd, N)
+    check_decode(to_f64(o), to_f64(lse), o_ref, lse_ref, "f32", "decode step f32")
+
+
 def test_prefill_compress_tiles_and_ragged_tail():
     """A prefill chunk that spans several 64-token tiles, starts at an odd row and ends ragged."""
     w = synth.BATCHED_32K
