@@ -52,6 +52,8 @@ def parse():
     p.add_argument("--warmup", type=int, default=3)
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-extra", action="store_true", help="skip the hybrid and 32-layer-step figures")
+    p.add_argument("--only", choices=("hybrid", "sweep"),
+                   help="run only the hybrid 128K figures or only the 32-layer-step sweep (for profiling)")
     p.add_argument("--cpu-seconds", type=float, default=15.0,
                    help="approximate CPU time budget of the oracle sample")
     return p.parse_args()
@@ -72,6 +74,11 @@ def main():
     lrkv.library()   # fails loudly when the HIP library is missing
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.only:
+        threads = min(16, len(os.sched_getaffinity(0)))
+        fig = (bench_hybrid if args.only == "hybrid" else bench_step_sweep)(torch, lrkv, bm, synth, dev, threads)
+        print(json.dumps({args.only: fig}), flush=True)
+        return 0
     w = synth.BATCHED_32K
     L, B, Hq, H, d = w.layers, w.batch, w.n_q_heads, w.n_kv_heads, w.head_dim
     N = w.n_ctx[0]
