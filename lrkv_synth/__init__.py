@@ -1,6 +1,7 @@
 """Seeded synthetic inputs for low-rank KV-cache decode attention.
 
 This module only *draws* inputs: per-kv-head orthonormal frames and bases,
+non-orthogonal encoder/decoder pairs (a query-aware key transform's shape),
 rank-r coefficient rows, full key/value vectors and queries, each rounded once
 to the storage dtype.  It holds no step of the method itself (no projection
 onto a basis for compression, no reconstruction, no attention): both the
@@ -39,6 +40,8 @@ TAG_QUERY = 4        # decode queries
 TAG_INJECT_SET = 5   # which tokens get an off-subspace component (hybrid workload)
 TAG_INJECT_DIR_K = 6
 TAG_INJECT_DIR_V = 9
+TAG_QMOMENT = 7      # eigenframe of the synthetic query second moment (query-aware transform)
+TAG_QUERY_AWARE = 8  # decode queries drawn with that second moment
 
 # "part" of a sequence a draw belongs to.
 PART_DIRECT = 0      # rows drawn directly as coefficients (an already-filled cache)
@@ -272,6 +275,59 @@ def hybrid_tokens(w: Workload, layer: int, which: str, b: int, h: int, n_tokens:
         g /= np.linalg.norm(g, axis=1, keepdims=True)
         x[inject] += w.inject_scale * m * g
     return quantize(x, w.dtype)
+
+
+# ----------------------------------------------------------------------------
+# query-aware (non-orthogonal) key transform: an encoder/decoder pair per kv
+# head of the form the NOVA-KV summary derives (Methodology, Key Transform
+# Derivation, Theorem 1): R = M_q^(1/2) E with E orthonormal columns,
+# coefficients r = k R, keys back as r R^-1
+# ----------------------------------------------------------------------------
+
+def query_moment_root(w: Workload, layer: int, h: int, kappa: float = 4.0):
+    """A synthetic square root W = M_q^(1/2) of a query second moment and its inverse (float64 [d, d]).
+
+    W = U diag(s) U^T with U a seeded orthonormal frame and s spaced
+    geometrically over [kappa^-1/2, kappa^1/2]; W^-1 = U diag(1/s) U^T.
+    """
+    g = rng(w, layer, 0, h, TAG_QMOMENT).standard_normal((w.head_dim, w.head_dim))
+    u, r = np.linalg.qr(g)
+    u = u * np.sign(np.diag(r))[None, :]
+    s = np.geomspace(kappa ** -0.5, kappa ** 0.5, w.head_dim)
+    return (u * s[None, :]) @ u.T, (u / s[None, :]) @ u.T
+
+
+def key_transform(w: Workload, layer: int, which: str = "k", kappa: float = 4.0):
+    """Encoder and decoder [Hkv, d, r] per kv head, each rounded to the storage dtype.
+
+    enc = W E and dec = W^-1 E, W from :func:`query_moment_root`, so that
+    dec^T enc = I (before rounding) and enc is not orthonormal.  E is the
+    orthonormalised W F_r, F_r the leading r columns of the kv head's frame,
+    so the decoder spans the subspace the synthetic tokens concentrate in.
+    The pair has the theorem's form; E is not solved for (the decode path
+    treats any such pair alike).  Returns (enc, dec) as Stored.
+    """
+    r = w.ranks(layer)[0 if which == "k" else 1]
+    encs, decs = [], []
+    for h in range(w.n_kv_heads):
+        root, root_inv = query_moment_root(w, layer, h, kappa)
+        e, rr = np.linalg.qr(root @ frame(w, layer, h, which)[:, :r])
+        e = e * np.sign(np.diag(rr))[None, :]
+        encs.append(root @ e)
+        decs.append(root_inv @ e)
+    return quantize(np.stack(encs), w.dtype), quantize(np.stack(decs), w.dtype)
+
+
+def query_aware_query(w: Workload, layer: int, kappa: float = 4.0, batch: Optional[int] = None) -> Stored:
+    """Decode queries [B, Hq, d] with second moment W^2 (q = z W, z standard
+    normal), W the square root of the query head's kv head."""
+    B = w.batch if batch is None else batch
+    roots = [query_moment_root(w, layer, h, kappa)[0] for h in range(w.n_kv_heads)]
+    q = np.stack([rng(w, layer, b, 0, TAG_QUERY_AWARE).standard_normal((w.n_q_heads, w.head_dim))
+                  for b in range(B)])
+    for hq in range(w.n_q_heads):
+        q[:, hq] = q[:, hq] @ roots[hq // w.group]
+    return quantize(q, w.dtype)
 
 
 def to_value_octets(c: np.ndarray) -> np.ndarray:

@@ -18,6 +18,13 @@ computed:
   on the fly and running standard attention ("OjaKV" README, Method Summary,
   StaticPCA).  That is the definition used here: K_hat = C_K B_K^T,
   V_hat = C_V B_V^T, then textbook softmax attention of one decode query.
+* A non-orthogonal transform splits the basis in two: an encoder E for the
+  coefficients (c = x E) and a decoder D for the reconstruction
+  (x_hat = c D^T), with D^T E = I.  compress takes the encoder and decode the
+  decoder; with an orthonormal basis both are B.  The attention-aware key
+  transform of the NOVA-KV summary (Methodology, Key Transform Derivation,
+  Theorem 1) is such a pair; query_aware_key_transform builds it from
+  queries and keys.
 * OjaKV keeps tokens whose reconstruction error is high in full rank and
   compresses the rest ("OjaKV" README, Method Summary, OjaKV).  The hybrid
   functions below select those tokens and attend the union of the
@@ -261,3 +268,61 @@ def decode_hybrid_rows(q, basis_k, basis_v, ck, cv, k_side, v_side, rows, scale:
         o, lse, _, _ = softmax_attention(q[b, hq], K, V, scale)
         out[(b, hq)] = (o, lse)
     return out
+
+
+# ----------------------------------------------------------------------------
+# query-aware key transform (NOVA-KV summary, Methodology, Key Transform
+# Derivation, Theorem 1 and Proposition 1)
+# ----------------------------------------------------------------------------
+
+def psd_sqrt(m: np.ndarray, inverse: bool = False) -> np.ndarray:
+    """Symmetric square root M^(1/2) (or M^(-1/2)) of a symmetric positive definite matrix.
+
+    From its eigendecomposition M = U diag(mu) U^T: M^(1/2) = U diag(sqrt(mu)) U^T.
+    """
+    m = np.asarray(m, dtype=np.float64)
+    mu, u = np.linalg.eigh(0.5 * (m + m.T))
+    if mu.min() <= 0:
+        raise ValueError("matrix is not positive definite")
+    root = np.sqrt(mu)
+    return (u * (1.0 / root if inverse else root)[None, :]) @ u.T
+
+
+def query_aware_key_transform(queries: np.ndarray, keys: np.ndarray, p: int):
+    """The attention-aware key transform of one kv head, truncated to p coefficients.
+
+    queries [Nq, d] (row vectors q), keys [Nk, d] (row vectors k).
+    The score error a reconstruction k_hat causes over the queries is
+    sum_i (q_i . (k - k_hat))^2 = (k - k_hat) M_q (k - k_hat)^T with
+    M_q = Q^T Q (Key Transform Derivation, eq. 5).  Theorem 1: with
+    E Lambda E^T the eigendecomposition of M_q^(1/2) S_k M_q^(1/2), S_k the
+    centred key scatter sum_j (k_j - mean)^T (k_j - mean), eigenvalues in
+    decreasing order, the optimal transform is R_K = M_q^(1/2) E; its first p
+    columns give the coefficients r = k R_K[:, :p].  Keys come back as
+    k = r R_K^(-1) (Proposition 1); R_K^(-1) = E^T M_q^(-1/2), whose first p
+    rows are the decoder for a truncated r: k_hat = r D^T with
+    D = M_q^(-1/2) E[:, :p].
+
+    Returns (encoder [d, p], decoder [d, p], eigenvalues [d] decreasing).
+    The encoder plays the part of a basis in compress (c = k enc) and the
+    decoder the part of a basis in decode (k_hat = c dec^T, fold q' = q dec).
+    """
+    Q = np.asarray(queries, dtype=np.float64)
+    K = np.asarray(keys, dtype=np.float64)
+    m_q = Q.T @ Q
+    root = psd_sqrt(m_q)
+    root_inv = psd_sqrt(m_q, inverse=True)
+    kc = K - K.mean(axis=0, keepdims=True)
+    s_k = kc.T @ kc
+    a = root @ s_k @ root
+    lam, e = np.linalg.eigh(0.5 * (a + a.T))
+    order = np.argsort(lam)[::-1]
+    lam, e = lam[order], e[:, order]
+    return root @ e[:, :p], root_inv @ e[:, :p], lam
+
+
+def score_error(queries: np.ndarray, keys: np.ndarray, keys_hat: np.ndarray) -> float:
+    """||Q K^T - Q K_hat^T||_F^2: every query's logit error over every key, summed (eq. 5, left side)."""
+    Q = np.asarray(queries, dtype=np.float64)
+    diff = Q @ np.asarray(keys, dtype=np.float64).T - Q @ np.asarray(keys_hat, dtype=np.float64).T
+    return float(np.sum(diff * diff))

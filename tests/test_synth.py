@@ -78,3 +78,25 @@ def test_hybrid_injection_structure():
     m = np.median(norms[base])
     assert np.allclose(np.linalg.norm(off[inj], axis=1) / m, 3.0, rtol=0.05)
     assert np.max(np.linalg.norm(off[base], axis=1) / norms[base]) < 0.01
+
+
+def test_key_transform_pairs_are_biorthogonal_and_not_orthonormal():
+    w = synth.LLAMA_LAYER
+    rk = w.ranks(0)[0]
+    enc, dec = synth.key_transform(w, 0, "k")
+    assert enc.shape == dec.shape == (8, 128, rk)
+    for h in range(w.n_kv_heads):
+        root, root_inv = synth.query_moment_root(w, 0, h)
+        assert np.allclose(root @ root_inv, np.eye(128), atol=1e-12)
+        assert np.allclose(root, root.T, atol=1e-13) and np.linalg.eigvalsh(root).min() > 0.49
+        # dec^T enc = I up to the bf16 rounding of both
+        assert np.max(np.abs(dec.exact[h].T @ enc.exact[h] - np.eye(rk))) < 2 ** -5
+        # the encoder is far from orthonormal, and the decoder spans F_r
+        assert np.max(np.abs(enc.exact[h].T @ enc.exact[h] - np.eye(rk))) > 0.5
+        fr = synth.frame(w, 0, h, "k")[:, :rk]
+        qd = np.linalg.qr(dec.exact[h])[0]
+        assert np.max(np.abs(fr - qd @ (qd.T @ fr))) < 2 ** -6
+    q = synth.query_aware_query(w, 0)
+    assert q.shape == (1, 32, 128)
+    q2 = synth.query_aware_query(w, 0)
+    assert _sha(q.store) == _sha(q2.store)
