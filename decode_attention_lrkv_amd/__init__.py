@@ -56,9 +56,9 @@ _SIG = {
     "lrkv_decode_attn": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, ctypes.POINTER(_Dims), _I64, _F,
                                         ctypes.c_int, _P, ctypes.c_size_t, _P]),
     "lrkv_decode_step_workspace_bytes": (ctypes.c_size_t, [ctypes.POINTER(_Dims), _I64]),
-    "lrkv_decode_step": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.POINTER(_Dims), _I64, _F,
+    "lrkv_decode_step": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.POINTER(_Dims), _I64, _F,
                                         ctypes.c_int, _P, ctypes.c_size_t, _P]),
-    "lrkv_decode_step_partial": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, ctypes.POINTER(_Dims), _I64, _F,
+    "lrkv_decode_step_partial": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, _P, ctypes.POINTER(_Dims), _I64, _F,
                                                 ctypes.c_int, _P, ctypes.c_size_t, _P]),
     "lrkv_decode_step_merge": (ctypes.c_int, [_P, _P, ctypes.POINTER(_Dims), _I64, ctypes.c_int, _P,
                                               ctypes.c_size_t, _P]),
@@ -200,11 +200,15 @@ def decode_step_workspace_bytes(batch, n_q_heads, n_kv_heads, head_dim, rank_k, 
 
 
 def decode_step(q, k_new, v_new, basis_k, coeff_k, basis_v, coeff_v, n_ctx: int, out=None, lse=None,
-                scale: float = 0.0, workspace: Optional[torch.Tensor] = None, with_lse: bool = True):
+                scale: float = 0.0, workspace: Optional[torch.Tensor] = None, with_lse: bool = True,
+                enc_k: Optional[torch.Tensor] = None):
     """Append the step's token at row n_ctx - 1 of both caches, then attend [0, n_ctx).
 
-    k_new, v_new [B, Hkv, d] (or [B, 1, Hkv, d]); other arguments as decode_attn.
-    Returns (out [B, Hq, d], lse [B, Hq] float32 or None).
+    k_new, v_new [B, Hkv, d] (or [B, 1, Hkv, d]); basis_k, basis_v decode (fold
+    and lift); enc_k [Hkv, d, r_K] encodes the new key when the key transform
+    is not an orthonormal basis (None: basis_k encodes; basis_v always encodes
+    the value).  Other arguments as decode_attn.  Returns (out [B, Hq, d],
+    lse [B, Hq] float32 or None).
     """
     B, Hq, d = q.shape
     H, _, rk = basis_k.shape
@@ -219,7 +223,7 @@ def decode_step(q, k_new, v_new, basis_k, coeff_k, basis_v, coeff_v, n_ctx: int,
     if lse is None and with_lse:
         lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
     _check(lib.lrkv_decode_step(_ptr(q), _ptr(k_new), _ptr(v_new), _ptr(basis_k), _ptr(coeff_k), _ptr(basis_v),
-                                _ptr(coeff_v), _ptr(out), _ptr(lse), ctypes.byref(dims), n_ctx, scale,
+                                _ptr(coeff_v), _ptr(enc_k), _ptr(out), _ptr(lse), ctypes.byref(dims), n_ctx, scale,
                                 _dtype_code(q), _ptr(ws), ws.numel(), _stream(q.device)))
     return out, lse
 
@@ -306,14 +310,14 @@ def decode_attn_merge(out, lse, n_ctx: int, workspace: torch.Tensor, n_kv_heads:
 
 
 def decode_step_partial(q, k_new, v_new, basis_k, coeff_k, basis_v, coeff_v, n_ctx: int, workspace: torch.Tensor,
-                        scale: float = 0.0):
+                        scale: float = 0.0, enc_k: Optional[torch.Tensor] = None):
     """First phase of decode_step: append the token, partial results into `workspace`."""
     B, Hq, d = q.shape
     H, _, rk = basis_k.shape
     dims = _Dims(B, Hq, H, d, rk, basis_v.shape[2], coeff_k.shape[2])
     _check(library().lrkv_decode_step_partial(_ptr(q), _ptr(k_new), _ptr(v_new), _ptr(basis_k), _ptr(coeff_k),
-                                              _ptr(basis_v), _ptr(coeff_v), ctypes.byref(dims), n_ctx, scale,
-                                              _dtype_code(q), _ptr(workspace), workspace.numel(),
+                                              _ptr(basis_v), _ptr(coeff_v), _ptr(enc_k), ctypes.byref(dims), n_ctx,
+                                              scale, _dtype_code(q), _ptr(workspace), workspace.numel(),
                                               _stream(q.device)))
 
 

@@ -230,7 +230,7 @@ struct SplitSmem {
 // also compresses the appended token (after the fold, while its first chunk
 // streams in), stores its cache rows and writes that token's partial as the
 // last one, a.n_parts - 1.
-template <int KC, int VB, bool FOLD, int STAGES>
+template <int KC, int VB, bool FOLD, int STAGES, bool ENC = false>
 __device__ __forceinline__ void split_bf16_body(const SplitArgs& a, int wg, int part, SplitSmem& sm,
                                                 bool append = false) {
   const int tid = threadIdx.x;
@@ -408,8 +408,9 @@ __device__ __forceinline__ void split_bf16_body(const SplitArgs& a, int wg, int 
   }
 
   if (append) {
-    // c = round(x B) for the key (threads < 128, column tid) and the value
-    // (threads >= 128, column tid - 128), stored at the appended row; then the
+    // c = round(x E) for the key (threads < 128, column tid) and the value
+    // (threads >= 128, column tid - 128), E the encoder (the basis itself
+    // unless a separate key encoder is given), stored at the appended row; then the
     // token's partial: m = q' . c_K (log2 units), l = 1, o = B_V c_V (every head)
     const int pa = a.n_parts - 1;
     const int64_t p = a.append_row;
@@ -417,10 +418,54 @@ __device__ __forceinline__ void split_bf16_body(const SplitArgs& a, int wg, int 
     const int col = tid & 127;
     const bool kind_v = tid >= 128;
     const int r = kind_v ? rv : rk;
+    if constexpr (ENC) {
+      // a separate key encoder (a non-orthogonal transform) is read from
+      // memory by every thread: thread (row group rg, column group cg) sums
+      // x[e] E[e][8 cg .. 8 cg + 7] over rows e = rg, rg + n_rg, ... into
+      // per-row-group partials in `raw` (B_K's copy there is dead after the
+      // fold), which the key column threads then add up
+      const int ng = rk >> 3;          // <= 16
+      const int n_rg = 256 / ng;       // >= 16, so a thread takes <= 8 rows of d <= 128
+      const int cg = tid % ng, rg = tid / ng;
+      float* s_part = reinterpret_cast<float*>(sm.raw);
+      if (rg < n_rg) {
+        const uint16_t* src = static_cast<const uint16_t*>(a.enc_k) + (int64_t)h * d * rk + 8 * cg;
+        float sum[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) sum[j] = 0.f;
+        // two batches of four rows in flight (the attention's first chunk is
+        // also in flight here, so registers are short)
+        for (int i0 = 0; i0 < 8; i0 += 4) {
+          u32x4 w[4];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int e = rg + n_rg * (i0 + i);
+            w[i] = e < d ? *reinterpret_cast<const u32x4*>(src + (int64_t)e * rk) : u32x4{0u, 0u, 0u, 0u};
+          }
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int e = rg + n_rg * (i0 + i);
+            const float xe = e < d ? s_q[e] : 0.f;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+              sum[2 * j] = fmaf(xe, bf16_lo(w[i][j]), sum[2 * j]);
+              sum[2 * j + 1] = fmaf(xe, bf16_hi(w[i][j]), sum[2 * j + 1]);
+            }
+          }
+        }
+#pragma unroll
+        for (int j = 0; j < 8; ++j) s_part[rg * rk + 8 * cg + j] = sum[j];
+      }
+      __syncthreads();
+    }
     if (col < r) {
       float acc = 0.f;
       if (kind_v) {
         for (int e = 0; e < d; ++e) acc = fmaf(s_q[128 + e], bf16_to_f32(sm.bv[e * (rv + 8) + col]), acc);
+      } else if (ENC) {
+        const float* s_part = reinterpret_cast<const float*>(sm.raw);
+        const int n_rg = 256 / (rk >> 3);
+        for (int i = 0; i < n_rg; ++i) acc += s_part[i * rk + col];
       } else {
         for (int e = 0; e < d; ++e) acc = fmaf(s_q[e], bf16_to_f32(s_bk[e * rk + col]), acc);
       }
@@ -646,12 +691,14 @@ template <int KC, int VB>
 constexpr int kStages = 2 * KC + VB < 16 ? 2 : 1;
 
 // Low-rank keys: two waves per SIMD (one round of workgroups fills the chip).
-template <int KC, int VB>
+// ENC: the appended key has its own encoder (a.enc_k), a separate
+// instantiation so that the plain kernel carries none of its code.
+template <int KC, int VB, bool ENC>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void split_bf16_kernel(SplitArgs a) {
   __shared__ SplitSmem sm;
-  split_bf16_body<KC, VB, true, kStages<KC, VB>>(a, blockIdx.x, blockIdx.x, sm,
-                                                  a.k_new != nullptr && blockIdx.x == gridDim.x - 1);
+  split_bf16_body<KC, VB, true, kStages<KC, VB>, ENC>(a, blockIdx.x, blockIdx.x, sm,
+                                                       a.k_new != nullptr && blockIdx.x == gridDim.x - 1);
 }
 
 // Hybrid cache in one launch: the gridDim.x workgroups of each (b, kv head)
@@ -834,7 +881,10 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeArgs a) {
 
 #define LRKV_SPLIT_CASE(KC, VB)                                                          \
   case (KC * 16 + VB):                                                                   \
-    hipLaunchKernelGGL((split_bf16_kernel<KC, VB>), grid, dim3(256), 0, s, a);           \
+    if (a.enc_k)                                                                         \
+      hipLaunchKernelGGL((split_bf16_kernel<KC, VB, true>), grid, dim3(256), 0, s, a);   \
+    else                                                                                 \
+      hipLaunchKernelGGL((split_bf16_kernel<KC, VB, false>), grid, dim3(256), 0, s, a);  \
     break;
 
 hipError_t launch_split_bf16(const SplitArgs& a, hipStream_t s) {
@@ -843,7 +893,7 @@ hipError_t launch_split_bf16(const SplitArgs& a, hipStream_t s) {
   // last one
   const dim3 grid(a.k_new ? a.n_parts - 1 : a.n_parts, a.hkv, a.batch);
   const int kc = (a.rk + 31) / 32, vb = (a.rv + 15) / 16;
-  if (a.basis_k == nullptr || a.basis_v == nullptr) return hipErrorInvalidValue;
+  if (a.basis_k == nullptr || a.basis_v == nullptr || (a.enc_k && !a.k_new)) return hipErrorInvalidValue;
   switch (kc * 16 + vb) {
     LRKV_SPLIT_CASE(1, 1) LRKV_SPLIT_CASE(1, 2) LRKV_SPLIT_CASE(1, 3) LRKV_SPLIT_CASE(1, 4)
     LRKV_SPLIT_CASE(1, 5) LRKV_SPLIT_CASE(1, 6) LRKV_SPLIT_CASE(1, 7) LRKV_SPLIT_CASE(1, 8)

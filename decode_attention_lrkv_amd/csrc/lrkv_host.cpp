@@ -282,7 +282,8 @@ lrkv_status check_decode_common(const lrkv_dims* dims, int64_t n_ctx, lrkv_dtype
 lrkv_status decode_partial(const void* q, const void* basis_k, const void* coeff_k, const void* basis_v,
                            const void* coeff_v, const lrkv_dims* dims, int64_t n_ctx, float scale,
                            lrkv_dtype dtype, void* workspace, const DecodeLayout& L, hipStream_t stream,
-                           const char* fn, const void* k_new = nullptr, const void* v_new = nullptr) {
+                           const char* fn, const void* k_new = nullptr, const void* v_new = nullptr,
+                           const void* enc_k = nullptr) {
   char* ws = static_cast<char*>(workspace);
   SplitArgs sa{};
   sa.q = q; sa.basis_k = basis_k; sa.ck = coeff_k; sa.cv = coeff_v; sa.basis_v = basis_v;
@@ -298,6 +299,7 @@ lrkv_status decode_partial(const void* q, const void* basis_k, const void* coeff
     sa.n_static = n_ctx - 1;
     sa.k_new = k_new;
     sa.v_new = v_new;
+    sa.enc_k = enc_k;
     sa.append_row = n_ctx - 1;
   }
   const hipError_t e = dtype == LRKV_BF16 ? launch_split_bf16(sa, stream) : launch_split_f32(sa, stream);
@@ -386,9 +388,9 @@ size_t lrkv_decode_step_workspace_bytes(const lrkv_dims* dims, int64_t n_ctx) {
 namespace {
 
 lrkv_status check_step(const void* q, const void* k_new, const void* v_new, const void* basis_k,
-                       const void* coeff_k, const void* basis_v, const void* coeff_v, const lrkv_dims* dims,
-                       int64_t n_ctx, float scale, lrkv_dtype dtype, void* workspace, size_t workspace_bytes,
-                       const char* fn) {
+                       const void* coeff_k, const void* basis_v, const void* coeff_v, const void* enc_k,
+                       const lrkv_dims* dims, int64_t n_ctx, float scale, lrkv_dtype dtype, void* workspace,
+                       size_t workspace_bytes, const char* fn) {
   lrkv_status st = check_dims(dims, dtype, fn);
   if (st != LRKV_OK) return st;
   if (n_ctx < 1 || n_ctx > dims->capacity)
@@ -403,6 +405,7 @@ lrkv_status check_step(const void* q, const void* k_new, const void* v_new, cons
   LRKV_CHECK_PTR(basis_v, fn);
   LRKV_CHECK_PTR(coeff_v, fn);
   LRKV_CHECK_PTR(workspace, fn);
+  if (enc_k && !aligned16(enc_k)) return fail(LRKV_ERR_INVALID_ARGUMENT, "%s: enc_k is not 16-byte aligned", fn);
   const size_t need = lrkv_decode_step_workspace_bytes(dims, n_ctx);
   if (workspace_bytes < need)
     return fail(LRKV_ERR_WORKSPACE_TOO_SMALL, "%s: workspace of %zu bytes, %zu needed", fn, workspace_bytes, need);
@@ -417,17 +420,16 @@ DecodeLayout step_layout(const lrkv_dims& d, int64_t n_ctx, lrkv_dtype dtype) {
 }
 
 lrkv_status step_partial(const void* q, const void* k_new, const void* v_new, const void* basis_k, void* coeff_k,
-                         const void* basis_v, void* coeff_v, const lrkv_dims* dims, int64_t n_ctx, float scale,
-                         lrkv_dtype dtype, void* workspace, const DecodeLayout& L, hipStream_t stream,
-                         const char* fn) {
+                         const void* basis_v, void* coeff_v, const void* enc_k, const lrkv_dims* dims, int64_t n_ctx, float scale, lrkv_dtype dtype, void* workspace,
+                         const DecodeLayout& L, hipStream_t stream, const char* fn) {
   if (dtype != LRKV_BF16) {
-    const lrkv_status st =
-        lrkv_compress_kv(k_new, v_new, basis_k, basis_v, coeff_k, coeff_v, dims, 1, n_ctx - 1, dtype, stream);
+    const lrkv_status st = lrkv_compress_kv(k_new, v_new, enc_k ? enc_k : basis_k, basis_v, coeff_k, coeff_v, dims,
+                                            1, n_ctx - 1, dtype, stream);
     if (st != LRKV_OK) return st;
     return decode_partial(q, basis_k, coeff_k, basis_v, coeff_v, dims, n_ctx, scale, dtype, workspace, L, stream, fn);
   }
   return decode_partial(q, basis_k, coeff_k, basis_v, coeff_v, dims, n_ctx, scale, dtype, workspace, L, stream, fn,
-                        k_new, v_new);
+                        k_new, v_new, enc_k);
 }
 
 }  // namespace
@@ -435,32 +437,31 @@ lrkv_status step_partial(const void* q, const void* k_new, const void* v_new, co
 extern "C" {
 
 lrkv_status lrkv_decode_step(const void* q, const void* k_new, const void* v_new, const void* basis_k,
-                             void* coeff_k, const void* basis_v, void* coeff_v, void* out, float* lse,
-                             const lrkv_dims* dims, int64_t n_ctx, float scale, lrkv_dtype dtype,
-                             void* workspace, size_t workspace_bytes, hipStream_t stream) {
+                             void* coeff_k, const void* basis_v, void* coeff_v, const void* enc_k, void* out, float* lse, const lrkv_dims* dims, int64_t n_ctx, float scale,
+                             lrkv_dtype dtype, void* workspace, size_t workspace_bytes, hipStream_t stream) {
   const char* fn = "lrkv_decode_step";
-  lrkv_status st = check_step(q, k_new, v_new, basis_k, coeff_k, basis_v, coeff_v, dims, n_ctx, scale, dtype,
+  lrkv_status st = check_step(q, k_new, v_new, basis_k, coeff_k, basis_v, coeff_v, enc_k, dims, n_ctx, scale, dtype,
                               workspace, workspace_bytes, fn);
   if (st != LRKV_OK) return st;
   LRKV_CHECK_PTR(out, fn);
   if (lse && !aligned16(lse)) return fail(LRKV_ERR_INVALID_ARGUMENT, "%s: lse is not 16-byte aligned", fn);
   const DecodeLayout L = step_layout(*dims, n_ctx, dtype);
-  st = step_partial(q, k_new, v_new, basis_k, coeff_k, basis_v, coeff_v, dims, n_ctx, scale, dtype, workspace, L,
-                    stream, fn);
+  st = step_partial(q, k_new, v_new, basis_k, coeff_k, basis_v, coeff_v, enc_k, dims, n_ctx, scale, dtype, workspace,
+                    L, stream, fn);
   if (st != LRKV_OK) return st;
   return decode_merge(out, lse, dims, dtype, workspace, L, stream, fn);
 }
 
 lrkv_status lrkv_decode_step_partial(const void* q, const void* k_new, const void* v_new, const void* basis_k,
-                                     void* coeff_k, const void* basis_v, void* coeff_v, const lrkv_dims* dims,
-                                     int64_t n_ctx, float scale, lrkv_dtype dtype, void* workspace,
-                                     size_t workspace_bytes, hipStream_t stream) {
+                                     void* coeff_k, const void* basis_v, void* coeff_v, const void* enc_k,
+                                     const lrkv_dims* dims, int64_t n_ctx, float scale, lrkv_dtype dtype,
+                                     void* workspace, size_t workspace_bytes, hipStream_t stream) {
   const char* fn = "lrkv_decode_step_partial";
-  const lrkv_status st = check_step(q, k_new, v_new, basis_k, coeff_k, basis_v, coeff_v, dims, n_ctx, scale, dtype,
-                                    workspace, workspace_bytes, fn);
+  const lrkv_status st = check_step(q, k_new, v_new, basis_k, coeff_k, basis_v, coeff_v, enc_k, dims, n_ctx, scale,
+                                    dtype, workspace, workspace_bytes, fn);
   if (st != LRKV_OK) return st;
-  return step_partial(q, k_new, v_new, basis_k, coeff_k, basis_v, coeff_v, dims, n_ctx, scale, dtype, workspace,
-                      step_layout(*dims, n_ctx, dtype), stream, fn);
+  return step_partial(q, k_new, v_new, basis_k, coeff_k, basis_v, coeff_v, enc_k, dims, n_ctx, scale, dtype,
+                      workspace, step_layout(*dims, n_ctx, dtype), stream, fn);
 }
 
 lrkv_status lrkv_decode_step_merge(void* out, float* lse, const lrkv_dims* dims, int64_t n_ctx, lrkv_dtype dtype,

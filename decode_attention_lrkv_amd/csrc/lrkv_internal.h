@@ -37,6 +37,7 @@ struct SplitArgs {
   // the other workgroups attend rows [0, n_static).
   const void* k_new;     // [B, Hkv, d] or null
   const void* v_new;     // [B, Hkv, d]
+  const void* enc_k;     // [Hkv, d, rk] encoder of the appended key, or null: basis_k encodes
   int64_t append_row;
 };
 

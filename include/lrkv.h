@@ -27,6 +27,18 @@
  *   lse and workspaces are float32.  Arithmetic accumulates in float32;
  *   rounding to bfloat16 is round-to-nearest-even.
  * - Grouped-query attention: q head h reads kv head h / (Hq / Hkv).
+ * - Bases and transforms: a cache row is c = x E for an encoder E and is read
+ *   back as x_hat = c D^T for a decoder D, both [Hkv, d, r].  With an
+ *   orthonormal basis B (StaticPCA) E = D = B and one array serves both.
+ *   A non-orthogonal transform passes E where a call encodes (lrkv_compress,
+ *   lrkv_compress_kv, the enc_k of a decode step) and D where it decodes
+ *   (basis_k folds the query, basis_v lifts the output), with D^T E = I:
+ *   the attention-aware key transform of the NOVA-KV summary (Methodology,
+ *   Key Transform Derivation, Theorem 1: R_K = M_q^(1/2) E, keys recovered
+ *   through R_K^-1) is such a pair.  Its value transform is orthogonal (same
+ *   summary, Value Transform, Corollary 1), so the decode step takes a
+ *   separate encoder for keys only.  The hybrid cache assumes an orthonormal
+ *   basis (its residual test reconstructs with the encoding basis).
  * - Layouts ("B" batch, "Hq"/"Hkv" query/kv heads, "d" head_dim, "cap" cache
  *   capacity in tokens):
  *     keys, row layout:     key coefficient cache [B, Hkv, cap, r_K],
@@ -88,7 +100,8 @@ typedef struct lrkv_dims {
  * and V; "OjaKV" README, StaticPCA: a fixed offline basis.)  One call writes
  * one cache (K or V) with its own basis and rank.
  *   x      [B, n_tokens, Hkv, d]   the new tokens' full keys or values
- *   basis  [Hkv, d, rank]          orthonormal columns (not checked)
+ *   basis  [Hkv, d, rank]          the encoder: an orthonormal basis, or the
+ *                                  encoding half of a transform (not checked)
  *   coeff  key row layout [B, Hkv, capacity, rank] (kind = LRKV_KEYS) or
  *          value octet layout [B, Hkv, capacity/8, rank, 8] (kind = LRKV_VALUES)
  * Rows outside [pos, pos + n_tokens) are not touched.  n_tokens = 0 is a no-op.
@@ -137,6 +150,7 @@ size_t lrkv_decode_workspace_bytes(const lrkv_dims* dims, int64_t n_ctx, int64_t
  *   q        [B, Hq, d]
  *   basis_k  [Hkv, d, r_K];   coeff_k  key row layout [B, Hkv, capacity, r_K]
  *   basis_v  [Hkv, d, r_V];   coeff_v  value octet layout [B, Hkv, capacity/8, r_V, 8]
+ *            (the decoders: the basis itself, or a transform's decoding half)
  *   out      [B, Hq, d] (storage dtype);  lse [B, Hq] float32 natural log, or NULL
  *   scale    softmax scale; 0 selects 1/sqrt(head_dim)
  *   workspace at least lrkv_decode_workspace_bytes(dims, n_ctx, 0) bytes
@@ -173,20 +187,25 @@ lrkv_status lrkv_decode_attn_merge(void* out, float* lse, const lrkv_dims* dims,
  * lrkv_compress_kv of one token at row n_ctx - 1 followed by
  * lrkv_decode_attn over [0, n_ctx) (the "Llama-3.1-NovaKV" model card,
  * results section, times whole decode steps with the cache written and read
- * inside the step; the cache row is c = round(x B) as in lrkv_compress).
- * For bfloat16 the append runs inside the attention launch: one extra
- * workgroup per (b, kv head) compresses the token, stores its rows and
- * contributes its softmax term, while the others attend rows [0, n_ctx - 1);
- * a second launch merges.  float32 runs lrkv_compress_kv, then the decode.
+ * inside the step; the cache row is c = round(x E) as in lrkv_compress).
+ * For bfloat16 the append runs inside the attention launch: per (b, kv head)
+ * one workgroup (an extra one when the grid has room for it, else the last
+ * attention workgroup, after its fold) compresses the token, stores its rows
+ * and contributes its softmax term, while the others attend rows
+ * [0, n_ctx - 1); a second launch merges.  float32 runs lrkv_compress_kv,
+ * then the decode.
  *   k_new, v_new  [B, Hkv, d] the new token's key and value
+ *   basis_k, basis_v  the decoders (fold and lift), as in lrkv_decode_attn
  *   coeff_k, coeff_v  the caches (row n_ctx - 1 is written; rows below are read)
+ *   enc_k    [Hkv, d, r_K] encoder of the new key, or NULL when basis_k is an
+ *            orthonormal basis that also encodes (the value is encoded by basis_v)
  *   workspace at least lrkv_decode_step_workspace_bytes(dims, n_ctx) bytes
  * Other arguments as lrkv_decode_attn.  Requires 1 <= n_ctx <= capacity.
  */
 size_t lrkv_decode_step_workspace_bytes(const lrkv_dims* dims, int64_t n_ctx);
 lrkv_status lrkv_decode_step(const void* q, const void* k_new, const void* v_new, const void* basis_k,
-                             void* coeff_k, const void* basis_v, void* coeff_v, void* out, float* lse,
-                             const lrkv_dims* dims, int64_t n_ctx, float scale, lrkv_dtype dtype,
+                             void* coeff_k, const void* basis_v, void* coeff_v, const void* enc_k, void* out,
+                             float* lse, const lrkv_dims* dims, int64_t n_ctx, float scale, lrkv_dtype dtype,
                              void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
@@ -196,9 +215,9 @@ lrkv_status lrkv_decode_step(const void* q, const void* k_new, const void* v_new
  * combines them into out and lse.
  */
 lrkv_status lrkv_decode_step_partial(const void* q, const void* k_new, const void* v_new, const void* basis_k,
-                                     void* coeff_k, const void* basis_v, void* coeff_v, const lrkv_dims* dims,
-                                     int64_t n_ctx, float scale, lrkv_dtype dtype, void* workspace,
-                                     size_t workspace_bytes, hipStream_t stream);
+                                     void* coeff_k, const void* basis_v, void* coeff_v, const void* enc_k,
+                                     const lrkv_dims* dims, int64_t n_ctx, float scale, lrkv_dtype dtype,
+                                     void* workspace, size_t workspace_bytes, hipStream_t stream);
 lrkv_status lrkv_decode_step_merge(void* out, float* lse, const lrkv_dims* dims, int64_t n_ctx, lrkv_dtype dtype,
                                    void* workspace, size_t workspace_bytes, hipStream_t stream);
 

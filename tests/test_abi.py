@@ -145,3 +145,19 @@ def test_workspace_queries():
     assert lib.lrkv_decode_workspace_bytes(ctypes.byref(_dims(lrkv, head_dim=96)), 256, 0) == 0
     assert lib.lrkv_decode_workspace_bytes(ctypes.byref(d), 256, 64) > n1
     assert lib.lrkv_compress_hybrid_workspace_bytes(ctypes.byref(d), 1000) > 0
+
+
+def test_decode_step_validation():
+    lrkv, lib = _lib()
+    d = _dims(lrkv)
+    f = lib.lrkv_decode_step
+    # q, k_new, v_new, basis_k, coeff_k, basis_v, coeff_v, enc_k, out, lse, dims, n_ctx, scale, dtype, ws, bytes, stream
+    args = lambda enc=None, k_new=P, n_ctx=100, ws_bytes=1 << 30: (P, k_new, P, P, P, P, P, enc, P, None,
+                                                                    ctypes.byref(d), n_ctx, 0.0, 1, P, ws_bytes,
+                                                                    None)
+    assert f(*args(enc=MIS)) == 1 and b"enc_k" in lib.lrkv_last_error()
+    assert f(*args(k_new=None)) == 1 and b"NULL" in lib.lrkv_last_error()
+    assert f(*args(n_ctx=0)) == 1
+    assert f(*args(enc=P, ws_bytes=16)) == 3
+    g = lib.lrkv_decode_step_partial
+    assert g(P, P, P, P, P, P, P, MIS, ctypes.byref(d), 100, 0.0, 1, P, 1 << 30, None) == 1
