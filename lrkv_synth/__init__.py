@@ -42,6 +42,7 @@ TAG_INJECT_DIR_K = 6
 TAG_INJECT_DIR_V = 9
 TAG_QMOMENT = 7      # eigenframe of the synthetic query second moment (query-aware transform)
 TAG_QUERY_AWARE = 8  # decode queries drawn with that second moment
+TAG_LATENT_QUERY = 10  # queries already in the key latent space (absorbed projections)
 
 # "part" of a sequence a draw belongs to.
 PART_DIRECT = 0      # rows drawn directly as coefficients (an already-filled cache)
@@ -188,6 +189,19 @@ def query(w: Workload, layer: int, batch: Optional[int] = None) -> Stored:
     B = w.batch if batch is None else batch
     q = np.stack([rng(w, layer, b, 0, TAG_QUERY).standard_normal((w.n_q_heads, w.head_dim))
                   for b in range(B)])
+    return quantize(q, w.dtype)
+
+
+def latent_query(w: Workload, layer: int, batch: Optional[int] = None) -> Stored:
+    """Queries already projected into the key latent space [B, Hq, r_K], standard normal.
+
+    With projections that absorb the key basis, a decode query arrives with
+    r_K coordinates; a standard normal query against an orthonormal basis has
+    standard normal coordinates, which is what is drawn here.
+    """
+    B = w.batch if batch is None else batch
+    rk = w.ranks(layer)[0]
+    q = np.stack([rng(w, layer, b, 0, TAG_LATENT_QUERY).standard_normal((w.n_q_heads, rk)) for b in range(B)])
     return quantize(q, w.dtype)
 
 

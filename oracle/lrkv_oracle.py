@@ -25,6 +25,8 @@ computed:
   transform of the NOVA-KV summary (Methodology, Key Transform Derivation,
   Theorem 1) is such a pair; query_aware_key_transform builds it from
   queries and keys.
+* With the bases absorbed into the query and output projections, decode
+  takes q' = q B_K and returns the latent output p C_V (decode_latent).
 * OjaKV keeps tokens whose reconstruction error is high in full rank and
   compresses the rest ("OjaKV" README, Method Summary, OjaKV).  The hybrid
   functions below select those tokens and attend the union of the
@@ -174,6 +176,38 @@ def decode_rows(q, basis_k, coeff_k, basis_v, coeff_v, n_ctx: int, rows, scale: 
         o, lse, _, _ = softmax_attention(q[b, hq], K, V, scale)
         out[(b, hq)] = (o, lse)
     return out
+
+
+def decode_latent(q_lat, coeff_k, coeff_v, n_ctx: int, scale: float):
+    """Decode attention in the latent space, for projections that absorb the bases.
+
+    When the bases are folded into the model's projections offline (the
+    NovaKV delta ships modified query and output projections alongside the K
+    and V factors: "Llama-3.1-NovaKV" model card, introduction), a query
+    arrives already as q' = q B_K and the output leaves as the latent
+    o' = p C_V, lifted by the absorbed output projection.  Attention is then
+    textbook attention with the coefficient rows as keys and values:
+    s_t = q' . C_K[t] * scale, p = softmax(s), o' = p C_V.
+
+    q_lat [B, Hq, r_K]; coeff_k [B, Hkv, >=n_ctx, r_K]; coeff_v [B, Hkv, >=n_ctx, r_V]
+    (row layout).  scale is explicit (the head dimension is not visible
+    here).  Returns o' [B, Hq, r_V] float64 and lse [B, Hq].
+    """
+    q_lat = np.asarray(q_lat, dtype=np.float64)
+    B, Hq, _ = q_lat.shape
+    Hkv = coeff_k.shape[1]
+    group = Hq // Hkv
+    rv = coeff_v.shape[-1]
+    o = np.zeros((B, Hq, rv))
+    lse = np.zeros((B, Hq))
+    for b in range(B):
+        for h in range(Hkv):
+            K = np.asarray(coeff_k[b, h, :n_ctx], dtype=np.float64)
+            V = np.asarray(coeff_v[b, h, :n_ctx], dtype=np.float64)
+            for j in range(group):
+                hq = h * group + j
+                o[b, hq], lse[b, hq], _, _ = softmax_attention(q_lat[b, hq], K, V, scale)
+    return o, lse
 
 
 # ----------------------------------------------------------------------------

@@ -497,3 +497,27 @@ def test_row_sampled_decoders_match_the_full_decoder():
         for r in (r1, r2):
             assert np.max(np.abs(r[(b, hq)][0] - o[b, hq])) <= 1e-14
             assert abs(r[(b, hq)][1] - lse[b, hq]) <= 1e-13
+
+
+def test_latent_decode_matches_sdpa_and_absorbs_the_bases():
+    """decode_latent is torch's dense attention on the coefficient rows (with
+    the scale passed explicitly), and lifting its output through B_V gives
+    the pinned decode over reconstructed keys and values with q' = q B_K, for
+    non-orthonormal bases too (absorbed projections change nothing)."""
+    rng = np.random.default_rng(21)
+    B, Hq, Hkv, d, rk, rv, n = 2, 8, 2, 16, 6, 10, 37
+    q = rng.standard_normal((B, Hq, d))
+    bk = rng.standard_normal((Hkv, d, rk)) / 3
+    bv = rng.standard_normal((Hkv, d, rv)) / 3
+    ck = rng.standard_normal((B, Hkv, n + 5, rk))
+    cv = rng.standard_normal((B, Hkv, n + 5, rv))
+    g = Hq // Hkv
+    q_lat = np.stack([np.stack([q[b, hq] @ bk[hq // g] for hq in range(Hq)]) for b in range(B)])
+    scale = 1 / math.sqrt(d)
+    o_lat, lse_lat = O.decode_latent(q_lat, ck, cv, n, scale)
+    assert np.max(np.abs(o_lat - _sdpa(q_lat, ck[:, :, :n], cv[:, :, :n], scale=scale))) <= 1e-13
+    assert np.max(np.abs(lse_lat - _sdpa_lse(q_lat, ck[:, :, :n], g, scale))) <= 1e-12
+    o, lse = O.decode(q, bk, ck, bv, cv, n)
+    lifted = np.stack([np.stack([o_lat[b, hq] @ bv[hq // g].T for hq in range(Hq)]) for b in range(B)])
+    assert np.max(np.abs(lifted - o)) <= 1e-12 * np.max(np.abs(o))
+    assert np.max(np.abs(lse - lse_lat)) <= 1e-12
