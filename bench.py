@@ -234,6 +234,8 @@ def main():
                      "bytes_per_launch": round(sum(attn_bytes[l % 2] for l in range(L)) / L)},
     }
 
+    if not args.no_extra:
+        result["variants_32k"] = bench_variants(torch, lrkv, bm, synth, dev, layers, ws, dev_bf16)
     del layers, ws
     torch.cuda.empty_cache()
     if not args.no_extra:
@@ -243,6 +245,49 @@ def main():
         result["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
     print(json.dumps(result), flush=True)
     return 0
+
+
+def bench_variants(torch, lrkv, bm, synth, dev, layers, ws, dev_bf16):
+    """The two variants of the decode on the same 32-layer batched caches:
+    latent queries and outputs (projections that absorb the bases: no fold,
+    no lift, no basis read) and the decode step with a separate,
+    non-orthogonal key encoder (decoder D folds the query, encoder E
+    compresses the appended key), with the plain decode step timed the same
+    way for comparison.  Each figure is two launches per layer (attention +
+    merge), averaged over 3 passes of the 32 layers."""
+    w = synth.BATCHED_32K
+    B, Hq, H, d, L = w.batch, w.n_q_heads, w.n_kv_heads, w.head_dim, w.layers
+    N = w.n_ctx[0]
+    lat = {p: dev_bf16(synth.latent_query(w, p).store) for p in (0, 1)}
+    tf = {p: tuple(dev_bf16(x.store) for x in synth.key_transform(w, p, "k")) for p in (0, 1)}
+    outs = {p: torch.empty((B, Hq, w.ranks(p)[1]), dtype=torch.bfloat16, device=dev) for p in (0, 1)}
+
+    def latent(i):
+        lay = layers[i % L]
+        lrkv.decode_attn_latent(lat[i % 2], lay["ck"], lay["cv"], N, d, out=outs[i % 2], lse=lay["lse"],
+                                workspace=ws)
+
+    def transform_step(i):
+        lay = layers[i % L]
+        enc, dec = tf[i % 2]
+        lrkv.decode_step(lay["q"], lay["ak"], lay["av"], dec, lay["ck"], lay["bv"], lay["cv"], N, out=lay["out"],
+                         lse=lay["lse"], workspace=ws, enc_k=enc)
+
+    def plain_step(i):
+        lay = layers[i % L]
+        lrkv.decode_step(lay["q"], lay["ak"], lay["av"], lay["bk"], lay["ck"], lay["bv"], lay["cv"], N,
+                         out=lay["out"], lse=lay["lse"], workspace=ws)
+
+    lat_us = _timed(torch, latent, 3 * L, warm=L)
+    tf_us = _timed(torch, transform_step, 3 * L, warm=L)
+    plain_us = _timed(torch, plain_step, 3 * L, warm=L)
+    lat_bytes = sum(bm.latent_decode_bytes(B, Hq, H, *w.ranks(p), N) for p in (0, 1)) / 2
+    return {"latent_decode_us_per_layer": round(lat_us, 3),
+            "latent_decode_GBps": round(lat_bytes / (lat_us * 1e-6) / 1e9, 1),
+            "transform_step_us_per_layer": round(tf_us, 3),
+            "plain_step_us_per_layer": round(plain_us, 3),
+            "note": "same caches and context as the main figure, layers run back to back (no prefill "
+                    "between them); two launches per layer"}
 
 
 def _timed(torch, fn, iters, warm=3):

@@ -55,6 +55,8 @@ _SIG = {
     "lrkv_decode_workspace_bytes": (ctypes.c_size_t, [ctypes.POINTER(_Dims), _I64, _I64]),
     "lrkv_decode_attn": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, ctypes.POINTER(_Dims), _I64, _F,
                                         ctypes.c_int, _P, ctypes.c_size_t, _P]),
+    "lrkv_decode_attn_latent": (ctypes.c_int, [_P, _P, _P, _P, _P, ctypes.POINTER(_Dims), _I64, _F, ctypes.c_int,
+                                               _P, ctypes.c_size_t, _P]),
     "lrkv_decode_step_workspace_bytes": (ctypes.c_size_t, [ctypes.POINTER(_Dims), _I64]),
     "lrkv_decode_step": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.POINTER(_Dims), _I64, _F,
                                         ctypes.c_int, _P, ctypes.c_size_t, _P]),
@@ -190,6 +192,31 @@ def decode_attn(q, basis_k, coeff_k, basis_v, coeff_v, n_ctx: int, out=None, lse
     _check(lib.lrkv_decode_attn(_ptr(q), _ptr(basis_k), _ptr(coeff_k), _ptr(basis_v), _ptr(coeff_v),
                                 _ptr(out), _ptr(lse), ctypes.byref(dims), n_ctx, scale, _dtype_code(q),
                                 _ptr(ws), ws.numel(), _stream(q.device)))
+    return out, lse
+
+
+def decode_attn_latent(q_lat, coeff_k, coeff_v, n_ctx: int, head_dim: int, out=None, lse=None, scale: float = 0.0,
+                       workspace: Optional[torch.Tensor] = None, with_lse: bool = True):
+    """Decode attention on latent queries, for projections that absorb the bases.
+
+    q_lat [B, Hq, r_K]; coeff_k [B, Hkv, cap, r_K]; coeff_v [B, Hkv, cap/8, r_V, 8];
+    head_dim is the model's head dimension (default scale 1/sqrt(head_dim)).
+    Returns (out_lat [B, Hq, r_V], lse [B, Hq] float32 or None).
+    """
+    B, Hq, rk = q_lat.shape
+    H, cap = coeff_k.shape[1], coeff_k.shape[2]
+    rv = coeff_v.shape[3]
+    dims = _Dims(B, Hq, H, head_dim, rk, rv, cap)
+    lib = library()
+    need = int(lib.lrkv_decode_workspace_bytes(ctypes.byref(dims), n_ctx, 0))
+    ws = _workspace(need, q_lat.device, workspace)
+    if out is None:
+        out = torch.empty((B, Hq, rv), dtype=q_lat.dtype, device=q_lat.device)
+    if lse is None and with_lse:
+        lse = torch.empty((B, Hq), dtype=torch.float32, device=q_lat.device)
+    _check(lib.lrkv_decode_attn_latent(_ptr(q_lat), _ptr(coeff_k), _ptr(coeff_v), _ptr(out), _ptr(lse),
+                                       ctypes.byref(dims), n_ctx, scale, _dtype_code(q_lat), _ptr(ws), ws.numel(),
+                                       _stream(q_lat.device)))
     return out, lse
 
 

@@ -60,6 +60,14 @@ def step_kernel_bytes(batch, n_q_heads, n_kv_heads, head_dim, rank_k, rank_v, n_
             + s * batch * n_kv_heads * (2 * head_dim + rank_k + rank_v))
 
 
+def latent_decode_bytes(batch, n_q_heads, n_kv_heads, rank_k, rank_v, n_ctx, elem_bytes=2):
+    """Decode with absorbed projections: coefficient rows, r_K-wide queries in
+    and r_V-wide outputs out; no basis is read."""
+    s = elem_bytes
+    return (s * batch * n_kv_heads * n_ctx * (rank_k + rank_v)
+            + s * batch * n_q_heads * (rank_k + rank_v))
+
+
 def compress_bytes(batch, n_tokens, n_kv_heads, head_dim, rank, elem_bytes=2):
     """One compress call: token rows in, basis in, coefficient rows out."""
     s = elem_bytes

@@ -103,9 +103,9 @@ __device__ void workgroup_partial(const SplitArgs& a, int b, int h, int part, co
       store_partial(po + ((row0 + j) * a.n_parts + part) * d + dd, o);
     }
   } else {
-    for (int i = tid; i < g * d; i += 256) {
-      const int j = i / d, dd = i - j * d;
-      store_partial(po + ((row0 + j) * a.n_parts + part) * d + dd, s_merged[j * 128 + dd]);
+    for (int i = tid; i < g * rv; i += 256) {
+      const int j = i / rv, c = i - j * rv;
+      store_partial(po + ((row0 + j) * a.n_parts + part) * rv + c, s_merged[j * 128 + c]);
     }
   }
   if (tid < g) {
@@ -148,7 +148,12 @@ __device__ void merge_unit(const MergeArgs& a, int64_t unit) {
   constexpr int kU = 16;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int S = a.n_parts, d = a.d, g = a.g;
-  const int cols = d / 4, groups = 64 / cols;
+  // d / 4 float4 columns, rounded up to a power of two lanes (a latent
+  // output's width r_V need not be one); lanes past the width compute
+  // unused values and store nothing
+  int cols = 1;
+  while (cols < d / 4) cols <<= 1;
+  const int groups = 64 / cols;
   const int col = lane % cols, grp = lane / cols;
   for (int j = wave; j < g; j += kWaves) {
     const int64_t row = unit * g + j;
@@ -186,7 +191,7 @@ __device__ void merge_unit(const MergeArgs& a, int64_t unit) {
       st = (lane & off) ? merge_two(other, st) : merge_two(st, other);
     }
     const float inv = st.l > 0.f ? 1.f / st.l : 0.f;
-    if (grp == 0) {
+    if (grp == 0 && 4 * col < d) {
 #pragma unroll
       for (int e = 0; e < 4; ++e) store_f(static_cast<T*>(a.out), row * d + 4 * col + e, st.o[e] * inv);
     }
@@ -298,8 +303,10 @@ __device__ __forceinline__ void split_bf16_body(const SplitArgs& a, int wg, int 
   Chunk<KC, VB> ca, cb;
   {
     // every load of the prologue, and the first chunk's, is issued before the first wait
-    const uint16_t* q = static_cast<const uint16_t*>(a.q) + ((int64_t)b * a.hq + (int64_t)h * g) * d;
-    const int nq = FOLD ? 0 : g * d / 8;            // <= 128 sixteen-byte pieces
+    // q rows are d wide for the fold; without it they are already r_K wide
+    // (a latent query, or a full-rank key list with r_K = d)
+    const uint16_t* q = static_cast<const uint16_t*>(a.q) + ((int64_t)b * a.hq + (int64_t)h * g) * (FOLD ? d : rk);
+    const int nq = FOLD ? 0 : g * rk / 8;           // <= 128 sixteen-byte pieces
     const u32x4 wq = tid < nq ? *reinterpret_cast<const u32x4*>(q + 8 * tid) : u32x4{0u, 0u, 0u, 0u};
     // the fold's row operand: lane (n16, grp) holds q[head n16][32 c + 8 grp .. + 7]
     u32x4 qa[4];
@@ -379,7 +386,7 @@ __device__ __forceinline__ void split_bf16_body(const SplitArgs& a, int wg, int 
           if (4 * grp + i < g && col < rk) s_qf[(4 * grp + i) * rk + col] = f[i] * a.qscale;
       }
     } else {
-      for (int i = tid; i < g * d; i += 256) s_qf[i] = s_q[i] * a.qscale;
+      for (int i = tid; i < g * rk; i += 256) s_qf[i] = s_q[i] * a.qscale;
     }
     __syncthreads();
   }
@@ -678,9 +685,10 @@ __device__ __forceinline__ void split_bf16_body(const SplitArgs& a, int wg, int 
         if (4 * grp + i < g) store_partial(po + ((row0 + 4 * grp + i) * a.n_parts + part) * d + dim, o[i]);
     }
   } else {
-    for (int i = tid; i < g * d; i += 256) {
-      const int j = i / d, dd = i - j * d;
-      store_partial(po + ((row0 + j) * a.n_parts + part) * d + dd, s_merged[j * 128 + dd]);
+    // no lift: the partial is the r_V-wide accumulator (d wide for a full-rank list)
+    for (int i = tid; i < g * rv; i += 256) {
+      const int j = i / rv, c = i - j * rv;
+      store_partial(po + ((row0 + j) * a.n_parts + part) * rv + c, s_merged[j * 128 + c]);
     }
   }
 }
@@ -699,6 +707,15 @@ void split_bf16_kernel(SplitArgs a) {
   __shared__ SplitSmem sm;
   split_bf16_body<KC, VB, true, kStages<KC, VB>, ENC>(a, blockIdx.x, blockIdx.x, sm,
                                                        a.k_new != nullptr && blockIdx.x == gridDim.x - 1);
+}
+
+// Latent queries and outputs (projections that absorb the bases): no fold,
+// no lift; q is [B, Hq, r_K] and each partial is r_V wide.
+template <int KC, int VB>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void split_bf16_latent_kernel(SplitArgs a) {
+  __shared__ SplitSmem sm;
+  split_bf16_body<KC, VB, false, kStages<KC, VB>>(a, blockIdx.x, blockIdx.x, sm);
 }
 
 // Hybrid cache in one launch: the gridDim.x workgroups of each (b, kv head)
@@ -757,7 +774,7 @@ __global__ __launch_bounds__(256) void split_f32_kernel(SplitArgs a) {
   const int rk = a.rk, rv = a.rv, d = a.d;
   const int64_t bh = (int64_t)b * a.hkv + h;
   const bool fold = a.basis_k != nullptr;
-  const int rq = fold ? rk : d;
+  const int qw = fold ? d : rk;   // q row width: d for the fold, else already r_K wide
 
   __shared__ float s_q[8 * 128];
   __shared__ float s_qf[8 * 128];
@@ -765,8 +782,8 @@ __global__ __launch_bounds__(256) void split_f32_kernel(SplitArgs a) {
   __shared__ float s_ml[kWaves][8][2];
   __shared__ __attribute__((aligned(16))) float s_acc[kWaves][16][128];   // rows 0..g-1 used
 
-  const float* q = static_cast<const float*>(a.q) + ((int64_t)b * a.hq + (int64_t)h * g) * d;
-  for (int i = tid; i < g * d; i += 256) s_q[i] = q[i];
+  const float* q = static_cast<const float*>(a.q) + ((int64_t)b * a.hq + (int64_t)h * g) * qw;
+  for (int i = tid; i < g * qw; i += 256) s_q[i] = q[i];
   __syncthreads();
   if (fold) {
     const float* bk = static_cast<const float*>(a.basis_k) + (int64_t)h * d * rk;
@@ -777,7 +794,7 @@ __global__ __launch_bounds__(256) void split_f32_kernel(SplitArgs a) {
       s_qf[i] = acc * a.qscale;
     }
   } else {
-    for (int i = tid; i < g * d; i += 256) s_qf[i] = s_q[i] * a.qscale;
+    for (int i = tid; i < g * rk; i += 256) s_qf[i] = s_q[i] * a.qscale;
   }
   __syncthreads();
 
@@ -815,7 +832,7 @@ __global__ __launch_bounds__(256) void split_f32_kernel(SplitArgs a) {
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
           if (j < g) {
-            const float* qq = s_qf + j * rq + k;
+            const float* qq = s_qf + j * rk + k;
             s[j] = fmaf(c4.x, qq[0], fmaf(c4.y, qq[1], fmaf(c4.z, qq[2], fmaf(c4.w, qq[3], s[j]))));
           }
         }
@@ -903,6 +920,30 @@ hipError_t launch_split_bf16(const SplitArgs& a, hipStream_t s) {
     LRKV_SPLIT_CASE(3, 5) LRKV_SPLIT_CASE(3, 6) LRKV_SPLIT_CASE(3, 7) LRKV_SPLIT_CASE(3, 8)
     LRKV_SPLIT_CASE(4, 1) LRKV_SPLIT_CASE(4, 2) LRKV_SPLIT_CASE(4, 3) LRKV_SPLIT_CASE(4, 4)
     LRKV_SPLIT_CASE(4, 5) LRKV_SPLIT_CASE(4, 6) LRKV_SPLIT_CASE(4, 7) LRKV_SPLIT_CASE(4, 8)
+    default:
+      return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+#define LRKV_LATENT_CASE(KC, VB)                                                         \
+  case (KC * 16 + VB):                                                                   \
+    hipLaunchKernelGGL((split_bf16_latent_kernel<KC, VB>), grid, dim3(256), 0, s, a);    \
+    break;
+
+hipError_t launch_split_bf16_latent(const SplitArgs& a, hipStream_t s) {
+  const dim3 grid(a.n_parts, a.hkv, a.batch);
+  const int kc = (a.rk + 31) / 32, vb = (a.rv + 15) / 16;
+  if (a.basis_k != nullptr || a.basis_v != nullptr || a.k_new != nullptr) return hipErrorInvalidValue;
+  switch (kc * 16 + vb) {
+    LRKV_LATENT_CASE(1, 1) LRKV_LATENT_CASE(1, 2) LRKV_LATENT_CASE(1, 3) LRKV_LATENT_CASE(1, 4)
+    LRKV_LATENT_CASE(1, 5) LRKV_LATENT_CASE(1, 6) LRKV_LATENT_CASE(1, 7) LRKV_LATENT_CASE(1, 8)
+    LRKV_LATENT_CASE(2, 1) LRKV_LATENT_CASE(2, 2) LRKV_LATENT_CASE(2, 3) LRKV_LATENT_CASE(2, 4)
+    LRKV_LATENT_CASE(2, 5) LRKV_LATENT_CASE(2, 6) LRKV_LATENT_CASE(2, 7) LRKV_LATENT_CASE(2, 8)
+    LRKV_LATENT_CASE(3, 1) LRKV_LATENT_CASE(3, 2) LRKV_LATENT_CASE(3, 3) LRKV_LATENT_CASE(3, 4)
+    LRKV_LATENT_CASE(3, 5) LRKV_LATENT_CASE(3, 6) LRKV_LATENT_CASE(3, 7) LRKV_LATENT_CASE(3, 8)
+    LRKV_LATENT_CASE(4, 1) LRKV_LATENT_CASE(4, 2) LRKV_LATENT_CASE(4, 3) LRKV_LATENT_CASE(4, 4)
+    LRKV_LATENT_CASE(4, 5) LRKV_LATENT_CASE(4, 6) LRKV_LATENT_CASE(4, 7) LRKV_LATENT_CASE(4, 8)
     default:
       return hipErrorInvalidValue;
   }

@@ -302,18 +302,21 @@ lrkv_status decode_partial(const void* q, const void* basis_k, const void* coeff
     sa.enc_k = enc_k;
     sa.append_row = n_ctx - 1;
   }
-  const hipError_t e = dtype == LRKV_BF16 ? launch_split_bf16(sa, stream) : launch_split_f32(sa, stream);
+  // no basis_k: latent queries (absorbed projections), no fold and no lift
+  const hipError_t e = dtype != LRKV_BF16 ? launch_split_f32(sa, stream)
+                                          : (basis_k ? launch_split_bf16(sa, stream) : launch_split_bf16_latent(sa, stream));
   return e == hipSuccess ? LRKV_OK : device_fail(fn, e);
 }
 
+// width: elements per output row (head_dim, or rank_v for latent outputs)
 lrkv_status decode_merge(void* out, float* lse, const lrkv_dims* dims, lrkv_dtype dtype, void* workspace,
-                         const DecodeLayout& L, hipStream_t stream, const char* fn) {
+                         const DecodeLayout& L, hipStream_t stream, const char* fn, int width = 0) {
   char* ws = static_cast<char*>(workspace);
   MergeArgs ma{};
   ma.part_o = reinterpret_cast<const float*>(ws + L.o);
   ma.part_ml = reinterpret_cast<const float*>(ws + L.ml);
   ma.n_parts = L.parts;
-  ma.d = dims->head_dim; ma.g = dims->n_q_heads / dims->n_kv_heads; ma.hq = dims->n_q_heads;
+  ma.d = width > 0 ? width : dims->head_dim; ma.g = dims->n_q_heads / dims->n_kv_heads; ma.hq = dims->n_q_heads;
   ma.hkv = dims->n_kv_heads; ma.batch = dims->batch;
   ma.out = out; ma.lse = lse;
   const hipError_t e = launch_merge(ma, dtype == LRKV_BF16, stream);
@@ -372,6 +375,25 @@ lrkv_status lrkv_decode_attn_merge(void* out, float* lse, const lrkv_dims* dims,
   LRKV_CHECK_PTR(out, fn);
   if (lse && !aligned16(lse)) return fail(LRKV_ERR_INVALID_ARGUMENT, "%s: lse is not 16-byte aligned", fn);
   return decode_merge(out, lse, dims, dtype, workspace, L, stream, fn);
+}
+
+lrkv_status lrkv_decode_attn_latent(const void* q_lat, const void* coeff_k, const void* coeff_v, void* out_lat,
+                                    float* lse, const lrkv_dims* dims, int64_t n_ctx, float scale, lrkv_dtype dtype,
+                                    void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  const char* fn = "lrkv_decode_attn_latent";
+  DecodeLayout L;
+  lrkv_status st = check_decode_common(dims, n_ctx, dtype, workspace, workspace_bytes, fn, &L);
+  if (st != LRKV_OK) return st;
+  if (!std::isfinite(scale)) return fail(LRKV_ERR_INVALID_ARGUMENT, "%s: scale is not finite", fn);
+  LRKV_CHECK_PTR(q_lat, fn);
+  LRKV_CHECK_PTR(coeff_k, fn);
+  LRKV_CHECK_PTR(coeff_v, fn);
+  LRKV_CHECK_PTR(out_lat, fn);
+  if (lse && !aligned16(lse)) return fail(LRKV_ERR_INVALID_ARGUMENT, "%s: lse is not 16-byte aligned", fn);
+  // the plain decode's workspace holds these partials: rank_v <= head_dim floats each
+  st = decode_partial(q_lat, nullptr, coeff_k, nullptr, coeff_v, dims, n_ctx, scale, dtype, workspace, L, stream, fn);
+  if (st != LRKV_OK) return st;
+  return decode_merge(out_lat, lse, dims, dtype, workspace, L, stream, fn, dims->rank_v);
 }
 
 size_t lrkv_decode_step_workspace_bytes(const lrkv_dims* dims, int64_t n_ctx) {

@@ -16,11 +16,12 @@ constexpr int kSplitsPerPart = 4;
 constexpr int kMaxSplits = 1 << 16;
 
 struct SplitArgs {
-  const void* q;         // [B, Hq, d]
-  const void* basis_k;   // [Hkv, d, rk] (nullptr: keys are full rank, no fold)
+  const void* q;         // [B, Hq, d], or [B, Hq, rk] without a fold
+  const void* basis_k;   // [Hkv, d, rk] (nullptr: no fold; q is already rk wide: a latent
+                         // query, or a full-rank key list with rk = d)
   const void* ck;        // key rows [B, Hkv, cap, rk]
   const void* cv;        // value octets [B, Hkv, cap/8, rv, 8]
-  const void* basis_v;   // [Hkv, d, rv] (nullptr: values are full rank, no lift)
+  const void* basis_v;   // [Hkv, d, rv] (nullptr: no lift; partials are rv wide)
   int64_t cap;
   int rk, rv, d, g, hq, hkv, batch;
   int64_t n_static;      // context length when n_dev is null
@@ -29,7 +30,7 @@ struct SplitArgs {
   int n_splits;
   int n_parts;           // partials per (b, q head): one per attention workgroup
   float qscale;          // softmax scale * log2(e)
-  float* part_o;         // [B, Hq, n_parts, d]  unnormalised outputs
+  float* part_o;         // [B, Hq, n_parts, d (rv without a lift)]  unnormalised outputs
   float* part_ml;        // [B, Hq, n_parts, 2]  running max (log2 units), softmax sum
   // Append (decode step): when k_new is non-null, the last workgroup of each
   // (b, kv head) compresses the new token's key and value, stores them at
@@ -72,6 +73,8 @@ hipError_t launch_split_bf16(const SplitArgs& a, hipStream_t s);
 hipError_t launch_split_bf16_hybrid(const SplitArgs& lr, const SplitArgs& side, int wgs_per_unit, hipStream_t s);
 hipError_t launch_compress_kv_small_bf16(const CompressKvArgs& a, hipStream_t s);
 hipError_t launch_split_f32(const SplitArgs& a, hipStream_t s);
+// Latent queries (basis_k and basis_v null, q [B, Hq, rk], partials rv wide).
+hipError_t launch_split_bf16_latent(const SplitArgs& a, hipStream_t s);
 hipError_t launch_merge(const MergeArgs& a, bool bf16, hipStream_t s);
 hipError_t launch_compress_bf16(const CompressArgs& a, hipStream_t s);
 hipError_t launch_compress_f32(const CompressArgs& a, hipStream_t s);

@@ -183,6 +183,28 @@ lrkv_status lrkv_decode_attn_merge(void* out, float* lse, const lrkv_dims* dims,
                                    hipStream_t stream);
 
 /*
+ * Decode attention with the bases absorbed into the model's projections.
+ * The NovaKV delta ships modified query and output projections together
+ * with the K and V factors ("Llama-3.1-NovaKV" model card, introduction);
+ * with W_q B_K and B_V^T W_o formed offline, a query arrives as
+ * q' = q B_K and the layer needs only the latent output
+ *   s_t = q' . C_K[t] * scale,  p = softmax(s),  out_lat = sum_t p_t C_V[t]
+ * (lse as lrkv_decode_attn).  No basis is read; the query fold and the
+ * output lift of lrkv_decode_attn are left to the absorbed projections.
+ *   q_lat    [B, Hq, r_K] latent queries (storage dtype)
+ *   coeff_k  key row layout [B, Hkv, capacity, r_K]
+ *   coeff_v  value octet layout [B, Hkv, capacity/8, r_V, 8]
+ *   out_lat  [B, Hq, r_V] (storage dtype);  lse [B, Hq] float32, or NULL
+ *   scale    softmax scale; 0 selects 1/sqrt(dims->head_dim), the model's
+ *            head dimension (dims->head_dim also sets the supported shapes)
+ *   workspace at least lrkv_decode_workspace_bytes(dims, n_ctx, 0) bytes
+ * Requires 1 <= n_ctx <= capacity.
+ */
+lrkv_status lrkv_decode_attn_latent(const void* q_lat, const void* coeff_k, const void* coeff_v, void* out_lat,
+                                    float* lse, const lrkv_dims* dims, int64_t n_ctx, float scale, lrkv_dtype dtype,
+                                    void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
  * Decode step: append the token of this step, then attend.  Equivalent to
  * lrkv_compress_kv of one token at row n_ctx - 1 followed by
  * lrkv_decode_attn over [0, n_ctx) (the "Llama-3.1-NovaKV" model card,

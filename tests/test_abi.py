@@ -30,7 +30,7 @@ def test_header_declares_the_entry_points():
               "lrkv_decode_workspace_bytes", "lrkv_status_string", "lrkv_last_error",
               "lrkv_decode_attn_partial", "lrkv_decode_attn_merge", "lrkv_compress_hybrid_workspace_bytes",
               "lrkv_decode_step", "lrkv_decode_step_workspace_bytes", "lrkv_decode_step_partial",
-              "lrkv_decode_step_merge"):
+              "lrkv_decode_step_merge", "lrkv_decode_attn_latent"):
         assert n in names
 
 
@@ -161,3 +161,15 @@ def test_decode_step_validation():
     assert f(*args(enc=P, ws_bytes=16)) == 3
     g = lib.lrkv_decode_step_partial
     assert g(P, P, P, P, P, P, P, MIS, ctypes.byref(d), 100, 0.0, 1, P, 1 << 30, None) == 1
+
+
+def test_latent_decode_validation():
+    lrkv, lib = _lib()
+    f = lib.lrkv_decode_attn_latent
+    d = _dims(lrkv)
+    # q_lat, coeff_k, coeff_v, out_lat, lse, dims, n_ctx, scale, dtype, ws, bytes, stream
+    assert f(None, P, P, P, None, ctypes.byref(d), 100, 0.0, 1, P, 1 << 30, None) == 1
+    assert f(P, P, P, MIS, None, ctypes.byref(d), 100, 0.0, 1, P, 1 << 30, None) == 1
+    assert f(P, P, P, P, None, ctypes.byref(d), 300, 0.0, 1, P, 1 << 30, None) == 1
+    assert f(P, P, P, P, None, ctypes.byref(d), 100, 0.0, 1, P, 16, None) == 3
+    assert f(P, P, P, P, None, ctypes.byref(_dims(lrkv, rank_v=12)), 100, 0.0, 1, P, 1 << 30, None) == 2

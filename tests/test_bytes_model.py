@@ -54,3 +54,12 @@ def test_hybrid_side_tokens_in_bytes():
     full = bm.decode_bytes(1, 32, 8, 128, 64, 64, 131072)
     hyb = bm.decode_bytes(1, 32, 8, 128, 64, 64, 131072, side_tokens=6554)
     assert hyb - full == 8 * 6554 * (2 * 128 * 2 + 4) - 2 * 8 * 6554 * 128
+
+
+def test_latent_decode_bytes_skip_the_bases():
+    """Absorbed projections: the cache rows, r_K-wide queries and r_V-wide outputs; no basis."""
+    lat = bm.latent_decode_bytes(16, 32, 8, 48, 112, 32768)
+    assert lat == 2 * 16 * 8 * 32768 * 160 + 2 * 16 * 32 * (48 + 112)
+    # against the full decode (bases read, d-wide query in and output out)
+    full = bm.decode_bytes(16, 32, 8, 128, 48, 112, 32768)
+    assert full - lat == 2 * 8 * 128 * 160 + 2 * 2 * 16 * 32 * 128 - 2 * 16 * 32 * 160
