@@ -1,0 +1,105 @@
+"""Parity at the benchmark's full size, in the benchmark's launch configuration.
+
+The batched 32K workload (batch 16, 32 query / 8 kv heads, d 128, context
+32768, ranks (32, 96) on even and (48, 112) on odd layers): one layer of each
+parity goes through exactly what a bench step runs (lrkv_compress_kv of the
+4096-token prefill chunk, then lrkv_decode_step_partial + _merge with the
+appended token), and sampled outputs are checked against the oracle computed
+one (batch, q head) at a time.  The sampled (batch, kv head) caches are also
+compared row by row: the drawn rows untouched, the prefill rows and the
+appended row within the compress gate.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import lrkv_synth as synth
+from oracle import lrkv_oracle as O
+from tests.gpu_helpers import DEV, bits, check_decode, to_dev, to_f64
+from tests.test_gpu_parity_small import check_compress
+
+pytestmark = pytest.mark.gpu
+
+lrkv = pytest.importorskip("decode_attention_lrkv_amd")
+
+W = synth.BATCHED_32K
+# (batch, q head) rows checked per layer: corners and a spread of the rest
+ROWS = [(0, 0), (0, 31), (3, 9), (7, 14), (8, 17), (11, 22), (15, 0), (15, 31)]
+
+
+@pytest.mark.parametrize("layer", [0, 1])
+def test_bench_layer_step_full_size(layer):
+    B, Hq, H, d = W.batch, W.n_q_heads, W.n_kv_heads, W.head_dim
+    N, P = W.n_ctx[0], W.prefill
+    p0 = N - 1 - P
+    rk, rv = W.ranks(layer)
+    g = W.group
+    print(f"[full-size] layer {layer}: B {B}, N {N}, ranks {rk}/{rv}, prefill rows [{p0}, {N - 1})", flush=True)
+
+    ck_rows = synth.stack_heads(W, lambda b, h: synth.direct_coeffs(W, layer, "k", b, h, p0, exact=False))
+    cv_rows = synth.stack_heads(W, lambda b, h: synth.direct_coeffs(W, layer, "v", b, h, p0, exact=False))
+    xk = synth.tokens_major(synth.stack_heads(W, lambda b, h: synth.full_tokens(W, layer, "k", b, h, P,
+                                                                               synth.PART_PREFILL)))
+    xv = synth.tokens_major(synth.stack_heads(W, lambda b, h: synth.full_tokens(W, layer, "v", b, h, P,
+                                                                               synth.PART_PREFILL)))
+    ak = synth.tokens_major(synth.stack_heads(W, lambda b, h: synth.full_tokens(W, layer, "k", b, h, 1,
+                                                                               synth.PART_APPEND)))
+    av = synth.tokens_major(synth.stack_heads(W, lambda b, h: synth.full_tokens(W, layer, "v", b, h, 1,
+                                                                               synth.PART_APPEND)))
+    bk, bv, q = synth.basis(W, layer, "k"), synth.basis(W, layer, "v"), synth.query(W, layer)
+
+    kc = np.zeros((B, H, N, rk), np.uint16)
+    vc = np.zeros((B, H, N, rv), np.uint16)
+    kc[:, :, :p0] = ck_rows.store
+    vc[:, :, :p0] = cv_rows.store
+    ckd, cvd = to_dev(kc, "bf16"), to_dev(synth.to_value_octets(vc), "bf16")
+    del vc
+    bkd, bvd, qd = to_dev(bk, "bf16"), to_dev(bv, "bf16"), to_dev(q, "bf16")
+    # the bench's launch sequence: prefill compress, then the two phases of the decode step
+    lrkv.compress_kv(to_dev(xk, "bf16"), to_dev(xv, "bf16"), bkd, bvd, ckd, cvd, p0)
+    ws = torch.zeros(lrkv.decode_step_workspace_bytes(B, Hq, H, d, rk, rv, N, N), dtype=torch.uint8, device=DEV)
+    out = torch.empty((B, Hq, d), dtype=torch.bfloat16, device=DEV)
+    lse = torch.empty((B, Hq), dtype=torch.float32, device=DEV)
+    lrkv.decode_step_partial(qd, to_dev(ak, "bf16"), to_dev(av, "bf16"), bkd, ckd, bvd, cvd, N, ws)
+    lrkv.decode_step_merge(out, lse, N, ws, H, rk, rv, N)
+    torch.cuda.synchronize()
+    ck_gpu = bits(ckd)
+    cv_gpu = synth.from_value_octets(bits(cvd))
+    o_gpu, lse_gpu = to_f64(out), to_f64(lse)
+    del ckd, cvd, ws
+
+    # oracle, one (batch, q head) at a time, on the cache it builds itself:
+    # drawn rows, its own rounded compress of the prefill chunk and of the new token
+    units = sorted({(b, hq // g) for b, hq in ROWS})
+    cks, cvs = {}, {}
+    for b, h in units:
+        pk = O.round_storage(O.compress(xk.exact[b:b + 1, :, h:h + 1], bk.exact[h:h + 1]), "bf16")[0, 0]
+        pv = O.round_storage(O.compress(xv.exact[b:b + 1, :, h:h + 1], bv.exact[h:h + 1]), "bf16")[0, 0]
+        nk = O.round_storage(O.compress(ak.exact[b:b + 1, :, h:h + 1], bk.exact[h:h + 1]), "bf16")[0, 0]
+        nv = O.round_storage(O.compress(av.exact[b:b + 1, :, h:h + 1], bv.exact[h:h + 1]), "bf16")[0, 0]
+        drawn_k = synth.direct_coeffs(W, layer, "k", b, h, p0).exact
+        drawn_v = synth.direct_coeffs(W, layer, "v", b, h, p0).exact
+        cks[(b, h)] = np.concatenate([drawn_k, pk, nk])
+        cvs[(b, h)] = np.concatenate([drawn_v, pv, nv])
+        # the cache rows of this unit on the GPU
+        assert np.array_equal(ck_gpu[b, h, :p0], kc[b, h, :p0]), f"drawn key rows changed at {(b, h)}"
+        assert np.array_equal(cv_gpu[b, h, :p0], cv_rows.store[b, h]), f"drawn value rows changed at {(b, h)}"
+        gk = synth.bf16_bits_to_f64(ck_gpu[b, h, p0:])[None, None]
+        gv = synth.bf16_bits_to_f64(cv_gpu[b, h, p0:])[None, None]
+        xk_u = np.concatenate([xk.exact[b:b + 1, :, h:h + 1], ak.exact[b:b + 1, :, h:h + 1]], axis=1)
+        xv_u = np.concatenate([xv.exact[b:b + 1, :, h:h + 1], av.exact[b:b + 1, :, h:h + 1]], axis=1)
+        check_compress(gk, O.compress(xk_u, bk.exact[h:h + 1]), xk_u, bk.exact[h:h + 1], "bf16", f"K rows {(b, h)}")
+        check_compress(gv, O.compress(xv_u, bv.exact[h:h + 1]), xv_u, bv.exact[h:h + 1], "bf16", f"V rows {(b, h)}")
+    ref = O.decode_rows(q.exact, bk.exact, cks, bv.exact, cvs, N, ROWS)
+    o_ref = np.stack([ref[r][0] for r in ROWS])
+    lse_ref = np.array([ref[r][1] for r in ROWS])
+    o_s = np.stack([o_gpu[b, hq] for b, hq in ROWS])
+    lse_s = np.array([lse_gpu[b, hq] for b, hq in ROWS])
+    worst = check_decode(o_s, lse_s, o_ref, lse_ref, "bf16", f"full-size layer {layer}")
+    print(f"[full-size] layer {layer}: worst sampled row error {worst:.3e} (gate 2e-2)", flush=True)
+    # every output row is finite, and no row is the all-zero output of a skipped unit
+    assert np.all(np.isfinite(o_gpu)) and np.all(np.isfinite(lse_gpu))
+    assert np.all(np.abs(o_gpu).max(axis=-1) > 0)
+    assert math.isfinite(worst)
