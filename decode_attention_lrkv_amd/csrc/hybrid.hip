@@ -488,37 +488,65 @@ void hybrid_write_kernel(HybridArgs a) {
          std::integral_constant<int, D>{});
 }
 
-// Exclusive scan of the per-sub-tile counts of one (b, kv head); advances the counters.
+// Exclusive scan of the per-sub-tile counts of one (b, kv head); advances the
+// counters.  Rounds of 8192 counts: wave w holds counts [w * 2048, + 2048) of
+// the round in registers (32 per lane, loaded coalesced, all in flight at
+// once), the four wave totals give each wave its base, and each wave then
+// sweeps its counts 64 at a time with a lane scan, writing the (low-rank row,
+// side row) pairs coalesced.  Counts past n_tiles read zero and their offsets
+// are dropped (buffer bounds).
 __global__ __launch_bounds__(256) void hybrid_scan_kernel(HybridArgs a) {
-  const int tid = threadIdx.x;
+  constexpr int kPer = 32;                       // counts per lane per round
+  constexpr int kWaveSpan = 64 * kPer;
+  constexpr int kRound = kWavesH * kWaveSpan;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int64_t bh = (int64_t)blockIdx.y * a.hkv + blockIdx.x;
   const int n = a.n_tiles;
-  const int seg = (n + 255) / 256;
-  const int j0 = tid * seg;
-  const int j1 = j0 + seg < n ? j0 + seg : n;
-  const int32_t* cnt = a.ws_counts + bh * n;
+  const __amdgpu_buffer_rsrc_t rs_cnt = make_rsrc(a.ws_counts + bh * n, (uint32_t)n * 4u);
+  const __amdgpu_buffer_rsrc_t rs_off = make_rsrc(a.ws_offsets + bh * n * 2, (uint32_t)n * 8u);
   const int64_t lr_base = a.n_lr[bh];
   const int64_t side_base = a.n_side[bh];
+  __shared__ int32_t s_tot[kWavesH];
 
-  __shared__ int64_t s_scan[256];
-  int64_t local = 0;
-  for (int j = j0; j < j1; ++j) local += cnt[j];
-  s_scan[tid] = local;
-  __syncthreads();
-  for (int o = 1; o < 256; o <<= 1) {
-    const int64_t v = tid >= o ? s_scan[tid - o] : 0;
+  int64_t carry = 0;                             // flagged tokens before this round
+  for (int r0 = 0; r0 < n; r0 += kRound) {
+    const int w0 = r0 + wave * kWaveSpan;
+    uint32_t c[kPer];
+#pragma unroll
+    for (int s = 0; s < kPer; ++s) c[s] = buf_load4(rs_cnt, (uint32_t)(w0 + 64 * s + lane) * 4u);
+    int32_t sum = 0;
+#pragma unroll
+    for (int s = 0; s < kPer; ++s) sum += (int32_t)c[s];
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) sum += __shfl_xor(sum, o);
+    if (lane == 0) s_tot[wave] = sum;
     __syncthreads();
-    s_scan[tid] += v;
-    __syncthreads();
+    int64_t base = carry, round_total = 0;
+#pragma unroll
+    for (int w = 0; w < kWavesH; ++w) {
+      if (w < wave) base += s_tot[w];
+      round_total += s_tot[w];
+    }
+    __syncthreads();                             // s_tot is rewritten next round
+#pragma unroll
+    for (int s = 0; s < kPer; ++s) {
+      const int32_t x = (int32_t)c[s];
+      int32_t incl = x;
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) {
+        const int32_t y = __shfl_up(incl, o);
+        if (lane >= o) incl += y;
+      }
+      const int64_t excl = base + incl - x;      // flagged tokens before sub-tile j
+      const int64_t j = w0 + 64 * s + lane;
+      buf_store8(rs_off, (uint32_t)j * 8u,
+                 u32x2{(uint32_t)(int32_t)(lr_base + j * kHybridTile - excl), (uint32_t)(int32_t)(side_base + excl)});
+      base += __shfl(incl, 63);
+    }
+    carry += round_total;
   }
-  int64_t run = s_scan[tid] - local;   // flagged tokens before this thread's first sub-tile
-  for (int j = j0; j < j1; ++j) {
-    a.ws_offsets[(bh * n + j) * 2 + 0] = (int32_t)(lr_base + (int64_t)j * kHybridTile - run);
-    a.ws_offsets[(bh * n + j) * 2 + 1] = (int32_t)(side_base + run);
-    run += cnt[j];
-  }
-  if (tid == 255) {
-    const int64_t flagged = s_scan[255];
+  if (tid == 0) {
+    const int64_t flagged = carry;
     int64_t new_side = side_base + flagged;
     int64_t new_lr = lr_base + (a.n_tokens - flagged);
     bool over = false;

@@ -53,7 +53,8 @@ def _valid_parts(snap, b, h):
         idx=snap["side_idx"][b, h, :n_side])
 
 
-@pytest.mark.parametrize("n", [8192, 131072])
+# 150000 tokens are 9375 sub-tiles: the counter scan runs two rounds of 8192
+@pytest.mark.parametrize("n", [8192, 131072, 150000])
 def test_hybrid_selection_compaction_and_decode(n):
     w, inj, k, v, bk, bv, q = _inputs(n)
     H, d = w.n_kv_heads, w.head_dim
