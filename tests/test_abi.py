@@ -4,6 +4,7 @@ import ctypes
 import os
 import re
 import subprocess
+import sys
 
 import pytest
 
@@ -173,3 +174,24 @@ def test_latent_decode_validation():
     assert f(P, P, P, P, None, ctypes.byref(d), 300, 0.0, 1, P, 1 << 30, None) == 1
     assert f(P, P, P, P, None, ctypes.byref(d), 100, 0.0, 1, P, 16, None) == 3
     assert f(P, P, P, P, None, ctypes.byref(_dims(lrkv, rank_v=12)), 100, 0.0, 1, P, 1 << 30, None) == 2
+
+
+def test_missing_library_fails_loudly():
+    """Without the built library every entry point raises; nothing falls back to another path."""
+    code = (
+        "import sys, torch\n"
+        "import decode_attention_lrkv_amd as lrkv\n"
+        "lrkv.LIB_PATH = '/nonexistent/liblrkv.so'\n"
+        "for call in (lambda: lrkv.library(),\n"
+        "             lambda: lrkv.decode_workspace_bytes(1, 8, 2, 128, 32, 64, 256, 100),\n"
+        "             lambda: lrkv.decode_attn_latent(torch.zeros(1, 8, 32), torch.zeros(1, 2, 256, 32),\n"
+        "                                             torch.zeros(1, 2, 32, 64, 8), 100, 128)):\n"
+        "    try:\n"
+        "        call()\n"
+        "    except lrkv.LrkvError as e:\n"
+        "        assert 'missing' in str(e), e\n"
+        "    else:\n"
+        "        sys.exit('no error')\n"
+        "print('ok')\n")
+    r = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, cwd=ROOT)
+    assert r.returncode == 0 and r.stdout.strip() == "ok", r.stdout + r.stderr
