@@ -489,12 +489,12 @@ void hybrid_write_kernel(HybridArgs a) {
 }
 
 // Exclusive scan of the per-sub-tile counts of one (b, kv head); advances the
-// counters.  Rounds of 8192 counts: wave w holds counts [w * 2048, + 2048) of
-// the round in registers (32 per lane, loaded coalesced, all in flight at
-// once), the four wave totals give each wave its base, and each wave then
-// sweeps its counts 64 at a time with a lane scan, writing the (low-rank row,
-// side row) pairs coalesced.  Counts past n_tiles read zero and their offsets
-// are dropped (buffer bounds).
+// counters.  Rounds of 8192 counts: lane l of wave w holds the 32 consecutive
+// counts [w * 2048 + 32 l, + 32) of the round in registers (all loads in
+// flight at once), takes their running sum, and one scan over the lanes and
+// one over the four wave totals give each lane its base; the lane then writes
+// its 32 (low-rank row, side row) pairs.  Counts past n_tiles read zero and
+// their offsets are dropped (buffer bounds).
 __global__ __launch_bounds__(256) void hybrid_scan_kernel(HybridArgs a) {
   constexpr int kPer = 32;                       // counts per lane per round
   constexpr int kWaveSpan = 64 * kPer;
@@ -510,18 +510,22 @@ __global__ __launch_bounds__(256) void hybrid_scan_kernel(HybridArgs a) {
 
   int64_t carry = 0;                             // flagged tokens before this round
   for (int r0 = 0; r0 < n; r0 += kRound) {
-    const int w0 = r0 + wave * kWaveSpan;
+    const int j0 = r0 + wave * kWaveSpan + kPer * lane;   // this lane's first sub-tile
     uint32_t c[kPer];
 #pragma unroll
-    for (int s = 0; s < kPer; ++s) c[s] = buf_load4(rs_cnt, (uint32_t)(w0 + 64 * s + lane) * 4u);
-    int32_t sum = 0;
+    for (int k = 0; k < kPer; ++k) c[k] = buf_load4(rs_cnt, (uint32_t)(j0 + k) * 4u);
+    int32_t lane_sum = 0;
 #pragma unroll
-    for (int s = 0; s < kPer; ++s) sum += (int32_t)c[s];
+    for (int k = 0; k < kPer; ++k) lane_sum += (int32_t)c[k];
+    int32_t incl = lane_sum;                     // inclusive scan over the lanes
 #pragma unroll
-    for (int o = 1; o < 64; o <<= 1) sum += __shfl_xor(sum, o);
-    if (lane == 0) s_tot[wave] = sum;
+    for (int o = 1; o < 64; o <<= 1) {
+      const int32_t y = __shfl_up(incl, o);
+      if (lane >= o) incl += y;
+    }
+    if (lane == 63) s_tot[wave] = incl;
     __syncthreads();
-    int64_t base = carry, round_total = 0;
+    int64_t base = carry + (incl - lane_sum), round_total = 0;
 #pragma unroll
     for (int w = 0; w < kWavesH; ++w) {
       if (w < wave) base += s_tot[w];
@@ -529,19 +533,11 @@ __global__ __launch_bounds__(256) void hybrid_scan_kernel(HybridArgs a) {
     }
     __syncthreads();                             // s_tot is rewritten next round
 #pragma unroll
-    for (int s = 0; s < kPer; ++s) {
-      const int32_t x = (int32_t)c[s];
-      int32_t incl = x;
-#pragma unroll
-      for (int o = 1; o < 64; o <<= 1) {
-        const int32_t y = __shfl_up(incl, o);
-        if (lane >= o) incl += y;
-      }
-      const int64_t excl = base + incl - x;      // flagged tokens before sub-tile j
-      const int64_t j = w0 + 64 * s + lane;
+    for (int k = 0; k < kPer; ++k) {
+      const int64_t j = j0 + k;                  // base = flagged tokens before sub-tile j
       buf_store8(rs_off, (uint32_t)j * 8u,
-                 u32x2{(uint32_t)(int32_t)(lr_base + j * kHybridTile - excl), (uint32_t)(int32_t)(side_base + excl)});
-      base += __shfl(incl, 63);
+                 u32x2{(uint32_t)(int32_t)(lr_base + j * kHybridTile - base), (uint32_t)(int32_t)(side_base + base)});
+      base += (int32_t)c[k];
     }
     carry += round_total;
   }
