@@ -468,13 +468,22 @@ __device__ __forceinline__ void split_bf16_body(const SplitArgs& a, int wg, int 
     if (col < r) {
       float acc = 0.f;
       if (kind_v) {
-        for (int e = 0; e < d; ++e) acc = fmaf(s_q[128 + e], bf16_to_f32(sm.bv[e * (rv + 8) + col]), acc);
+        // four partial sums: the token's compress is on this workgroup's critical path
+        float p4[4] = {0.f, 0.f, 0.f, 0.f};
+        for (int e = 0; e < d; e += 4)
+#pragma unroll
+          for (int u = 0; u < 4; ++u) p4[u] = fmaf(s_q[128 + e + u], bf16_to_f32(sm.bv[(e + u) * (rv + 8) + col]), p4[u]);
+        acc = (p4[0] + p4[1]) + (p4[2] + p4[3]);
       } else if (ENC) {
         const float* s_part = reinterpret_cast<const float*>(sm.raw);
         const int n_rg = 256 / (rk >> 3);
         for (int i = 0; i < n_rg; ++i) acc += s_part[i * rk + col];
       } else {
-        for (int e = 0; e < d; ++e) acc = fmaf(s_q[e], bf16_to_f32(s_bk[e * rk + col]), acc);
+        float p4[4] = {0.f, 0.f, 0.f, 0.f};
+        for (int e = 0; e < d; e += 4)
+#pragma unroll
+          for (int u = 0; u < 4; ++u) p4[u] = fmaf(s_q[e + u], bf16_to_f32(s_bk[(e + u) * rk + col]), p4[u]);
+        acc = (p4[0] + p4[1]) + (p4[2] + p4[3]);
       }
       const uint16_t c16 = f32_to_bf16(acc);
       s_c[(kind_v ? 128 : 0) + col] = bf16_to_f32(c16);
@@ -486,14 +495,24 @@ __device__ __forceinline__ void split_bf16_body(const SplitArgs& a, int wg, int 
     __syncthreads();
     const int64_t row0 = (int64_t)b * a.hq + (int64_t)h * g;
     if (tid < g) {
-      float s = 0.f;
-      for (int k = 0; k < rk; ++k) s = fmaf(s_qf[tid * rk + k], s_c[k], s);
-      store_partial(a.part_ml + ((row0 + tid) * a.n_parts + pa) * 2 + 0, s);
-      store_partial(a.part_ml + ((row0 + tid) * a.n_parts + pa) * 2 + 1, 1.f);
+      float p4[4] = {0.f, 0.f, 0.f, 0.f};
+      for (int k = 0; k < rk; k += 4)   // rk is a multiple of 8
+#pragma unroll
+        for (int u = 0; u < 4; ++u) p4[u] = fmaf(s_qf[tid * rk + k + u], s_c[k + u], p4[u]);
+      const float s = (p4[0] + p4[1]) + (p4[2] + p4[3]);
+      if (a.out) {
+        s_q[512 + tid] = s;   // folded into this workgroup's merge in the epilogue (c_V stays in s_c)
+      } else {
+        store_partial(a.part_ml + ((row0 + tid) * a.n_parts + pa) * 2 + 0, s);
+        store_partial(a.part_ml + ((row0 + tid) * a.n_parts + pa) * 2 + 1, 1.f);
+      }
     }
-    if (tid < d) {
-      float o = 0.f;
-      for (int c = 0; c < rv; ++c) o = fmaf(bf16_to_f32(sm.bv[tid * (rv + 8) + c]), s_c[128 + c], o);
+    if (tid < d && !a.out) {
+      float p4[4] = {0.f, 0.f, 0.f, 0.f};
+      for (int c = 0; c < rv; c += 4)   // rv is a multiple of 8
+#pragma unroll
+        for (int u = 0; u < 4; ++u) p4[u] = fmaf(bf16_to_f32(sm.bv[tid * (rv + 8) + c + u]), s_c[128 + c + u], p4[u]);
+      const float o = (p4[0] + p4[1]) + (p4[2] + p4[3]);
       for (int j = 0; j < g; ++j) store_partial(a.part_o + ((row0 + j) * a.n_parts + pa) * d + tid, o);
     }
   }
@@ -622,14 +641,21 @@ __device__ __forceinline__ void split_bf16_body(const SplitArgs& a, int wg, int 
     s_ml[wave][lane][1] = l_tot;
   }
   __syncthreads();
-  // 2. the four waves merged: M = max_w m_w, acc = sum_w 2^(m_w - M) acc_w, likewise the sum
+  // 2. the four waves merged: M = max_w m_w, acc = sum_w 2^(m_w - M) acc_w,
+  //    likewise the sum.  With final outputs, the appended token of this
+  //    workgroup (score in s_q[512 + j], latent value c_V in s_c) is one more
+  //    term, and the sum is inverted for the lift instead of being stored.
   float* s_merged = s_qf;   // the query operand was read before the main loop
+  const bool fin = a.out != nullptr;
+  const bool tok = fin && append;
+  const float* s_tok_c = s_q + 256 + 128;
+  float* s_inv = s_q + 520;
   for (int i = tid; i < g * rv; i += 256) {
     const int j = i / rv, c = i - j * rv;
-    float M = -INFINITY;
+    float M = tok ? s_q[512 + j] : -INFINITY;
 #pragma unroll
     for (int w = 0; w < kWaves; ++w) M = fmaxf(M, s_ml[w][j][0]);
-    float o = 0.f;
+    float o = tok ? exp2_fast(s_q[512 + j] - M) * s_tok_c[c] : 0.f;
 #pragma unroll
     for (int w = 0; w < kWaves; ++w) {
       const float m = s_ml[w][j][0];
@@ -639,17 +665,22 @@ __device__ __forceinline__ void split_bf16_body(const SplitArgs& a, int wg, int 
   }
   const int64_t row0 = (int64_t)b * a.hq + (int64_t)h * g;
   if (tid < g) {
-    float M = -INFINITY;
+    float M = tok ? s_q[512 + tid] : -INFINITY;
 #pragma unroll
     for (int w = 0; w < kWaves; ++w) M = fmaxf(M, s_ml[w][tid][0]);
-    float L = 0.f;
+    float L = tok ? exp2_fast(s_q[512 + tid] - M) : 0.f;
 #pragma unroll
     for (int w = 0; w < kWaves; ++w) {
       const float m = s_ml[w][tid][0];
       L = fmaf(m == -INFINITY ? 0.f : exp2_fast(m - M), s_ml[w][tid][1], L);
     }
-    store_partial(a.part_ml + ((row0 + tid) * a.n_parts + part) * 2 + 0, M);
-    store_partial(a.part_ml + ((row0 + tid) * a.n_parts + part) * 2 + 1, L);
+    if (fin) {
+      s_inv[tid] = L > 0.f ? 1.f / L : 0.f;
+      if (a.lse) a.lse[row0 + tid] = L > 0.f ? (M + __log2f(L)) * kLn2 : -INFINITY;
+    } else {
+      store_partial(a.part_ml + ((row0 + tid) * a.n_parts + part) * 2 + 0, M);
+      store_partial(a.part_ml + ((row0 + tid) * a.n_parts + part) * 2 + 1, L);
+    }
   }
   __syncthreads();
   // 3. lift o = acc B_V^T on the matrix cores: wave w takes the 16-dim blocks
@@ -681,8 +712,13 @@ __device__ __forceinline__ void split_bf16_body(const SplitArgs& a, int wg, int 
       }
       // lane (n16, grp) register i: head 4 grp + i, dim
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-        if (4 * grp + i < g) store_partial(po + ((row0 + 4 * grp + i) * a.n_parts + part) * d + dim, o[i]);
+      for (int i = 0; i < 4; ++i) {
+        if (4 * grp + i >= g) continue;
+        if (fin)
+          static_cast<uint16_t*>(a.out)[(row0 + 4 * grp + i) * d + dim] = f32_to_bf16(o[i] * s_inv[4 * grp + i]);
+        else
+          store_partial(po + ((row0 + 4 * grp + i) * a.n_parts + part) * d + dim, o[i]);
+      }
     }
   } else {
     // no lift: the partial is the r_V-wide accumulator (d wide for a full-rank list)

@@ -283,7 +283,7 @@ lrkv_status decode_partial(const void* q, const void* basis_k, const void* coeff
                            const void* coeff_v, const lrkv_dims* dims, int64_t n_ctx, float scale,
                            lrkv_dtype dtype, void* workspace, const DecodeLayout& L, hipStream_t stream,
                            const char* fn, const void* k_new = nullptr, const void* v_new = nullptr,
-                           const void* enc_k = nullptr) {
+                           const void* enc_k = nullptr, void* out = nullptr, float* lse = nullptr) {
   char* ws = static_cast<char*>(workspace);
   SplitArgs sa{};
   sa.q = q; sa.basis_k = basis_k; sa.ck = coeff_k; sa.cv = coeff_v; sa.basis_v = basis_v;
@@ -302,6 +302,8 @@ lrkv_status decode_partial(const void* q, const void* basis_k, const void* coeff
     sa.enc_k = enc_k;
     sa.append_row = n_ctx - 1;
   }
+  sa.out = out;   // final outputs (one attention workgroup per unit), or partials
+  sa.lse = lse;
   // no basis_k: latent queries (absorbed projections), no fold and no lift
   const hipError_t e = dtype != LRKV_BF16 ? launch_split_f32(sa, stream)
                                           : (basis_k ? launch_split_bf16(sa, stream) : launch_split_bf16_latent(sa, stream));
@@ -343,6 +345,9 @@ lrkv_status lrkv_decode_attn(const void* q, const void* basis_k, const void* coe
   LRKV_CHECK_PTR(coeff_v, fn);
   LRKV_CHECK_PTR(out, fn);
   if (lse && !aligned16(lse)) return fail(LRKV_ERR_INVALID_ARGUMENT, "%s: lse is not 16-byte aligned", fn);
+  if (dtype == LRKV_BF16 && L.parts == 1)   // one workgroup per unit: it writes the outputs, no merge launch
+    return decode_partial(q, basis_k, coeff_k, basis_v, coeff_v, dims, n_ctx, scale, dtype, workspace, L, stream,
+                          fn, nullptr, nullptr, nullptr, out, lse);
   st = decode_partial(q, basis_k, coeff_k, basis_v, coeff_v, dims, n_ctx, scale, dtype, workspace, L, stream, fn);
   if (st != LRKV_OK) return st;
   return decode_merge(out, lse, dims, dtype, workspace, L, stream, fn);
@@ -467,6 +472,16 @@ lrkv_status lrkv_decode_step(const void* q, const void* k_new, const void* v_new
   if (st != LRKV_OK) return st;
   LRKV_CHECK_PTR(out, fn);
   if (lse && !aligned16(lse)) return fail(LRKV_ERR_INVALID_ARGUMENT, "%s: lse is not 16-byte aligned", fn);
+  if (dtype == LRKV_BF16) {
+    // one attention workgroup per unit: it also appends the token (after its
+    // fold) and writes the outputs itself; no merge launch
+    DecodeLayout F = decode_layout(*dims, std::max<int64_t>(n_ctx - 1, 1), 0);
+    if (F.parts == 1) {
+      F.parts = 2;   // the workgroup's slot and the token's (neither is written)
+      return decode_partial(q, basis_k, coeff_k, basis_v, coeff_v, dims, n_ctx, scale, dtype, workspace, F, stream,
+                            fn, k_new, v_new, enc_k, out, lse);
+    }
+  }
   const DecodeLayout L = step_layout(*dims, n_ctx, dtype);
   st = step_partial(q, k_new, v_new, basis_k, coeff_k, basis_v, coeff_v, enc_k, dims, n_ctx, scale, dtype, workspace,
                     L, stream, fn);

@@ -40,6 +40,11 @@ struct SplitArgs {
   const void* v_new;     // [B, Hkv, d]
   const void* enc_k;     // [Hkv, d, rk] encoder of the appended key, or null: basis_k encodes
   int64_t append_row;
+  // Final outputs: with one attention workgroup per (b, kv head) (and the
+  // append, if any, in that workgroup) the kernel normalises and writes
+  // out [B, Hq, d] and lse [B, Hq] itself, and no partials or merge are needed.
+  void* out;             // or null: write partials
+  float* lse;            // or null
 };
 
 // Log-sum-exp merge of n_parts partials per (b, q head).

@@ -146,7 +146,9 @@ size_t lrkv_decode_workspace_bytes(const lrkv_dims* dims, int64_t n_ctx, int64_t
  * V_hat = C_V B_V^T ("OjaKV" README, StaticPCA: standard attention over
  * keys and values reconstructed from the low-rank cache).  The context is
  * split into chunks attended in parallel (one launch) and the partial
- * results are merged by log-sum-exp (a second launch).
+ * results are merged by log-sum-exp (a second launch).  For bfloat16, when
+ * one workgroup per (b, kv head) covers the whole context (short contexts),
+ * that workgroup normalises and writes out and lse itself: one launch.
  *   q        [B, Hq, d]
  *   basis_k  [Hkv, d, r_K];   coeff_k  key row layout [B, Hkv, capacity, r_K]
  *   basis_v  [Hkv, d, r_V];   coeff_v  value octet layout [B, Hkv, capacity/8, r_V, 8]
@@ -214,8 +216,11 @@ lrkv_status lrkv_decode_attn_latent(const void* q_lat, const void* coeff_k, cons
  * one workgroup (an extra one when the grid has room for it, else the last
  * attention workgroup, after its fold) compresses the token, stores its rows
  * and contributes its softmax term, while the others attend rows
- * [0, n_ctx - 1); a second launch merges.  float32 runs lrkv_compress_kv,
- * then the decode.
+ * [0, n_ctx - 1); a second launch merges.  When one attention workgroup per
+ * (b, kv head) covers rows [0, n_ctx - 1) (short contexts), it also appends
+ * and writes out and lse itself: one launch.  float32 runs lrkv_compress_kv,
+ * then the decode.  The two-phase entry points below always use the
+ * partials and the merge launch.
  *   k_new, v_new  [B, Hkv, d] the new token's key and value
  *   basis_k, basis_v  the decoders (fold and lift), as in lrkv_decode_attn
  *   coeff_k, coeff_v  the caches (row n_ctx - 1 is written; rows below are read)
