@@ -62,7 +62,7 @@ def parse():
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py runs on one GPU only: this build has no multi-GPU path "
+        print(f"bench.py runs on one GPU only: the decode path has no multi-GPU mode "
               f"(asked for --gpus {args.gpus}).", flush=True)
         return 2
 

@@ -32,7 +32,7 @@ computed:
   functions below select those tokens and attend the union of the
   reconstructed low-rank tokens and the full-rank tokens in one softmax.
 
-Readings where the pages are silent (each is listed in the design doc):
+Readings where the pages are silent:
 * softmax scale 1/sqrt(head_dim) (the NOVA-KV summary's logit bound divides
   by sqrt(d), d the head dimension);
 * grouped-query attention: q head h reads kv head h // (Hq/Hkv);
