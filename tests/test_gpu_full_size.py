@@ -1,5 +1,9 @@
 """Parity at the benchmark's full size, in the benchmark's launch configuration.
 
+Also the two variants the benchmark times on the same caches: the latent
+decode (absorbed projections) and the decode step with a separate key
+encoder.
+
 The batched 32K workload (batch 16, 32 query / 8 kv heads, d 128, context
 32768, ranks (32, 96) on even and (48, 112) on odd layers): one layer of each
 parity goes through exactly what a bench step runs (lrkv_compress_kv of the
@@ -68,7 +72,21 @@ def test_bench_layer_step_full_size(layer):
     ck_gpu = bits(ckd)
     cv_gpu = synth.from_value_octets(bits(cvd))
     o_gpu, lse_gpu = to_f64(out), to_f64(lse)
-    del ckd, cvd, ws
+    # the two variants the bench times on these caches: the latent decode of
+    # absorbed projections over all N rows, and the decode step with a
+    # separate (non-orthogonal) key encoder, whose decoder folds the query
+    q_lat = synth.latent_query(W, layer)
+    o_lat, lse_lat = lrkv.decode_attn_latent(to_dev(q_lat, "bf16"), ckd, cvd, N, d)
+    enc, dec = synth.key_transform(W, layer, "k")
+    ck_t, cv_t = ckd.clone(), cvd.clone()
+    out_t = torch.empty_like(out)
+    lse_t = torch.empty_like(lse)
+    lrkv.decode_step(qd, to_dev(ak, "bf16"), to_dev(av, "bf16"), to_dev(dec, "bf16"), ck_t, bvd, cv_t, N,
+                     out=out_t, lse=lse_t, workspace=ws, enc_k=to_dev(enc, "bf16"))
+    torch.cuda.synchronize()
+    o_lat, lse_lat, o_t, lse_t = to_f64(o_lat), to_f64(lse_lat), to_f64(out_t), to_f64(lse_t)
+    ck_t_bits = bits(ck_t)
+    del ckd, cvd, ws, ck_t, cv_t
 
     # oracle, one (batch, q head) at a time, on the cache it builds itself:
     # drawn rows, its own rounded compress of the prefill chunk and of the new token
@@ -103,3 +121,23 @@ def test_bench_layer_step_full_size(layer):
     assert np.all(np.isfinite(o_gpu)) and np.all(np.isfinite(lse_gpu))
     assert np.all(np.abs(o_gpu).max(axis=-1) > 0)
     assert math.isfinite(worst)
+
+    # latent decode on the same cache rows
+    lat_ref, lat_lse = [], []
+    for b, hq in ROWS:
+        o_r, l_r = O.decode_latent(q_lat.exact[b:b + 1, hq:hq + 1], cks[(b, hq // g)][None, None],
+                                   cvs[(b, hq // g)][None, None], N, 1 / math.sqrt(d))
+        lat_ref.append(o_r[0, 0]); lat_lse.append(l_r[0, 0])
+    check_decode(np.stack([o_lat[b, hq] for b, hq in ROWS]), np.array([lse_lat[b, hq] for b, hq in ROWS]),
+                 np.stack(lat_ref), np.array(lat_lse), "bf16", f"full-size latent layer {layer}")
+    # key-encoder step: rows [0, N - 1) as before, the new row round(k E), read through D
+    cks_t = {}
+    for b, h in units:
+        nk = O.compress(ak.exact[b:b + 1, :, h:h + 1], enc.exact[h:h + 1])
+        check_compress(synth.bf16_bits_to_f64(ck_t_bits[b, h, N - 1:N])[None, None], nk,
+                       ak.exact[b:b + 1, :, h:h + 1], enc.exact[h:h + 1], "bf16", f"encoder row {(b, h)}")
+        cks_t[(b, h)] = np.concatenate([cks[(b, h)][:N - 1], O.round_storage(nk, "bf16")[0, 0]])
+    ref_t = O.decode_rows(q.exact, dec.exact, cks_t, bv.exact, cvs, N, ROWS)
+    check_decode(np.stack([o_t[b, hq] for b, hq in ROWS]), np.array([lse_t[b, hq] for b, hq in ROWS]),
+                 np.stack([ref_t[r][0] for r in ROWS]), np.array([ref_t[r][1] for r in ROWS]), "bf16",
+                 f"full-size key-encoder step layer {layer}")
