@@ -23,8 +23,24 @@ __device__ __forceinline__ int64_t coeff_index(int values_layout, int64_t bh, in
                        : (bh * cap + p) * r + col;
 }
 
+// The LDS of one compress workgroup.
 template <int D, int NB>
-__global__ __launch_bounds__(256) void compress_bf16_kernel(CompressArgs a) {
+struct CompressSmem {
+  static constexpr int kOutRow = NB * 16 + 4;
+  static constexpr int kOutCol = kTile + 12;
+  static constexpr int kOutElems = kTile * kOutRow > NB * 16 * kOutCol ? kTile * kOutRow : NB * 16 * kOutCol;
+  // basis, transposed; a pitch of 8 x odd dwords keeps the 16-byte operand reads conflict-free
+  __attribute__((aligned(16))) uint16_t bt[NB * 16][D + 16];
+  // the tile's coefficients: keys as [token][column]; values as [column][slot]
+  // with slot = token + (p0 % 8), so each destination octet is 16 aligned
+  // bytes.  Both row pitches are 2 x odd dwords, which keeps the 2-byte writes
+  // from the matrix-core layout and the 8-byte reads free of bank conflicts.
+  __attribute__((aligned(16))) uint16_t out[kOutElems];
+};
+
+// One cache's coefficients for this workgroup's run of tiles (stages the basis first).
+template <int D, int NB>
+__device__ __forceinline__ void compress_part(const CompressArgs& a, CompressSmem<D, NB>& sm) {
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
   const int lane = tid & 63;
@@ -34,16 +50,10 @@ __global__ __launch_bounds__(256) void compress_bf16_kernel(CompressArgs a) {
   const int b = blockIdx.z;
   const int r = a.rank;
   const int64_t bh = (int64_t)b * a.hkv + h;
-  // basis, transposed; a pitch of 8 x odd dwords keeps the 16-byte operand reads conflict-free
-  __shared__ __attribute__((aligned(16))) uint16_t s_bt[NB * 16][D + 16];
-  // the tile's coefficients: keys as [token][column]; values as [column][slot]
-  // with slot = token + (p0 % 8), so each destination octet is 16 aligned
-  // bytes.  Both row pitches are 2 x odd dwords, which keeps the 2-byte writes
-  // from the matrix-core layout and the 8-byte reads free of bank conflicts.
-  constexpr int kOutRow = NB * 16 + 4;
-  constexpr int kOutCol = kTile + 12;
-  constexpr int kOutElems = kTile * kOutRow > NB * 16 * kOutCol ? kTile * kOutRow : NB * 16 * kOutCol;
-  __shared__ __attribute__((aligned(16))) uint16_t s_out[kOutElems];
+  auto& s_bt = sm.bt;
+  uint16_t* s_out = sm.out;
+  constexpr int kOutRow = CompressSmem<D, NB>::kOutRow;
+  constexpr int kOutCol = CompressSmem<D, NB>::kOutCol;
 
   // basis rows arrive as 16-byte runs of 8 coefficients (all loads issued
   // before the first wait) and are written transposed
@@ -175,6 +185,23 @@ __global__ __launch_bounds__(256) void compress_bf16_kernel(CompressArgs a) {
   }
 }
 
+template <int D, int NB>
+__global__ __launch_bounds__(256) void compress_bf16_kernel(CompressArgs a) {
+  __shared__ CompressSmem<D, NB> sm;
+  compress_part<D, NB>(a, sm);
+}
+
+// Both caches of a prefill chunk in one launch: every workgroup writes the
+// key coefficients of its run of tiles, then (basis restaged) the value
+// coefficients of the same tokens.  NB covers the larger rank.
+template <int D, int NB>
+__global__ __launch_bounds__(256) void compress_pair_bf16_kernel(CompressArgs k, CompressArgs v) {
+  __shared__ CompressSmem<D, NB> sm;
+  compress_part<D, NB>(k, sm);
+  __syncthreads();   // the value basis is staged over the key basis
+  compress_part<D, NB>(v, sm);
+}
+
 // Few tokens (an appended decode token): both caches in one launch, one
 // workgroup per (batch, kv head), no LDS staging of the bases.  Threads
 // 0..127 compute the key coefficients and 128..255 the value coefficients:
@@ -275,6 +302,30 @@ hipError_t launch_compress_bf16(const CompressArgs& a, hipStream_t s) {
     LRKV_COMPRESS_CASE(128, 1) LRKV_COMPRESS_CASE(128, 2) LRKV_COMPRESS_CASE(128, 3)
     LRKV_COMPRESS_CASE(128, 4) LRKV_COMPRESS_CASE(128, 5) LRKV_COMPRESS_CASE(128, 6)
     LRKV_COMPRESS_CASE(128, 7) LRKV_COMPRESS_CASE(128, 8)
+    default:
+      return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+#define LRKV_PAIR_CASE(D, NB)                                                            \
+  case (D * 16 + NB):                                                                    \
+    hipLaunchKernelGGL((compress_pair_bf16_kernel<D, NB>), grid, dim3(256), 0, s, k, v); \
+    break;
+
+hipError_t launch_compress_pair_bf16(const CompressArgs& k, const CompressArgs& v, hipStream_t s) {
+  if (k.n_tokens != v.n_tokens || k.batch != v.batch || k.hkv != v.hkv || k.d != v.d) return hipErrorInvalidValue;
+  const int64_t tiles = (k.n_tokens + kTile - 1) / kTile;
+  const int64_t units = (int64_t)k.hkv * k.batch;
+  int64_t per_unit = (512 + units - 1) / units;
+  if (per_unit > tiles) per_unit = tiles;
+  if (per_unit < 1) per_unit = 1;
+  const dim3 grid((unsigned)per_unit, k.hkv, k.batch);
+  const int nb = ((k.rank > v.rank ? k.rank : v.rank) + 15) / 16;
+  switch (k.d * 16 + nb) {
+    LRKV_PAIR_CASE(64, 1) LRKV_PAIR_CASE(64, 2) LRKV_PAIR_CASE(64, 3) LRKV_PAIR_CASE(64, 4)
+    LRKV_PAIR_CASE(128, 1) LRKV_PAIR_CASE(128, 2) LRKV_PAIR_CASE(128, 3) LRKV_PAIR_CASE(128, 4)
+    LRKV_PAIR_CASE(128, 5) LRKV_PAIR_CASE(128, 6) LRKV_PAIR_CASE(128, 7) LRKV_PAIR_CASE(128, 8)
     default:
       return hipErrorInvalidValue;
   }

@@ -245,9 +245,13 @@ lrkv_status lrkv_compress_kv(const void* xk, const void* xv, const void* basis_k
                   n_tokens, pos, dims->capacity};
   CompressArgs av{xv, basis_v, coeff_v, 1, dims->batch, dims->n_kv_heads, dims->head_dim, dims->rank_v,
                   n_tokens, pos, dims->capacity};
-  hipError_t e = dtype == LRKV_BF16 ? launch_compress_bf16(ak, stream) : launch_compress_f32(ak, stream);
+  if (dtype == LRKV_BF16) {   // both caches in one launch
+    const hipError_t e = launch_compress_pair_bf16(ak, av, stream);
+    return e == hipSuccess ? LRKV_OK : device_fail(fn, e);
+  }
+  hipError_t e = launch_compress_f32(ak, stream);
   if (e != hipSuccess) return device_fail(fn, e);
-  e = dtype == LRKV_BF16 ? launch_compress_bf16(av, stream) : launch_compress_f32(av, stream);
+  e = launch_compress_f32(av, stream);
   return e == hipSuccess ? LRKV_OK : device_fail(fn, e);
 }
 

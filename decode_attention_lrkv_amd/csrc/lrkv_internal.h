@@ -82,6 +82,8 @@ hipError_t launch_split_f32(const SplitArgs& a, hipStream_t s);
 hipError_t launch_split_bf16_latent(const SplitArgs& a, hipStream_t s);
 hipError_t launch_merge(const MergeArgs& a, bool bf16, hipStream_t s);
 hipError_t launch_compress_bf16(const CompressArgs& a, hipStream_t s);
+// Keys and values of the same tokens in one launch (same batch, heads, d, tokens).
+hipError_t launch_compress_pair_bf16(const CompressArgs& k, const CompressArgs& v, hipStream_t s);
 hipError_t launch_compress_f32(const CompressArgs& a, hipStream_t s);
 
 struct HybridArgs {
