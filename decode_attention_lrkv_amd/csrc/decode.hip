@@ -16,9 +16,13 @@
 // precision.  At the end the workgroup's four waves are merged in LDS and the
 // merged latent accumulator is lifted through B_V^T, so each workgroup leaves
 // one head_dim-wide partial (running max, sum, unnormalised output) per query
-// head.
+// head.  When one workgroup covers a (batch, kv head) it writes the final
+// output and lse itself instead, and there is no second launch.
 // Launch 2, the merge kernel: log-sum-exp combination of those partials
 // (and of the full-rank side list's partials in the hybrid cache).
+// Variants: a decode step's appended token is compressed and attended inside
+// launch 1 (with the basis, or a separate key encoder); latent queries and
+// outputs (projections that absorb the bases) skip the fold and the lift.
 #include "lrkv_device.h"
 #include "lrkv_internal.h"
 
@@ -234,7 +238,8 @@ struct SplitSmem {
 // this (b, kv head); part: the partial it writes.  append: this workgroup
 // also compresses the appended token (after the fold, while its first chunk
 // streams in), stores its cache rows and writes that token's partial as the
-// last one, a.n_parts - 1.
+// last one, a.n_parts - 1 (or, with final outputs, adds the token to its own
+// merge).  ENC: the appended key has a separate encoder (a.enc_k).
 template <int KC, int VB, bool FOLD, int STAGES, bool ENC = false>
 __device__ __forceinline__ void split_bf16_body(const SplitArgs& a, int wg, int part, SplitSmem& sm,
                                                 bool append = false) {
