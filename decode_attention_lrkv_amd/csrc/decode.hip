@@ -1,8 +1,10 @@
 // Split-K decode attention over a low-rank KV cache (gfx950).
 //
-// Launch 1, the attention kernel: one wave attends one split (a run of
-// 32-token chunks) of one (batch, kv head) for all g query heads of that kv
-// head, so every coefficient row is read from HBM once per kv head.  Per chunk:
+// Launch 1, the attention kernel: one workgroup attends a run of 32-token
+// chunks of one (batch, kv head) for all g query heads of that kv head, so
+// every coefficient row is read from HBM once per kv head; its four waves
+// take the run's chunks in turn (wave w: chunks w, w + 4, ...), so that they
+// read one dense window of the cache together.  Per chunk:
 //   scores  s = C_K q'             matrix cores, tokens as rows, heads as columns
 //   softmax running max / sum per head, rescaling the accumulator
 //   acc    += P C_V                matrix cores, heads as rows, value columns as columns
@@ -250,7 +252,6 @@ __device__ __forceinline__ void split_bf16_body(const SplitArgs& a, int wg, int 
   const int grp = lane >> 4;     // k-slot group
   const int h = blockIdx.y;
   const int b = blockIdx.z;
-  const int split = wg * kWaves + wave;
   const int g = a.g;
   const int rk = a.rk, rv = a.rv, d = a.d;
   const int64_t bh = (int64_t)b * a.hkv + h;
@@ -268,10 +269,18 @@ __device__ __forceinline__ void split_bf16_body(const SplitArgs& a, int wg, int 
     if (n_end > a.cap) n_end = a.cap;
     if (n_end < 0) n_end = 0;
   }
+  // The workgroup owns kWaves * chunks_per_split consecutive chunks and its
+  // waves take them in turn: wave w reads chunks w, w + kWaves, ...  Four
+  // waves reading adjacent chunks keep the workgroup's loads in one dense
+  // window of the cache (measured: 1.4 % faster than one contiguous run per
+  // wave with ranks 32/96, where every per-wave run starts at a multiple of
+  // 128 KB).  The online softmax does not depend on the order.
   const int64_t n_chunks = (n_end + kChunk - 1) / kChunk;
-  const int64_t c_begin = (int64_t)split * a.chunks_per_split;
-  int64_t c_end = c_begin + a.chunks_per_split;
+  const int64_t w_begin = (int64_t)wg * kWaves * a.chunks_per_split;
+  const int64_t c_begin = w_begin + wave;
+  int64_t c_end = w_begin + (int64_t)kWaves * a.chunks_per_split;
   if (c_end > n_chunks) c_end = n_chunks;
+  constexpr int64_t kStep = kWaves;
 
   const uint16_t* ck = static_cast<const uint16_t*>(a.ck) + bh * a.cap * rk;
   const uint16_t* cv = static_cast<const uint16_t*>(a.cv) + bh * a.cap * rv;
@@ -605,17 +614,17 @@ __device__ __forceinline__ void split_bf16_body(const SplitArgs& a, int wg, int 
   };
 
   if (STAGES == 2) {
-    for (int64_t chunk = c_begin; chunk < c_end; chunk += 2) {
-      if (chunk + 1 < c_end) load(cb, chunk + 1);
+    for (int64_t chunk = c_begin; chunk < c_end; chunk += 2 * kStep) {
+      if (chunk + kStep < c_end) load(cb, chunk + kStep);
       process(ca, chunk);
-      if (chunk + 1 >= c_end) break;
-      if (chunk + 2 < c_end) load(ca, chunk + 2);
-      process(cb, chunk + 1);
+      if (chunk + kStep >= c_end) break;
+      if (chunk + 2 * kStep < c_end) load(ca, chunk + 2 * kStep);
+      process(cb, chunk + kStep);
     }
   } else {
-    for (int64_t chunk = c_begin; chunk < c_end; ++chunk) {
+    for (int64_t chunk = c_begin; chunk < c_end; chunk += kStep) {
       process(ca, chunk);
-      if (chunk + 1 < c_end) load(ca, chunk + 1);
+      if (chunk + kStep < c_end) load(ca, chunk + kStep);
     }
   }
 
