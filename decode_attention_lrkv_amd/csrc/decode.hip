@@ -215,9 +215,10 @@ __device__ void merge_unit(const MergeArgs& a, int64_t unit) {
 //
 // Each chunk is read through buffer resources based at the chunk and sized to
 // its valid tokens: rows past the context, and lanes pointed past the end on
-// purpose (columns beyond the rank), read as zero without a branch.  Chunks
-// are double-buffered in registers: the loads of chunk i+1 are in flight while
-// chunk i is scored and accumulated.
+// purpose (columns beyond the rank), read as zero without a branch.  The rows
+// are read once, so the loads are non-temporal (they do not fill the caches).
+// Chunks are double-buffered in registers: the loads of chunk i+1 are in
+// flight while chunk i is scored and accumulated.
 template <int KC, int VB>
 struct Chunk {
   u32x4 k[2][KC];
@@ -308,9 +309,9 @@ __device__ __forceinline__ void split_bf16_body(const SplitArgs& a, int wg, int 
 #pragma unroll
     for (int T = 0; T < 2; ++T)
 #pragma unroll
-      for (int cc = 0; cc < KC; ++cc) c.k[T][cc] = buf_load16(rs_k, vo_k[T][cc]);
+      for (int cc = 0; cc < KC; ++cc) c.k[T][cc] = buf_load16_stream(rs_k, vo_k[T][cc]);
 #pragma unroll
-    for (int vb = 0; vb < VB; ++vb) c.v[vb] = buf_load16(rs_v, vo_v[vb]);
+    for (int vb = 0; vb < VB; ++vb) c.v[vb] = buf_load16_stream(rs_v, vo_v[vb]);
   };
 
   // --- fold q' = q B_K * scale * log2(e) for the g query heads of this kv head
