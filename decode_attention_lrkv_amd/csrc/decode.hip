@@ -240,9 +240,9 @@ struct SplitSmem {
 // wg: this workgroup's index among the workgroups attending this list of
 // this (b, kv head); part: the partial it writes.  append: this workgroup
 // also compresses the appended token (after the fold, while its first chunk
-// streams in), stores its cache rows and writes that token's partial as the
-// last one, a.n_parts - 1 (or, with final outputs, adds the token to its own
-// merge).  ENC: the appended key has a separate encoder (a.enc_k).
+// streams in), stores its cache rows and adds the token as one more term of
+// the workgroup's merge, so the token's own partial slot, a.n_parts - 1, is
+// left empty.  ENC: the appended key has a separate encoder (a.enc_k).
 template <int KC, int VB, bool FOLD, int STAGES, bool ENC = false>
 __device__ __forceinline__ void split_bf16_body(const SplitArgs& a, int wg, int part, SplitSmem& sm,
                                                 bool append = false) {
@@ -432,8 +432,8 @@ __device__ __forceinline__ void split_bf16_body(const SplitArgs& a, int wg, int 
   if (append) {
     // c = round(x E) for the key (threads < 128, column tid) and the value
     // (threads >= 128, column tid - 128), E the encoder (the basis itself
-    // unless a separate key encoder is given), stored at the appended row; then the
-    // token's partial: m = q' . c_K (log2 units), l = 1, o = B_V c_V (every head)
+    // unless a separate key encoder is given), stored at the appended row; then
+    // the token's score q' . c_K (log2 units), kept with c_V for the epilogue
     const int pa = a.n_parts - 1;
     const int64_t p = a.append_row;
     float* s_c = s_q + 256;   // past the token's key and value
@@ -515,20 +515,13 @@ __device__ __forceinline__ void split_bf16_body(const SplitArgs& a, int wg, int 
 #pragma unroll
         for (int u = 0; u < 4; ++u) p4[u] = fmaf(s_qf[tid * rk + k + u], s_c[k + u], p4[u]);
       const float s = (p4[0] + p4[1]) + (p4[2] + p4[3]);
-      if (a.out) {
-        s_q[512 + tid] = s;   // folded into this workgroup's merge in the epilogue (c_V stays in s_c)
-      } else {
-        store_partial(a.part_ml + ((row0 + tid) * a.n_parts + pa) * 2 + 0, s);
-        store_partial(a.part_ml + ((row0 + tid) * a.n_parts + pa) * 2 + 1, 1.f);
+      // the token joins this workgroup's merge in the epilogue (c_V stays in
+      // s_c), before the lift; its own partial slot is marked empty
+      s_q[512 + tid] = s;
+      if (!a.out) {
+        store_partial(a.part_ml + ((row0 + tid) * a.n_parts + pa) * 2 + 0, -INFINITY);
+        store_partial(a.part_ml + ((row0 + tid) * a.n_parts + pa) * 2 + 1, 0.f);
       }
-    }
-    if (tid < d && !a.out) {
-      float p4[4] = {0.f, 0.f, 0.f, 0.f};
-      for (int c = 0; c < rv; c += 4)   // rv is a multiple of 8
-#pragma unroll
-        for (int u = 0; u < 4; ++u) p4[u] = fmaf(bf16_to_f32(sm.bv[tid * (rv + 8) + c + u]), s_c[128 + c + u], p4[u]);
-      const float o = (p4[0] + p4[1]) + (p4[2] + p4[3]);
-      for (int j = 0; j < g; ++j) store_partial(a.part_o + ((row0 + j) * a.n_parts + pa) * d + tid, o);
     }
   }
 
@@ -657,12 +650,12 @@ __device__ __forceinline__ void split_bf16_body(const SplitArgs& a, int wg, int 
   }
   __syncthreads();
   // 2. the four waves merged: M = max_w m_w, acc = sum_w 2^(m_w - M) acc_w,
-  //    likewise the sum.  With final outputs, the appended token of this
-  //    workgroup (score in s_q[512 + j], latent value c_V in s_c) is one more
-  //    term, and the sum is inverted for the lift instead of being stored.
+  //    likewise the sum.  The appended token of this workgroup (score in
+  //    s_q[512 + j], latent value c_V in s_c) is one more term.  With final
+  //    outputs the sum is inverted for the lift instead of being stored.
   float* s_merged = s_qf;   // the query operand was read before the main loop
   const bool fin = a.out != nullptr;
-  const bool tok = fin && append;
+  const bool tok = append;
   const float* s_tok_c = s_q + 256 + 128;
   float* s_inv = s_q + 520;
   for (int i = tid; i < g * rv; i += 256) {

@@ -87,7 +87,9 @@ struct DecodeLayout {
   size_t o = 0, ml = 0, total = 0;
 };
 
-// append (decode step): one more partial, the appended token's.  The token is
+// append (decode step): one more partial slot, the appended token's, which
+// stays empty (max -inf): the appending workgroup adds the token to its own
+// partial.  The token is
 // compressed by one more workgroup per (b, kv head) when the grid still fits
 // one round of two workgroups per compute unit (then it runs beside the
 // attention), else by the last attention workgroup before its own chunks.
@@ -115,7 +117,7 @@ DecodeLayout decode_layout(const lrkv_dims& d, int64_t n_lr_tokens, int64_t side
     L.parts = (int)cdiv(L.lr.n_splits, kSplitsPerPart);
     if (append) {
       const bool own_wg = (int64_t)(L.parts + 1) * units <= 2 * (int64_t)cus;
-      L.parts += own_wg ? 2 : 1;   // workgroups (the appending one included) + the token's partial
+      L.parts += own_wg ? 2 : 1;   // workgroups (the appending one included) + the token's slot, left empty
     }
   }
   size_t off = 0;
@@ -444,7 +446,7 @@ lrkv_status check_step(const void* q, const void* k_new, const void* v_new, cons
 }
 
 // Workspace layout of a decode step: the attention workgroups of rows
-// [0, n_ctx - 1) plus the appended token's partial (bfloat16); float32 runs
+// [0, n_ctx - 1) plus the appended token's (empty) slot (bfloat16); float32 runs
 // the plain decode over n_ctx rows after the compress kernel.
 DecodeLayout step_layout(const lrkv_dims& d, int64_t n_ctx, lrkv_dtype dtype) {
   return dtype == LRKV_BF16 ? decode_layout(d, std::max<int64_t>(n_ctx - 1, 1), 0, true) : decode_layout(d, n_ctx, 0);

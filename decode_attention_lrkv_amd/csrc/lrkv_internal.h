@@ -34,7 +34,8 @@ struct SplitArgs {
   float* part_ml;        // [B, Hq, n_parts, 2]  running max (log2 units), softmax sum
   // Append (decode step): when k_new is non-null, the last workgroup of each
   // (b, kv head) compresses the new token's key and value, stores them at
-  // cache row append_row (through ck / cv) and writes that token's partial;
+  // cache row append_row (through ck / cv) and adds the token to its own
+  // partial (the token's slot, n_parts - 1, is marked empty);
   // the other workgroups attend rows [0, n_static).
   const void* k_new;     // [B, Hkv, d] or null
   const void* v_new;     // [B, Hkv, d]
