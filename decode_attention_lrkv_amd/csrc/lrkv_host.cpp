@@ -89,10 +89,10 @@ struct DecodeLayout {
 
 // append (decode step): one more partial slot, the appended token's, which
 // stays empty (max -inf): the appending workgroup adds the token to its own
-// partial.  The token is
-// compressed by one more workgroup per (b, kv head) when the grid still fits
-// one round of two workgroups per compute unit (then it runs beside the
-// attention), else by the last attention workgroup before its own chunks.
+// partial.  The token is compressed by one more workgroup per (b, kv head)
+// when the grid still fits one round of two workgroups per compute unit
+// (then it runs beside the attention), else by the last attention workgroup
+// before its own chunks.
 DecodeLayout decode_layout(const lrkv_dims& d, int64_t n_lr_tokens, int64_t side_cap, bool append = false) {
   DecodeLayout L;
   const int cus = device_cu_count();
