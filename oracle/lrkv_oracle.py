@@ -31,6 +31,8 @@ computed:
   compresses the rest ("OjaKV" README, Method Summary, OjaKV).  The hybrid
   functions below select those tokens and attend the union of the
   reconstructed low-rank tokens and the full-rank tokens in one softmax.
+* OjaKV also updates the subspace online with Oja's algorithm (same
+  section); oja_update is Oja's subspace rule, summed over a call's tokens.
 
 Readings where the pages are silent:
 * softmax scale 1/sqrt(head_dim) (the NOVA-KV summary's logit bound divides
@@ -43,7 +45,10 @@ Readings where the pages are silent:
 * hybrid selection: relative residual ||x - round(x B) B^T|| / ||x|| > tau for
   the key or the value (strict), decided in float32 because the kernel decides
   it in float32; tokens of zero norm are never selected; low-rank rows and the
-  full-rank side list both keep ascending token order.
+  full-rank side list both keep ascending token order;
+* Oja update: one basis per kv head, updated from every token of the call
+  (all batch rows) against the same B, step size eta given by the caller, no
+  re-orthonormalisation, cached coefficients left as stored.
 """
 from __future__ import annotations
 
@@ -360,3 +365,33 @@ def score_error(queries: np.ndarray, keys: np.ndarray, keys_hat: np.ndarray) -> 
     Q = np.asarray(queries, dtype=np.float64)
     diff = Q @ np.asarray(keys, dtype=np.float64).T - Q @ np.asarray(keys_hat, dtype=np.float64).T
     return float(np.sum(diff * diff))
+
+
+# ----------------------------------------------------------------------------
+# online basis update ("OjaKV" README, Method Summary, OjaKV: the low-rank
+# subspace is updated with Oja's algorithm during prefill and decoding)
+# ----------------------------------------------------------------------------
+
+def oja_update(basis: np.ndarray, x: np.ndarray, eta: float) -> np.ndarray:
+    """One step of Oja's subspace rule for the basis of one kv head.
+
+    basis [d, r], x [n, d] (the new tokens' vectors as rows).  Every token t
+    projects onto the basis, y_t = x_t B, and pulls the basis towards itself
+    along its residual: B <- B + eta * sum_t (x_t - y_t B^T)^T y_t.  The sum
+    runs over the tokens of the call against the same B (the batched form of
+    the per-token rule), i.e. B + eta (X^T Y - B Y^T Y) with Y = X B.  No
+    re-orthonormalisation: for an orthonormal B the step keeps B^T B = I up
+    to the second-order term eta^2 (.)^T (.).
+    """
+    B = np.asarray(basis, dtype=np.float64)
+    X = np.asarray(x, dtype=np.float64)
+    Y = X @ B
+    return B + eta * (X.T @ Y - B @ (Y.T @ Y))
+
+
+def oja_update_heads(basis: np.ndarray, x: np.ndarray, eta: float) -> np.ndarray:
+    """oja_update for every kv head of a chunk: basis [Hkv, d, r], x [B, T, Hkv, d];
+    head h is updated from the tokens of every batch row (one basis per kv head)."""
+    x = np.asarray(x, dtype=np.float64)
+    return np.stack([oja_update(basis[h], x[:, :, h, :].reshape(-1, x.shape[-1]), eta)
+                     for h in range(x.shape[2])])
