@@ -24,6 +24,7 @@ __all__ = [
     "decode_step", "decode_step_workspace_bytes", "decode_step_partial", "decode_step_merge",
     "compress_hybrid", "compress_hybrid_workspace_bytes", "decode_attn_hybrid",
     "HybridCache", "value_cache_shape", "LIB_PATH", "decode_attn_partial", "decode_attn_merge",
+    "decode_attn_latent", "oja_update", "oja_workspace_bytes",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "liblrkv.so")
@@ -52,6 +53,8 @@ _SIG = {
     "lrkv_compress": (ctypes.c_int, [_P, _P, _P, ctypes.c_int, _I32, _I32, _I32, _I32, _I64, _I64, _I64,
                                      ctypes.c_int, _P]),
     "lrkv_compress_kv": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, ctypes.POINTER(_Dims), _I64, _I64, ctypes.c_int, _P]),
+    "lrkv_oja_workspace_bytes": (ctypes.c_size_t, [_I32, _I32, _I32, _I32, _I64]),
+    "lrkv_oja_update": (ctypes.c_int, [_P, _P, _P, _I32, _I32, _I32, _I32, _I64, _F, _P, ctypes.c_size_t, _P]),
     "lrkv_decode_workspace_bytes": (ctypes.c_size_t, [ctypes.POINTER(_Dims), _I64, _I64]),
     "lrkv_decode_attn": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, ctypes.POINTER(_Dims), _I64, _F,
                                         ctypes.c_int, _P, ctypes.c_size_t, _P]),
@@ -154,6 +157,32 @@ def compress_kv(xk, xv, basis_k, basis_v, coeff_k, coeff_v, pos: int) -> None:
     _check(library().lrkv_compress_kv(_ptr(xk), _ptr(xv), _ptr(basis_k), _ptr(basis_v), _ptr(coeff_k),
                                       _ptr(coeff_v), ctypes.byref(dims), T, pos, _dtype_code(xk),
                                       _stream(xk.device)))
+
+
+def oja_workspace_bytes(batch: int, n_kv_heads: int, head_dim: int, rank: int, n_tokens: int) -> int:
+    return int(library().lrkv_oja_workspace_bytes(batch, n_kv_heads, head_dim, rank, n_tokens))
+
+
+def oja_update(x: torch.Tensor, basis: torch.Tensor, eta: float, basis_bf16: Optional[torch.Tensor] = None,
+               workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """One Oja subspace step of every kv head's basis from a chunk of tokens.
+
+    x [B, T, Hkv, d] bfloat16; basis [Hkv, d, r] float32, updated in place:
+    B <- B + eta (X^T Y - B Y^T Y), Y = X B, over the chunk's tokens of all
+    batch rows.  Returns basis_bf16 [Hkv, d, r] (the updated basis rounded to
+    bfloat16; allocated when not given).
+    """
+    if x.dtype != torch.bfloat16 or basis.dtype != torch.float32:
+        raise LrkvError(1, "oja_update takes bfloat16 tokens and a float32 basis")
+    B, T, H, d = x.shape
+    r = basis.shape[2]
+    lib = library()
+    ws = _workspace(int(lib.lrkv_oja_workspace_bytes(B, H, d, r, T)), x.device, workspace)
+    if basis_bf16 is None:
+        basis_bf16 = torch.empty(basis.shape, dtype=torch.bfloat16, device=basis.device)
+    _check(lib.lrkv_oja_update(_ptr(x), _ptr(basis), _ptr(basis_bf16), B, H, d, r, T, eta, _ptr(ws), ws.numel(),
+                               _stream(x.device)))
+    return basis_bf16
 
 
 def decode_workspace_bytes(batch, n_q_heads, n_kv_heads, head_dim, rank_k, rank_v, capacity,

@@ -15,7 +15,7 @@ LIB = os.path.join(PKG, "liblrkv.so")
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
-SOURCES = ["decode.hip", "compress.hip", "hybrid.hip", "lrkv_host.cpp"]
+SOURCES = ["decode.hip", "compress.hip", "hybrid.hip", "oja.hip", "lrkv_host.cpp"]
 FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
          # packed fp32 VALU ops are kept out of all device code
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",

@@ -172,6 +172,14 @@ lrkv_status check_dims(const lrkv_dims* d, lrkv_dtype dt, const char* fn) {
     if (!aligned16(p)) return fail(LRKV_ERR_INVALID_ARGUMENT, "%s: %s is not 16-byte aligned", fn, #p); \
   } while (0)
 
+// Stats workgroups per kv head for an Oja update: one round over the chip,
+// no more than there are 64-token steps.
+int oja_workgroups(int hkv, int64_t tokens) {
+  const int64_t steps = std::max<int64_t>(1, (tokens + 63) / 64);
+  const int64_t per_head = std::max<int64_t>(1, device_cu_count() / std::max(1, hkv));
+  return (int)std::min<int64_t>(std::min<int64_t>(steps, per_head), 65535);
+}
+
 float resolve_scale(float scale, int head_dim) {
   return scale == 0.f ? 1.f / std::sqrt((float)head_dim) : scale;
 }
@@ -640,6 +648,48 @@ lrkv_status lrkv_decode_attn_hybrid(const void* q, const void* basis_k, const vo
   ma.d = dims->head_dim; ma.g = g; ma.hq = dims->n_q_heads; ma.hkv = dims->n_kv_heads; ma.batch = dims->batch;
   ma.out = out; ma.lse = lse;
   e = launch_merge(ma, true, stream);
+  return e == hipSuccess ? LRKV_OK : device_fail(fn, e);
+}
+
+size_t lrkv_oja_workspace_bytes(int32_t batch, int32_t n_kv_heads, int32_t head_dim, int32_t rank,
+                                int64_t n_tokens) {
+  if (batch < 1 || n_kv_heads < 1 || head_dim < 16 || rank < 1 || n_tokens < 0) return 0;
+  const int n_wg = oja_workgroups(n_kv_heads, (int64_t)batch * n_tokens);
+  return sizeof(float) * oja_workspace_floats(n_kv_heads, head_dim, rank, n_wg);
+}
+
+lrkv_status lrkv_oja_update(const void* x, float* basis, void* basis_bf16, int32_t batch,
+                            int32_t n_kv_heads, int32_t head_dim, int32_t rank, int64_t n_tokens,
+                            float eta, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  const char* fn = "lrkv_oja_update";
+  if (batch < 1 || n_kv_heads < 1) return fail(LRKV_ERR_INVALID_ARGUMENT, "%s: batch and n_kv_heads must be >= 1", fn);
+  if (n_kv_heads > 65535) return fail(LRKV_ERR_UNSUPPORTED, "%s: n_kv_heads must be <= 65535", fn);
+  if (head_dim != 64 && head_dim != 128)
+    return fail(LRKV_ERR_UNSUPPORTED, "%s: head_dim = %d (supported: 64, 128)", fn, head_dim);
+  lrkv_status st = check_rank(rank, head_dim, LRKV_BF16, fn, "rank");
+  if (st != LRKV_OK) return st;
+  if (n_tokens < 0) return fail(LRKV_ERR_INVALID_ARGUMENT, "%s: n_tokens = %lld < 0", fn, (long long)n_tokens);
+  if (!std::isfinite(eta)) return fail(LRKV_ERR_INVALID_ARGUMENT, "%s: eta is not finite", fn);
+  LRKV_CHECK_PTR(basis, fn);
+  if (basis_bf16 && !aligned16(basis_bf16))
+    return fail(LRKV_ERR_INVALID_ARGUMENT, "%s: basis_bf16 is not 16-byte aligned", fn);
+  if (n_tokens == 0) return LRKV_OK;   // x may be NULL then
+  LRKV_CHECK_PTR(x, fn);
+  const int64_t tokens = (int64_t)batch * n_tokens;
+  if (tokens * n_kv_heads * head_dim > ((int64_t)1 << 40))
+    return fail(LRKV_ERR_UNSUPPORTED, "%s: chunk of %lld tokens is too large", fn, (long long)tokens);
+  LRKV_CHECK_PTR(workspace, fn);
+  const size_t need = lrkv_oja_workspace_bytes(batch, n_kv_heads, head_dim, rank, n_tokens);
+  if (workspace_bytes < need)
+    return fail(LRKV_ERR_WORKSPACE_TOO_SMALL, "%s: workspace of %zu bytes, %zu needed", fn, workspace_bytes, need);
+  OjaArgs a{};
+  a.x = x; a.basis = basis; a.basis_bf16 = basis_bf16;
+  a.hkv = n_kv_heads; a.d = head_dim; a.rank = rank; a.n_tokens = tokens; a.eta = eta;
+  a.n_wg = oja_workgroups(n_kv_heads, tokens);
+  a.ws = static_cast<float*>(workspace);
+  a.ws_sum = a.ws + oja_workspace_floats(n_kv_heads, head_dim, rank, a.n_wg)
+             - (size_t)n_kv_heads * ((size_t)head_dim * oja_rank_pad(rank) + (size_t)oja_rank_pad(rank) * oja_rank_pad(rank));
+  const hipError_t e = launch_oja_update(a, stream);
   return e == hipSuccess ? LRKV_OK : device_fail(fn, e);
 }
 

@@ -71,6 +71,22 @@ struct CompressKvArgs {
   int64_t n_tokens, pos, cap;
 };
 
+// Oja subspace update of the bases from a chunk of tokens (all batch rows).
+struct OjaArgs {
+  const void* x;         // [B, T, Hkv, d] bf16; n_tokens = B * T rows per head
+  float* basis;          // [Hkv, d, rank] float32, updated in place
+  void* basis_bf16;      // [Hkv, d, rank] bf16 copy, or null
+  int hkv, d, rank;
+  int64_t n_tokens;
+  float eta;
+  float* ws;             // [Hkv, n_wg, d * R + R * R] partial sums (R = rank padded to 16)
+  float* ws_sum;         // [Hkv, d * R + R * R] their sums
+  int n_wg;              // stats workgroups per kv head
+};
+int oja_rank_pad(int rank);
+size_t oja_workspace_floats(int hkv, int d, int rank, int n_wg);
+hipError_t launch_oja_update(const OjaArgs& a, hipStream_t s);
+
 hipError_t launch_split_bf16(const SplitArgs& a, hipStream_t s);
 // Hybrid cache: low-rank rows (lr) and full-rank side list (side) in one
 // launch of wgs_per_unit workgroups per (b, kv head), divided between the two

@@ -304,6 +304,37 @@ lrkv_status lrkv_decode_attn_hybrid(const void* q, const void* basis_k, const vo
                                     lrkv_dtype dtype, void* workspace, size_t workspace_bytes,
                                     hipStream_t stream);
 
+/* Bytes of workspace lrkv_oja_update needs. */
+size_t lrkv_oja_workspace_bytes(int32_t batch, int32_t n_kv_heads, int32_t head_dim, int32_t rank,
+                                int64_t n_tokens);
+
+/*
+ * Online basis update by Oja's subspace rule ("OjaKV" README, Method
+ * Summary, OjaKV: the low-rank subspace is updated online with Oja's
+ * algorithm, in prefill and in decoding).  For every kv head h, with the
+ * n_tokens new tokens x_t of every batch row as the rows of X:
+ *   Y = X B[h],   B[h] <- B[h] + eta (X^T Y - B[h] Y^T Y)
+ * i.e. the per-token rule B <- B + eta (x - y B^T)^T y summed over the
+ * chunk's tokens against the same B.  No re-orthonormalisation (the rule
+ * keeps B^T B = I to first order in eta); coefficients already in a cache
+ * are left as they are.
+ *   x           [B, n_tokens, Hkv, d] bfloat16 (a chunk, as for lrkv_compress)
+ *   basis       [Hkv, d, rank] float32, read and overwritten: the basis kept
+ *               at full precision, since steps of this size vanish in bfloat16
+ *   basis_bf16  [Hkv, d, rank] bfloat16, written with the updated basis
+ *               rounded to nearest even (the copy the compress and decode
+ *               calls take), or NULL
+ *   eta         step size (finite)
+ *   workspace   at least lrkv_oja_workspace_bytes(...) bytes, 16-byte aligned;
+ *               scratch, no initial contents needed
+ * head_dim 64 or 128; rank a multiple of 8, at most head_dim.  The result
+ * is deterministic (fixed summation order).  n_tokens = 0 leaves the basis
+ * as it is (x may then be NULL).  Three launches on the stream.
+ */
+lrkv_status lrkv_oja_update(const void* x, float* basis, void* basis_bf16, int32_t batch,
+                            int32_t n_kv_heads, int32_t head_dim, int32_t rank, int64_t n_tokens,
+                            float eta, void* workspace, size_t workspace_bytes, hipStream_t stream);
+
 /* Static description of a status code. */
 const char* lrkv_status_string(lrkv_status status);
 

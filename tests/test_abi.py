@@ -31,7 +31,8 @@ def test_header_declares_the_entry_points():
               "lrkv_decode_workspace_bytes", "lrkv_status_string", "lrkv_last_error",
               "lrkv_decode_attn_partial", "lrkv_decode_attn_merge", "lrkv_compress_hybrid_workspace_bytes",
               "lrkv_decode_step", "lrkv_decode_step_workspace_bytes", "lrkv_decode_step_partial",
-              "lrkv_decode_step_merge", "lrkv_decode_attn_latent"):
+              "lrkv_decode_step_merge", "lrkv_decode_attn_latent", "lrkv_oja_update",
+              "lrkv_oja_workspace_bytes"):
         assert n in names
 
 
@@ -174,6 +175,28 @@ def test_latent_decode_validation():
     assert f(P, P, P, P, None, ctypes.byref(d), 300, 0.0, 1, P, 1 << 30, None) == 1
     assert f(P, P, P, P, None, ctypes.byref(d), 100, 0.0, 1, P, 16, None) == 3
     assert f(P, P, P, P, None, ctypes.byref(_dims(lrkv, rank_v=12)), 100, 0.0, 1, P, 1 << 30, None) == 2
+
+
+def test_oja_update_validation():
+    lrkv, lib = _lib()
+    f = lib.lrkv_oja_update
+    need = lib.lrkv_oja_workspace_bytes(2, 8, 128, 48, 100)
+    assert need > 0
+    assert lib.lrkv_oja_workspace_bytes(2, 8, 128, 48, 100) == need       # deterministic plan
+    assert lib.lrkv_oja_workspace_bytes(2, 8, 128, 48, 0) > 0
+    # x, basis, basis_bf16, batch, Hkv, d, rank, n_tokens, eta, ws, bytes, stream
+    assert f(None, P, None, 2, 8, 128, 48, 100, 1e-3, P, need, None) == 1
+    assert f(P, None, None, 2, 8, 128, 48, 100, 1e-3, P, need, None) == 1
+    assert f(P, P, MIS, 2, 8, 128, 48, 100, 1e-3, P, need, None) == 1
+    assert f(P, P, None, 2, 8, 96, 48, 100, 1e-3, P, need, None) == 2
+    assert f(P, P, None, 2, 8, 128, 12, 100, 1e-3, P, need, None) != 0
+    assert f(P, P, None, 2, 8, 128, 48, -1, 1e-3, P, need, None) == 1
+    assert f(P, P, None, 2, 8, 128, 48, 100, float("nan"), P, need, None) == 1
+    assert f(P, P, None, 0, 8, 128, 48, 100, 1e-3, P, need, None) == 1
+    assert f(P, P, None, 2, 8, 128, 48, 100, 1e-3, P, need - 4, None) == 3
+    assert f(P, P, None, 2, 8, 128, 48, 100, 1e-3, None, need, None) == 1
+    assert f(P, P, None, 2, 8, 128, 48, 0, 1e-3, None, 0, None) == 0      # nothing to do, nothing launched
+    assert f(None, P, None, 2, 8, 128, 48, 0, 1e-3, None, 0, None) == 0
 
 
 def test_missing_library_fails_loudly():
