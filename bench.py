@@ -278,16 +278,38 @@ def bench_variants(torch, lrkv, bm, synth, dev, layers, ws, dev_bf16):
         lrkv.decode_step(lay["q"], lay["ak"], lay["av"], lay["bk"], lay["ck"], lay["bv"], lay["cv"], N,
                          out=lay["out"], lse=lay["lse"], workspace=ws)
 
+    # Oja update of both bases of a layer from its 4096-token prefill chunk
+    # (float32 master bases; the bfloat16 copies go to buffers of their own,
+    # so the caches' bases stay as they are)
+    oja = {p: [] for p in (0, 1)}
+    for l, lay in enumerate(layers[:2]):
+        for key in ("bk", "bv"):
+            oja[l].append((lay["xk" if key == "bk" else "xv"], lay[key].float().contiguous(), torch.empty_like(lay[key])))
+    P = lay["xk"].shape[1]
+    oja_ws = torch.empty(max(lrkv.oja_workspace_bytes(B, H, d, b32.shape[2], P) for p in (0, 1)
+                             for _, b32, _ in oja[p]), dtype=torch.uint8, device=dev)
+
+    def oja_layer(i):
+        for x, b32, b16 in oja[i % 2]:
+            lrkv.oja_update(x, b32, 1e-9, basis_bf16=b16, workspace=oja_ws)
+
     lat_us = _timed(torch, latent, 3 * L, warm=L)
     tf_us = _timed(torch, transform_step, 3 * L, warm=L)
     plain_us = _timed(torch, plain_step, 3 * L, warm=L)
+    oja_us = _timed(torch, oja_layer, 20, warm=4)
+    oja_bytes = sum(bm.oja_bytes(B, P, H, d, r) for p in (0, 1) for r in w.ranks(p)) / 2
+    oja_flops = sum(bm.oja_flops(B, P, H, d, r) for p in (0, 1) for r in w.ranks(p)) / 2
     lat_bytes = sum(bm.latent_decode_bytes(B, Hq, H, *w.ranks(p), N) for p in (0, 1)) / 2
     return {"latent_decode_us_per_layer": round(lat_us, 3),
             "latent_decode_GBps": round(lat_bytes / (lat_us * 1e-6) / 1e9, 1),
             "transform_step_us_per_layer": round(tf_us, 3),
             "plain_step_us_per_layer": round(plain_us, 3),
+            "oja_update_us_per_layer": round(oja_us, 3),
+            "oja_update_GBps": round(oja_bytes / (oja_us * 1e-6) / 1e9, 1),
+            "oja_update_TFLOPs": round(oja_flops / (oja_us * 1e-6) / 1e12, 1),
             "note": "same caches and context as the main figure, layers run back to back (no prefill "
-                    "between them); two launches per layer"}
+                    "between them); two launches per layer; the Oja update is of both bases of a layer "
+                    "from its 4096-token prefill chunk (three launches per basis)"}
 
 
 def _timed(torch, fn, iters, warm=3):

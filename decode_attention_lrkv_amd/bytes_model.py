@@ -81,3 +81,17 @@ def decode_flops(batch, n_q_heads, n_ctx, rank_k, rank_v):
 
 def compress_flops(batch, n_tokens, n_kv_heads, head_dim, rank):
     return 2 * batch * n_tokens * n_kv_heads * head_dim * rank
+
+
+def oja_bytes(batch, n_tokens, n_kv_heads, head_dim, rank):
+    """One Oja update: the chunk's bfloat16 token rows in, the float32 basis in
+    and out, its bfloat16 copy out."""
+    return (2 * batch * n_tokens * n_kv_heads * head_dim
+            + (4 + 4 + 2) * n_kv_heads * head_dim * rank)
+
+
+def oja_flops(batch, n_tokens, n_kv_heads, head_dim, rank):
+    """Multiply-adds x 2 of Y = X B, X^T Y and Y^T Y (the update itself, B S2 and the
+    step, is d r (r + 2) per head: negligible)."""
+    n = batch * n_tokens * n_kv_heads
+    return 2 * n * (2 * head_dim * rank + rank * rank)

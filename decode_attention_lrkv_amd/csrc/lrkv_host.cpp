@@ -172,11 +172,13 @@ lrkv_status check_dims(const lrkv_dims* d, lrkv_dtype dt, const char* fn) {
     if (!aligned16(p)) return fail(LRKV_ERR_INVALID_ARGUMENT, "%s: %s is not 16-byte aligned", fn, #p); \
   } while (0)
 
-// Stats workgroups per kv head for an Oja update: one round over the chip,
-// no more than there are 64-token steps.
-int oja_workgroups(int hkv, int64_t tokens) {
+// Stats workgroups per kv head for an Oja update: one round over the chip
+// (two workgroups per compute unit up to rank 64, where two fit), no more
+// than there are 64-token steps.
+int oja_workgroups(int hkv, int rank, int64_t tokens) {
   const int64_t steps = std::max<int64_t>(1, (tokens + 63) / 64);
-  const int64_t per_head = std::max<int64_t>(1, device_cu_count() / std::max(1, hkv));
+  const int per_cu = rank <= 64 ? 2 : 1;
+  const int64_t per_head = std::max<int64_t>(1, (int64_t)per_cu * device_cu_count() / std::max(1, hkv));
   return (int)std::min<int64_t>(std::min<int64_t>(steps, per_head), 65535);
 }
 
@@ -654,7 +656,7 @@ lrkv_status lrkv_decode_attn_hybrid(const void* q, const void* basis_k, const vo
 size_t lrkv_oja_workspace_bytes(int32_t batch, int32_t n_kv_heads, int32_t head_dim, int32_t rank,
                                 int64_t n_tokens) {
   if (batch < 1 || n_kv_heads < 1 || head_dim < 16 || rank < 1 || n_tokens < 0) return 0;
-  const int n_wg = oja_workgroups(n_kv_heads, (int64_t)batch * n_tokens);
+  const int n_wg = oja_workgroups(n_kv_heads, rank, (int64_t)batch * n_tokens);
   return sizeof(float) * oja_workspace_floats(n_kv_heads, head_dim, rank, n_wg);
 }
 
@@ -685,7 +687,7 @@ lrkv_status lrkv_oja_update(const void* x, float* basis, void* basis_bf16, int32
   OjaArgs a{};
   a.x = x; a.basis = basis; a.basis_bf16 = basis_bf16;
   a.hkv = n_kv_heads; a.d = head_dim; a.rank = rank; a.n_tokens = tokens; a.eta = eta;
-  a.n_wg = oja_workgroups(n_kv_heads, tokens);
+  a.n_wg = oja_workgroups(n_kv_heads, rank, tokens);
   a.ws = static_cast<float*>(workspace);
   a.ws_sum = a.ws + oja_workspace_floats(n_kv_heads, head_dim, rank, a.n_wg)
              - (size_t)n_kv_heads * ((size_t)head_dim * oja_rank_pad(rank) + (size_t)oja_rank_pad(rank) * oja_rank_pad(rank));

@@ -5,13 +5,13 @@
 // is kept in float32 (steps of the size Oja's rule takes fall below bfloat16
 // resolution), and a rounded bfloat16 copy is written for the compress and
 // decode calls.  Three launches, all deterministic:
-//   stats   per (run of 64-token steps, kv head).  Each wave takes 16 tokens
-//           of a step and computes their Y on the matrix cores (B split into
-//           high and low bfloat16 parts, so Y keeps float32 accuracy).  X^T
-//           and Y^T (again as high + low parts) go to LDS, and each wave
-//           accumulates its tiles of S1 = X^T Y [d, r] and S2 = Y^T Y [r, r]
-//           on the matrix cores, contracting over the step's 64 tokens.  The
-//           workgroup writes its partial sums.
+//   stats   per (run of 16 W-token steps, kv head).  A step's tokens go to LDS
+//           (as X and X^T); each wave owns some 16-column coefficient blocks,
+//           computes their Y on the matrix cores (B split into high and low
+//           bfloat16 parts, held in registers, so Y keeps float32 accuracy),
+//           stores it (again as high + low parts) and accumulates its columns
+//           of S1 = X^T Y [d, r] and S2 = Y^T Y [r, r], contracting over the
+//           step's tokens.  The workgroup writes its partial sums.
 //   reduce  sums every kv head's partials in a fixed order.
 //   apply   B + eta (S1 - B S2) in float32 per 16-row block of B, written
 //           back to the float32 basis and, rounded to nearest even, to the
@@ -23,65 +23,86 @@ namespace lrkv {
 
 namespace {
 
-constexpr int kOjaWaves = 4;
-constexpr int kOjaStep = 16 * kOjaWaves;   // tokens per step, 16 per wave
-constexpr int kOjaPitchT = kOjaStep + 8;   // bf16 pitch of the token-major LDS rows (144 bytes)
+// W waves per stats workgroup; a step is 16 tokens per wave.  Token-major
+// LDS rows have a pitch of 16 W + 8 bfloat16 (16-byte aligned, and not a
+// multiple of 128 bytes).
+template <int W> constexpr int oja_step() { return 16 * W; }
+template <int W> constexpr int oja_pitch_t() { return 16 * W + 8; }
 
-template <int D, int NB>
+template <int D, int NB, int W>
 struct OjaSmem {
   static constexpr int R = 16 * NB;        // rank padded to whole 16-column blocks
-  uint16_t bt_hi[R][D + 8];                // B^T (row = coefficient), high parts; rows >= rank are zero
-  uint16_t bt_lo[R][D + 8];                // low parts: B - high
-  uint16_t xt[D][kOjaPitchT];              // X^T of the step: [dim][token]
-  uint16_t yt_hi[R][kOjaPitchT];           // Y^T of the step: [coefficient][token]
-  uint16_t yt_lo[R][kOjaPitchT];
+  uint16_t xs[oja_step<W>()][D + 8];       // X of the step, token-major (Y's column operand)
+  uint16_t xt[D][oja_pitch_t<W>()];        // X^T of the step: [dim][token] (S1's row operand)
+  uint16_t yt_hi[R][oja_pitch_t<W>()];     // Y^T of the step: [coefficient][token], high parts
+  uint16_t yt_lo[R][oja_pitch_t<W>()];     // low parts: Y - high
 };
 
 // Per-head partial sums of one stats workgroup: S1 [D][R] then S2 [R][R].
 __host__ __device__ inline int64_t oja_head_floats(int d, int r_pad) { return (int64_t)d * r_pad + (int64_t)r_pad * r_pad; }
 
-template <int D, int NB>
-__global__ __launch_bounds__(256) void oja_stats_kernel(OjaArgs a) {
+// Wave w owns the 16-column coefficient blocks w, w + W, ... (NBW of them at
+// most): it keeps their B^T rows in registers for the whole launch, computes
+// their Y for all tokens of a step, and accumulates their columns of S1 and
+// S2, so each Y operand it reads from LDS serves every row block.  W = 8 for
+// ranks above 64 (one block per wave, registers for two waves per SIMD).
+template <int D, int NB, int W>
+__global__ __launch_bounds__(64 * W) void oja_stats_kernel(OjaArgs a) {
   constexpr int R = 16 * NB;
-  constexpr int DB = D / 64;               // 16-dim blocks of S1 per wave (blocks wave, wave + 4, ...)
-  constexpr int NA = (NB + 3) / 4;         // 16-row blocks of S2 per wave (blocks wave, wave + 4, ...)
-  __shared__ __attribute__((aligned(16))) OjaSmem<D, NB> sm;
+  constexpr int NBW = (NB + W - 1) / W;    // coefficient blocks per wave
+  constexpr int KD = D / 32;               // 32-dim k-steps of Y = X B
+  constexpr int STEP = oja_step<W>();
+  constexpr int UNROLL = W == 4 ? 4 : 2;   // token-block and k-step loops (full unroll at 8 waves spills)
+  __shared__ __attribute__((aligned(16))) OjaSmem<D, NB, W> sm;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int n16 = lane & 15, grp = lane >> 4;
   const int h = blockIdx.y;
   const int r = a.rank;
 
-  // B^T as high and low bfloat16 parts; consecutive threads read consecutive
-  // coefficients of one basis row
-  const float* bs = a.basis + (int64_t)h * D * r;
-  for (int i = tid; i < R * D; i += 256) {
-    const int j = i % R, dd = i / R;
-    const float v = j < r ? bs[dd * r + j] : 0.f;
-    const uint16_t hi = f32_to_bf16(v);
-    sm.bt_hi[j][dd] = hi;
-    sm.bt_lo[j][dd] = f32_to_bf16(v - bf16_to_f32(hi));
+  // this wave's B^T rows as matrix-core row operands, high and low bfloat16
+  // parts: lane (n16, grp) of block k, step c holds B[32 c + 8 grp + e][16 nb + n16]
+  u32x4 bt_hi[NBW][KD], bt_lo[NBW][KD];
+  {
+    const float* bs = a.basis + (int64_t)h * D * r;
+#pragma unroll
+    for (int k = 0; k < NBW; ++k) {
+      const int col = 16 * (wave + W * k) + n16;
+#pragma unroll
+      for (int c = 0; c < KD; ++c) {
+        uint32_t hi[4], lo[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int r0 = 32 * c + 8 * grp + 2 * e;
+          const float v0 = col < r ? bs[r0 * r + col] : 0.f;
+          const float v1 = col < r ? bs[(r0 + 1) * r + col] : 0.f;
+          hi[e] = pack_bf16(v0, v1);
+          lo[e] = pack_bf16(v0 - bf16_lo(hi[e]), v1 - bf16_hi(hi[e]));
+        }
+        bt_hi[k][c] = u32x4{hi[0], hi[1], hi[2], hi[3]};
+        bt_lo[k][c] = u32x4{lo[0], lo[1], lo[2], lo[3]};
+      }
+    }
   }
 
-  f32x4 s1[DB][NB], s2[NA][NB];
+  f32x4 s1[D / 16][NBW], s2[NB][NBW];
 #pragma unroll
-  for (int k = 0; k < DB; ++k)
+  for (int k = 0; k < NBW; ++k) {
 #pragma unroll
-    for (int nb = 0; nb < NB; ++nb) s1[k][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int db = 0; db < D / 16; ++db) s1[db][k] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-  for (int k = 0; k < NA; ++k)
-#pragma unroll
-    for (int nb = 0; nb < NB; ++nb) s2[k][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int na = 0; na < NB; ++na) s2[na][k] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
 
   const int64_t n_tok = a.n_tokens;
-  const int64_t n_steps = (n_tok + kOjaStep - 1) / kOjaStep;
+  const int64_t n_steps = (n_tok + STEP - 1) / STEP;
   const int64_t per_wg = (n_steps + gridDim.x - 1) / gridDim.x;
   const int64_t s_begin = (int64_t)blockIdx.x * per_wg;
   const int64_t s_end = s_begin + per_wg < n_steps ? s_begin + per_wg : n_steps;
 
-  // this wave's 16 tokens of a step as matrix-core operands: lane (n16, grp)
-  // holds token n16's dims 32 c + 8 grp .. + 7; tokens past the end read zero
-  auto load_x = [&](u32x4 (&xa)[D / 32], int64_t step) {
-    const int64_t t0 = step * kOjaStep + 16 * wave;
+  // this wave's 16 tokens of a step as loaded: lane (n16, grp) holds token
+  // n16's dims 32 c + 8 grp .. + 7; tokens past the end read zero
+  auto load_x = [&](u32x4 (&xa)[KD], int64_t step) {
+    const int64_t t0 = step * STEP + 16 * wave;
     const int64_t left = n_tok - t0;
     const int nt = left <= 0 ? 0 : (left < 16 ? (int)left : 16);
     const int64_t t_base = nt > 0 ? t0 : 0;
@@ -90,88 +111,93 @@ __global__ __launch_bounds__(256) void oja_stats_kernel(OjaArgs a) {
     const __amdgpu_buffer_rsrc_t rs = make_rsrc(x, bytes);
     const uint32_t voff = (uint32_t)((n16 * a.hkv * D + 8 * grp) * 2);
 #pragma unroll
-    for (int c = 0; c < D / 32; ++c) xa[c] = buf_load16(rs, voff + 64 * c);
+    for (int c = 0; c < KD; ++c) xa[c] = buf_load16(rs, voff + 64 * c);
   };
 
-  __syncthreads();   // B^T staged
-
-  u32x4 xa[D / 32], xb[D / 32];
+  u32x4 xa[KD], xb[KD];
   if (s_begin < s_end) load_x(xa, s_begin);
   for (int64_t step = s_begin; step < s_end; ++step) {
     if (step + 1 < s_end) load_x(xb, step + 1);
-    // 1. Y^T of this wave's tokens: lane (n16, grp) register i of block nb is
-    //    coefficient 16 nb + 4 grp + i of token n16
-    f32x4 y[NB];
+    // 1. X (token-major) and X^T into LDS, token 16 wave + n16
+    const int tok = 16 * wave + n16;
 #pragma unroll
-    for (int nb = 0; nb < NB; ++nb) {
-      y[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int c = 0; c < D / 32; ++c) {
-        const int k = 32 * c + 8 * grp;
-        y[nb] = mfma_16x16x32(*reinterpret_cast<const u32x4*>(&sm.bt_hi[16 * nb + n16][k]), xa[c], y[nb]);
-        y[nb] = mfma_16x16x32(*reinterpret_cast<const u32x4*>(&sm.bt_lo[16 * nb + n16][k]), xa[c], y[nb]);
-      }
-    }
-    // 2. X^T and Y^T (high, low) of these tokens into LDS, token column 16 wave + n16
-    const int col = 16 * wave + n16;
-#pragma unroll
-    for (int c = 0; c < D / 32; ++c)
+    for (int c = 0; c < KD; ++c) {
+      *reinterpret_cast<u32x4*>(&sm.xs[tok][32 * c + 8 * grp]) = xa[c];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        sm.xt[32 * c + 8 * grp + 2 * e][col] = (uint16_t)(xa[c][e] & 0xFFFFu);
-        sm.xt[32 * c + 8 * grp + 2 * e + 1][col] = (uint16_t)(xa[c][e] >> 16);
-      }
-#pragma unroll
-    for (int nb = 0; nb < NB; ++nb)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float v = y[nb][i];
-        const uint16_t hi = f32_to_bf16(v);
-        sm.yt_hi[16 * nb + 4 * grp + i][col] = hi;
-        sm.yt_lo[16 * nb + 4 * grp + i][col] = f32_to_bf16(v - bf16_to_f32(hi));
-      }
-    __syncthreads();
-    // 3. S1 += X^T Y over the step's 64 tokens: row operand X^T (dim 16 db + n16),
-    //    column operand Y (coefficient 16 nb + n16), k = tokens 32 kk + 8 grp .. + 7
-#pragma unroll
-    for (int k = 0; k < DB; ++k) {
-      const int db = wave + 4 * k;
-#pragma unroll
-      for (int kk = 0; kk < 2; ++kk) {
-        const int t = 32 * kk + 8 * grp;
-        const u32x4 xr = *reinterpret_cast<const u32x4*>(&sm.xt[16 * db + n16][t]);
-#pragma unroll
-        for (int nb = 0; nb < NB; ++nb) {
-          s1[k][nb] = mfma_16x16x32(xr, *reinterpret_cast<const u32x4*>(&sm.yt_hi[16 * nb + n16][t]), s1[k][nb]);
-          s1[k][nb] = mfma_16x16x32(xr, *reinterpret_cast<const u32x4*>(&sm.yt_lo[16 * nb + n16][t]), s1[k][nb]);
-        }
+        sm.xt[32 * c + 8 * grp + 2 * e][tok] = (uint16_t)(xa[c][e] & 0xFFFFu);
+        sm.xt[32 * c + 8 * grp + 2 * e + 1][tok] = (uint16_t)(xa[c][e] >> 16);
       }
     }
-    // 4. S2 += Y^T Y: row operand Y^T (coefficient 16 na + n16), column operand
-    //    Y (coefficient 16 nb + n16); high x high + high x low + low x high
+    __syncthreads();
+    // 2. Y^T of this wave's coefficient blocks for the step's W 16-token
+    //    blocks: lane (n16, grp) register i is coefficient 16 nb + 4 grp + i of
+    //    token 16 tb + n16; stored as high and low parts
+#pragma unroll UNROLL
+    for (int tb = 0; tb < W; ++tb) {
+      u32x4 xo[KD];
 #pragma unroll
-    for (int k = 0; k < NA; ++k) {
-      const int na = wave + 4 * k;
-      if (na < NB) {
+      for (int c = 0; c < KD; ++c) xo[c] = *reinterpret_cast<const u32x4*>(&sm.xs[16 * tb + n16][32 * c + 8 * grp]);
 #pragma unroll
-        for (int kk = 0; kk < 2; ++kk) {
-          const int t = 32 * kk + 8 * grp;
-          const u32x4 ah = *reinterpret_cast<const u32x4*>(&sm.yt_hi[16 * na + n16][t]);
-          const u32x4 al = *reinterpret_cast<const u32x4*>(&sm.yt_lo[16 * na + n16][t]);
+      for (int k = 0; k < NBW; ++k) {
+        const int nb = wave + W * k;
+        if (nb < NB) {
+          f32x4 y = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-          for (int nb = 0; nb < NB; ++nb) {
-            const u32x4 bh = *reinterpret_cast<const u32x4*>(&sm.yt_hi[16 * nb + n16][t]);
-            const u32x4 bl = *reinterpret_cast<const u32x4*>(&sm.yt_lo[16 * nb + n16][t]);
-            s2[k][nb] = mfma_16x16x32(ah, bh, s2[k][nb]);
-            s2[k][nb] = mfma_16x16x32(ah, bl, s2[k][nb]);
-            s2[k][nb] = mfma_16x16x32(al, bh, s2[k][nb]);
+          for (int c = 0; c < KD; ++c) {
+            y = mfma_16x16x32(bt_hi[k][c], xo[c], y);
+            y = mfma_16x16x32(bt_lo[k][c], xo[c], y);
+          }
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const uint16_t hi = f32_to_bf16(y[i]);
+            sm.yt_hi[16 * nb + 4 * grp + i][16 * tb + n16] = hi;
+            sm.yt_lo[16 * nb + 4 * grp + i][16 * tb + n16] = f32_to_bf16(y[i] - bf16_to_f32(hi));
           }
         }
       }
     }
-    __syncthreads();   // the next step rewrites X^T and Y^T
+    __syncthreads();
+    // 3. S1 += X^T Y and S2 += Y^T Y over the step's 16 W tokens, for this
+    //    wave's coefficient columns: k-slots are tokens 32 kk + 8 grp .. + 7
+#pragma unroll UNROLL
+    for (int kk = 0; kk < W / 2; ++kk) {
+      const int t = 32 * kk + 8 * grp;
+      u32x4 bh[NBW], bl[NBW];
 #pragma unroll
-    for (int c = 0; c < D / 32; ++c) xa[c] = xb[c];
+      for (int k = 0; k < NBW; ++k) {
+        const int nb = wave + W * k < NB ? wave + W * k : 0;
+        bh[k] = *reinterpret_cast<const u32x4*>(&sm.yt_hi[16 * nb + n16][t]);
+        bl[k] = *reinterpret_cast<const u32x4*>(&sm.yt_lo[16 * nb + n16][t]);
+      }
+#pragma unroll
+      for (int db = 0; db < D / 16; ++db) {
+        const u32x4 xr = *reinterpret_cast<const u32x4*>(&sm.xt[16 * db + n16][t]);
+#pragma unroll
+        for (int k = 0; k < NBW; ++k) {
+          if (wave + W * k < NB) {
+            s1[db][k] = mfma_16x16x32(xr, bh[k], s1[db][k]);
+            s1[db][k] = mfma_16x16x32(xr, bl[k], s1[db][k]);
+          }
+        }
+      }
+#pragma unroll
+      for (int na = 0; na < NB; ++na) {
+        const u32x4 ah = *reinterpret_cast<const u32x4*>(&sm.yt_hi[16 * na + n16][t]);
+        const u32x4 al = *reinterpret_cast<const u32x4*>(&sm.yt_lo[16 * na + n16][t]);
+#pragma unroll
+        for (int k = 0; k < NBW; ++k) {
+          if (wave + W * k < NB) {
+            s2[na][k] = mfma_16x16x32(ah, bh[k], s2[na][k]);
+            s2[na][k] = mfma_16x16x32(ah, bl[k], s2[na][k]);
+            s2[na][k] = mfma_16x16x32(al, bh[k], s2[na][k]);
+          }
+        }
+      }
+    }
+    __syncthreads();   // the next step rewrites X, X^T and Y^T
+#pragma unroll
+    for (int c = 0; c < KD; ++c) xa[c] = xb[c];
   }
 
   // partial sums of this workgroup (zeros when it had no steps); result lane
@@ -179,19 +205,17 @@ __global__ __launch_bounds__(256) void oja_stats_kernel(OjaArgs a) {
   float* w1 = a.ws + ((int64_t)h * gridDim.x + blockIdx.x) * oja_head_floats(D, R);
   float* w2 = w1 + (int64_t)D * R;
 #pragma unroll
-  for (int k = 0; k < DB; ++k)
+  for (int k = 0; k < NBW; ++k) {
+    const int nb = wave + W * k;
+    if (nb < NB) {
 #pragma unroll
-    for (int nb = 0; nb < NB; ++nb)
+      for (int db = 0; db < D / 16; ++db)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) w1[(16 * (wave + 4 * k) + 4 * grp + i) * R + 16 * nb + n16] = s1[k][nb][i];
+        for (int i = 0; i < 4; ++i) w1[(16 * db + 4 * grp + i) * R + 16 * nb + n16] = s1[db][k][i];
 #pragma unroll
-  for (int k = 0; k < NA; ++k) {
-    const int na = wave + 4 * k;
-    if (na < NB) {
+      for (int na = 0; na < NB; ++na)
 #pragma unroll
-      for (int nb = 0; nb < NB; ++nb)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) w2[(16 * na + 4 * grp + i) * R + 16 * nb + n16] = s2[k][nb][i];
+        for (int i = 0; i < 4; ++i) w2[(16 * na + 4 * grp + i) * R + 16 * nb + n16] = s2[na][k][i];
     }
   }
 }
@@ -247,9 +271,13 @@ size_t oja_workspace_floats(int hkv, int d, int rank, int n_wg) {
   return (size_t)((int64_t)hkv * n_wg * per_head + (int64_t)hkv * per_head);
 }
 
-#define LRKV_OJA_CASE(D, NB)                                                                 \
-  case NB:                                                                                   \
-    hipLaunchKernelGGL((oja_stats_kernel<D, NB>), dim3(a.n_wg, a.hkv), dim3(256), 0, s, a); \
+#define LRKV_OJA_CASE4(D, NB)                                                                   \
+  case NB:                                                                                      \
+    hipLaunchKernelGGL((oja_stats_kernel<D, NB, 4>), dim3(a.n_wg, a.hkv), dim3(256), 0, s, a); \
+    break;
+#define LRKV_OJA_CASE8(D, NB)                                                                   \
+  case NB:                                                                                      \
+    hipLaunchKernelGGL((oja_stats_kernel<D, NB, 8>), dim3(a.n_wg, a.hkv), dim3(512), 0, s, a); \
     break;
 
 hipError_t launch_oja_update(const OjaArgs& a, hipStream_t s) {
@@ -258,13 +286,13 @@ hipError_t launch_oja_update(const OjaArgs& a, hipStream_t s) {
   if (nb < 1 || nb > a.d / 16) return hipErrorInvalidValue;
   if (a.d == 128) {
     switch (nb) {
-      LRKV_OJA_CASE(128, 1) LRKV_OJA_CASE(128, 2) LRKV_OJA_CASE(128, 3) LRKV_OJA_CASE(128, 4)
-      LRKV_OJA_CASE(128, 5) LRKV_OJA_CASE(128, 6) LRKV_OJA_CASE(128, 7) LRKV_OJA_CASE(128, 8)
+      LRKV_OJA_CASE4(128, 1) LRKV_OJA_CASE4(128, 2) LRKV_OJA_CASE4(128, 3) LRKV_OJA_CASE4(128, 4)
+      LRKV_OJA_CASE8(128, 5) LRKV_OJA_CASE8(128, 6) LRKV_OJA_CASE8(128, 7) LRKV_OJA_CASE8(128, 8)
       default: return hipErrorInvalidValue;
     }
   } else {
     switch (nb) {
-      LRKV_OJA_CASE(64, 1) LRKV_OJA_CASE(64, 2) LRKV_OJA_CASE(64, 3) LRKV_OJA_CASE(64, 4)
+      LRKV_OJA_CASE4(64, 1) LRKV_OJA_CASE4(64, 2) LRKV_OJA_CASE4(64, 3) LRKV_OJA_CASE4(64, 4)
       default: return hipErrorInvalidValue;
     }
   }

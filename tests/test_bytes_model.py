@@ -63,3 +63,11 @@ def test_latent_decode_bytes_skip_the_bases():
     # against the full decode (bases read, d-wide query in and output out)
     full = bm.decode_bytes(16, 32, 8, 128, 48, 112, 32768)
     assert full - lat == 2 * 8 * 128 * 160 + 2 * 2 * 16 * 32 * 128 - 2 * 16 * 32 * 160
+
+
+def test_oja_bytes_and_flops_of_the_prefill_chunk():
+    # 16 x 4096 tokens x 8 heads x 128 dims of bf16 in; float32 basis in and out, bf16 copy out
+    assert bm.oja_bytes(16, 4096, 8, 128, 48) == 2 * 16 * 4096 * 8 * 128 + 10 * 8 * 128 * 48
+    # Y = X B and X^T Y: 2 d r each; Y^T Y: r^2; times 2 flops per multiply-add
+    n = 16 * 4096 * 8
+    assert bm.oja_flops(16, 4096, 8, 128, 48) == 2 * n * (2 * 128 * 48 + 48 * 48)
