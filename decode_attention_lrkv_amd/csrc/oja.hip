@@ -13,7 +13,7 @@
 //           of S1 = X^T Y [d, r] and S2 = Y^T Y [r, r], contracting over the
 //           step's tokens.  The workgroup writes its partial sums.
 //   reduce  sums every kv head's partials in a fixed order.
-//   apply   B + eta (S1 - B S2) in float32 per 16-row block of B, written
+//   apply   B + eta (S1 - B S2) in float32 per 4-row block of B, written
 //           back to the float32 basis and, rounded to nearest even, to the
 //           bfloat16 copy.
 #include "lrkv_device.h"
@@ -235,23 +235,25 @@ __global__ __launch_bounds__(256) void oja_reduce_kernel(OjaArgs a, int64_t per_
   *reinterpret_cast<f32x4*>(a.ws_sum + (int64_t)h * per_head + i) = s;
 }
 
-// B <- B + eta (S1 - B S2) for 16 rows of one head's basis.  The rows are
-// staged in LDS before any is written, and no other workgroup touches them.
+// B <- B + eta (S1 - B S2) for kOjaRows rows of one head's basis.  The rows
+// are staged in LDS before any is written, and no other workgroup touches
+// them.
+constexpr int kOjaRows = 4;
 template <int R>
 __global__ __launch_bounds__(256) void oja_apply_kernel(OjaArgs a) {
   __shared__ float s_s2[R][R + 1];
-  __shared__ float s_b[16][R + 1];
-  const int h = blockIdx.y, row0 = 16 * blockIdx.x;
+  __shared__ float s_b[kOjaRows][R + 1];
+  const int h = blockIdx.y, row0 = kOjaRows * blockIdx.x;
   const int tid = threadIdx.x;
   const int r = a.rank, d = a.d;
   const int64_t per_head = oja_head_floats(d, R);
   const float* sum = a.ws_sum + (int64_t)h * per_head;
   float* bs = a.basis + (int64_t)h * d * r;
   for (int i = tid; i < R * R; i += 256) s_s2[i / R][i % R] = sum[(int64_t)d * R + i];
-  for (int i = tid; i < 16 * r; i += 256) s_b[i / r][i % r] = bs[(int64_t)(row0 + i / r) * r + i % r];
+  for (int i = tid; i < kOjaRows * r; i += 256) s_b[i / r][i % r] = bs[(int64_t)(row0 + i / r) * r + i % r];
   __syncthreads();
   uint16_t* bb = static_cast<uint16_t*>(a.basis_bf16);
-  for (int i = tid; i < 16 * r; i += 256) {
+  for (int i = tid; i < kOjaRows * r; i += 256) {
     const int rr = i / r, j = i % r;
     float dot = 0.f;
     for (int k = 0; k < r; ++k) dot = fmaf(s_b[rr][k], s_s2[k][j], dot);
@@ -303,7 +305,7 @@ hipError_t launch_oja_update(const OjaArgs& a, hipStream_t s) {
   hipLaunchKernelGGL(oja_reduce_kernel, rgrid, dim3(256), 0, s, a, per_head);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const dim3 agrid((unsigned)(a.d / 16), a.hkv);
+  const dim3 agrid((unsigned)(a.d / kOjaRows), a.hkv);
   switch (nb) {
     case 1: hipLaunchKernelGGL(oja_apply_kernel<16>, agrid, dim3(256), 0, s, a); break;
     case 2: hipLaunchKernelGGL(oja_apply_kernel<32>, agrid, dim3(256), 0, s, a); break;
