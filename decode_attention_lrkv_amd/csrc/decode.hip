@@ -37,8 +37,6 @@ constexpr int kWaves = 4;
 template <typename T>
 __device__ __forceinline__ float load_f(const T* p, int64_t i);
 template <>
-__device__ __forceinline__ float load_f<uint16_t>(const uint16_t* p, int64_t i) { return bf16_to_f32(p[i]); }
-template <>
 __device__ __forceinline__ float load_f<float>(const float* p, int64_t i) { return p[i]; }
 
 __device__ __forceinline__ void store_partial(float* p, float v) { *p = v; }
@@ -766,8 +764,8 @@ void split_bf16_latent_kernel(SplitArgs a) {
 // are divided between the low-rank rows and the full-rank side list (r = d,
 // no fold and no lift, single-buffered so that both fit two waves per SIMD)
 // in proportion to the bytes each list holds, from the counts on the device;
-// within a list, each wave takes an equal run of chunks.  Every workgroup
-// writes partial blockIdx.x.
+// within a list, each workgroup takes an equal run of chunks, which its four
+// waves take in turn.  Every workgroup writes partial blockIdx.x.
 template <int KC, int VB, int SKC, int SVB>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void split_bf16_hybrid_kernel(SplitArgs lr, SplitArgs side) {
@@ -950,8 +948,8 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeArgs a) {
 
 hipError_t launch_split_bf16(const SplitArgs& a, hipStream_t s) {
   // one workgroup per partial; with k_new set, the last workgroup of each
-  // (b, kv head) also appends, and the appended token's partial is the extra
-  // last one
+  // (b, kv head) also appends (adding the token to its own partial), and the
+  // token's slot is the extra last one, left empty
   const dim3 grid(a.k_new ? a.n_parts - 1 : a.n_parts, a.hkv, a.batch);
   const int kc = (a.rk + 31) / 32, vb = (a.rv + 15) / 16;
   if (a.basis_k == nullptr || a.basis_v == nullptr || (a.enc_k && !a.k_new)) return hipErrorInvalidValue;
