@@ -142,3 +142,35 @@ def test_oja_repeated_steps_track_the_principal_subspace():
     s = np.linalg.svd(top.T @ np.linalg.qr(b_gpu)[0], compute_uv=False)
     assert np.sqrt(max(0.0, 1.0 - s.min() ** 2)) < 0.1
     assert np.abs(b_gpu - ref[0]).max() < 1e-4 * np.abs(ref[0]).max()
+
+
+def test_oja_graph_replays_equal_eager_steps():
+    """A captured update replayed four times (with unrelated eager work
+    between replays) gives, bit for bit, the bases of four eager updates."""
+    w = synth.scaled(synth.LLAMA_LAYER, batch=2, n_kv_heads=2, ranks_even=(96, 96))
+    x = to_dev(_tokens(w, 0, "k", 300), "bf16")
+    b0 = torch.from_numpy(synth.basis(w, 0, "k").exact.astype(np.float32)).to(DEV)
+    ws = torch.zeros(lrkv.oja_workspace_bytes(2, 2, 128, 96, 300), dtype=torch.uint8, device=DEV)
+    eager = b0.clone()
+    eager_bf = []
+    for _ in range(4):
+        eager_bf.append(lrkv.oja_update(x, eager, 1e-3, workspace=ws).clone())
+    torch.cuda.synchronize()
+    basis = b0.clone()
+    bf = torch.empty_like(eager_bf[0])
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        lrkv.oja_update(x, basis.clone(), 1e-3, basis_bf16=bf, workspace=ws)   # warm up on the capture stream
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        lrkv.oja_update(x, basis, 1e-3, basis_bf16=bf, workspace=ws)
+    basis.copy_(b0)
+    torch.cuda.synchronize()
+    for i in range(4):
+        bf.zero_()
+        _ = (x.float() * 2).sum()                       # unrelated eager work between replays
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(bf.view(torch.int16), eager_bf[i].view(torch.int16)), f"replay {i}"
+    assert torch.equal(basis, eager)
