@@ -10,8 +10,9 @@
 //           computes their Y on the matrix cores (B split into high and low
 //           bfloat16 parts, held in registers, so Y keeps float32 accuracy),
 //           stores it (again as high + low parts) and accumulates its columns
-//           of S1 = X^T Y [d, r] and S2 = Y^T Y [r, r], contracting over the
-//           step's tokens.  The workgroup writes its partial sums.
+//           of S1 = X^T Y [d, r] and its half of the symmetric S2 = Y^T Y
+//           [r, r], contracting over the step's tokens.  The workgroup writes
+//           its partial sums.
 //   reduce  sums every kv head's partials in a fixed order.
 //   apply   B + eta (S1 - B S2) in float32 per 4-row block of B, written
 //           back to the float32 basis and, rounded to nearest even, to the
@@ -38,7 +39,19 @@ struct OjaSmem {
   uint16_t yt_lo[R][oja_pitch_t<W>()];     // low parts: Y - high
 };
 
-// Per-head partial sums of one stats workgroup: S1 [D][R] then S2 [R][R].
+// S2 = Y^T Y is symmetric, so of its 16 x 16 tiles (row block na, column
+// block nb) only one of each mirrored pair is formed: the tiles
+// ((nb + j) mod NB, nb) for j < NB / 2 + 1, the last of them (j = NB / 2,
+// its own mirror when NB is even) only for nb < NB / 2.  Every unordered pair
+// of blocks is then formed exactly once, and each column block forms about
+// half a column.  The apply step reads the others transposed.
+__host__ __device__ constexpr bool oja_s2_formed(int na, int nb, int nb_total) {
+  return ((na - nb + nb_total) % nb_total) < (nb_total + 1) / 2 ||
+         (nb_total % 2 == 0 && (na - nb + nb_total) % nb_total == nb_total / 2 && nb < nb_total / 2);
+}
+
+// Per-head partial sums of one stats workgroup: S1 [D][R] then S2 [R][R]
+// (the tiles oja_s2_formed names; the others are not written).
 __host__ __device__ inline int64_t oja_head_floats(int d, int r_pad) { return (int64_t)d * r_pad + (int64_t)r_pad * r_pad; }
 
 // Wave w owns the 16-column coefficient blocks w, w + W, ... (NBW of them at
@@ -84,13 +97,14 @@ __global__ __launch_bounds__(64 * W) void oja_stats_kernel(OjaArgs a) {
     }
   }
 
-  f32x4 s1[D / 16][NBW], s2[NB][NBW];
+  constexpr int NJ = NB / 2 + 1;            // S2 tiles per column block: row blocks (nb + j) mod NB
+  f32x4 s1[D / 16][NBW], s2[NJ][NBW];
 #pragma unroll
   for (int k = 0; k < NBW; ++k) {
 #pragma unroll
     for (int db = 0; db < D / 16; ++db) s1[db][k] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int na = 0; na < NB; ++na) s2[na][k] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < NJ; ++j) s2[j][k] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
 
   const int64_t n_tok = a.n_tokens;
@@ -182,15 +196,19 @@ __global__ __launch_bounds__(64 * W) void oja_stats_kernel(OjaArgs a) {
         }
       }
 #pragma unroll
-      for (int na = 0; na < NB; ++na) {
-        const u32x4 ah = *reinterpret_cast<const u32x4*>(&sm.yt_hi[16 * na + n16][t]);
-        const u32x4 al = *reinterpret_cast<const u32x4*>(&sm.yt_lo[16 * na + n16][t]);
+      for (int k = 0; k < NBW; ++k) {
+        const int nb = wave + W * k;
+        if (nb < NB) {
 #pragma unroll
-        for (int k = 0; k < NBW; ++k) {
-          if (wave + W * k < NB) {
-            s2[na][k] = mfma_16x16x32(ah, bh[k], s2[na][k]);
-            s2[na][k] = mfma_16x16x32(ah, bl[k], s2[na][k]);
-            s2[na][k] = mfma_16x16x32(al, bh[k], s2[na][k]);
+          for (int j = 0; j < NJ; ++j) {
+            const int na = (nb + j) % NB;
+            if (oja_s2_formed(na, nb, NB)) {
+              const u32x4 ah = *reinterpret_cast<const u32x4*>(&sm.yt_hi[16 * na + n16][t]);
+              const u32x4 al = *reinterpret_cast<const u32x4*>(&sm.yt_lo[16 * na + n16][t]);
+              s2[j][k] = mfma_16x16x32(ah, bh[k], s2[j][k]);
+              s2[j][k] = mfma_16x16x32(ah, bl[k], s2[j][k]);
+              s2[j][k] = mfma_16x16x32(al, bh[k], s2[j][k]);
+            }
           }
         }
       }
@@ -213,9 +231,13 @@ __global__ __launch_bounds__(64 * W) void oja_stats_kernel(OjaArgs a) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) w1[(16 * db + 4 * grp + i) * R + 16 * nb + n16] = s1[db][k][i];
 #pragma unroll
-      for (int na = 0; na < NB; ++na)
+      for (int j = 0; j < NJ; ++j) {
+        const int na = (nb + j) % NB;
+        if (oja_s2_formed(na, nb, NB)) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) w2[(16 * na + 4 * grp + i) * R + 16 * nb + n16] = s2[na][k][i];
+          for (int i = 0; i < 4; ++i) w2[(16 * na + 4 * grp + i) * R + 16 * nb + n16] = s2[j][k][i];
+        }
+      }
     }
   }
 }
@@ -249,7 +271,11 @@ __global__ __launch_bounds__(256) void oja_apply_kernel(OjaArgs a) {
   const int64_t per_head = oja_head_floats(d, R);
   const float* sum = a.ws_sum + (int64_t)h * per_head;
   float* bs = a.basis + (int64_t)h * d * r;
-  for (int i = tid; i < R * R; i += 256) s_s2[i / R][i % R] = sum[(int64_t)d * R + i];
+  // tiles that were not formed are the transposes of their mirrors
+  for (int i = tid; i < R * R; i += 256) {
+    const int k = i / R, j = i % R;
+    s_s2[k][j] = oja_s2_formed(k / 16, j / 16, R / 16) ? sum[(int64_t)d * R + i] : sum[(int64_t)d * R + j * R + k];
+  }
   for (int i = tid; i < kOjaRows * r; i += 256) s_b[i / r][i % r] = bs[(int64_t)(row0 + i / r) * r + i % r];
   __syncthreads();
   uint16_t* bb = static_cast<uint16_t*>(a.basis_bf16);
