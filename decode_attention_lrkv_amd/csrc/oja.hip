@@ -249,6 +249,8 @@ __global__ __launch_bounds__(256) void oja_reduce_kernel(OjaArgs a, int64_t per_
   if (i >= per_head) return;
   f32x4 s = f32x4{0.f, 0.f, 0.f, 0.f};
   const float* src = a.ws + (int64_t)h * a.n_wg * per_head + i;
+  // the loads of eight partials in flight; the sum keeps workgroup order
+#pragma unroll 8
   for (int w = 0; w < a.n_wg; ++w) {
     const f32x4 v = *reinterpret_cast<const f32x4*>(src + (int64_t)w * per_head);
 #pragma unroll
@@ -281,8 +283,12 @@ __global__ __launch_bounds__(256) void oja_apply_kernel(OjaArgs a) {
   uint16_t* bb = static_cast<uint16_t*>(a.basis_bf16);
   for (int i = tid; i < kOjaRows * r; i += 256) {
     const int rr = i / r, j = i % r;
-    float dot = 0.f;
-    for (int k = 0; k < r; ++k) dot = fmaf(s_b[rr][k], s_s2[k][j], dot);
+    // four partial sums (r is a multiple of 8): no single dependent chain
+    float d4[4] = {0.f, 0.f, 0.f, 0.f};
+    for (int k = 0; k < r; k += 4)
+#pragma unroll
+      for (int u = 0; u < 4; ++u) d4[u] = fmaf(s_b[rr][k + u], s_s2[k + u][j], d4[u]);
+    const float dot = (d4[0] + d4[1]) + (d4[2] + d4[3]);
     const float v = s_b[rr][j] + a.eta * (sum[(int64_t)(row0 + rr) * R + j] - dot);
     const int64_t o = (int64_t)(row0 + rr) * r + j;
     bs[o] = v;
