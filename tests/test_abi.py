@@ -208,7 +208,8 @@ def test_missing_library_fails_loudly():
         "for call in (lambda: lrkv.library(),\n"
         "             lambda: lrkv.decode_workspace_bytes(1, 8, 2, 128, 32, 64, 256, 100),\n"
         "             lambda: lrkv.decode_attn_latent(torch.zeros(1, 8, 32), torch.zeros(1, 2, 256, 32),\n"
-        "                                             torch.zeros(1, 2, 32, 64, 8), 100, 128)):\n"
+        "                                             torch.zeros(1, 2, 32, 64, 8), 100, 128),\n"
+        "             lambda: lrkv.oja_workspace_bytes(1, 2, 128, 32, 64)):\n"
         "    try:\n"
         "        call()\n"
         "    except lrkv.LrkvError as e:\n"
@@ -218,3 +219,10 @@ def test_missing_library_fails_loudly():
         "print('ok')\n")
     r = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, cwd=ROOT)
     assert r.returncode == 0 and r.stdout.strip() == "ok", r.stdout + r.stderr
+
+
+def test_build_compiles_every_source():
+    """Every kernel and host source in csrc/ goes into the library."""
+    from decode_attention_lrkv_amd import build as B
+    on_disk = sorted(f for f in os.listdir(B.CSRC) if f.endswith((".hip", ".cpp")))
+    assert sorted(B.SOURCES) == on_disk
