@@ -41,10 +41,12 @@ struct OjaSmem {
 
 // S2 = Y^T Y is symmetric, so of its 16 x 16 tiles (row block na, column
 // block nb) only one of each mirrored pair is formed: the tiles
-// ((nb + j) mod NB, nb) for j < NB / 2 + 1, the last of them (j = NB / 2,
-// its own mirror when NB is even) only for nb < NB / 2.  Every unordered pair
-// of blocks is then formed exactly once, and each column block forms about
-// half a column.  The apply step reads the others transposed.
+// ((nb + j) mod NB, nb) for j < NB / 2 + 1; when NB is even the tile at
+// j = NB / 2 has its mirror at j = NB / 2 too, so it is formed only for
+// nb < NB / 2.  Every unordered pair of blocks is then formed exactly once,
+// and each column block forms about half a column.  Tiles that are not
+// formed hold no partial sums (their reduced values are never read); the
+// apply step reads them transposed from their mirrors.
 __host__ __device__ constexpr bool oja_s2_formed(int na, int nb, int nb_total) {
   return ((na - nb + nb_total) % nb_total) < (nb_total + 1) / 2 ||
          (nb_total % 2 == 0 && (na - nb + nb_total) % nb_total == nb_total / 2 && nb < nb_total / 2);
