@@ -6,7 +6,8 @@
 // resolution), and a rounded bfloat16 copy is written for the compress and
 // decode calls.  Three launches, all deterministic:
 //   stats   per (run of 16 W-token steps, kv head).  A step's tokens go to LDS
-//           (as X and X^T); each wave owns some 16-column coefficient blocks,
+//           (as X, and as X^T transposed on the matrix cores), loaded three
+//           steps ahead; each wave owns some 16-column coefficient blocks,
 //           computes their Y on the matrix cores (B split into high and low
 //           bfloat16 parts, held in registers, so Y keeps float32 accuracy),
 //           stores it (again as high + low parts) and accumulates its columns
@@ -33,7 +34,7 @@ template <int W> constexpr int oja_pitch_t() { return 16 * W + 8; }
 template <int D, int NB, int W>
 struct OjaSmem {
   static constexpr int R = 16 * NB;        // rank padded to whole 16-column blocks
-  uint16_t xs[oja_step<W>()][D + 8];       // X of the step, token-major (Y's column operand)
+  uint16_t xs[oja_step<W>()][D + 8];       // X of the step, token-major (Y's row operand)
   uint16_t xt[D][oja_pitch_t<W>()];        // X^T of the step: [dim][token] (S1's row operand)
   uint16_t yt_hi[R][oja_pitch_t<W>()];     // Y^T of the step: [coefficient][token], high parts
   uint16_t yt_lo[R][oja_pitch_t<W>()];     // low parts: Y - high
@@ -130,45 +131,78 @@ __global__ __launch_bounds__(64 * W) void oja_stats_kernel(OjaArgs a) {
     for (int c = 0; c < KD; ++c) xa[c] = buf_load16(rs, voff + 64 * c);
   };
 
-  u32x4 xa[KD], xb[KD];
-  if (s_begin < s_end) load_x(xa, s_begin);
-  for (int64_t step = s_begin; step < s_end; ++step) {
-    if (step + 1 < s_end) load_x(xb, step + 1);
-    // 1. X (token-major) and X^T into LDS, token 16 wave + n16
+  // 32 x 16 slices of the identity as column operands: lane (n16, grp) slot
+  // e of slice hf is 1 where 8 grp + e = 16 hf + n16
+  u32x4 eye[2];
+#pragma unroll
+  for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      eye[hf][q] = (8 * grp + 2 * q == 16 * hf + n16 ? 0x3F80u : 0u) |
+                   (8 * grp + 2 * q + 1 == 16 * hf + n16 ? 0x3F800000u : 0u);
+  // only waves that own a coefficient block take part in Y, S1 and S2
+  const bool owns = wave < NB;
+
+  // A step's tokens are loaded kAhead steps before it runs, into a ring of
+  // kAhead + 1 register buffers that the loop below rotates by name (a copy
+  // between buffers would wait for the newest load).
+  constexpr int kAhead = 3;
+  static_assert(kAhead == 3, "the ring below has four buffers");
+  u32x4 x0[KD], x1[KD], x2[KD], x3[KD];
+  if (s_begin < s_end) load_x(x0, s_begin);
+  if (s_begin + 1 < s_end) load_x(x1, s_begin + 1);
+  if (s_begin + 2 < s_end) load_x(x2, s_begin + 2);
+  auto run_step = [&](const u32x4 (&xa)[KD], u32x4 (&ahead)[KD], int64_t step) {
+    if (step + kAhead < s_end) load_x(ahead, step + kAhead);
+    // 1. X (token-major) and X^T into LDS.  The wave's own 16 tokens are
+    //    transposed on the matrix cores: X times a slice of the identity puts
+    //    dim 32 c + 16 hf + n16 of tokens 4 grp .. + 3 in lane (n16, grp)
+    //    (exactly for finite tokens: each sum is one product by one and the
+    //    rest products by zero), so
+    //    X^T is stored four tokens at a time
     const int tok = 16 * wave + n16;
 #pragma unroll
     for (int c = 0; c < KD; ++c) {
       *reinterpret_cast<u32x4*>(&sm.xs[tok][32 * c + 8 * grp]) = xa[c];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        sm.xt[32 * c + 8 * grp + 2 * e][tok] = (uint16_t)(xa[c][e] & 0xFFFFu);
-        sm.xt[32 * c + 8 * grp + 2 * e + 1][tok] = (uint16_t)(xa[c][e] >> 16);
+      for (int hf = 0; hf < 2; ++hf) {
+        const f32x4 t = mfma_16x16x32(xa[c], eye[hf], f32x4{0.f, 0.f, 0.f, 0.f});
+        const u32x2 w = u32x2{(__float_as_uint(t[0]) >> 16) | (__float_as_uint(t[1]) & 0xFFFF0000u),
+                              (__float_as_uint(t[2]) >> 16) | (__float_as_uint(t[3]) & 0xFFFF0000u)};
+        *reinterpret_cast<u32x2*>(&sm.xt[32 * c + 16 * hf + n16][16 * wave + 4 * grp]) = w;
       }
     }
     __syncthreads();
-    // 2. Y^T of this wave's coefficient blocks for the step's W 16-token
-    //    blocks: lane (n16, grp) register i is coefficient 16 nb + 4 grp + i of
-    //    token 16 tb + n16; stored as high and low parts
+    // 2. Y of this wave's coefficient blocks for the step's W 16-token
+    //    blocks, with the tokens as rows: lane (n16, grp) register i is
+    //    coefficient 16 nb + n16 of token 16 tb + 4 grp + i, so its Y^T row
+    //    is stored four tokens at a time, as high and low parts
+    if (owns) {
 #pragma unroll UNROLL
-    for (int tb = 0; tb < W; ++tb) {
-      u32x4 xo[KD];
+      for (int tb = 0; tb < W; ++tb) {
+        u32x4 xo[KD];
 #pragma unroll
-      for (int c = 0; c < KD; ++c) xo[c] = *reinterpret_cast<const u32x4*>(&sm.xs[16 * tb + n16][32 * c + 8 * grp]);
+        for (int c = 0; c < KD; ++c) xo[c] = *reinterpret_cast<const u32x4*>(&sm.xs[16 * tb + n16][32 * c + 8 * grp]);
 #pragma unroll
-      for (int k = 0; k < NBW; ++k) {
-        const int nb = wave + W * k;
-        if (nb < NB) {
-          f32x4 y = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int k = 0; k < NBW; ++k) {
+          const int nb = wave + W * k;
+          if (nb < NB) {
+            f32x4 y = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-          for (int c = 0; c < KD; ++c) {
-            y = mfma_16x16x32(bt_hi[k][c], xo[c], y);
-            y = mfma_16x16x32(bt_lo[k][c], xo[c], y);
-          }
+            for (int c = 0; c < KD; ++c) {
+              y = mfma_16x16x32(xo[c], bt_hi[k][c], y);
+              y = mfma_16x16x32(xo[c], bt_lo[k][c], y);
+            }
+            uint32_t hi[4], lo[4];
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const uint16_t hi = f32_to_bf16(y[i]);
-            sm.yt_hi[16 * nb + 4 * grp + i][16 * tb + n16] = hi;
-            sm.yt_lo[16 * nb + 4 * grp + i][16 * tb + n16] = f32_to_bf16(y[i] - bf16_to_f32(hi));
+            for (int i = 0; i < 4; ++i) {
+              hi[i] = f32_to_bf16(y[i]);
+              lo[i] = f32_to_bf16(y[i] - bf16_to_f32((uint16_t)hi[i]));
+            }
+            *reinterpret_cast<u32x2*>(&sm.yt_hi[16 * nb + n16][16 * tb + 4 * grp]) =
+                u32x2{hi[0] | (hi[1] << 16), hi[2] | (hi[3] << 16)};
+            *reinterpret_cast<u32x2*>(&sm.yt_lo[16 * nb + n16][16 * tb + 4 * grp]) =
+                u32x2{lo[0] | (lo[1] << 16), lo[2] | (lo[3] << 16)};
           }
         }
       }
@@ -176,48 +210,54 @@ __global__ __launch_bounds__(64 * W) void oja_stats_kernel(OjaArgs a) {
     __syncthreads();
     // 3. S1 += X^T Y and S2 += Y^T Y over the step's 16 W tokens, for this
     //    wave's coefficient columns: k-slots are tokens 32 kk + 8 grp .. + 7
+    if (owns) {
 #pragma unroll UNROLL
-    for (int kk = 0; kk < W / 2; ++kk) {
-      const int t = 32 * kk + 8 * grp;
-      u32x4 bh[NBW], bl[NBW];
-#pragma unroll
-      for (int k = 0; k < NBW; ++k) {
-        const int nb = wave + W * k < NB ? wave + W * k : 0;
-        bh[k] = *reinterpret_cast<const u32x4*>(&sm.yt_hi[16 * nb + n16][t]);
-        bl[k] = *reinterpret_cast<const u32x4*>(&sm.yt_lo[16 * nb + n16][t]);
-      }
-#pragma unroll
-      for (int db = 0; db < D / 16; ++db) {
-        const u32x4 xr = *reinterpret_cast<const u32x4*>(&sm.xt[16 * db + n16][t]);
+      for (int kk = 0; kk < W / 2; ++kk) {
+        const int t = 32 * kk + 8 * grp;
+        u32x4 bh[NBW], bl[NBW];
 #pragma unroll
         for (int k = 0; k < NBW; ++k) {
-          if (wave + W * k < NB) {
-            s1[db][k] = mfma_16x16x32(xr, bh[k], s1[db][k]);
-            s1[db][k] = mfma_16x16x32(xr, bl[k], s1[db][k]);
+          const int nb = wave + W * k < NB ? wave + W * k : 0;
+          bh[k] = *reinterpret_cast<const u32x4*>(&sm.yt_hi[16 * nb + n16][t]);
+          bl[k] = *reinterpret_cast<const u32x4*>(&sm.yt_lo[16 * nb + n16][t]);
+        }
+#pragma unroll
+        for (int db = 0; db < D / 16; ++db) {
+          const u32x4 xr = *reinterpret_cast<const u32x4*>(&sm.xt[16 * db + n16][t]);
+#pragma unroll
+          for (int k = 0; k < NBW; ++k) {
+            if (wave + W * k < NB) {
+              s1[db][k] = mfma_16x16x32(xr, bh[k], s1[db][k]);
+              s1[db][k] = mfma_16x16x32(xr, bl[k], s1[db][k]);
+            }
           }
         }
-      }
 #pragma unroll
-      for (int k = 0; k < NBW; ++k) {
-        const int nb = wave + W * k;
-        if (nb < NB) {
+        for (int k = 0; k < NBW; ++k) {
+          const int nb = wave + W * k;
+          if (nb < NB) {
 #pragma unroll
-          for (int j = 0; j < NJ; ++j) {
-            const int na = (nb + j) % NB;
-            if (oja_s2_formed(na, nb, NB)) {
-              const u32x4 ah = *reinterpret_cast<const u32x4*>(&sm.yt_hi[16 * na + n16][t]);
-              const u32x4 al = *reinterpret_cast<const u32x4*>(&sm.yt_lo[16 * na + n16][t]);
-              s2[j][k] = mfma_16x16x32(ah, bh[k], s2[j][k]);
-              s2[j][k] = mfma_16x16x32(ah, bl[k], s2[j][k]);
-              s2[j][k] = mfma_16x16x32(al, bh[k], s2[j][k]);
+            for (int j = 0; j < NJ; ++j) {
+              const int na = (nb + j) % NB;
+              if (oja_s2_formed(na, nb, NB)) {
+                const u32x4 ah = *reinterpret_cast<const u32x4*>(&sm.yt_hi[16 * na + n16][t]);
+                const u32x4 al = *reinterpret_cast<const u32x4*>(&sm.yt_lo[16 * na + n16][t]);
+                s2[j][k] = mfma_16x16x32(ah, bh[k], s2[j][k]);
+                s2[j][k] = mfma_16x16x32(ah, bl[k], s2[j][k]);
+                s2[j][k] = mfma_16x16x32(al, bh[k], s2[j][k]);
+              }
             }
           }
         }
       }
     }
     __syncthreads();   // the next step rewrites X, X^T and Y^T
-#pragma unroll
-    for (int c = 0; c < KD; ++c) xa[c] = xb[c];
+  };
+  for (int64_t step = s_begin; step < s_end; step += kAhead + 1) {
+    run_step(x0, x3, step);
+    if (step + 1 < s_end) run_step(x1, x0, step + 1);
+    if (step + 2 < s_end) run_step(x2, x1, step + 2);
+    if (step + 3 < s_end) run_step(x3, x2, step + 3);
   }
 
   // partial sums of this workgroup (zeros when it had no steps); result lane
