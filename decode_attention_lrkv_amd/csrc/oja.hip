@@ -74,6 +74,15 @@ __global__ __launch_bounds__(64 * W) void oja_stats_kernel(OjaArgs a) {
   const int n16 = lane & 15, grp = lane >> 4;
   const int h = blockIdx.y;
   const int r = a.rank;
+  // With fewer coefficient blocks than waves (W a multiple of NB), the
+  // G = W / NB waves of a block share its work: wave w takes block w mod NB,
+  // and of the token blocks, S1 row blocks and S2 tiles of that block the
+  // ones numbered part, part + G, ... (part = w / NB).
+  constexpr int G = (NB < W && W % NB == 0) ? W / NB : 1;
+  constexpr int DBW = D / 16 / G;           // S1 row blocks per wave
+  constexpr int NJW = (NB / 2 + G) / G;     // S2 tiles per wave and block
+  const int part = G > 1 ? wave / NB : 0;
+  const int bw = G > 1 ? wave % NB : wave;  // the wave's first coefficient block
 
   // this wave's B^T rows as matrix-core row operands, high and low bfloat16
   // parts: lane (n16, grp) of block k, step c holds B[32 c + 8 grp + e][16 nb + n16]
@@ -82,7 +91,7 @@ __global__ __launch_bounds__(64 * W) void oja_stats_kernel(OjaArgs a) {
     const float* bs = a.basis + (int64_t)h * D * r;
 #pragma unroll
     for (int k = 0; k < NBW; ++k) {
-      const int col = 16 * (wave + W * k) + n16;
+      const int col = 16 * (bw + W * k) + n16;
 #pragma unroll
       for (int c = 0; c < KD; ++c) {
         uint32_t hi[4], lo[4];
@@ -101,13 +110,13 @@ __global__ __launch_bounds__(64 * W) void oja_stats_kernel(OjaArgs a) {
   }
 
   constexpr int NJ = NB / 2 + 1;            // S2 tiles per column block: row blocks (nb + j) mod NB
-  f32x4 s1[D / 16][NBW], s2[NJ][NBW];
+  f32x4 s1[DBW][NBW], s2[NJW][NBW];
 #pragma unroll
   for (int k = 0; k < NBW; ++k) {
 #pragma unroll
-    for (int db = 0; db < D / 16; ++db) s1[db][k] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int i = 0; i < DBW; ++i) s1[i][k] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int j = 0; j < NJ; ++j) s2[j][k] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int jj = 0; jj < NJW; ++jj) s2[jj][k] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
 
   const int64_t n_tok = a.n_tokens;
@@ -141,7 +150,7 @@ __global__ __launch_bounds__(64 * W) void oja_stats_kernel(OjaArgs a) {
       eye[hf][q] = (8 * grp + 2 * q == 16 * hf + n16 ? 0x3F80u : 0u) |
                    (8 * grp + 2 * q + 1 == 16 * hf + n16 ? 0x3F800000u : 0u);
   // only waves that own a coefficient block take part in Y, S1 and S2
-  const bool owns = wave < NB;
+  const bool owns = bw < NB;
 
   // A step's tokens are loaded kAhead steps before it runs, into a ring of
   // kAhead + 1 register buffers that the loop below rotates by name (a copy
@@ -179,13 +188,14 @@ __global__ __launch_bounds__(64 * W) void oja_stats_kernel(OjaArgs a) {
     //    is stored four tokens at a time, as high and low parts
     if (owns) {
 #pragma unroll UNROLL
-      for (int tb = 0; tb < W; ++tb) {
+      for (int ti = 0; ti < W / G; ++ti) {
+        const int tb = part + G * ti;
         u32x4 xo[KD];
 #pragma unroll
         for (int c = 0; c < KD; ++c) xo[c] = *reinterpret_cast<const u32x4*>(&sm.xs[16 * tb + n16][32 * c + 8 * grp]);
 #pragma unroll
         for (int k = 0; k < NBW; ++k) {
-          const int nb = wave + W * k;
+          const int nb = bw + W * k;
           if (nb < NB) {
             f32x4 y = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -217,34 +227,36 @@ __global__ __launch_bounds__(64 * W) void oja_stats_kernel(OjaArgs a) {
         u32x4 bh[NBW], bl[NBW];
 #pragma unroll
         for (int k = 0; k < NBW; ++k) {
-          const int nb = wave + W * k < NB ? wave + W * k : 0;
+          const int nb = bw + W * k < NB ? bw + W * k : 0;
           bh[k] = *reinterpret_cast<const u32x4*>(&sm.yt_hi[16 * nb + n16][t]);
           bl[k] = *reinterpret_cast<const u32x4*>(&sm.yt_lo[16 * nb + n16][t]);
         }
 #pragma unroll
-        for (int db = 0; db < D / 16; ++db) {
+        for (int i = 0; i < DBW; ++i) {
+          const int db = part + G * i;
           const u32x4 xr = *reinterpret_cast<const u32x4*>(&sm.xt[16 * db + n16][t]);
 #pragma unroll
           for (int k = 0; k < NBW; ++k) {
-            if (wave + W * k < NB) {
-              s1[db][k] = mfma_16x16x32(xr, bh[k], s1[db][k]);
-              s1[db][k] = mfma_16x16x32(xr, bl[k], s1[db][k]);
+            if (bw + W * k < NB) {
+              s1[i][k] = mfma_16x16x32(xr, bh[k], s1[i][k]);
+              s1[i][k] = mfma_16x16x32(xr, bl[k], s1[i][k]);
             }
           }
         }
 #pragma unroll
         for (int k = 0; k < NBW; ++k) {
-          const int nb = wave + W * k;
+          const int nb = bw + W * k;
           if (nb < NB) {
 #pragma unroll
-            for (int j = 0; j < NJ; ++j) {
+            for (int jj = 0; jj < NJW; ++jj) {
+              const int j = part + G * jj;
               const int na = (nb + j) % NB;
-              if (oja_s2_formed(na, nb, NB)) {
+              if (j < NJ && oja_s2_formed(na, nb, NB)) {
                 const u32x4 ah = *reinterpret_cast<const u32x4*>(&sm.yt_hi[16 * na + n16][t]);
                 const u32x4 al = *reinterpret_cast<const u32x4*>(&sm.yt_lo[16 * na + n16][t]);
-                s2[j][k] = mfma_16x16x32(ah, bh[k], s2[j][k]);
-                s2[j][k] = mfma_16x16x32(ah, bl[k], s2[j][k]);
-                s2[j][k] = mfma_16x16x32(al, bh[k], s2[j][k]);
+                s2[jj][k] = mfma_16x16x32(ah, bh[k], s2[jj][k]);
+                s2[jj][k] = mfma_16x16x32(ah, bl[k], s2[jj][k]);
+                s2[jj][k] = mfma_16x16x32(al, bh[k], s2[jj][k]);
               }
             }
           }
@@ -266,18 +278,21 @@ __global__ __launch_bounds__(64 * W) void oja_stats_kernel(OjaArgs a) {
   float* w2 = w1 + (int64_t)D * R;
 #pragma unroll
   for (int k = 0; k < NBW; ++k) {
-    const int nb = wave + W * k;
+    const int nb = bw + W * k;
     if (nb < NB) {
 #pragma unroll
-      for (int db = 0; db < D / 16; ++db)
+      for (int di = 0; di < DBW; ++di) {
+        const int db = part + G * di;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) w1[(16 * db + 4 * grp + i) * R + 16 * nb + n16] = s1[db][k][i];
+        for (int i = 0; i < 4; ++i) w1[(16 * db + 4 * grp + i) * R + 16 * nb + n16] = s1[di][k][i];
+      }
 #pragma unroll
-      for (int j = 0; j < NJ; ++j) {
+      for (int jj = 0; jj < NJW; ++jj) {
+        const int j = part + G * jj;
         const int na = (nb + j) % NB;
-        if (oja_s2_formed(na, nb, NB)) {
+        if (j < NJ && oja_s2_formed(na, nb, NB)) {
 #pragma unroll
-          for (int i = 0; i < 4; ++i) w2[(16 * na + 4 * grp + i) * R + 16 * nb + n16] = s2[j][k][i];
+          for (int i = 0; i < 4; ++i) w2[(16 * na + 4 * grp + i) * R + 16 * nb + n16] = s2[jj][k][i];
         }
       }
     }
