@@ -53,10 +53,12 @@ def _run(x, b0, eta, workspace=None):
 
 
 @pytest.mark.parametrize("d,r,B,T,H", [(64, 16, 2, 100, 2), (64, 24, 1, 333, 3), (128, 56, 2, 96, 8),
-                                       (128, 72, 1, 1, 2), (128, 128, 1, 130, 1), (128, 8, 3, 64, 4)])
+                                       (128, 72, 1, 1, 2), (128, 128, 1, 130, 1), (128, 8, 3, 64, 4),
+                                       (128, 32, 2, 77, 3), (64, 48, 1, 200, 2), (128, 112, 1, 250, 2)])
 def test_oja_update_small(d, r, B, T, H):
     """Ragged token counts (a last step with 1..63 tokens, or one token), ranks
-    that pad to whole 16-column blocks, both head dims."""
+    that pad to whole 16-column blocks, both head dims; one and two
+    coefficient blocks put four and two waves on each block."""
     w = synth.scaled(synth.LLAMA_LAYER, batch=B, n_kv_heads=H, head_dim=d, ranks_even=(r, r), ranks_odd=(r, r))
     x = _tokens(w, 0, "k", T)
     b0 = synth.basis(w, 0, "k").exact
