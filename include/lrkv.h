@@ -48,6 +48,10 @@
  *   In the octet layout element (t, c) of a token-by-column matrix lives at
  *   ((t / 8) * ncols + c) * 8 + t % 8: each column's 8 consecutive tokens are
  *   contiguous.  cap and side_cap must be multiples of 8.
+ *   Value caches and value side lists are ONLY read and written in the octet
+ *   layout: a value array in the row layout [B, Hkv, cap, r_V] is not
+ *   accepted, and since a pointer does not carry its layout, passing one
+ *   returns LRKV_OK with wrong results.
  * - Every call is asynchronous on `stream` (0 = the null stream), allocates
  *   nothing and synchronizes nothing, so it can be captured in a HIP graph.
  * - Errors: arguments are validated before any HIP call; an invalid call
@@ -256,7 +260,7 @@ size_t lrkv_compress_hybrid_workspace_bytes(const lrkv_dims* dims, int64_t n_tok
  * reconstruction error are kept in full rank, the rest are compressed).
  * For every new token t of (b, h) with key k and value v:
  *   c = round(x B) (the stored coefficients), x_hat = c B^T,
- *   selected(x) = ||x - x_hat||^2 > tau^2 ||x||^2   (float32),
+ *   selected(x) = ||x - x_hat||^2 > tau^2 ||x||^2   (evaluated in float32),
  *   flag_t = selected(k) or selected(v).
  * Unflagged tokens are appended, in ascending t, to the low-rank caches at
  * rows n_lr[b, h], n_lr[b, h] + 1, ...; flagged tokens are appended, in

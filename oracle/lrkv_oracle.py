@@ -43,9 +43,10 @@ Readings where the pages are silent:
   token appended at this step;
 * bfloat16 rounding is round-to-nearest-even;
 * hybrid selection: relative residual ||x - round(x B) B^T|| / ||x|| > tau for
-  the key or the value (strict), decided in float32 because the kernel decides
-  it in float32; tokens of zero norm are never selected; low-rank rows and the
-  full-rank side list both keep ascending token order;
+  the key or the value (strict), with round(x B) the coefficients the cache
+  stores, evaluated in float64 like the rest of this module; tokens of zero
+  norm are never selected; low-rank rows and the full-rank side list both keep
+  ascending token order;
 * Oja update: one basis per kv head, updated from every token of the call
   (all batch rows) against the same B, step size eta given by the caller, no
   re-orthonormalisation, cached coefficients left as stored.
@@ -225,20 +226,20 @@ def hybrid_flags(x: np.ndarray, basis: np.ndarray, tau: float, dtype: str) -> np
     x [T, d] token vectors; basis [d, r].  The token is stored as the rounded
     coefficients round(x B); its reconstruction is round(x B) B^T.  The token
     is selected when ||x - x_hat|| > tau ||x||, evaluated as
-    ||x - x_hat||^2 > tau^2 ||x||^2 in float32 (the precision the kernel
-    decides in).  (OjaKV README, Method Summary, OjaKV: tokens with high
-    reconstruction error stay full rank.)
+    ||x - x_hat||^2 > tau^2 ||x||^2 in float64.  A token of zero norm is never
+    selected (0 > 0 is false); tau = +inf selects nothing.  (OjaKV README,
+    Method Summary, OjaKV: tokens with high reconstruction error stay full
+    rank.)
     """
-    x32 = np.asarray(x, dtype=np.float32)
-    b32 = np.asarray(basis, dtype=np.float32)
-    c = (x32 @ b32).astype(np.float64)
-    c_stored = round_storage(c, dtype).astype(np.float32)
-    xhat = c_stored @ b32.T
-    r = x32 - xhat
-    err2 = np.sum(r * r, axis=1, dtype=np.float32)
-    nrm2 = np.sum(x32 * x32, axis=1, dtype=np.float32)
-    t2 = np.float32(tau) * np.float32(tau) if math.isfinite(tau) else np.float32(np.inf)
-    return err2 > t2 * nrm2
+    x = np.asarray(x, dtype=np.float64)
+    b = np.asarray(basis, dtype=np.float64)
+    if not math.isfinite(tau):
+        return np.zeros(x.shape[0], dtype=bool)
+    c_stored = round_storage(x @ b, dtype)
+    r = x - c_stored @ b.T
+    err2 = np.sum(r * r, axis=1)
+    nrm2 = np.sum(x * x, axis=1)
+    return err2 > (tau * tau) * nrm2
 
 
 def relative_residual(x: np.ndarray, basis: np.ndarray) -> np.ndarray:

@@ -253,6 +253,27 @@ def test_least_squares_normal_equations():
 # storage rounding against torch's bfloat16 conversion
 # ----------------------------------------------------------------------------
 
+def test_round_storage_f32_matches_the_c_conversion():
+    """round_storage(x, "f32") against Python's struct packing, which converts
+    a double to an IEEE single through the C cast (round to nearest even):
+    random values over a wide exponent range, and doubles exactly halfway
+    between float32 neighbours (both parities of the lower neighbour)."""
+    import struct
+    rng = np.random.default_rng(12)
+    x = rng.standard_normal(3000) * np.exp(rng.uniform(-30, 30, 3000))
+    lo = rng.standard_normal(500).astype(np.float32)
+    hi = np.nextafter(lo, np.float32(np.inf), dtype=np.float32)
+    mid = (lo.astype(np.float64) + hi.astype(np.float64)) / 2.0     # exact in float64
+    vals = np.concatenate([x, mid, [0.0, -0.0, 1.0, -3.5, 2.0 ** -126, 3.0e38]])
+    ref = np.array([struct.unpack("<f", struct.pack("<f", float(v)))[0] for v in vals])
+    got = O.round_storage(vals, "f32")
+    assert np.array_equal(got, ref)
+    assert np.array_equal(np.signbit(got), np.signbit(ref))
+    # the halfway cases went to the neighbour with an even last bit
+    bits = got[len(x):len(x) + len(mid)].astype(np.float32).view(np.uint32)
+    assert np.all((bits & 1) == 0)
+
+
 def test_round_bf16_matches_torch():
     rng = np.random.default_rng(10)
     x = (rng.standard_normal(200000) * np.exp(rng.uniform(-20, 20, 200000))).astype(np.float32)
@@ -294,6 +315,26 @@ def test_hybrid_flags_closed_form():
     assert not O.hybrid_flags(z, b, 0.0, "bf16").any()
     # tau = +inf selects nothing
     assert not O.hybrid_flags(x, b, math.inf, "bf16").any()
+
+
+def test_hybrid_flags_use_the_stored_coefficients():
+    """The residual is taken against the reconstruction from the coefficients
+    the cache stores.  A token exactly in the span whose coefficient is not
+    representable in the storage dtype has residual |c - round(c)| / |x|:
+    here x = (1 + 2^-8) e_0 against B = e_0, stored in bfloat16 as 1 (the tie
+    goes to even), so its relative residual is 2^-8 / (1 + 2^-8) ~ 0.0039 and
+    it is selected at tau = 0.002, although x B B^T = x.  Stored in float32
+    the coefficient is exact, and nothing is selected."""
+    d = 4
+    b = np.zeros((d, 1))
+    b[0, 0] = 1.0
+    x = np.zeros((2, d))
+    x[0, 0] = 1.0 + 2.0 ** -8     # halfway between bfloat16 neighbours 1 and 1 + 2^-7
+    x[1, 0] = 1.0                 # representable: residual 0
+    assert np.array_equal(O.hybrid_flags(x, b, 0.002, "bf16"), [True, False])
+    assert not O.hybrid_flags(x, b, 0.005, "bf16").any()
+    assert not O.hybrid_flags(x, b, 0.002, "f32").any()
+    assert np.allclose(O.relative_residual(x, b), 0.0)
 
 
 def test_hybrid_compaction_order_golden():
@@ -372,6 +413,16 @@ def test_hybrid_workload_margin_and_selection():
             assert not np.any((e >= 0.25) & (e <= 0.75))
             flags = O.hybrid_flags(x, bb[h], 0.5, "bf16")
             assert np.array_equal(np.nonzero(flags)[0], inj)
+            # The selection is defined in float64 on the stored coefficients;
+            # a kernel may decide it in float32.  The two agree on every token
+            # when err^2 / |x|^2 stays far from tau^2 compared with float32's
+            # relative error on a d-term sum of squares (about d 2^-24 = 8e-6
+            # at d = 128, plus the reconstruction's own float32 error, of the
+            # same order relative to |x|^2): here the gap is at least 0.1.
+            c = O.round_storage(x @ bb[h], "bf16")
+            res = x - c @ bb[h].T
+            e2 = np.sum(res * res, axis=1) / np.sum(x * x, axis=1)
+            assert np.min(np.abs(e2 - 0.25)) >= 0.1
 
 
 # ----------------------------------------------------------------------------

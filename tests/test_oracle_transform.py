@@ -37,6 +37,27 @@ def _score_error_by_loops(Q, K, K_hat):
     return tot
 
 
+def test_score_error_equals_the_term_by_term_sum():
+    """O.score_error (the yardstick of the optimality and brute-force pins
+    below) equals the sum over queries and keys of the squared logit
+    differences taken one term at a time, for reconstructions from the
+    transform, from an unrelated map, and the empty reconstruction K_hat = 0."""
+    rng = np.random.default_rng(8)
+    for seed, (d, nq, nk) in enumerate([(5, 7, 9), (12, 20, 31), (3, 1, 1)]):
+        Q, K = _data(100 + seed, d=d, nq=nq, nk=nk)
+        p = max(1, d // 2)
+        enc, dec, _ = O.query_aware_key_transform(Q, K, p) if nq >= d else (None, None, None)
+        hats = [np.zeros_like(K), K @ rng.standard_normal((d, d)) / d, K + rng.standard_normal(K.shape)]
+        if enc is not None:
+            hats.append(K @ enc @ dec.T)
+        for K_hat in hats:
+            ref = _score_error_by_loops(Q, K, K_hat)
+            assert abs(O.score_error(Q, K, K_hat) - ref) <= 1e-12 * max(1.0, ref)
+    # a single query and key by hand: q = (1, 2), k = (3, -1), k_hat = (1, 1):
+    # q.k = 1, q.k_hat = 3, error (1 - 3)^2 = 4
+    assert O.score_error(np.array([[1.0, 2.0]]), np.array([[3.0, -1.0]]), np.array([[1.0, 1.0]])) == 4.0
+
+
 def _centred(K):
     return K - K.mean(axis=0, keepdims=True)
 
