@@ -24,7 +24,8 @@ __all__ = [
     "decode_step", "decode_step_workspace_bytes", "decode_step_partial", "decode_step_merge",
     "compress_hybrid", "compress_hybrid_workspace_bytes", "decode_attn_hybrid",
     "HybridCache", "value_cache_shape", "LIB_PATH", "decode_attn_partial", "decode_attn_merge",
-    "decode_attn_latent", "oja_update", "oja_workspace_bytes",
+    "decode_attn_latent", "oja_update", "oja_workspace_bytes", "decode_step_noalloc",
+    "decode_step_noalloc_max_bytes",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "liblrkv.so")
@@ -63,6 +64,9 @@ _SIG = {
     "lrkv_decode_step_workspace_bytes": (ctypes.c_size_t, [ctypes.POINTER(_Dims), _I64]),
     "lrkv_decode_step": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.POINTER(_Dims), _I64, _F,
                                         ctypes.c_int, _P, ctypes.c_size_t, _P]),
+    "lrkv_decode_step_noalloc_max_bytes": (ctypes.c_size_t, []),
+    "lrkv_decode_step_noalloc": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.POINTER(_Dims), _I64,
+                                                _F, ctypes.c_int, _P]),
     "lrkv_decode_step_partial": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, _P, ctypes.POINTER(_Dims), _I64, _F,
                                                 ctypes.c_int, _P, ctypes.c_size_t, _P]),
     "lrkv_decode_step_merge": (ctypes.c_int, [_P, _P, ctypes.POINTER(_Dims), _I64, ctypes.c_int, _P,
@@ -281,6 +285,28 @@ def decode_step(q, k_new, v_new, basis_k, coeff_k, basis_v, coeff_v, n_ctx: int,
     _check(lib.lrkv_decode_step(_ptr(q), _ptr(k_new), _ptr(v_new), _ptr(basis_k), _ptr(coeff_k), _ptr(basis_v),
                                 _ptr(coeff_v), _ptr(enc_k), _ptr(out), _ptr(lse), ctypes.byref(dims), n_ctx, scale,
                                 _dtype_code(q), _ptr(ws), ws.numel(), _stream(q.device)))
+    return out, lse
+
+
+def decode_step_noalloc_max_bytes() -> int:
+    """Size of the library's fixed decode-step workspace (per GPU)."""
+    return int(library().lrkv_decode_step_noalloc_max_bytes())
+
+
+def decode_step_noalloc(q, k_new, v_new, basis_k, coeff_k, basis_v, coeff_v, n_ctx: int, out, lse=None,
+                        scale: float = 0.0, enc_k: Optional[torch.Tensor] = None):
+    """decode_step with the library's fixed workspace instead of a caller's.
+
+    Allocates nothing: out [B, Hq, d] (and lse [B, Hq] float32, if wanted)
+    must be given.  Calls on one GPU share the fixed workspace; order them on
+    one stream.
+    """
+    B, Hq, d = q.shape
+    H, _, rk = basis_k.shape
+    dims = _Dims(B, Hq, H, d, rk, basis_v.shape[2], coeff_k.shape[2])
+    _check(library().lrkv_decode_step_noalloc(_ptr(q), _ptr(k_new), _ptr(v_new), _ptr(basis_k), _ptr(coeff_k),
+                                              _ptr(basis_v), _ptr(coeff_v), _ptr(enc_k), _ptr(out), _ptr(lse),
+                                              ctypes.byref(dims), n_ctx, scale, _dtype_code(q), _stream(q.device)))
     return out, lse
 
 

@@ -14,9 +14,10 @@
 using namespace lrkv;
 
 namespace {
-
 thread_local std::string g_last_error;
+}  // namespace
 
+namespace lrkv {
 lrkv_status fail(lrkv_status st, const char* fmt, ...) {
   char buf[512];
   va_list ap;
@@ -26,6 +27,9 @@ lrkv_status fail(lrkv_status st, const char* fmt, ...) {
   g_last_error = buf;
   return st;
 }
+}  // namespace lrkv
+
+namespace {
 
 lrkv_status device_fail(const char* fn, hipError_t e) {
   return fail(LRKV_ERR_DEVICE, "%s: kernel launch failed: %s", fn, hipGetErrorString(e));

@@ -4,7 +4,12 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "lrkv.h"
+
 namespace lrkv {
+
+// Records a printf-style message for lrkv_last_error() on this thread and returns st.
+lrkv_status fail(lrkv_status st, const char* fmt, ...);
 
 constexpr float kLog2eHost = 1.4426950408889634f;
 

@@ -22,7 +22,9 @@
  *   row-major arrays in the layouts stated per argument.  The caller
  *   allocates and owns every buffer (inputs, outputs, caches, counters,
  *   workspace); the library allocates no device memory and keeps no state
- *   beyond a per-device compute-unit count and a thread-local error string.
+ *   beyond a per-device compute-unit count, a thread-local error string and
+ *   the fixed scratch array of lrkv_decode_step_noalloc (a static device
+ *   array of the library, not an allocation).
  * - One storage dtype (lrkv_dtype) for every floating-point tensor of a call;
  *   lse and workspaces are float32.  Arithmetic accumulates in float32;
  *   rounding to bfloat16 is round-to-nearest-even.
@@ -251,6 +253,26 @@ lrkv_status lrkv_decode_step_partial(const void* q, const void* k_new, const voi
                                      void* workspace, size_t workspace_bytes, hipStream_t stream);
 lrkv_status lrkv_decode_step_merge(void* out, float* lse, const lrkv_dims* dims, int64_t n_ctx, lrkv_dtype dtype,
                                    void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * lrkv_decode_step without a workspace argument, for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation.  Same arguments (minus the workspace),
+ * same kernels and same result as lrkv_decode_step.  The workspace is a fixed
+ * device array inside this library of lrkv_decode_step_noalloc_max_bytes()
+ * bytes (8 MiB) per GPU, held until the process ends; each GPU has its own.
+ * Calls whose lrkv_decode_step_workspace_bytes(dims, n_ctx) exceeds that size
+ * return LRKV_ERR_WORKSPACE_TOO_SMALL before any device call.  The call
+ * allocates nothing.  All calls on one GPU share that GPU's array: calls that
+ * overlap in time on one GPU (other streams, other threads) race, so order
+ * them on one stream.  The first call on a device looks up the array's
+ * address there (LRKV_ERR_DEVICE if that fails).
+ */
+size_t lrkv_decode_step_noalloc_max_bytes(void);
+lrkv_status lrkv_decode_step_noalloc(const void* q, const void* k_new, const void* v_new, const void* basis_k,
+                                     void* coeff_k, const void* basis_v, void* coeff_v, const void* enc_k, void* out,
+                                     float* lse, const lrkv_dims* dims, int64_t n_ctx, float scale, lrkv_dtype dtype,
+                                     hipStream_t stream);
 
 /* Bytes of workspace lrkv_compress_hybrid needs for n_tokens new tokens. */
 size_t lrkv_compress_hybrid_workspace_bytes(const lrkv_dims* dims, int64_t n_tokens);

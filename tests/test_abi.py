@@ -32,7 +32,7 @@ def test_header_declares_the_entry_points():
               "lrkv_decode_attn_partial", "lrkv_decode_attn_merge", "lrkv_compress_hybrid_workspace_bytes",
               "lrkv_decode_step", "lrkv_decode_step_workspace_bytes", "lrkv_decode_step_partial",
               "lrkv_decode_step_merge", "lrkv_decode_attn_latent", "lrkv_oja_update",
-              "lrkv_oja_workspace_bytes"):
+              "lrkv_oja_workspace_bytes", "lrkv_decode_step_noalloc", "lrkv_decode_step_noalloc_max_bytes"):
         assert n in names
 
 
@@ -163,6 +163,23 @@ def test_decode_step_validation():
     assert f(*args(enc=P, ws_bytes=16)) == 3
     g = lib.lrkv_decode_step_partial
     assert g(P, P, P, P, P, P, P, MIS, ctypes.byref(d), 100, 0.0, 1, P, 1 << 30, None) == 1
+
+
+def test_noalloc_refuses_oversized_requests_before_any_device_call():
+    """The fixed-workspace step refuses dims whose workspace exceeds the
+    library's array, with a message, and without touching a device (this
+    runs without a GPU)."""
+    lrkv, lib = _lib()
+    cap = lib.lrkv_decode_step_noalloc_max_bytes()
+    assert cap == 8 << 20
+    big = _dims(lrkv, batch=1024, n_q_heads=64, n_kv_heads=8)
+    assert lib.lrkv_decode_step_workspace_bytes(ctypes.byref(big), 200) > cap
+    f = lib.lrkv_decode_step_noalloc
+    # q, k_new, v_new, basis_k, coeff_k, basis_v, coeff_v, enc_k, out, lse, dims, n_ctx, scale, dtype, stream
+    assert f(P, P, P, P, P, P, P, None, P, None, ctypes.byref(big), 200, 0.0, 1, None) == 3
+    assert b"fixed" in lib.lrkv_last_error()
+    assert f(P, P, P, P, P, P, P, None, P, None, None, 200, 0.0, 1, None) == 1
+    assert f(P, P, P, P, P, P, P, None, P, None, ctypes.byref(_dims(lrkv)), 0, 0.0, 1, None) == 1
 
 
 def test_latent_decode_validation():
