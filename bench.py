@@ -203,6 +203,7 @@ def main():
     copy_gbps = 5 * 2 * src.numel() * 2 / (e0.elapsed_time(e1) * 1e-3) / 1e9
     del src, dst
 
+    peak_dev = device_peak_gbps(lrkv)
     result = {
         "metric": METRIC,
         "value": round(dec_us, 3),
@@ -219,13 +220,15 @@ def main():
         "config": {"workload": w.name, "layers": L, "batch": B, "n_q_heads": Hq, "n_kv_heads": H,
                    "head_dim": d, "context": N, "ranks_even": list(w.ranks(0)), "ranks_odd": list(w.ranks(1)),
                    "prefill_chunk": P, "cache_dtype": "bf16", "accumulate": "fp32"},
+        "decode_us_per_layer_step": stats(decode_us),
         "decode_GBps": round(dec_gbps, 1),
         "decode_pct_peak": round(100 * dec_gbps / HBM_PEAK_GBPS, 2),
+        "device_peak": peak_dev,
         "attn_tokens_per_s": round(tok_s, 1),
         "decode_us_per_step_32_layers": round(step_decode_us, 1),
-        "attn_kernel_us": {"even": round(attn_mean[0], 3), "odd": round(attn_mean[1], 3)},
-        "merge_us": round(mean(merge_us), 3),
-        "prefill_compress_us_per_layer": round(mean(prefill_us), 3),
+        "attn_kernel_us": {"even": stats(attn_by_par[0]), "odd": stats(attn_by_par[1])},
+        "merge_us": stats(merge_us),
+        "prefill_compress_us_per_layer": stats(prefill_us),
         "prefill_compress_GBps": round(pre_gbps, 1),
         "device_copy_GBps": round(copy_gbps, 1),
         "roofline": {"bound": "hbm", "kernel": "split_bf16_kernel",
@@ -248,13 +251,16 @@ def main():
 
 
 def bench_variants(torch, lrkv, bm, synth, dev, layers, ws, dev_bf16):
-    """The two variants of the decode on the same 32-layer batched caches:
-    latent queries and outputs (projections that absorb the bases: no fold,
-    no lift, no basis read) and the decode step with a separate,
-    non-orthogonal key encoder (decoder D folds the query, encoder E
-    compresses the appended key), with the plain decode step timed the same
-    way for comparison.  Each figure is two launches per layer (attention +
-    merge), averaged over 3 passes of the 32 layers."""
+    """Variants of the decode on the same 32-layer batched caches, each timed
+    per call (TIMED_ITERS calls after WARM_ITERS, cycling over the layers):
+    - latent queries and outputs (projections that absorb the bases: no fold,
+      no lift, no basis read);
+    - the decode step with a separate, non-orthogonal key encoder (decoder D
+      folds the query, encoder E compresses the appended key), and the plain
+      decode step timed the same way for comparison;
+    - the Oja update of both bases of a layer, from its 4096-token prefill
+      chunk and at decode shape (the step's one appended token per sequence).
+    Each decode figure is two launches (attention + merge)."""
     w = synth.BATCHED_32K
     B, Hq, H, d, L = w.batch, w.n_q_heads, w.n_kv_heads, w.head_dim, w.layers
     N = w.n_ctx[0]
@@ -278,51 +284,80 @@ def bench_variants(torch, lrkv, bm, synth, dev, layers, ws, dev_bf16):
         lrkv.decode_step(lay["q"], lay["ak"], lay["av"], lay["bk"], lay["ck"], lay["bv"], lay["cv"], N,
                          out=lay["out"], lse=lay["lse"], workspace=ws)
 
-    # Oja update of both bases of a layer from its 4096-token prefill chunk
-    # (float32 master bases; the bfloat16 copies go to buffers of their own,
-    # so the caches' bases stay as they are)
+    # Oja update of both bases of a layer (float32 master bases; the bfloat16
+    # copies go to buffers of their own, so the caches' bases stay as they are)
+    # from the layer's 4096-token prefill chunk, and from the decode step's
+    # appended token (batch 16 x 1 token)
     oja = {p: [] for p in (0, 1)}
+    oja_dec = {p: [] for p in (0, 1)}
     for l, lay in enumerate(layers[:2]):
-        for key in ("bk", "bv"):
-            oja[l].append((lay["xk" if key == "bk" else "xv"], lay[key].float().contiguous(), torch.empty_like(lay[key])))
-    P = lay["xk"].shape[1]
-    oja_ws = torch.empty(max(lrkv.oja_workspace_bytes(B, H, d, b32.shape[2], P) for p in (0, 1)
-                             for _, b32, _ in oja[p]), dtype=torch.uint8, device=dev)
+        for key, x in (("bk", "xk"), ("bv", "xv")):
+            b32 = lay[key].float().contiguous()
+            oja[l].append((lay[x], b32, torch.empty_like(lay[key])))
+            tok = lay["ak" if key == "bk" else "av"].view(B, 1, H, d)
+            oja_dec[l].append((tok, b32.clone(), torch.empty_like(lay[key])))
+    P = layers[0]["xk"].shape[1]
+    oja_ws = torch.empty(max(lrkv.oja_workspace_bytes(B, H, d, r, P) for p in (0, 1) for r in w.ranks(p)),
+                         dtype=torch.uint8, device=dev)
 
     def oja_layer(i):
         for x, b32, b16 in oja[i % 2]:
             lrkv.oja_update(x, b32, 1e-9, basis_bf16=b16, workspace=oja_ws)
 
-    lat_us = _timed(torch, latent, 3 * L, warm=L)
-    tf_us = _timed(torch, transform_step, 3 * L, warm=L)
-    plain_us = _timed(torch, plain_step, 3 * L, warm=L)
-    oja_us = _timed(torch, oja_layer, 20, warm=4)
+    def oja_decode(i):
+        for x, b32, b16 in oja_dec[i % 2]:
+            lrkv.oja_update(x, b32, 1e-9, basis_bf16=b16, workspace=oja_ws)
+
+    lat_us = _timed(torch, latent)
+    tf_us = _timed(torch, transform_step)
+    plain_us = _timed(torch, plain_step)
+    oja_us = _timed(torch, oja_layer)
+    oja_dec_us = _timed(torch, oja_decode)
     oja_bytes = sum(bm.oja_bytes(B, P, H, d, r) for p in (0, 1) for r in w.ranks(p)) / 2
     oja_flops = sum(bm.oja_flops(B, P, H, d, r) for p in (0, 1) for r in w.ranks(p)) / 2
+    oja_dec_bytes = sum(bm.oja_bytes(B, 1, H, d, r) for p in (0, 1) for r in w.ranks(p)) / 2
     lat_bytes = sum(bm.latent_decode_bytes(B, Hq, H, *w.ranks(p), N) for p in (0, 1)) / 2
-    return {"latent_decode_us_per_layer": round(lat_us, 3),
-            "latent_decode_GBps": round(lat_bytes / (lat_us * 1e-6) / 1e9, 1),
-            "transform_step_us_per_layer": round(tf_us, 3),
-            "plain_step_us_per_layer": round(plain_us, 3),
-            "oja_update_us_per_layer": round(oja_us, 3),
-            "oja_update_GBps": round(oja_bytes / (oja_us * 1e-6) / 1e9, 1),
-            "oja_update_TFLOPs": round(oja_flops / (oja_us * 1e-6) / 1e12, 1),
-            "note": "same caches and context as the main figure, layers run back to back (no prefill "
-                    "between them); two launches per layer; the Oja update is of both bases of a layer "
-                    "from its 4096-token prefill chunk (three launches per basis)"}
+    return {"latent_decode_us_per_layer": lat_us,
+            "latent_decode_GBps": round(lat_bytes / (lat_us["mean"] * 1e-6) / 1e9, 1),
+            "transform_step_us_per_layer": tf_us,
+            "plain_step_us_per_layer": plain_us,
+            "oja_update_us_per_layer": oja_us,
+            "oja_update_GBps": round(oja_bytes / (oja_us["mean"] * 1e-6) / 1e9, 1),
+            "oja_update_TFLOPs": round(oja_flops / (oja_us["mean"] * 1e-6) / 1e12, 1),
+            "oja_update_decode_us_per_layer": oja_dec_us,
+            "oja_update_decode_GBps": round(oja_dec_bytes / (oja_dec_us["mean"] * 1e-6) / 1e9, 1),
+            "note": "same caches and context as the main figure, layers cycled call after call (no prefill "
+                    "between them); two launches per decode call; the Oja update is of both bases of a layer "
+                    "(three launches per basis), from its 4096-token prefill chunk and at decode shape "
+                    "(batch 16 x the step's one appended token)"}
 
 
-def _timed(torch, fn, iters, warm=3):
-    for _ in range(warm):
-        fn(0)
-    torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record()
-    for i in range(iters):
+TIMED_ITERS = 200   # timed calls per figure
+WARM_ITERS = 20     # untimed calls before them
+
+
+def stats(us):
+    """mean and p10 / p50 / p90 of per-call times (microseconds)."""
+    a = np.asarray(us, dtype=np.float64)
+    return {"mean": round(float(a.mean()), 3), "p10": round(float(np.percentile(a, 10)), 3),
+            "p50": round(float(np.percentile(a, 50)), 3), "p90": round(float(np.percentile(a, 90)), 3),
+            "n": int(a.size)}
+
+
+def _timed(torch, fn, iters=TIMED_ITERS, warm=WARM_ITERS):
+    """Call fn(i) `warm` times untimed, then `iters` times, each call between
+    its own pair of HIP events on the current stream (the stream the library
+    launches on).  Returns stats() of the per-call times in microseconds."""
+    for i in range(warm):
         fn(i)
-    e1.record()
     torch.cuda.synchronize()
-    return e0.elapsed_time(e1) * 1e3 / iters
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(iters)]
+    for i in range(iters):
+        ev[i][0].record()
+        fn(i)
+        ev[i][1].record()
+    torch.cuda.synchronize()
+    return stats([a.elapsed_time(b) * 1e3 for a, b in ev])
 
 
 def bench_hybrid(torch, lrkv, bm, synth, dev, threads):
@@ -355,36 +390,50 @@ def bench_hybrid(torch, lrkv, bm, synth, dev, threads):
         c.n_side.zero_()
         lrkv.compress_hybrid(c, kd, vd, bk, bv, 0.5, 0, workspace=cws)
 
-    comp_us = _timed(torch, compress, 6)
+    comp_us = _timed(torch, compress)
     n_side = int(caches[0].n_side[0, 0].item())
     dws = torch.zeros(lrkv.decode_workspace_bytes(1, w.n_q_heads, H, d, rk, rv, n, 0, side_cap),
                       dtype=torch.uint8, device=dev)
     out = torch.empty_like(q)
     lse = torch.empty((1, w.n_q_heads), dtype=torch.float32, device=dev)
     dec_us = _timed(torch, lambda i: lrkv.decode_attn_hybrid(q, bk, bv, caches[i % 3], out=out, lse=lse,
-                                                             workspace=dws), 30)
+                                                             workspace=dws))
     comp_bytes = (2 * n * H * d * 2 + (n - n_side) * H * (rk + rv) * 2 + n_side * H * (2 * d * 2 + 4)
                   + H * d * (rk + rv) * 2)
     dec_bytes = bm.decode_bytes(1, w.n_q_heads, H, d, rk, rv, n, side_tokens=n_side)
     log(f"hybrid figures in {time.time() - t0:.1f}s")
     return {"workload": w.name, "context": n, "side_tokens_per_kv_head": n_side,
-            "compress_us": round(comp_us, 1), "compress_GBps": round(comp_bytes / comp_us / 1e3, 1),
-            "decode_us": round(dec_us, 2), "decode_GBps": round(dec_bytes / dec_us / 1e3, 1),
-            "decode_pct_peak": round(100 * dec_bytes / dec_us / 1e3 / HBM_PEAK_GBPS, 2)}
+            "compress_us": comp_us, "compress_bytes": comp_bytes,
+            "compress_GBps": round(comp_bytes / comp_us["mean"] / 1e3, 1),
+            "decode_us": dec_us, "decode_bytes": dec_bytes,
+            "decode_GBps": round(dec_bytes / dec_us["mean"] / 1e3, 1),
+            "decode_pct_peak": round(100 * dec_bytes / dec_us["mean"] / 1e3 / HBM_PEAK_GBPS, 2),
+            "decode_pct_peak_p50": round(100 * dec_bytes / dec_us["p50"] / 1e3 / HBM_PEAK_GBPS, 2)}
 
 
 def bench_step_sweep(torch, lrkv, bm, synth, dev, threads):
-    """32-layer decode step at batch 1 (lrkv_decode_step per layer: append + attention, merge), eager and as
-    a HIP graph; and, for comparison, the unfused sequence (compress launch + decode) as a graph."""
+    """32-layer decode step at batch 1, context 256 / 2048 / 8192: one
+    lrkv_decode_step per layer (append + attention [+ merge]), eager and as a
+    HIP graph replayed at one context; the same step through the device-length
+    entry point as one graph that advances the context by one token per
+    replay (the graph appends a token to every layer's cache and increments
+    the length); and, for comparison, the unfused sequence (compress launch +
+    decode) as a graph."""
     w = synth.LLAMA_STEP
     L, Hq, H, d = w.layers, w.n_q_heads, w.n_kv_heads, w.head_dim
     rk, rv = w.ranks(0)
     dv = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
     bk, bv = dv(synth.basis(w, 0, "k").store), dv(synth.basis(w, 0, "v").store)
+    grow = TIMED_ITERS + WARM_ITERS          # tokens the advancing graph appends
     res = {}
     for n in w.n_ctx:
-        ck0 = synth.stack_heads(w, lambda b, h: synth.direct_coeffs(w, 0, "k", b, h, n, exact=False), threads=threads).store
-        cv0 = synth.stack_heads(w, lambda b, h: synth.direct_coeffs(w, 0, "v", b, h, n, exact=False), threads=threads).store
+        cap = (n + grow + 7) // 8 * 8
+        ck0 = np.zeros((1, H, cap, rk), np.uint16)
+        cv0 = np.zeros((1, H, cap, rv), np.uint16)
+        ck0[:, :, :n] = synth.stack_heads(w, lambda b, h: synth.direct_coeffs(w, 0, "k", b, h, n, exact=False),
+                                          threads=threads).store
+        cv0[:, :, :n] = synth.stack_heads(w, lambda b, h: synth.direct_coeffs(w, 0, "v", b, h, n, exact=False),
+                                          threads=threads).store
         ck0, cv0 = dv(ck0), dv(synth.to_value_octets(cv0))
         lay = [dict(ck=ck0.clone(), cv=cv0.clone(), q=dv(synth.query(w, l).store),
                     ak=dv(synth.tokens_major(synth.stack_heads(w, lambda b, h: synth.full_tokens(
@@ -393,16 +442,24 @@ def bench_step_sweep(torch, lrkv, bm, synth, dev, threads):
                         w, l, "v", b, h, 1, synth.PART_APPEND))).store),
                     out=torch.empty((1, Hq, d), dtype=torch.bfloat16, device=dev),
                     lse=torch.empty((1, Hq), dtype=torch.float32, device=dev)) for l in range(L)]
-        ws = torch.zeros(max(lrkv.decode_workspace_bytes(1, Hq, H, d, rk, rv, n, n),
-                             lrkv.decode_step_workspace_bytes(1, Hq, H, d, rk, rv, n, n)),
+        ws = torch.zeros(max(lrkv.decode_workspace_bytes(1, Hq, H, d, rk, rv, cap, n),
+                             lrkv.decode_step_workspace_bytes(1, Hq, H, d, rk, rv, cap, n),
+                             lrkv.decode_step_workspace_bytes(1, Hq, H, d, rk, rv, cap, n + grow)),
                          dtype=torch.uint8, device=dev)
+        seq_lens = torch.full((1,), n, dtype=torch.int32, device=dev)
 
-        def step(_i=0):      # one lrkv_decode_step per layer: two launches
+        def step(_i=0):      # one lrkv_decode_step per layer at context n
             for x in lay:
                 lrkv.decode_step(x["q"], x["ak"], x["av"], bk, x["ck"], bv, x["cv"], n, out=x["out"], lse=x["lse"],
                                  workspace=ws)
 
-        def step_unfused(_i=0):   # compress of the token, then the decode: three launches
+        def step_advancing():   # the same with the length on the device, then one more token
+            for x in lay:
+                lrkv.decode_step_seqlens(x["q"], x["ak"], x["av"], bk, x["ck"], bv, x["cv"], seq_lens, n + grow,
+                                         out=x["out"], lse=x["lse"], workspace=ws)
+            seq_lens.add_(1)
+
+        def step_unfused(_i=0):   # compress of the token, then the decode
             for x in lay:
                 lrkv.compress_kv(x["ak"], x["av"], bk, bv, x["ck"], x["cv"], n - 1)
                 lrkv.decode_attn(x["q"], bk, x["ck"], bv, x["cv"], n, out=x["out"], lse=x["lse"], workspace=ws)
@@ -417,21 +474,57 @@ def bench_step_sweep(torch, lrkv, bm, synth, dev, threads):
                 fn()
             return g
 
-        eager = _timed(torch, step, 20)
+        eager = _timed(torch, step)
         g = graph_of(step)
-        graph = _timed(torch, lambda i: g.replay(), 50)
+        graph = _timed(torch, lambda i: g.replay())
         g2 = graph_of(step_unfused)
-        graph_unfused = _timed(torch, lambda i: g2.replay(), 50)
+        graph_unfused = _timed(torch, lambda i: g2.replay())
+        g3 = graph_of(step_advancing)       # the eager warm-up and the capture leave the length at n + 1
+        seq_lens.fill_(n)
+        torch.cuda.synchronize()
+        advancing = _timed(torch, lambda i: g3.replay())
+        reached = int(seq_lens.item())
         step_bytes = L * (bm.decode_bytes(1, Hq, H, d, rk, rv, n) + bm.compress_bytes(1, 1, H, d, rk)
                           + bm.compress_bytes(1, 1, H, d, rv))
-        res[str(n)] = {"eager_us_per_step": round(eager, 1), "graph_us_per_step": round(graph, 1),
-                       "graph_us_per_layer": round(graph / L, 2),
-                       "unfused_graph_us_per_step": round(graph_unfused, 1),
-                       "graph_GBps_effective": round(step_bytes / graph / 1e3, 1)}
-        del lay, g, g2, ws
+        res[str(n)] = {"eager_us_per_step": eager, "graph_us_per_step": graph,
+                       "graph_us_per_layer": round(graph["mean"] / L, 2),
+                       "advancing_graph_us_per_step": advancing,
+                       "advancing_context_range": [n + WARM_ITERS, reached - 1],
+                       "unfused_graph_us_per_step": graph_unfused,
+                       "graph_GBps_effective": round(step_bytes / graph["mean"] / 1e3, 1)}
+        del lay, g, g2, g3, ws
         torch.cuda.empty_cache()
     return {"workload": w.name, "layers": L, "by_context": res,
-            "note": "working set <= 0.6 GB per step; 'effective' bandwidth can include last-level-cache hits"}
+            "note": "working set <= 0.6 GB per step; 'effective' bandwidth can include last-level-cache hits; "
+                    "the advancing graph appends one token per replay (its context grows from n by "
+                    f"{WARM_ITERS} warm-up and {TIMED_ITERS} timed replays)"}
+
+
+def device_peak_gbps(lrkv):
+    """HBM peak from the device's own properties (memory clock x bus width),
+    next to the published 8 TB/s.  The attributes are read through the HIP
+    runtime the library itself uses (hipDeviceGetAttribute, attributes 59 =
+    memory bus width in bits and 60 = peak memory clock in kHz in
+    hip_runtime_api.h).  The double-data-rate formula clock x 2 x width / 8 is
+    the one the properties are usually read with; HBM's actual transfers per
+    clock are not among the properties, so the figure is reported as read."""
+    import ctypes
+    try:
+        lib = lrkv.library()
+        get = lib.hipDeviceGetAttribute
+        get.restype = ctypes.c_int
+        get.argtypes = [ctypes.POINTER(ctypes.c_int), ctypes.c_int, ctypes.c_int]
+        dev = ctypes.c_int(0)
+        lib.hipGetDevice.argtypes = [ctypes.POINTER(ctypes.c_int)]
+        lib.hipGetDevice(ctypes.byref(dev))
+        width, clock = ctypes.c_int(0), ctypes.c_int(0)
+        if get(ctypes.byref(width), 59, dev.value) or get(ctypes.byref(clock), 60, dev.value):
+            return None
+    except (AttributeError, OSError):
+        return None
+    ddr = clock.value * 1e3 * 2 * width.value / 8 / 1e9
+    return {"memory_clock_khz": clock.value, "memory_bus_width_bits": width.value,
+            "clock_x2_x_width_GBps": round(ddr, 1), "published_GBps": HBM_PEAK_GBPS}
 
 
 def measured_traffic():
@@ -488,8 +581,10 @@ def cpu_baseline(w, budget_s):
         u += 1
     per_unit = float(np.mean(times))
     us = per_unit * w.batch * w.n_kv_heads * 1e6
+    spread = stats(np.asarray(times) * w.batch * w.n_kv_heads * 1e6)
     return {"value": round(us, 1), "unit": "us/layer-step", "cores": n_threads, "kind": "oracle",
             "host_cpus": len(os.sched_getaffinity(0)),
+            "per_unit_scaled_us": {k: spread[k] for k in ("p10", "p50", "p90")},
             "sample": f"{len(times)} (batch, kv-head) units of the decode at N={N} (reconstruct K_hat, V_hat; "
                       f"attend {g} query heads; compress the appended token), odd and even layers alternating, "
                       f"mean {per_unit:.3f}s per unit, scaled x{w.batch * w.n_kv_heads} to one layer-step"}

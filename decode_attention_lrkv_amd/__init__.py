@@ -25,7 +25,7 @@ __all__ = [
     "compress_hybrid", "compress_hybrid_workspace_bytes", "decode_attn_hybrid",
     "HybridCache", "value_cache_shape", "LIB_PATH", "decode_attn_partial", "decode_attn_merge",
     "decode_attn_latent", "oja_update", "oja_workspace_bytes", "decode_step_noalloc",
-    "decode_step_noalloc_max_bytes",
+    "decode_step_noalloc_max_bytes", "decode_attn_seqlens", "decode_step_seqlens",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "liblrkv.so")
@@ -64,6 +64,10 @@ _SIG = {
     "lrkv_decode_step_workspace_bytes": (ctypes.c_size_t, [ctypes.POINTER(_Dims), _I64]),
     "lrkv_decode_step": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.POINTER(_Dims), _I64, _F,
                                         ctypes.c_int, _P, ctypes.c_size_t, _P]),
+    "lrkv_decode_attn_seqlens": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, ctypes.POINTER(_Dims), _P, _I64, _F,
+                                                ctypes.c_int, _P, ctypes.c_size_t, _P]),
+    "lrkv_decode_step_seqlens": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.POINTER(_Dims), _P,
+                                                _I64, _F, ctypes.c_int, _P, ctypes.c_size_t, _P]),
     "lrkv_decode_step_noalloc_max_bytes": (ctypes.c_size_t, []),
     "lrkv_decode_step_noalloc": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.POINTER(_Dims), _I64,
                                                 _F, ctypes.c_int, _P]),
@@ -285,6 +289,57 @@ def decode_step(q, k_new, v_new, basis_k, coeff_k, basis_v, coeff_v, n_ctx: int,
     _check(lib.lrkv_decode_step(_ptr(q), _ptr(k_new), _ptr(v_new), _ptr(basis_k), _ptr(coeff_k), _ptr(basis_v),
                                 _ptr(coeff_v), _ptr(enc_k), _ptr(out), _ptr(lse), ctypes.byref(dims), n_ctx, scale,
                                 _dtype_code(q), _ptr(ws), ws.numel(), _stream(q.device)))
+    return out, lse
+
+
+def _seq_lens(seq_lens: torch.Tensor, batch: int):
+    if seq_lens.dtype != torch.int32 or seq_lens.numel() != batch:
+        raise LrkvError(1, f"seq_lens must be an int32 tensor of {batch} lengths")
+    return _ptr(seq_lens)
+
+
+def decode_attn_seqlens(q, basis_k, coeff_k, basis_v, coeff_v, seq_lens: torch.Tensor, max_seq_len: int,
+                        out=None, lse=None, scale: float = 0.0, workspace: Optional[torch.Tensor] = None,
+                        with_lse: bool = True):
+    """decode_attn with per-sequence lengths on the device: sequence b attends
+    rows [0, seq_lens[b]).  The split plan is made for max_seq_len (host), so
+    a captured graph stays valid while the lengths advance."""
+    B, Hq, d = q.shape
+    H, _, rk = basis_k.shape
+    dims = _Dims(B, Hq, H, d, rk, basis_v.shape[2], coeff_k.shape[2])
+    lib = library()
+    ws = _workspace(int(lib.lrkv_decode_workspace_bytes(ctypes.byref(dims), max_seq_len, 0)), q.device, workspace)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None and with_lse:
+        lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
+    _check(lib.lrkv_decode_attn_seqlens(_ptr(q), _ptr(basis_k), _ptr(coeff_k), _ptr(basis_v), _ptr(coeff_v),
+                                        _ptr(out), _ptr(lse), ctypes.byref(dims), _seq_lens(seq_lens, B),
+                                        max_seq_len, scale, _dtype_code(q), _ptr(ws), ws.numel(),
+                                        _stream(q.device)))
+    return out, lse
+
+
+def decode_step_seqlens(q, k_new, v_new, basis_k, coeff_k, basis_v, coeff_v, seq_lens: torch.Tensor,
+                        max_seq_len: int, out=None, lse=None, scale: float = 0.0,
+                        workspace: Optional[torch.Tensor] = None, with_lse: bool = True,
+                        enc_k: Optional[torch.Tensor] = None):
+    """decode_step with per-sequence lengths on the device: sequence b appends
+    its token at row seq_lens[b] - 1 and attends rows [0, seq_lens[b]).  The
+    lengths are read, not advanced."""
+    B, Hq, d = q.shape
+    H, _, rk = basis_k.shape
+    dims = _Dims(B, Hq, H, d, rk, basis_v.shape[2], coeff_k.shape[2])
+    lib = library()
+    ws = _workspace(int(lib.lrkv_decode_step_workspace_bytes(ctypes.byref(dims), max_seq_len)), q.device, workspace)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None and with_lse:
+        lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
+    _check(lib.lrkv_decode_step_seqlens(_ptr(q), _ptr(k_new), _ptr(v_new), _ptr(basis_k), _ptr(coeff_k),
+                                        _ptr(basis_v), _ptr(coeff_v), _ptr(enc_k), _ptr(out), _ptr(lse),
+                                        ctypes.byref(dims), _seq_lens(seq_lens, B), max_seq_len, scale,
+                                        _dtype_code(q), _ptr(ws), ws.numel(), _stream(q.device)))
     return out, lse
 
 

@@ -268,16 +268,34 @@ __device__ __forceinline__ void split_bf16_body(const SplitArgs& a, int wg, int 
     if (n_end > a.cap) n_end = a.cap;
     if (n_end < 0) n_end = 0;
   }
-  // The workgroup owns kWaves * chunks_per_split consecutive chunks and its
-  // waves take them in turn: wave w reads chunks w, w + kWaves, ...  Four
-  // waves reading adjacent chunks keep the workgroup's loads in one dense
-  // window of the cache (measured: 1.4 % faster than one contiguous run per
-  // wave with ranks 32/96, where every per-wave run starts at a multiple of
-  // 128 KB).  The online softmax does not depend on the order.
+  // the appended token's row (decode step), and whether this workgroup owns
+  // the token's partial slot (it marks the slot empty even when a device
+  // length outside [1, cap] leaves nothing to append)
+  int64_t append_row = a.append_row;
+  const bool tok_slot = append;
+  int64_t cps = a.chunks_per_split;
+  if (a.n_ctx_b) {
+    const int64_t total = a.n_ctx_b[b];
+    const bool ok = total >= 1 && total <= a.cap;
+    n_end = ok ? (a.k_new ? total - 1 : total) : 0;
+    append_row = total - 1;
+    append = append && ok;
+    // the host planned n_splits splits (ceil(n_splits / kWaves) attention
+    // workgroups) for a length bound; ceil(chunks / n_splits) chunks per
+    // split needs at most n_splits splits for any length, and is the host's
+    // own plan when the length is the bound
+    cps = ((n_end + kChunk - 1) / kChunk + a.n_splits - 1) / a.n_splits;
+  }
+  // The workgroup owns kWaves * cps consecutive chunks and its waves take
+  // them in turn: wave w reads chunks w, w + kWaves, ...  Four waves reading
+  // adjacent chunks keep the workgroup's loads in one dense window of the
+  // cache (measured: 1.4 % faster than one contiguous run per wave with ranks
+  // 32/96, where every per-wave run starts at a multiple of 128 KB).  The
+  // online softmax does not depend on the order.
   const int64_t n_chunks = (n_end + kChunk - 1) / kChunk;
-  const int64_t w_begin = (int64_t)wg * kWaves * a.chunks_per_split;
+  const int64_t w_begin = (int64_t)wg * kWaves * cps;
   const int64_t c_begin = w_begin + wave;
-  int64_t c_end = w_begin + (int64_t)kWaves * a.chunks_per_split;
+  int64_t c_end = w_begin + (int64_t)kWaves * cps;
   if (c_end > n_chunks) c_end = n_chunks;
   constexpr int64_t kStep = kWaves;
 
@@ -433,7 +451,7 @@ __device__ __forceinline__ void split_bf16_body(const SplitArgs& a, int wg, int 
     // unless a separate key encoder is given), stored at the appended row; then
     // the token's score q' . c_K (log2 units), kept with c_V for the epilogue
     const int pa = a.n_parts - 1;
-    const int64_t p = a.append_row;
+    const int64_t p = append_row;
     float* s_c = s_q + 256;   // past the token's key and value
     const int col = tid & 127;
     const bool kind_v = tid >= 128;
@@ -521,6 +539,11 @@ __device__ __forceinline__ void split_bf16_body(const SplitArgs& a, int wg, int 
         store_partial(a.part_ml + ((row0 + tid) * a.n_parts + pa) * 2 + 1, 0.f);
       }
     }
+  } else if (tok_slot && !a.out && tid < g) {
+    // no token to append (a device length outside [1, cap]): its slot stays empty
+    const int64_t row0 = (int64_t)b * a.hq + (int64_t)h * g;
+    store_partial(a.part_ml + ((row0 + tid) * a.n_parts + a.n_parts - 1) * 2 + 0, -INFINITY);
+    store_partial(a.part_ml + ((row0 + tid) * a.n_parts + a.n_parts - 1) * 2 + 1, 0.f);
   }
 
 

@@ -299,11 +299,14 @@ lrkv_status check_decode_common(const lrkv_dims* dims, int64_t n_ctx, lrkv_dtype
   return LRKV_OK;
 }
 
+// seq_lens: per-sequence lengths on the device (the plan L was made for an
+// upper bound n_ctx of them), or null: n_ctx is the length of every sequence
 lrkv_status decode_partial(const void* q, const void* basis_k, const void* coeff_k, const void* basis_v,
                            const void* coeff_v, const lrkv_dims* dims, int64_t n_ctx, float scale,
                            lrkv_dtype dtype, void* workspace, const DecodeLayout& L, hipStream_t stream,
                            const char* fn, const void* k_new = nullptr, const void* v_new = nullptr,
-                           const void* enc_k = nullptr, void* out = nullptr, float* lse = nullptr) {
+                           const void* enc_k = nullptr, void* out = nullptr, float* lse = nullptr,
+                           const int32_t* seq_lens = nullptr) {
   char* ws = static_cast<char*>(workspace);
   SplitArgs sa{};
   sa.q = q; sa.basis_k = basis_k; sa.ck = coeff_k; sa.cv = coeff_v; sa.basis_v = basis_v;
@@ -324,6 +327,7 @@ lrkv_status decode_partial(const void* q, const void* basis_k, const void* coeff
   }
   sa.out = out;   // final outputs (one attention workgroup per unit), or partials
   sa.lse = lse;
+  sa.n_ctx_b = seq_lens;
   // no basis_k: latent queries (absorbed projections), no fold and no lift
   const hipError_t e = dtype != LRKV_BF16 ? launch_split_f32(sa, stream)
                                           : (basis_k ? launch_split_bf16(sa, stream) : launch_split_bf16_latent(sa, stream));
@@ -536,6 +540,62 @@ lrkv_status lrkv_decode_step_merge(void* out, float* lse, const lrkv_dims* dims,
   if (workspace_bytes < need)
     return fail(LRKV_ERR_WORKSPACE_TOO_SMALL, "%s: workspace of %zu bytes, %zu needed", fn, workspace_bytes, need);
   return decode_merge(out, lse, dims, dtype, workspace, step_layout(*dims, n_ctx, dtype), stream, fn);
+}
+
+lrkv_status lrkv_decode_attn_seqlens(const void* q, const void* basis_k, const void* coeff_k,
+                                     const void* basis_v, const void* coeff_v, void* out, float* lse,
+                                     const lrkv_dims* dims, const int32_t* seq_lens, int64_t max_seq_len,
+                                     float scale, lrkv_dtype dtype, void* workspace, size_t workspace_bytes,
+                                     hipStream_t stream) {
+  const char* fn = "lrkv_decode_attn_seqlens";
+  DecodeLayout L;
+  lrkv_status st = check_decode_common(dims, max_seq_len, dtype, workspace, workspace_bytes, fn, &L);
+  if (st != LRKV_OK) return st;
+  if (dtype != LRKV_BF16) return fail(LRKV_ERR_UNSUPPORTED, "%s: only bfloat16 caches are supported", fn);
+  if (!std::isfinite(scale)) return fail(LRKV_ERR_INVALID_ARGUMENT, "%s: scale is not finite", fn);
+  if (!seq_lens || (reinterpret_cast<uintptr_t>(seq_lens) & 3u))
+    return fail(LRKV_ERR_INVALID_ARGUMENT, "%s: seq_lens is NULL or not 4-byte aligned", fn);
+  LRKV_CHECK_PTR(q, fn);
+  LRKV_CHECK_PTR(basis_k, fn);
+  LRKV_CHECK_PTR(coeff_k, fn);
+  LRKV_CHECK_PTR(basis_v, fn);
+  LRKV_CHECK_PTR(coeff_v, fn);
+  LRKV_CHECK_PTR(out, fn);
+  if (lse && !aligned16(lse)) return fail(LRKV_ERR_INVALID_ARGUMENT, "%s: lse is not 16-byte aligned", fn);
+  if (L.parts == 1)
+    return decode_partial(q, basis_k, coeff_k, basis_v, coeff_v, dims, max_seq_len, scale, dtype, workspace, L,
+                          stream, fn, nullptr, nullptr, nullptr, out, lse, seq_lens);
+  st = decode_partial(q, basis_k, coeff_k, basis_v, coeff_v, dims, max_seq_len, scale, dtype, workspace, L, stream,
+                      fn, nullptr, nullptr, nullptr, nullptr, nullptr, seq_lens);
+  if (st != LRKV_OK) return st;
+  return decode_merge(out, lse, dims, dtype, workspace, L, stream, fn);
+}
+
+lrkv_status lrkv_decode_step_seqlens(const void* q, const void* k_new, const void* v_new, const void* basis_k,
+                                     void* coeff_k, const void* basis_v, void* coeff_v, const void* enc_k, void* out,
+                                     float* lse, const lrkv_dims* dims, const int32_t* seq_lens, int64_t max_seq_len,
+                                     float scale, lrkv_dtype dtype, void* workspace, size_t workspace_bytes,
+                                     hipStream_t stream) {
+  const char* fn = "lrkv_decode_step_seqlens";
+  lrkv_status st = check_step(q, k_new, v_new, basis_k, coeff_k, basis_v, coeff_v, enc_k, dims, max_seq_len, scale,
+                              dtype, workspace, workspace_bytes, fn);
+  if (st != LRKV_OK) return st;
+  if (dtype != LRKV_BF16) return fail(LRKV_ERR_UNSUPPORTED, "%s: only bfloat16 caches are supported", fn);
+  if (!seq_lens || (reinterpret_cast<uintptr_t>(seq_lens) & 3u))
+    return fail(LRKV_ERR_INVALID_ARGUMENT, "%s: seq_lens is NULL or not 4-byte aligned", fn);
+  LRKV_CHECK_PTR(out, fn);
+  if (lse && !aligned16(lse)) return fail(LRKV_ERR_INVALID_ARGUMENT, "%s: lse is not 16-byte aligned", fn);
+  DecodeLayout F = decode_layout(*dims, std::max<int64_t>(max_seq_len - 1, 1), 0);
+  if (F.parts == 1) {   // one workgroup per unit attends, appends and writes the outputs
+    F.parts = 2;
+    return decode_partial(q, basis_k, coeff_k, basis_v, coeff_v, dims, max_seq_len, scale, dtype, workspace, F,
+                          stream, fn, k_new, v_new, enc_k, out, lse, seq_lens);
+  }
+  const DecodeLayout L = step_layout(*dims, max_seq_len, dtype);
+  st = decode_partial(q, basis_k, coeff_k, basis_v, coeff_v, dims, max_seq_len, scale, dtype, workspace, L, stream,
+                      fn, k_new, v_new, enc_k, nullptr, nullptr, seq_lens);
+  if (st != LRKV_OK) return st;
+  return decode_merge(out, lse, dims, dtype, workspace, L, stream, fn);
 }
 
 size_t lrkv_compress_hybrid_workspace_bytes(const lrkv_dims* dims, int64_t n_tokens) {

@@ -29,8 +29,14 @@ struct SplitArgs {
   const void* basis_v;   // [Hkv, d, rv] (nullptr: no lift; partials are rv wide)
   int64_t cap;
   int rk, rv, d, g, hq, hkv, batch;
-  int64_t n_static;      // context length when n_dev is null
+  int64_t n_static;      // context length when n_dev and n_ctx_b are null
   const int32_t* n_dev;  // per-(b, h) token counts on the device, or null
+  // Per-sequence context lengths on the device ([B], the appended token
+  // included), or null.  A length outside [1, cap] attends nothing (out 0,
+  // lse -inf) and appends nothing.  With it the host plans n_splits splits
+  // for a length bound and each workgroup's run of chunks is derived on the
+  // device from the length (chunks_per_split is not used).
+  const int32_t* n_ctx_b;
   int chunks_per_split;
   int n_splits;
   int n_parts;           // partials per (b, q head): one per attention workgroup
@@ -88,8 +94,15 @@ struct OjaArgs {
   float* ws_sum;         // [Hkv, d * R + R * R] their sums
   int n_wg;              // stats workgroups per kv head
 };
-int oja_rank_pad(int rank);
-size_t oja_workspace_floats(int hkv, int d, int rank, int n_wg);
+// Oja workspace layout: per head and stats workgroup, the partial sums
+// S1 [d][R] then S2 [R][R], R = rank padded to whole 16-column blocks; then
+// per head their sums.
+__host__ __device__ inline int64_t oja_head_floats(int d, int r_pad) { return (int64_t)d * r_pad + (int64_t)r_pad * r_pad; }
+inline int oja_rank_pad(int rank) { return 16 * ((rank + 15) / 16); }
+inline size_t oja_workspace_floats(int hkv, int d, int rank, int n_wg) {
+  const int64_t per_head = oja_head_floats(d, oja_rank_pad(rank));
+  return (size_t)((int64_t)hkv * n_wg * per_head + (int64_t)hkv * per_head);
+}
 hipError_t launch_oja_update(const OjaArgs& a, hipStream_t s);
 
 hipError_t launch_split_bf16(const SplitArgs& a, hipStream_t s);

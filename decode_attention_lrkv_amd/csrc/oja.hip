@@ -54,8 +54,8 @@ __host__ __device__ constexpr bool oja_s2_formed(int na, int nb, int nb_total) {
 }
 
 // Per-head partial sums of one stats workgroup: S1 [D][R] then S2 [R][R]
-// (the tiles oja_s2_formed names; the others are not written).
-__host__ __device__ inline int64_t oja_head_floats(int d, int r_pad) { return (int64_t)d * r_pad + (int64_t)r_pad * r_pad; }
+// (the tiles oja_s2_formed names; the others are not written); the layout
+// helper oja_head_floats is in lrkv_internal.h.
 
 // Wave w owns the 16-column coefficient blocks w, w + W, ... (NBW of them at
 // most): it keeps their B^T rows in registers for the whole launch, computes
@@ -354,13 +354,6 @@ __global__ __launch_bounds__(256) void oja_apply_kernel(OjaArgs a) {
 }
 
 }  // namespace
-
-int oja_rank_pad(int rank) { return 16 * ((rank + 15) / 16); }
-
-size_t oja_workspace_floats(int hkv, int d, int rank, int n_wg) {
-  const int64_t per_head = oja_head_floats(d, oja_rank_pad(rank));
-  return (size_t)((int64_t)hkv * n_wg * per_head + (int64_t)hkv * per_head);
-}
 
 #define LRKV_OJA_CASE4(D, NB)                                                                   \
   case NB:                                                                                      \

@@ -255,6 +255,40 @@ lrkv_status lrkv_decode_step_merge(void* out, float* lse, const lrkv_dims* dims,
                                    void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * Decode with the context lengths on the device, so that one captured HIP
+ * graph serves a decode that advances ("Llama-3.1-NovaKV" model card, results
+ * section: decode runs from a fixed-shape cache through a captured graph; a
+ * graph replays its launches with the same arguments, so a length the host
+ * passes by value would be frozen into it).  Same computation as
+ * lrkv_decode_attn / lrkv_decode_step, with sequence b of the batch taking
+ * its own length n = seq_lens[b]:
+ *   _attn_seqlens   attends rows [0, n) of sequence b;
+ *   _step_seqlens   appends the step's token at row n - 1 of sequence b
+ *                   (compress as lrkv_decode_step) and attends rows [0, n).
+ * A length outside [1, capacity] gives out = 0 and lse = -inf for that
+ * sequence's heads, and the step writes no cache row for it.
+ *   seq_lens     [B] int32, device, read only (the caller advances it, for
+ *                example with a kernel of its own recorded in the same graph)
+ *   max_seq_len  host upper bound the split plan is made for, in
+ *                [1, capacity]; any lengths are attended correctly, but
+ *                lengths far above it use fewer workgroups than the chip has
+ *   workspace    at least lrkv_decode_workspace_bytes(dims, max_seq_len, 0)
+ *                (_attn_seqlens) or lrkv_decode_step_workspace_bytes(dims,
+ *                max_seq_len) (_step_seqlens) bytes
+ * Other arguments as lrkv_decode_attn / lrkv_decode_step.  bfloat16 only.
+ */
+lrkv_status lrkv_decode_attn_seqlens(const void* q, const void* basis_k, const void* coeff_k,
+                                     const void* basis_v, const void* coeff_v, void* out, float* lse,
+                                     const lrkv_dims* dims, const int32_t* seq_lens, int64_t max_seq_len,
+                                     float scale, lrkv_dtype dtype, void* workspace, size_t workspace_bytes,
+                                     hipStream_t stream);
+lrkv_status lrkv_decode_step_seqlens(const void* q, const void* k_new, const void* v_new, const void* basis_k,
+                                     void* coeff_k, const void* basis_v, void* coeff_v, const void* enc_k, void* out,
+                                     float* lse, const lrkv_dims* dims, const int32_t* seq_lens, int64_t max_seq_len,
+                                     float scale, lrkv_dtype dtype, void* workspace, size_t workspace_bytes,
+                                     hipStream_t stream);
+
+/*
  * lrkv_decode_step without a workspace argument, for callers that cannot
  * allocate device memory: code under HIP graph capture, tight serving loops,
  * harnesses that forbid allocation.  Same arguments (minus the workspace),

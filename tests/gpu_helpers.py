@@ -69,9 +69,21 @@ GATE = {"f32": 1e-4, "bf16": 2e-2}
 LSE_GATE = {"f32": 1e-5, "bf16": 1e-3}
 
 
-def check_decode(o_gpu, lse_gpu, o_ref, lse_ref, dtype: str, what: str = ""):
+def check_decode(o_gpu, lse_gpu, o_ref, lse_ref, dtype: str, what: str = "", storage_rounding: bool = False):
+    """Decode gate per output row (see GATE).  storage_rounding=True (latent
+    outputs, whose elements scale with the coefficient spectrum instead of
+    being unit scale) also allows each element the half bfloat16 ulp that
+    storing the exact result itself costs: |o_gpu - o_ref| <= 2e-2 rms(o_ref)
+    + ulp(o_ref) / 2.  On the latent rows of the batched workload that rounding
+    alone reaches 2.0e-2 of the row RMS (a row's largest element is up to 7x
+    its RMS), so no bfloat16 output could meet the plain gate there."""
     mode = "max" if dtype == "f32" else "rms"
-    e = row_errors(o_gpu, o_ref, mode)
+    if storage_rounding and dtype == "bf16":
+        den = np.maximum(np.sqrt(np.mean(o_ref ** 2, axis=-1)), 1e-30)
+        excess = np.abs(o_gpu - o_ref) - 0.5 * bf16_ulp(o_ref)
+        e = np.max(excess, axis=-1) / den
+    else:
+        e = row_errors(o_gpu, o_ref, mode)
     assert np.all(np.isfinite(o_gpu)), f"{what}: non-finite output"
     assert e.max() <= GATE[dtype], f"{what}: worst row error {e.max():.3e} > {GATE[dtype]}"
     if lse_gpu is not None:

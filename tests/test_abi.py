@@ -32,7 +32,8 @@ def test_header_declares_the_entry_points():
               "lrkv_decode_attn_partial", "lrkv_decode_attn_merge", "lrkv_compress_hybrid_workspace_bytes",
               "lrkv_decode_step", "lrkv_decode_step_workspace_bytes", "lrkv_decode_step_partial",
               "lrkv_decode_step_merge", "lrkv_decode_attn_latent", "lrkv_oja_update",
-              "lrkv_oja_workspace_bytes", "lrkv_decode_step_noalloc", "lrkv_decode_step_noalloc_max_bytes"):
+              "lrkv_oja_workspace_bytes", "lrkv_decode_attn_seqlens", "lrkv_decode_step_seqlens",
+              "lrkv_decode_step_noalloc", "lrkv_decode_step_noalloc_max_bytes"):
         assert n in names
 
 
@@ -163,6 +164,36 @@ def test_decode_step_validation():
     assert f(*args(enc=P, ws_bytes=16)) == 3
     g = lib.lrkv_decode_step_partial
     assert g(P, P, P, P, P, P, P, MIS, ctypes.byref(d), 100, 0.0, 1, P, 1 << 30, None) == 1
+
+
+def test_seqlens_validation():
+    """The device-length calls check the plan bound, the lengths pointer,
+    the dtype and the workspace before any launch."""
+    lrkv, lib = _lib()
+    d = _dims(lrkv)
+    need = lib.lrkv_decode_workspace_bytes(ctypes.byref(d), 256, 0)
+    f = lib.lrkv_decode_attn_seqlens
+    # q, basis_k, coeff_k, basis_v, coeff_v, out, lse, dims, seq_lens, max_seq_len, scale, dtype, ws, bytes, stream
+    args = lambda lens=P, mx=256, dtype=1, ws_bytes=need, scale=0.0: (P, P, P, P, P, P, None, ctypes.byref(d),
+                                                                      lens, mx, scale, dtype, P, ws_bytes, None)
+    assert f(*args(lens=None)) == 1 and b"seq_lens" in lib.lrkv_last_error()
+    assert f(*args(lens=ctypes.c_void_p(18))) == 1 and b"seq_lens" in lib.lrkv_last_error()
+    assert f(*args(mx=0)) == 1 and f(*args(mx=257)) == 1
+    assert f(*args(dtype=0)) == 2
+    assert f(*args(ws_bytes=need - 256)) == 3
+    assert f(*args(scale=float("nan"))) == 1
+    g = lib.lrkv_decode_step_seqlens
+    need_s = lib.lrkv_decode_step_workspace_bytes(ctypes.byref(d), 256)
+    # q, k_new, v_new, basis_k, coeff_k, basis_v, coeff_v, enc_k, out, lse, dims, seq_lens, max_seq_len,
+    # scale, dtype, ws, bytes, stream
+    sargs = lambda lens=P, mx=256, dtype=1, ws_bytes=need_s, k_new=P: (P, k_new, P, P, P, P, P, None, P, None,
+                                                                       ctypes.byref(d), lens, mx, 0.0, dtype, P,
+                                                                       ws_bytes, None)
+    assert g(*sargs(lens=None)) == 1
+    assert g(*sargs(k_new=None)) == 1
+    assert g(*sargs(mx=300)) == 1
+    assert g(*sargs(dtype=0)) == 2
+    assert g(*sargs(ws_bytes=16)) == 3
 
 
 def test_noalloc_refuses_oversized_requests_before_any_device_call():

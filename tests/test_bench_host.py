@@ -1,0 +1,39 @@
+"""Host-side pieces of the benchmark that run without a GPU: the percentile
+summary and the HIP device attributes it reads the memory clock and bus width
+with."""
+import os
+import subprocess
+
+import numpy as np
+import pytest
+
+import bench
+
+
+def test_stats_percentiles():
+    s = bench.stats(np.arange(1, 101, dtype=np.float64))
+    assert s["n"] == 100 and s["mean"] == 50.5 and s["p50"] == 50.5
+    assert s["p10"] == pytest.approx(np.percentile(np.arange(1, 101), 10))
+    assert s["p90"] == pytest.approx(np.percentile(np.arange(1, 101), 90))
+    assert bench.stats([7.0])["p10"] == 7.0
+
+
+def test_device_attribute_numbers_match_the_installed_header():
+    """device_peak_gbps asks hipDeviceGetAttribute for attributes 59 and 60;
+    the installed HIP header must give those numbers to the memory bus width
+    and the memory clock rate."""
+    header = "/opt/rocm/include/hip/hip_runtime_api.h"
+    if not os.path.exists(header):
+        pytest.skip("no HIP headers")
+    src = ("#include <hip/hip_runtime_api.h>\n#include <stdio.h>\n"
+           "int main(void) { printf(\"%d %d\", (int)hipDeviceAttributeMemoryBusWidth,"
+           " (int)hipDeviceAttributeMemoryClockRate); return 0; }\n")
+    exe = os.path.join("/tmp", f"lrkv_attr_{os.getpid()}")
+    r = subprocess.run(["gcc", "-x", "c", "-D__HIP_PLATFORM_AMD__", "-I/opt/rocm/include", "-", "-o", exe],
+                       input=src, capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr
+    try:
+        out = subprocess.run([exe], capture_output=True, text=True).stdout.split()
+    finally:
+        os.remove(exe)
+    assert out == ["59", "60"]

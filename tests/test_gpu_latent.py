@@ -5,6 +5,8 @@ projections: "Llama-3.1-NovaKV" model card, introduction).
 The oracle attends the coefficient rows as keys and values (decode_latent);
 the GPU runs lrkv_decode_attn_latent on the same bits.  Value ranks whose
 quarter is not a power of two (72, 112, 20) exercise the merge's masked lanes.
+The bfloat16 gate allows each latent element the half ulp its own storage
+costs (the elements scale with the coefficient spectrum; see check_decode).
 """
 import math
 
@@ -51,5 +53,5 @@ def test_latent_decode(case):
     o, lse = lrkv.decode_attn_latent(to_dev(q, dtype), ckd, cvd, N, d)
     torch.cuda.synchronize()
     assert tuple(o.shape) == (B, w.n_q_heads, rv)
-    check_decode(to_f64(o), to_f64(lse), o_ref, lse_ref, dtype, f"latent {case}")
+    check_decode(to_f64(o), to_f64(lse), o_ref, lse_ref, dtype, f"latent {case}", storage_rounding=True)
 

@@ -16,7 +16,7 @@ import torch
 
 import lrkv_synth as synth
 from oracle import lrkv_oracle as O
-from tests.gpu_helpers import DEV, bits, to_dev, to_f64
+from tests.gpu_helpers import DEV, bits, check_decode, to_dev, to_f64
 
 pytestmark = pytest.mark.gpu
 
@@ -176,3 +176,53 @@ def test_oja_graph_replays_equal_eager_steps():
         torch.cuda.synchronize()
         assert torch.equal(bf.view(torch.int16), eager_bf[i].view(torch.int16)), f"replay {i}"
     assert torch.equal(basis, eager)
+
+
+@pytest.mark.parametrize("eta", [2e-3, 8e-3])
+def test_decode_step_after_an_update_at_decode_shape(eta):
+    """The update in decoding ("OjaKV" README, Method Summary, OjaKV: the
+    subspace is updated during decoding too), at the decode step's shape:
+    batch 16, one token per sequence, 8 kv heads, ranks 48 / 112.  Both bases
+    are updated from the step's token, then the decode step compresses that
+    token with the updated bases and attends all N rows through them; rows
+    already in the cache keep the coefficients of the starting bases (they are
+    not re-projected).  GPU and oracle each run the whole sequence from the
+    same tokens and starting bases.  The drift those old rows cause (the
+    output through the updated bases against the output through the starting
+    bases, in units of the output's RMS) is printed."""
+    w = synth.scaled(synth.BATCHED_32K, n_ctx=(2048,))
+    layer, N = 1, 2048
+    B, Hq, H, d = w.batch, w.n_q_heads, w.n_kv_heads, w.head_dim
+    ck = synth.stack_heads(w, lambda b, h: synth.direct_coeffs(w, layer, "k", b, h, N - 1))
+    cv = synth.stack_heads(w, lambda b, h: synth.direct_coeffs(w, layer, "v", b, h, N - 1))
+    xk = _tokens(w, layer, "k", 1, synth.PART_APPEND)
+    xv = _tokens(w, layer, "v", 1, synth.PART_APPEND)
+    q = synth.query(w, layer)
+    bk0, bv0 = synth.basis(w, layer, "k").exact, synth.basis(w, layer, "v").exact
+    # GPU: update both float32 bases from the token, then one decode step through the bfloat16 copies
+    bk32 = torch.from_numpy(bk0.astype(np.float32)).to(DEV)
+    bv32 = torch.from_numpy(bv0.astype(np.float32)).to(DEV)
+    kn, vn = to_dev(xk, "bf16"), to_dev(xv, "bf16")
+    bkb = lrkv.oja_update(kn, bk32, eta)
+    bvb = lrkv.oja_update(vn, bv32, eta)
+    ckd = to_dev(np.concatenate([ck.store, np.zeros((B, H, 1, ck.store.shape[-1]), np.uint16)], 2), "bf16")
+    cvd = to_dev(synth.to_value_octets(np.concatenate([cv.store, np.zeros((B, H, 1, cv.store.shape[-1]),
+                                                                            np.uint16)], 2)), "bf16")
+    o, lse = lrkv.decode_step(to_dev(q, "bf16"), kn.view(B, H, d), vn.view(B, H, d), bkb, ckd, bvb, cvd, N)
+    torch.cuda.synchronize()
+    # oracle: the same sequence in float64 (bases rounded to bfloat16 where the cache and decode take them)
+    bk1 = O.round_storage(O.oja_update_heads(bk0, xk.exact, eta), "bf16")
+    bv1 = O.round_storage(O.oja_update_heads(bv0, xv.exact, eta), "bf16")
+    assert np.any(bk1 != bk0) and np.any(bv1 != bv0)   # the step moved both bfloat16 bases
+
+    def run(bk, bv):
+        ak = O.round_storage(O.compress(xk.exact, bk), "bf16")
+        av = O.round_storage(O.compress(xv.exact, bv), "bf16")
+        return O.decode(q.exact, bk, np.concatenate([ck.exact, ak], 2), bv, np.concatenate([cv.exact, av], 2), N)
+
+    o_ref, lse_ref = run(bk1, bv1)
+    check_decode(to_f64(o), to_f64(lse), o_ref, lse_ref, "bf16", f"decode after an update, eta {eta}")
+    o_start, _ = run(bk0, bv0)
+    drift = np.max(np.abs(o_ref - o_start), -1) / np.sqrt(np.mean(o_ref ** 2, -1))
+    print(f"[oja decode] eta {eta}: drift of the output through the updated bases, max {drift.max():.3e}, "
+          f"median {np.median(drift):.3e} of the row RMS", flush=True)

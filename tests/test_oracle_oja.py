@@ -155,3 +155,34 @@ def test_planted_oja_mistakes_are_caught(monkeypatch, mutant):
             except (AssertionError, np.linalg.LinAlgError):
                 failed += 1
     assert failed > 0, f"{mutant.__name__} passed every pin"
+
+
+def test_old_rows_read_through_an_updated_basis_drift_in_proportion_to_the_step():
+    """Rows compressed with the starting basis keep their coefficients after an
+    update, so decoding them through the updated bases moves the output.  The
+    move is first order in eta (doubling eta doubles it, to within the
+    second-order term) and vanishes when the update's tokens lie in the span
+    (the fixed point): the size of the drift that leaving old rows as stored
+    causes."""
+    rng = np.random.default_rng(31)
+    d, rk, rv, n, T = 16, 6, 8, 40, 12
+    bk0 = _orthonormal(rng, d, rk)[None]
+    bv0 = _orthonormal(rng, d, rv)[None]
+    ck = rng.standard_normal((1, 1, n, rk))
+    cv = rng.standard_normal((1, 1, n, rv))
+    q = rng.standard_normal((1, 2, d))
+    xk = rng.standard_normal((1, T, 1, d))
+    xv = rng.standard_normal((1, T, 1, d))
+    o0, _ = O.decode(q, bk0, ck, bv0, cv, n)
+
+    def drift(eta, xk=xk, xv=xv):
+        o1, _ = O.decode(q, O.oja_update_heads(bk0, xk, eta), ck, O.oja_update_heads(bv0, xv, eta), cv, n)
+        return np.abs(o1 - o0).max()
+
+    d1, d2, d4 = drift(1e-5), drift(2e-5), drift(4e-5)
+    assert d1 > 0
+    assert abs(d2 / d1 - 2) < 0.01 and abs(d4 / d2 - 2) < 0.01
+    # tokens inside the span leave the bases, and so the output, unchanged
+    in_k = (rng.standard_normal((1, T, 1, rk)) @ bk0[0].T)
+    in_v = (rng.standard_normal((1, T, 1, rv)) @ bv0[0].T)
+    assert drift(1e-2, in_k, in_v) < 1e-12
