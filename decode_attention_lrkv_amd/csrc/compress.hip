@@ -42,7 +42,7 @@ struct CompressSmem {
 template <int D, int NB>
 __device__ __forceinline__ void compress_part(const CompressArgs& a, CompressSmem<D, NB>& sm) {
   const int tid = threadIdx.x;
-  const int wave = tid >> 6;
+  const int wave = wave_id();
   const int lane = tid & 63;
   const int n16 = lane & 15;
   const int grp = lane >> 4;

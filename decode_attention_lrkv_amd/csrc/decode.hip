@@ -150,7 +150,7 @@ __device__ __forceinline__ MergeState merge_two(const MergeState& a, const Merge
 template <typename T>
 __device__ void merge_unit(const MergeArgs& a, int64_t unit) {
   constexpr int kU = 16;
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int wave = wave_id(), lane = threadIdx.x & 63;
   const int S = a.n_parts, d = a.d, g = a.g;
   // d / 4 float4 columns, rounded up to a power of two lanes (a latent
   // output's width r_V need not be one); lanes past the width compute
@@ -245,7 +245,7 @@ template <int KC, int VB, bool FOLD, int STAGES, bool ENC = false>
 __device__ __forceinline__ void split_bf16_body(const SplitArgs& a, int wg, int part, SplitSmem& sm,
                                                 bool append = false) {
   const int tid = threadIdx.x;
-  const int wave = tid >> 6;
+  const int wave = wave_id();
   const int lane = tid & 63;
   const int n16 = lane & 15;     // matrix row/column index this lane supplies
   const int grp = lane >> 4;     // k-slot group
@@ -262,9 +262,11 @@ __device__ __forceinline__ void split_bf16_body(const SplitArgs& a, int wg, int 
   uint16_t* s_bk = reinterpret_cast<uint16_t*>(sm.raw);
   float (*s_acc)[16][VB * 16] = reinterpret_cast<float (*)[16][VB * 16]>(sm.raw);
 
+  // lengths on the device are the same for the whole workgroup: read as
+  // scalars, so that the buffer resources built from them stay scalar
   int64_t n_end = a.n_static;
   if (a.n_dev) {
-    n_end = a.n_dev[bh];
+    n_end = __builtin_amdgcn_readfirstlane(a.n_dev[bh]);
     if (n_end > a.cap) n_end = a.cap;
     if (n_end < 0) n_end = 0;
   }
@@ -275,7 +277,7 @@ __device__ __forceinline__ void split_bf16_body(const SplitArgs& a, int wg, int 
   const bool tok_slot = append;
   int64_t cps = a.chunks_per_split;
   if (a.n_ctx_b) {
-    const int64_t total = a.n_ctx_b[b];
+    const int64_t total = __builtin_amdgcn_readfirstlane(a.n_ctx_b[b]);
     const bool ok = total >= 1 && total <= a.cap;
     n_end = ok ? (a.k_new ? total - 1 : total) : 0;
     append_row = total - 1;
@@ -795,7 +797,7 @@ void split_bf16_hybrid_kernel(SplitArgs lr, SplitArgs side) {
   __shared__ SplitSmem sm;
   const int64_t bh = (int64_t)blockIdx.z * lr.hkv + blockIdx.y;
   auto count = [](const SplitArgs& a, int64_t bh) {
-    int64_t n = a.n_dev[bh];
+    int64_t n = __builtin_amdgcn_readfirstlane(a.n_dev[bh]);
     return n < 0 ? (int64_t)0 : (n > a.cap ? a.cap : n);
   };
   const int64_t ch_lr = (count(lr, bh) + kChunk - 1) / kChunk;
@@ -830,7 +832,7 @@ void split_bf16_hybrid_kernel(SplitArgs lr, SplitArgs side) {
 // ----------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void split_f32_kernel(SplitArgs a) {
   const int tid = threadIdx.x;
-  const int wave = tid >> 6;
+  const int wave = wave_id();
   const int lane = tid & 63;
   const int h = blockIdx.y;
   const int b = blockIdx.z;

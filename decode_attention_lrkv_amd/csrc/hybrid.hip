@@ -152,7 +152,7 @@ template <int D, int NB>
 __global__ __launch_bounds__(kThreadsH) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void hybrid_select_kernel(HybridArgs a) {
   extern __shared__ __attribute__((aligned(16))) uint16_t smem[];
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int tid = threadIdx.x, wave = wave_id(), lane = tid & 63;
   const int n16 = lane & 15, grp = lane >> 4;
   const int h = blockIdx.y, b = blockIdx.z;
   const int64_t bh = (int64_t)b * a.hkv + h;
@@ -323,7 +323,7 @@ __global__ __launch_bounds__(kThreadsH) __attribute__((amdgpu_waves_per_eu(2, 2)
 void hybrid_write_kernel(HybridArgs a) {
   extern __shared__ __attribute__((aligned(16))) uint16_t smem[];
   using R = WriteRings<D, NB>;
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int tid = threadIdx.x, wave = wave_id(), lane = tid & 63;
   const int n16 = lane & 15, grp = lane >> 4;
   const int h = blockIdx.y, b = blockIdx.z;
   const int64_t bh = (int64_t)b * a.hkv + h;
@@ -499,7 +499,7 @@ __global__ __launch_bounds__(256) void hybrid_scan_kernel(HybridArgs a) {
   constexpr int kPer = 32;                       // counts per lane per round
   constexpr int kWaveSpan = 64 * kPer;
   constexpr int kRound = kWavesH * kWaveSpan;
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int tid = threadIdx.x, wave = wave_id(), lane = tid & 63;
   const int64_t bh = (int64_t)blockIdx.y * a.hkv + blockIdx.x;
   const int n = a.n_tiles;
   const __amdgpu_buffer_rsrc_t rs_cnt = make_rsrc(a.ws_counts + bh * n, (uint32_t)n * 4u);

@@ -83,6 +83,15 @@ __device__ __forceinline__ void buf_store1(__amdgpu_buffer_rsrc_t r, uint32_t vo
   __builtin_amdgcn_raw_buffer_store_b8(v, r, (int)voff, 0, 0);
 }
 
+// Index of the calling wave in its workgroup as a wave-uniform (scalar)
+// value.  threadIdx.x / 64 is the same on every lane of a wave, but the
+// compiler's divergence analysis does not know that; chunk indices and buffer
+// resources derived from it would then count as per-lane, and every buffer
+// load through such a resource becomes a loop over the lanes' distinct
+// resources (readfirstlane, compare, exec mask, branch) instead of one
+// instruction.
+__device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
+
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 
 __device__ __forceinline__ float wave_max(float v) {

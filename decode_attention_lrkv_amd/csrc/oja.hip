@@ -70,7 +70,7 @@ __global__ __launch_bounds__(64 * W) void oja_stats_kernel(OjaArgs a) {
   constexpr int STEP = oja_step<W>();
   constexpr int UNROLL = W == 4 ? 4 : 2;   // token-block and k-step loops (full unroll at 8 waves spills)
   __shared__ __attribute__((aligned(16))) OjaSmem<D, NB, W> sm;
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int tid = threadIdx.x, wave = wave_id(), lane = tid & 63;
   const int n16 = lane & 15, grp = lane >> 4;
   const int h = blockIdx.y;
   const int r = a.rank;
