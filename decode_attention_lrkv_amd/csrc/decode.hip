@@ -796,33 +796,43 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void split_bf16_hybrid_kernel(SplitArgs lr, SplitArgs side) {
   __shared__ SplitSmem sm;
   const int64_t bh = (int64_t)blockIdx.z * lr.hkv + blockIdx.y;
+  // the two lists' lengths, read once as scalars and handed to the body as
+  // static lengths (the body reads no count of its own); a cache holds fewer
+  // than 2^31 tokens, so 32-bit arithmetic suffices for the division
   auto count = [](const SplitArgs& a, int64_t bh) {
-    int64_t n = __builtin_amdgcn_readfirstlane(a.n_dev[bh]);
-    return n < 0 ? (int64_t)0 : (n > a.cap ? a.cap : n);
+    const int n = __builtin_amdgcn_readfirstlane(a.n_dev[bh]);
+    return n < 0 ? 0 : (n > a.cap ? (int)a.cap : n);
   };
-  const int64_t ch_lr = (count(lr, bh) + kChunk - 1) / kChunk;
-  const int64_t ch_side = (count(side, bh) + kChunk - 1) / kChunk;
-  const int64_t P = gridDim.x;
-  int64_t p_side = 0;
+  const int n_lr = count(lr, bh), n_side = count(side, bh);
+  const int ch_lr = (n_lr + kChunk - 1) / kChunk;
+  const int ch_side = (n_side + kChunk - 1) / kChunk;
+  const int P = gridDim.x;
+  int p_side = 0;
   if (ch_side > 0) {
     if (ch_lr == 0) {
       p_side = P;
     } else {
-      const int64_t w_lr = ch_lr * (lr.rk + lr.rv), w_side = ch_side * 2 * lr.d;
-      p_side = (P * w_side + (w_lr + w_side) / 2) / (w_lr + w_side);
+      // round(P * bytes_side / (bytes_lr + bytes_side)) in double (exact
+      // enough for these ranges, and without a 64-bit integer division)
+      const double w_lr = (double)ch_lr * (lr.rk + lr.rv), w_side = (double)ch_side * (2 * lr.d);
+      p_side = (int)floor(P * w_side / (w_lr + w_side) + 0.5);
       p_side = p_side < 1 ? 1 : (p_side > P - 1 ? P - 1 : p_side);
     }
   }
-  const int64_t p_lr = P - p_side;
+  const int p_lr = P - p_side;
   const int x = blockIdx.x;
   if (x < p_lr) {
     SplitArgs a = lr;
-    a.chunks_per_split = (int)((ch_lr + p_lr * kWaves - 1) / (p_lr * kWaves));
+    a.n_dev = nullptr;
+    a.n_static = n_lr;
+    a.chunks_per_split = (int)(((unsigned)ch_lr + (unsigned)p_lr * kWaves - 1) / ((unsigned)p_lr * kWaves));
     split_bf16_body<KC, VB, true, kStages<KC, VB>>(a, x, x, sm);
   } else {
     SplitArgs a = side;
-    a.chunks_per_split = (int)((ch_side + p_side * kWaves - 1) / (p_side * kWaves));
-    split_bf16_body<SKC, SVB, false, 1>(a, x - (int)p_lr, x, sm);
+    a.n_dev = nullptr;
+    a.n_static = n_side;
+    a.chunks_per_split = (int)(((unsigned)ch_side + (unsigned)p_side * kWaves - 1) / ((unsigned)p_side * kWaves));
+    split_bf16_body<SKC, SVB, false, 1>(a, x - p_lr, x, sm);
   }
 }
 
