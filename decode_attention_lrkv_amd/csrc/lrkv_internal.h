@@ -94,6 +94,9 @@ struct OjaArgs {
   float* ws_sum;         // [Hkv, d * R + R * R] their sums
   int n_wg;              // stats workgroups per kv head
 };
+// Oja updates of at most this many tokens per head (a decode step's) run as
+// a single launch that needs no workspace.
+constexpr int kOjaSmallTokens = 64;
 // Oja workspace layout: per head and stats workgroup, the partial sums
 // S1 [d][R] then S2 [R][R], R = rank padded to whole 16-column blocks; then
 // per head their sums.

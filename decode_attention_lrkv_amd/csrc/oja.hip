@@ -18,6 +18,8 @@
 //   apply   B + eta (S1 - B S2) in float32 per 4-row block of B, written
 //           back to the float32 basis and, rounded to nearest even, to the
 //           bfloat16 copy.
+// Chunks of at most kOjaSmallTokens tokens per head take a single launch
+// instead (oja_small_kernel, the same update in its per-token form).
 #include "lrkv_device.h"
 #include "lrkv_internal.h"
 
@@ -353,6 +355,124 @@ __global__ __launch_bounds__(256) void oja_apply_kernel(OjaArgs a) {
   }
 }
 
+// Chunks of at most kOjaSmallTokens tokens per head (a decode step's
+// tokens): the whole update of a head's basis in one workgroup, in float32
+// on the vector ALUs, in the per-token form of the rule.  With
+// Y = X B and the residuals R = X - Y B^T,
+//   X^T Y - B Y^T Y = (X - Y B^T)^T Y = R^T Y,
+// which takes 3 n d r multiply-adds against the d r^2 of forming B Y^T Y,
+// and one launch instead of three.  The workgroup reads its head's basis
+// into LDS before anything is written, and no other workgroup touches that
+// head, so the update is in place.
+constexpr int kOjaSmallThreads = 512;
+template <int D>
+__global__ __launch_bounds__(kOjaSmallThreads) void oja_small_kernel(OjaArgs a) {
+  constexpr int P = D + 4;                  // row pitch of the token-by-dim and basis rows (floats)
+  __shared__ __attribute__((aligned(16))) float s_x[kOjaSmallTokens][P];   // X, then R
+  __shared__ __attribute__((aligned(16))) float s_b[D][P];                 // B [dim][coefficient]
+  __shared__ __attribute__((aligned(16))) float s_y[kOjaSmallTokens][P];   // Y [token][coefficient]
+  const int tid = threadIdx.x, h = blockIdx.x;
+  const int r = a.rank, n = (int)a.n_tokens;
+  float* bs = a.basis + (int64_t)h * D * r;
+  // 1. the basis and the tokens (zero rows past n) into LDS, as float32;
+  //    every load of a thread is issued before the first store
+  constexpr int kB4 = D * D / 4 / kOjaSmallThreads;              // float4 of B per thread, at most
+  constexpr int kX8 = kOjaSmallTokens * D / 8 / kOjaSmallThreads; // 8-token-element pieces per thread
+  const uint16_t* x = static_cast<const uint16_t*>(a.x);
+  f32x4 bv[kB4];
+  u32x4 xv[kX8];
+#pragma unroll
+  for (int k = 0; k < kB4; ++k) {
+    const int i = tid + kOjaSmallThreads * k;
+    if (i < D * r / 4) bv[k] = *reinterpret_cast<const f32x4*>(bs + 4 * i);
+  }
+#pragma unroll
+  for (int k = 0; k < kX8; ++k) {
+    const int i = tid + kOjaSmallThreads * k;
+    const int t = (8 * i) / D, e = (8 * i) % D;
+    xv[k] = t < n ? *reinterpret_cast<const u32x4*>(x + ((int64_t)t * a.hkv + h) * D + e) : u32x4{0u, 0u, 0u, 0u};
+  }
+#pragma unroll
+  for (int k = 0; k < kB4; ++k) {
+    const int i = tid + kOjaSmallThreads * k;
+    const int e = (4 * i) / r, c = (4 * i) % r;   // r is a multiple of 8
+    if (i < D * r / 4) *reinterpret_cast<f32x4*>(&s_b[e][c]) = bv[k];
+  }
+#pragma unroll
+  for (int k = 0; k < kX8; ++k) {
+    const int i = tid + kOjaSmallThreads * k;
+    const int t = (8 * i) / D, e = (8 * i) % D;
+    *reinterpret_cast<f32x4*>(&s_x[t][e]) = f32x4{bf16_lo(xv[k][0]), bf16_hi(xv[k][0]), bf16_lo(xv[k][1]), bf16_hi(xv[k][1])};
+    *reinterpret_cast<f32x4*>(&s_x[t][e + 4]) = f32x4{bf16_lo(xv[k][2]), bf16_hi(xv[k][2]), bf16_lo(xv[k][3]), bf16_hi(xv[k][3])};
+  }
+  __syncthreads();
+  // 2. Y = X B: a thread takes one token and 8 coefficients, contracting
+  //    over the dims (a broadcast X value and two 16-byte rows of B per dim)
+  for (int i = tid; i < n * (r / 8); i += kOjaSmallThreads) {
+    const int t = i / (r / 8), c0 = 8 * (i % (r / 8));
+    float y[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+#pragma unroll 8
+    for (int e = 0; e < D; ++e) {
+      const float xv = s_x[t][e];
+      const f32x4 b0 = *reinterpret_cast<const f32x4*>(&s_b[e][c0]);
+      const f32x4 b1 = *reinterpret_cast<const f32x4*>(&s_b[e][c0 + 4]);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        y[q] = fmaf(xv, b0[q], y[q]);
+        y[4 + q] = fmaf(xv, b1[q], y[4 + q]);
+      }
+    }
+    *reinterpret_cast<f32x4*>(&s_y[t][c0]) = f32x4{y[0], y[1], y[2], y[3]};
+    *reinterpret_cast<f32x4*>(&s_y[t][c0 + 4]) = f32x4{y[4], y[5], y[6], y[7]};
+  }
+  __syncthreads();
+  // 3. R = X - Y B^T in place of X: a thread takes one token and 4 dims,
+  //    contracting over the coefficients (both rows contiguous in them)
+  for (int i = tid; i < n * (D / 4); i += kOjaSmallThreads) {
+    const int t = i / (D / 4), e0 = 4 * (i % (D / 4));
+    float acc[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll 2
+    for (int c = 0; c < r; c += 4) {
+      const f32x4 yv = *reinterpret_cast<const f32x4*>(&s_y[t][c]);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const f32x4 bv = *reinterpret_cast<const f32x4*>(&s_b[e0 + q][c]);
+        acc[q] = fmaf(yv[0], bv[0], fmaf(yv[1], bv[1], fmaf(yv[2], bv[2], fmaf(yv[3], bv[3], acc[q]))));
+      }
+    }
+#pragma unroll
+    for (int q = 0; q < 4; ++q) s_x[t][e0 + q] -= acc[q];
+  }
+  __syncthreads();
+  // 4. B += eta R^T Y: a thread takes one dim and 8 coefficients,
+  //    contracting over the tokens; float32 result and its bfloat16 copy
+  uint16_t* bb = a.basis_bf16 ? static_cast<uint16_t*>(a.basis_bf16) + (int64_t)h * D * r : nullptr;
+  for (int i = tid; i < D * (r / 8); i += kOjaSmallThreads) {
+    const int e = i / (r / 8), c0 = 8 * (i % (r / 8));
+    float g[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+#pragma unroll 4
+    for (int t = 0; t < n; ++t) {
+      const float rv = s_x[t][e];
+      const f32x4 y0 = *reinterpret_cast<const f32x4*>(&s_y[t][c0]);
+      const f32x4 y1 = *reinterpret_cast<const f32x4*>(&s_y[t][c0 + 4]);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        g[q] = fmaf(rv, y0[q], g[q]);
+        g[4 + q] = fmaf(rv, y1[q], g[4 + q]);
+      }
+    }
+    float v[8];
+#pragma unroll
+    for (int q = 0; q < 8; ++q) v[q] = fmaf(a.eta, g[q], s_b[e][c0 + q]);
+    *reinterpret_cast<f32x4*>(bs + (int64_t)e * r + c0) = f32x4{v[0], v[1], v[2], v[3]};
+    *reinterpret_cast<f32x4*>(bs + (int64_t)e * r + c0 + 4) = f32x4{v[4], v[5], v[6], v[7]};
+    if (bb) {
+      *reinterpret_cast<u32x4*>(bb + (int64_t)e * r + c0) =
+          u32x4{pack_bf16(v[0], v[1]), pack_bf16(v[2], v[3]), pack_bf16(v[4], v[5]), pack_bf16(v[6], v[7])};
+    }
+  }
+}
+
 }  // namespace
 
 #define LRKV_OJA_CASE4(D, NB)                                                                   \
@@ -367,7 +487,12 @@ __global__ __launch_bounds__(256) void oja_apply_kernel(OjaArgs a) {
 hipError_t launch_oja_update(const OjaArgs& a, hipStream_t s) {
   const int nb = (a.rank + 15) / 16;
   if (a.d != 64 && a.d != 128) return hipErrorInvalidValue;
-  if (nb < 1 || nb > a.d / 16) return hipErrorInvalidValue;
+  if (nb < 1 || nb > a.d / 16 || a.rank % 8) return hipErrorInvalidValue;
+  if (a.n_tokens <= kOjaSmallTokens) {   // a decode step's tokens: one launch
+    if (a.d == 128) hipLaunchKernelGGL(oja_small_kernel<128>, dim3(a.hkv), dim3(kOjaSmallThreads), 0, s, a);
+    else hipLaunchKernelGGL(oja_small_kernel<64>, dim3(a.hkv), dim3(kOjaSmallThreads), 0, s, a);
+    return hipGetLastError();
+  }
   if (a.d == 128) {
     switch (nb) {
       LRKV_OJA_CASE4(128, 1) LRKV_OJA_CASE4(128, 2) LRKV_OJA_CASE4(128, 3) LRKV_OJA_CASE4(128, 4)

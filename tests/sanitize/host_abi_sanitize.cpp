@@ -152,6 +152,8 @@ hipError_t launch_hybrid_bf16(const HybridArgs& a, hipStream_t) {
   return hipSuccess;
 }
 hipError_t launch_oja_update(const OjaArgs& a, hipStream_t) {
+  EXPECT(a.n_tokens >= 1, "Oja update of no tokens launched");
+  if (a.n_tokens <= kOjaSmallTokens) return hipSuccess;   // one workgroup per head, no workspace
   const int64_t per_head = oja_head_floats(a.d, oja_rank_pad(a.rank));
   EXPECT(a.ws_sum == a.ws + (int64_t)a.hkv * a.n_wg * per_head, "Oja sums not after the partials");
   touch_write(a.ws, (int64_t)a.hkv * a.n_wg * per_head);
@@ -235,7 +237,7 @@ static void decode_shapes(const lrkv_dims& d, int64_t n) {
     expect_status(lrkv_compress_kv(P, P, P, P, P, P, &d, 1, n - 1, dt, nullptr), LRKV_OK, "compress_kv one token");
   }
   for (int rank : {d.rank_k, d.rank_v}) {
-    for (int64_t T : {int64_t(1), int64_t(333), n}) {
+    for (int64_t T : {int64_t(1), int64_t(64), int64_t(65), int64_t(333), n}) {
       Buf ws(lrkv_oja_workspace_bytes(d.batch, d.n_kv_heads, d.head_dim, rank, T));
       std::vector<float> basis((size_t)d.n_kv_heads * d.head_dim * rank);
       expect_status(lrkv_oja_update(P, basis.data(), nullptr, d.batch, d.n_kv_heads, d.head_dim, rank, T, 1e-3f, ws.p,
