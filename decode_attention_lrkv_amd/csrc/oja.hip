@@ -6,7 +6,8 @@
 // resolution), and a rounded bfloat16 copy is written for the compress and
 // decode calls.  Three launches, all deterministic:
 //   stats   per (run of 16 W-token steps, kv head).  A step's tokens go to LDS
-//           (as X, and as X^T transposed on the matrix cores), loaded three
+//           (as X, and as X^T transposed on the matrix cores; tiles in a
+//           bank-conflict-free swizzled layout), loaded three
 //           steps ahead; each wave owns some 16-column coefficient blocks,
 //           computes their Y on the matrix cores (B split into high and low
 //           bfloat16 parts, held in registers, so Y keeps float32 accuracy),
@@ -27,19 +28,34 @@ namespace lrkv {
 
 namespace {
 
-// W waves per stats workgroup; a step is 16 tokens per wave.  Token-major
-// LDS rows have a pitch of 16 W + 8 bfloat16 (16-byte aligned, and not a
-// multiple of 128 bytes).
+// W waves per stats workgroup; a step is 16 tokens per wave.
 template <int W> constexpr int oja_step() { return 16 * W; }
-template <int W> constexpr int oja_pitch_t() { return 16 * W + 8; }
+
+// LDS layout of the step's bfloat16 tiles, whose rows hold COLS = 64 or 128
+// elements: rows are packed into 256-byte lines (two 64-element rows share
+// a line), and the 16-byte chunk c of line l is stored at chunk c ^ (l mod 16).
+// A matrix-core operand read (16 consecutive rows, the same 16-byte chunk of
+// each, 4 chunk groups) then touches 16 distinct chunks per group: no bank
+// conflicts, where rows padded to a 272-byte pitch spent half of the LDS's
+// active cycles in them (measured with a read probe, 3.9 conflict cycles
+// per 16-byte read).  8-byte writes of half a chunk stay conflict-free.
+// Element offset of (row, col):
+template <int COLS>
+__device__ __forceinline__ int oja_swz(int row, int col) {
+  static_assert(COLS == 64 || COLS == 128, "rows of 64 or 128 elements");
+  if (COLS == 128) return row * 128 + ((((col >> 3) ^ row) & 15) << 3) + (col & 7);
+  const int line = row >> 1, chunk = ((row & 1) << 3) | (col >> 3);
+  return line * 128 + (((chunk ^ line) & 15) << 3) + (col & 7);
+}
 
 template <int D, int NB, int W>
 struct OjaSmem {
   static constexpr int R = 16 * NB;        // rank padded to whole 16-column blocks
-  uint16_t xs[oja_step<W>()][D + 8];       // X of the step, token-major (Y's row operand)
-  uint16_t xt[D][oja_pitch_t<W>()];        // X^T of the step: [dim][token] (S1's row operand)
-  uint16_t yt_hi[R][oja_pitch_t<W>()];     // Y^T of the step: [coefficient][token], high parts
-  uint16_t yt_lo[R][oja_pitch_t<W>()];     // low parts: Y - high
+  static constexpr int S = oja_step<W>();
+  uint16_t xs[S * D];                      // X of the step, token-major [token][dim] (Y's row operand)
+  uint16_t xt[D * S];                      // X^T of the step: [dim][token] (S1's row operand)
+  uint16_t yt_hi[R * S];                   // Y^T of the step: [coefficient][token], high parts
+  uint16_t yt_lo[R * S];                   // low parts: Y - high
 };
 
 // S2 = Y^T Y is symmetric, so of its 16 x 16 tiles (row block na, column
@@ -174,13 +190,13 @@ __global__ __launch_bounds__(64 * W) void oja_stats_kernel(OjaArgs a) {
     const int tok = 16 * wave + n16;
 #pragma unroll
     for (int c = 0; c < KD; ++c) {
-      *reinterpret_cast<u32x4*>(&sm.xs[tok][32 * c + 8 * grp]) = xa[c];
+      *reinterpret_cast<u32x4*>(&sm.xs[oja_swz<D>(tok, 32 * c + 8 * grp)]) = xa[c];
 #pragma unroll
       for (int hf = 0; hf < 2; ++hf) {
         const f32x4 t = mfma_16x16x32(xa[c], eye[hf], f32x4{0.f, 0.f, 0.f, 0.f});
         const u32x2 w = u32x2{(__float_as_uint(t[0]) >> 16) | (__float_as_uint(t[1]) & 0xFFFF0000u),
                               (__float_as_uint(t[2]) >> 16) | (__float_as_uint(t[3]) & 0xFFFF0000u)};
-        *reinterpret_cast<u32x2*>(&sm.xt[32 * c + 16 * hf + n16][16 * wave + 4 * grp]) = w;
+        *reinterpret_cast<u32x2*>(&sm.xt[oja_swz<STEP>(32 * c + 16 * hf + n16, 16 * wave + 4 * grp)]) = w;
       }
     }
     __syncthreads();
@@ -194,7 +210,7 @@ __global__ __launch_bounds__(64 * W) void oja_stats_kernel(OjaArgs a) {
         const int tb = part + G * ti;
         u32x4 xo[KD];
 #pragma unroll
-        for (int c = 0; c < KD; ++c) xo[c] = *reinterpret_cast<const u32x4*>(&sm.xs[16 * tb + n16][32 * c + 8 * grp]);
+        for (int c = 0; c < KD; ++c) xo[c] = *reinterpret_cast<const u32x4*>(&sm.xs[oja_swz<D>(16 * tb + n16, 32 * c + 8 * grp)]);
 #pragma unroll
         for (int k = 0; k < NBW; ++k) {
           const int nb = bw + W * k;
@@ -211,10 +227,9 @@ __global__ __launch_bounds__(64 * W) void oja_stats_kernel(OjaArgs a) {
               hi[i] = f32_to_bf16(y[i]);
               lo[i] = f32_to_bf16(y[i] - bf16_to_f32((uint16_t)hi[i]));
             }
-            *reinterpret_cast<u32x2*>(&sm.yt_hi[16 * nb + n16][16 * tb + 4 * grp]) =
-                u32x2{hi[0] | (hi[1] << 16), hi[2] | (hi[3] << 16)};
-            *reinterpret_cast<u32x2*>(&sm.yt_lo[16 * nb + n16][16 * tb + 4 * grp]) =
-                u32x2{lo[0] | (lo[1] << 16), lo[2] | (lo[3] << 16)};
+            const int yo = oja_swz<STEP>(16 * nb + n16, 16 * tb + 4 * grp);
+            *reinterpret_cast<u32x2*>(&sm.yt_hi[yo]) = u32x2{hi[0] | (hi[1] << 16), hi[2] | (hi[3] << 16)};
+            *reinterpret_cast<u32x2*>(&sm.yt_lo[yo]) = u32x2{lo[0] | (lo[1] << 16), lo[2] | (lo[3] << 16)};
           }
         }
       }
@@ -230,13 +245,13 @@ __global__ __launch_bounds__(64 * W) void oja_stats_kernel(OjaArgs a) {
 #pragma unroll
         for (int k = 0; k < NBW; ++k) {
           const int nb = bw + W * k < NB ? bw + W * k : 0;
-          bh[k] = *reinterpret_cast<const u32x4*>(&sm.yt_hi[16 * nb + n16][t]);
-          bl[k] = *reinterpret_cast<const u32x4*>(&sm.yt_lo[16 * nb + n16][t]);
+          bh[k] = *reinterpret_cast<const u32x4*>(&sm.yt_hi[oja_swz<STEP>(16 * nb + n16, t)]);
+          bl[k] = *reinterpret_cast<const u32x4*>(&sm.yt_lo[oja_swz<STEP>(16 * nb + n16, t)]);
         }
 #pragma unroll
         for (int i = 0; i < DBW; ++i) {
           const int db = part + G * i;
-          const u32x4 xr = *reinterpret_cast<const u32x4*>(&sm.xt[16 * db + n16][t]);
+          const u32x4 xr = *reinterpret_cast<const u32x4*>(&sm.xt[oja_swz<STEP>(16 * db + n16, t)]);
 #pragma unroll
           for (int k = 0; k < NBW; ++k) {
             if (bw + W * k < NB) {
@@ -254,8 +269,8 @@ __global__ __launch_bounds__(64 * W) void oja_stats_kernel(OjaArgs a) {
               const int j = part + G * jj;
               const int na = (nb + j) % NB;
               if (j < NJ && oja_s2_formed(na, nb, NB)) {
-                const u32x4 ah = *reinterpret_cast<const u32x4*>(&sm.yt_hi[16 * na + n16][t]);
-                const u32x4 al = *reinterpret_cast<const u32x4*>(&sm.yt_lo[16 * na + n16][t]);
+                const u32x4 ah = *reinterpret_cast<const u32x4*>(&sm.yt_hi[oja_swz<STEP>(16 * na + n16, t)]);
+                const u32x4 al = *reinterpret_cast<const u32x4*>(&sm.yt_lo[oja_swz<STEP>(16 * na + n16, t)]);
                 s2[jj][k] = mfma_16x16x32(ah, bh[k], s2[jj][k]);
                 s2[jj][k] = mfma_16x16x32(ah, bl[k], s2[jj][k]);
                 s2[jj][k] = mfma_16x16x32(al, bh[k], s2[jj][k]);
