@@ -33,30 +33,29 @@ constexpr int kWavesH = 4;                 // waves per hybrid workgroup
 constexpr int kThreadsH = 64 * kWavesH;
 
 // LDS layout of one workgroup, in bfloat16 elements: both bases transposed
-// ([coefficient][dim], 16 NB rows each) and, for select, as stored ([dim]
-// [coefficient], 32 ceil(NB/2) columns each); rows and columns past a rank
-// are zero.  Row pitches are chosen so that the per-item reads are free of
-// bank conflicts on gfx950: the transposed basis is read 16 bytes per lane
-// from 16 consecutive rows (pitch of 8 x odd dwords), the natural one 8 bytes
-// per lane (pitch of 2 x odd dwords).
+// ([coefficient][dim], 16 NB rows each, unpadded in the swizzled layout of
+// lds_swz, read 16 bytes per lane from 16 consecutive rows without bank
+// conflicts) and, for select, as stored ([dim][coefficient], 32 ceil(NB/2)
+// columns each, read 8 bytes per lane, pitch of 2 x odd dwords); rows and
+// columns past a rank are zero.  Without row padding the bases and the write
+// kernel's rings of two workgroups fit one compute unit's LDS.
 struct HybridLds {
-  int rows, pitch_t, cols_n, pitch_n;
+  int rows, cols_n, pitch_n;
   int off_t[2], off_n[2];
-  int elems_write, elems_select;
+  int elems_t, elems_select;
 };
 
 __host__ __device__ inline HybridLds hybrid_lds(int d, int nb) {
   HybridLds L;
   L.rows = 16 * nb;
-  L.pitch_t = d + 16;
   L.cols_n = 32 * ((nb + 1) / 2);
   L.pitch_n = L.cols_n + 4;
   L.off_t[0] = 0;
-  L.off_t[1] = L.rows * L.pitch_t;
-  L.elems_write = 2 * L.rows * L.pitch_t;
-  L.off_n[0] = L.elems_write;
-  L.off_n[1] = L.elems_write + d * L.pitch_n;
-  L.elems_select = L.elems_write + 2 * d * L.pitch_n;
+  L.off_t[1] = L.rows * d;
+  L.elems_t = 2 * L.rows * d;
+  L.off_n[0] = L.elems_t;
+  L.off_n[1] = L.elems_t + d * L.pitch_n;
+  L.elems_select = L.elems_t + 2 * d * L.pitch_n;
   return L;
 }
 
@@ -84,13 +83,13 @@ __device__ void stage_transposed(const HybridArgs& a, const HybridLds& L, int h,
           const int dd = i % D, c = (i / D) * 8;
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
-            st[(c + 2 * e) * L.pitch_t + dd] = (uint16_t)(w[u][e] & 0xFFFFu);
-            st[(c + 2 * e + 1) * L.pitch_t + dd] = (uint16_t)(w[u][e] >> 16);
+            st[lds_swz<D>(c + 2 * e, dd)] = (uint16_t)(w[u][e] & 0xFFFFu);
+            st[lds_swz<D>(c + 2 * e + 1, dd)] = (uint16_t)(w[u][e] >> 16);
           }
         }
       }
     }
-    for (int i = tid; i < (L.rows - r) * D; i += kThreadsH) st[(r + i / D) * L.pitch_t + i % D] = 0;
+    for (int i = tid; i < (L.rows - r) * D; i += kThreadsH) st[lds_swz<D>(r + i / D, i % D)] = 0;
   }
 }
 
@@ -130,20 +129,39 @@ __device__ __forceinline__ void load_rows(const HybridArgs& a, int b, int h, int
   for (int c = 0; c < D / 32; ++c) xa[c] = buf_load16(rs, voff + 64 * c);
 }
 
+// This lane's element offsets of its transposed-basis operands (row
+// 16 nb + n16, dims 32 c + 8 grp .. + 7), computed once per kernel.  The
+// swizzle of a row depends on the row's line modulo 16 only, so blocks nb and
+// nb + P (P = 1 for 128-element rows, 2 for 64-element rows, whose 16-row
+// block fills 8 lines) differ by a constant, which the loop adds as an
+// immediate to one of P x D/32 live addresses.
+template <int D, int NB>
+struct BasisOffsets {
+  static constexpr int P = D == 64 ? 2 : 1;
+  static constexpr int kStep = P * 16 * D;
+  int o[P][D / 32];
+  __device__ __forceinline__ BasisOffsets(int n16, int grp) {
+#pragma unroll
+    for (int p = 0; p < P; ++p)
+#pragma unroll
+      for (int c = 0; c < D / 32; ++c) o[p][c] = lds_swz<D>(16 * p + n16, 32 * c + 8 * grp);
+  }
+  __device__ __forceinline__ int at(int nb, int c) const { return o[nb % P][c] + (nb / P) * kStep; }
+};
+
 // c^T = B^T x^T for the sub-tile (transposed basis as the row operand, the
 // token rows as loaded as the column operand): acc[nb] lane (n16, grp)
 // register i is coefficient 16 nb + 4 grp + i of token n16.
 template <int D, int NB>
-__device__ __forceinline__ void coeffs_t(const u32x4 (&xa)[D / 32], const uint16_t* bt, int pitch, int n16, int grp,
+__device__ __forceinline__ void coeffs_t(const u32x4 (&xa)[D / 32], const uint16_t* bt, const BasisOffsets<D, NB>& bo,
                                          f32x4 (&acc)[NB]) {
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) acc[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int c = 0; c < D / 32; ++c) {
-    const int k = 32 * c + 8 * grp;
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb)
-      acc[nb] = mfma_16x16x32(*reinterpret_cast<const u32x4*>(bt + (16 * nb + n16) * pitch + k), xa[c], acc[nb]);
+      acc[nb] = mfma_16x16x32(*reinterpret_cast<const u32x4*>(bt + bo.at(nb, c)), xa[c], acc[nb]);
   }
 }
 
@@ -163,6 +181,7 @@ void hybrid_select_kernel(HybridArgs a) {
   stage_transposed<D>(a, L, h, smem);
   stage_natural<D>(a, L, h, smem);
   __syncthreads();
+  const BasisOffsets<D, NB> bo(n16, grp);
 
   const int64_t n_waves = (int64_t)gridDim.x * kWavesH;
   const int64_t per_wave = (a.n_tiles + n_waves - 1) / n_waves;
@@ -176,7 +195,7 @@ void hybrid_select_kernel(HybridArgs a) {
   // ||x - x_hat||^2 > tau^2 ||x||^2 for token n16 of the sub-tile, one kind
   auto flagged = [&](const u32x4 (&xa)[D / 32], int kind) -> bool {
     f32x4 acc1[NB];
-    coeffs_t<D, NB>(xa, smem + L.off_t[kind], L.pitch_t, n16, grp, acc1);
+    coeffs_t(xa, smem + L.off_t[kind], bo, acc1);
     // stored coefficients round(c), packed as the column operand of x_hat^T = B round(c)^T:
     // k-slots 0..3 of block kk are coefficients 32 kk + 4 grp + 0..3, slots 4..7 are 32 kk + 16 + 4 grp + 0..3
     float cc = 0.f;
@@ -281,14 +300,14 @@ void hybrid_select_kernel(HybridArgs a) {
 // previous wave and is written slot by slot at the end).
 template <int D, int NB>
 struct WriteRings {
-  static constexpr int kLrRow = 16 * NB * 8 + 8;   // elements per ring row, padded
-  static constexpr int kSideRow = D * 8 + 8;
+  static constexpr int kLrRow = 16 * NB * 8;       // elements per ring row
+  static constexpr int kSideRow = D * 8;
   static constexpr int kPerWave = 4 * kLrRow + 4 * kSideRow;
 };
 
 template <int D, int NB>
 size_t write_lds_bytes(const HybridLds& L) {
-  return 2 * ((size_t)L.elems_write + (size_t)kWavesH * WriteRings<D, NB>::kPerWave);
+  return 2 * ((size_t)L.elems_t + (size_t)kWavesH * WriteRings<D, NB>::kPerWave);
 }
 
 // Octet row o of a ring: flush its columns col0 + 64 j with 16-byte stores
@@ -317,7 +336,8 @@ __device__ void flush_row_part(__amdgpu_buffer_rsrc_t rs, const uint16_t* ring_r
   }
 }
 
-// Two waves per SIMD: the bases and the rings of two workgroups fill a compute unit's LDS.
+// Two waves per SIMD: the bases and the rings of two workgroups fill a compute
+// unit's LDS (exactly, at head_dim 128 and ranks up to 64: 80 KB each).
 template <int D, int NB>
 __global__ __launch_bounds__(kThreadsH) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void hybrid_write_kernel(HybridArgs a) {
@@ -330,11 +350,12 @@ void hybrid_write_kernel(HybridArgs a) {
   const int64_t n_slots = (int64_t)a.n_tiles * kHybridTile;
   const HybridLds L = hybrid_lds(D, NB);
   const int rk = a.rk, rv = a.rv;
-  uint16_t* ring_lr = smem + L.elems_write + wave * R::kPerWave;
+  uint16_t* ring_lr = smem + L.elems_t + wave * R::kPerWave;
   uint16_t* ring_side = ring_lr + 4 * R::kLrRow;
 
   stage_transposed<D>(a, L, h, smem);
   __syncthreads();
+  const BasisOffsets<D, NB> bo(n16, grp);
 
   const int64_t n_waves = (int64_t)gridDim.x * kWavesH;
   const int64_t per_wave = (a.n_tiles + n_waves - 1) / n_waves;
@@ -398,7 +419,7 @@ void hybrid_write_kernel(HybridArgs a) {
 
     f32x4 acc[NB];
     // keys: coefficients 16 nb + 4 grp + 0..3 of token n16, one 8-byte store per block
-    coeffs_t<D, NB>(r.k, smem + L.off_t[0], L.pitch_t, n16, grp, acc);
+    coeffs_t(r.k, smem + L.off_t[0], bo, acc);
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
       const int col = 16 * nb + 4 * grp;
@@ -407,7 +428,7 @@ void hybrid_write_kernel(HybridArgs a) {
     }
     __builtin_amdgcn_sched_barrier(0);
     // values: into the octet rows being assembled
-    coeffs_t<D, NB>(r.v, smem + L.off_t[1], L.pitch_t, n16, grp, acc);
+    coeffs_t(r.v, smem + L.off_t[1], bo, acc);
     if (lr_ok) {
       uint16_t* rr = lr_row(p_lr >> 3) + (p_lr & 7);
 #pragma unroll
@@ -576,13 +597,12 @@ hipError_t launch_persistent(K kernel, const HybridArgs& a, size_t lds_bytes, hi
 
 template <int D, int NB>
 hipError_t launch_hybrid_nb(const HybridArgs& a, hipStream_t s) {
-  const HybridLds L = hybrid_lds(D, NB);
-  hipError_t e = launch_persistent(hybrid_select_kernel<D, NB>, a, 2 * (size_t)L.elems_select, s);
+  hipError_t e = launch_persistent(hybrid_select_kernel<D, NB>, a, 2 * (size_t)hybrid_lds(D, NB).elems_select, s);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(hybrid_scan_kernel, dim3(a.hkv, a.batch), dim3(256), 0, s, a);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  return launch_persistent(hybrid_write_kernel<D, NB>, a, write_lds_bytes<D, NB>(L), s);
+  return launch_persistent(hybrid_write_kernel<D, NB>, a, write_lds_bytes<D, NB>(hybrid_lds(D, NB)), s);
 }
 
 }  // namespace

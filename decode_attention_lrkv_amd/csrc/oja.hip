@@ -31,23 +31,9 @@ namespace {
 // W waves per stats workgroup; a step is 16 tokens per wave.
 template <int W> constexpr int oja_step() { return 16 * W; }
 
-// LDS layout of the step's bfloat16 tiles, whose rows hold COLS = 64 or 128
-// elements: rows are packed into 256-byte lines (two 64-element rows share
-// a line), and the 16-byte chunk c of line l is stored at chunk c ^ (l mod 16).
-// A matrix-core operand read (16 consecutive rows, the same 16-byte chunk of
-// each, 4 chunk groups) then touches 16 distinct chunks per group: no bank
-// conflicts, where rows padded to a 272-byte pitch spent half of the LDS's
-// active cycles in them (measured with a read probe, 3.9 conflict cycles
-// per 16-byte read).  8-byte writes of half a chunk stay conflict-free.
-// Element offset of (row, col):
-template <int COLS>
-__device__ __forceinline__ int oja_swz(int row, int col) {
-  static_assert(COLS == 64 || COLS == 128, "rows of 64 or 128 elements");
-  if (COLS == 128) return row * 128 + ((((col >> 3) ^ row) & 15) << 3) + (col & 7);
-  const int line = row >> 1, chunk = ((row & 1) << 3) | (col >> 3);
-  return line * 128 + (((chunk ^ line) & 15) << 3) + (col & 7);
-}
-
+// The step's bfloat16 tiles use the swizzled LDS layout of lds_swz (rows of
+// 64 or 128 elements), so that the matrix-core operand reads are free of bank
+// conflicts.
 template <int D, int NB, int W>
 struct OjaSmem {
   static constexpr int R = 16 * NB;        // rank padded to whole 16-column blocks
@@ -190,13 +176,13 @@ __global__ __launch_bounds__(64 * W) void oja_stats_kernel(OjaArgs a) {
     const int tok = 16 * wave + n16;
 #pragma unroll
     for (int c = 0; c < KD; ++c) {
-      *reinterpret_cast<u32x4*>(&sm.xs[oja_swz<D>(tok, 32 * c + 8 * grp)]) = xa[c];
+      *reinterpret_cast<u32x4*>(&sm.xs[lds_swz<D>(tok, 32 * c + 8 * grp)]) = xa[c];
 #pragma unroll
       for (int hf = 0; hf < 2; ++hf) {
         const f32x4 t = mfma_16x16x32(xa[c], eye[hf], f32x4{0.f, 0.f, 0.f, 0.f});
         const u32x2 w = u32x2{(__float_as_uint(t[0]) >> 16) | (__float_as_uint(t[1]) & 0xFFFF0000u),
                               (__float_as_uint(t[2]) >> 16) | (__float_as_uint(t[3]) & 0xFFFF0000u)};
-        *reinterpret_cast<u32x2*>(&sm.xt[oja_swz<STEP>(32 * c + 16 * hf + n16, 16 * wave + 4 * grp)]) = w;
+        *reinterpret_cast<u32x2*>(&sm.xt[lds_swz<STEP>(32 * c + 16 * hf + n16, 16 * wave + 4 * grp)]) = w;
       }
     }
     __syncthreads();
@@ -210,7 +196,7 @@ __global__ __launch_bounds__(64 * W) void oja_stats_kernel(OjaArgs a) {
         const int tb = part + G * ti;
         u32x4 xo[KD];
 #pragma unroll
-        for (int c = 0; c < KD; ++c) xo[c] = *reinterpret_cast<const u32x4*>(&sm.xs[oja_swz<D>(16 * tb + n16, 32 * c + 8 * grp)]);
+        for (int c = 0; c < KD; ++c) xo[c] = *reinterpret_cast<const u32x4*>(&sm.xs[lds_swz<D>(16 * tb + n16, 32 * c + 8 * grp)]);
 #pragma unroll
         for (int k = 0; k < NBW; ++k) {
           const int nb = bw + W * k;
@@ -227,7 +213,7 @@ __global__ __launch_bounds__(64 * W) void oja_stats_kernel(OjaArgs a) {
               hi[i] = f32_to_bf16(y[i]);
               lo[i] = f32_to_bf16(y[i] - bf16_to_f32((uint16_t)hi[i]));
             }
-            const int yo = oja_swz<STEP>(16 * nb + n16, 16 * tb + 4 * grp);
+            const int yo = lds_swz<STEP>(16 * nb + n16, 16 * tb + 4 * grp);
             *reinterpret_cast<u32x2*>(&sm.yt_hi[yo]) = u32x2{hi[0] | (hi[1] << 16), hi[2] | (hi[3] << 16)};
             *reinterpret_cast<u32x2*>(&sm.yt_lo[yo]) = u32x2{lo[0] | (lo[1] << 16), lo[2] | (lo[3] << 16)};
           }
@@ -245,13 +231,13 @@ __global__ __launch_bounds__(64 * W) void oja_stats_kernel(OjaArgs a) {
 #pragma unroll
         for (int k = 0; k < NBW; ++k) {
           const int nb = bw + W * k < NB ? bw + W * k : 0;
-          bh[k] = *reinterpret_cast<const u32x4*>(&sm.yt_hi[oja_swz<STEP>(16 * nb + n16, t)]);
-          bl[k] = *reinterpret_cast<const u32x4*>(&sm.yt_lo[oja_swz<STEP>(16 * nb + n16, t)]);
+          bh[k] = *reinterpret_cast<const u32x4*>(&sm.yt_hi[lds_swz<STEP>(16 * nb + n16, t)]);
+          bl[k] = *reinterpret_cast<const u32x4*>(&sm.yt_lo[lds_swz<STEP>(16 * nb + n16, t)]);
         }
 #pragma unroll
         for (int i = 0; i < DBW; ++i) {
           const int db = part + G * i;
-          const u32x4 xr = *reinterpret_cast<const u32x4*>(&sm.xt[oja_swz<STEP>(16 * db + n16, t)]);
+          const u32x4 xr = *reinterpret_cast<const u32x4*>(&sm.xt[lds_swz<STEP>(16 * db + n16, t)]);
 #pragma unroll
           for (int k = 0; k < NBW; ++k) {
             if (bw + W * k < NB) {
@@ -269,8 +255,8 @@ __global__ __launch_bounds__(64 * W) void oja_stats_kernel(OjaArgs a) {
               const int j = part + G * jj;
               const int na = (nb + j) % NB;
               if (j < NJ && oja_s2_formed(na, nb, NB)) {
-                const u32x4 ah = *reinterpret_cast<const u32x4*>(&sm.yt_hi[oja_swz<STEP>(16 * na + n16, t)]);
-                const u32x4 al = *reinterpret_cast<const u32x4*>(&sm.yt_lo[oja_swz<STEP>(16 * na + n16, t)]);
+                const u32x4 ah = *reinterpret_cast<const u32x4*>(&sm.yt_hi[lds_swz<STEP>(16 * na + n16, t)]);
+                const u32x4 al = *reinterpret_cast<const u32x4*>(&sm.yt_lo[lds_swz<STEP>(16 * na + n16, t)]);
                 s2[jj][k] = mfma_16x16x32(ah, bh[k], s2[jj][k]);
                 s2[jj][k] = mfma_16x16x32(ah, bl[k], s2[jj][k]);
                 s2[jj][k] = mfma_16x16x32(al, bh[k], s2[jj][k]);
