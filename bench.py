@@ -527,18 +527,31 @@ def device_peak_gbps(lrkv):
             "clock_x2_x_width_GBps": round(ddr, 1), "published_GBps": HBM_PEAK_GBPS}
 
 
+# the sources the attention kernel is compiled from; the counter record is
+# valid for the kernel built from exactly these
+KERNEL_SOURCES = ("decode_body.h", "decode_split.hip", "lrkv_device.h", "lrkv_internal.h")
+
+
+def kernel_sources_sha256():
+    """SHA-256 over the attention kernel's sources, in KERNEL_SOURCES order."""
+    import hashlib
+    h = hashlib.sha256()
+    for name in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "decode_attention_lrkv_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
 def measured_traffic():
     """HBM bytes per launch of the attention kernel from the committed counter
-    summary, or None when the kernel source changed since it was taken."""
-    import hashlib
+    summary, or None when the kernel's sources changed since it was taken."""
     path = os.path.join(ROOT, "profiles", "split_bf16_kernel_llama8b-b16-32k.txt")
-    src = os.path.join(ROOT, "decode_attention_lrkv_amd", "csrc", "decode.hip")
     try:
         rec = next(json.loads(l.split("TRAFFIC", 1)[1]) for l in open(path) if l.strip().startswith("TRAFFIC"))
-        sha = hashlib.sha256(open(src, "rb").read()).hexdigest()
+        sha = kernel_sources_sha256()
     except (OSError, StopIteration, ValueError):
         return None
-    return rec["mean_bytes_per_launch"] if rec.get("decode_hip_sha256") == sha else None
+    return rec["mean_bytes_per_launch"] if rec.get("kernel_src_sha256") == sha else None
 
 
 def cpu_baseline(w, budget_s):

@@ -37,3 +37,24 @@ def test_device_attribute_numbers_match_the_installed_header():
     finally:
         os.remove(exe)
     assert out == ["59", "60"]
+
+
+def test_traffic_record_is_used_only_for_the_sources_it_was_taken_with(tmp_path, monkeypatch):
+    """measured_traffic returns the profile's bytes per launch while the
+    attention kernel's sources hash to the recorded value, and None once any
+    of them changes."""
+    import json
+    import shutil
+    csrc = tmp_path / "decode_attention_lrkv_amd" / "csrc"
+    csrc.mkdir(parents=True)
+    for name in bench.KERNEL_SOURCES:
+        shutil.copy(os.path.join(bench.ROOT, "decode_attention_lrkv_amd", "csrc", name), csrc / name)
+    (tmp_path / "profiles").mkdir()
+    monkeypatch.setattr(bench, "ROOT", str(tmp_path))
+    rec = {"mean_bytes_per_launch": 12345, "kernel_src_sha256": bench.kernel_sources_sha256()}
+    (tmp_path / "profiles" / "split_bf16_kernel_llama8b-b16-32k.txt").write_text(
+        "# summary\n\n    TRAFFIC " + json.dumps(rec) + "\n")
+    assert bench.measured_traffic() == 12345
+    with open(csrc / bench.KERNEL_SOURCES[-1], "a") as f:
+        f.write("\n// changed\n")
+    assert bench.measured_traffic() is None
