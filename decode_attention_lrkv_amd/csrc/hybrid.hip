@@ -192,103 +192,134 @@ void hybrid_select_kernel(HybridArgs a) {
       make_rsrc(a.flags ? a.flags + bh * a.n_tokens : a.ws_flags, a.flags ? (uint32_t)a.n_tokens : 0u);
   const __amdgpu_buffer_rsrc_t rs_cnt = make_rsrc(a.ws_counts + bh * a.n_tiles, (uint32_t)(a.n_tiles * 4));
 
-  // ||x - x_hat||^2 > tau^2 ||x||^2 for token n16 of the sub-tile, one kind
-  auto flagged = [&](const u32x4 (&xa)[D / 32], int kind) -> bool {
-    f32x4 acc1[NB];
-    coeffs_t(xa, smem + L.off_t[kind], bo, acc1);
+  // ||x - x_hat||^2 > tau^2 ||x||^2 for token n16 of two sub-tiles, one kind.
+  // The two sub-tiles share every basis operand read from LDS (the basis is
+  // the row operand of both products), so each read feeds two matrix-core
+  // operations and the two dependency chains interleave.
+  auto flagged2 = [&](const u32x4 (&xa)[2][D / 32], int kind, bool (&fl)[2]) {
+    const uint16_t* bt = smem + L.off_t[kind];
+    f32x4 acc1[2][NB];
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) acc1[t][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int c = 0; c < D / 32; ++c) {
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) {
+        const u32x4 bop = *reinterpret_cast<const u32x4*>(bt + bo.at(nb, c));
+        acc1[0][nb] = mfma_16x16x32(bop, xa[0][c], acc1[0][nb]);
+        acc1[1][nb] = mfma_16x16x32(bop, xa[1][c], acc1[1][nb]);
+      }
+    }
     // stored coefficients round(c), packed as the column operand of x_hat^T = B round(c)^T:
     // k-slots 0..3 of block kk are coefficients 32 kk + 4 grp + 0..3, slots 4..7 are 32 kk + 16 + 4 grp + 0..3
-    float cc = 0.f;
-    uint32_t cw[2 * KK][2];
+    float cc[2] = {0.f, 0.f};
+    uint32_t cw[2][2 * KK][2];
 #pragma unroll
-    for (int nb = 0; nb < 2 * KK; ++nb) {
-      uint16_t t[4] = {0, 0, 0, 0};
-      if (nb < NB) {
+    for (int t = 0; t < 2; ++t)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          t[i] = f32_to_bf16(acc1[nb < NB ? nb : 0][i]);
-          cc = fmaf(acc1[nb < NB ? nb : 0][i], bf16_to_f32(t[i]), cc);
+      for (int nb = 0; nb < 2 * KK; ++nb) {
+        uint16_t tb[4] = {0, 0, 0, 0};
+        if (nb < NB) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            tb[i] = f32_to_bf16(acc1[t][nb < NB ? nb : 0][i]);
+            cc[t] = fmaf(acc1[t][nb < NB ? nb : 0][i], bf16_to_f32(tb[i]), cc[t]);
+          }
         }
+        cw[t][nb][0] = (uint32_t)tb[0] | ((uint32_t)tb[1] << 16);
+        cw[t][nb][1] = (uint32_t)tb[2] | ((uint32_t)tb[3] << 16);
       }
-      cw[nb][0] = (uint32_t)t[0] | ((uint32_t)t[1] << 16);
-      cw[nb][1] = (uint32_t)t[2] | ((uint32_t)t[3] << 16);
-    }
     __builtin_amdgcn_sched_barrier(0);
     const uint16_t* bn = smem + L.off_n[kind];
-    float xh2 = 0.f;
+    float xh2[2] = {0.f, 0.f};
 #pragma unroll
     for (int db = 0; db < D / 16; ++db) {
-      f32x4 acc2 = f32x4{0.f, 0.f, 0.f, 0.f};
+      f32x4 acc2[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
       for (int kk = 0; kk < KK; ++kk) {
         const uint16_t* row = bn + (16 * db + n16) * L.pitch_n + 32 * kk + 4 * grp;
         const uint2 lo = *reinterpret_cast<const uint2*>(row);
         const uint2 hi = *reinterpret_cast<const uint2*>(row + 16);
-        acc2 = mfma_16x16x32(u32x4{lo.x, lo.y, hi.x, hi.y},
-                             u32x4{cw[2 * kk][0], cw[2 * kk][1], cw[2 * kk + 1][0], cw[2 * kk + 1][1]}, acc2);
+        const u32x4 aop = u32x4{lo.x, lo.y, hi.x, hi.y};
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+          acc2[t] = mfma_16x16x32(
+              aop, u32x4{cw[t][2 * kk][0], cw[t][2 * kk][1], cw[t][2 * kk + 1][0], cw[t][2 * kk + 1][1]}, acc2[t]);
       }
       // lane (n16, grp) register i: x_hat of token n16 at dim 16 db + 4 grp + i
 #pragma unroll
-      for (int i = 0; i < 4; ++i) xh2 = fmaf(acc2[i], acc2[i], xh2);
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) xh2[t] = fmaf(acc2[t][i], acc2[t][i], xh2[t]);
     }
-    float n2 = 0.f;
 #pragma unroll
-    for (int c = 0; c < D / 32; ++c)
+    for (int t = 0; t < 2; ++t) {
+      float n2 = 0.f;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const float lo = bf16_lo(xa[c][e]), hi = bf16_hi(xa[c][e]);
-        n2 = fmaf(lo, lo, n2);
-        n2 = fmaf(hi, hi, n2);
+      for (int c = 0; c < D / 32; ++c)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float lo = bf16_lo(xa[t][c][e]), hi = bf16_hi(xa[t][c][e]);
+          n2 = fmaf(lo, lo, n2);
+          n2 = fmaf(hi, hi, n2);
+        }
+      float ct = cc[t], xt = xh2[t];
+#pragma unroll
+      for (int o = 16; o < 64; o <<= 1) {
+        ct += __shfl_xor(ct, o);
+        xt += __shfl_xor(xt, o);
+        n2 += __shfl_xor(n2, o);
       }
-#pragma unroll
-    for (int o = 16; o < 64; o <<= 1) {
-      cc += __shfl_xor(cc, o);
-      xh2 += __shfl_xor(xh2, o);
-      n2 += __shfl_xor(n2, o);
+      const float e2 = n2 - 2.f * ct + xt;
+      fl[t] = e2 > a.tau2 * n2;
     }
-    const float e2 = n2 - 2.f * cc + xh2;
-    return e2 > a.tau2 * n2;
   };
 
-  // keys and values of three consecutive sub-tiles: two stream in while one
-  // is tested.  The buffers rotate statically (the loop is unrolled by three),
-  // so no register copy has to wait for a load in flight.
-  struct Rows {
-    u32x4 k[D / 32], v[D / 32];
+  // keys and values of two pairs of consecutive sub-tiles: one pair streams
+  // in while the other is tested.  The buffers rotate statically (the loop is
+  // unrolled by two pairs), so no register copy waits for a load in flight; a
+  // sub-tile past the wave's run reads zero and writes nothing.
+  struct Rows2 {
+    u32x4 k[2][D / 32], v[2][D / 32];
   };
-  auto fetch = [&](Rows& r, int64_t s) {
-    const bool live = s < sub_end;
-    load_rows<D>(a, b, h, 0, live ? s : sub, live, n16, grp, r.k);
-    load_rows<D>(a, b, h, 1, live ? s : sub, live, n16, grp, r.v);
+  auto fetch2 = [&](Rows2& r, int64_t s) {
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      const bool live = s + t < sub_end;
+      load_rows<D>(a, b, h, 0, live ? s + t : sub, live, n16, grp, r.k[t]);
+      load_rows<D>(a, b, h, 1, live ? s + t : sub, live, n16, grp, r.v[t]);
+    }
   };
-  auto test = [&](const Rows& r, int64_t s) {
+  auto test2 = [&](const Rows2& r, int64_t s) {
     __builtin_amdgcn_sched_barrier(0);   // keep the prefetch ahead and the two kinds apart
-    const bool fk = flagged(r.k, 0);
+    bool fk[2], fv[2];
+    flagged2(r.k, 0, fk);
     __builtin_amdgcn_sched_barrier(0);
-    const bool fv = flagged(r.v, 1);
+    flagged2(r.v, 1, fv);
     __builtin_amdgcn_sched_barrier(0);
-    const int64_t tok = s * kHybridTile + n16;
-    const bool f = (fk || fv) && tok < a.n_tokens;
-    const uint32_t slot = grp == 0 ? (uint32_t)tok : kOob;
-    buf_store1(rs_wsf, slot, (uint8_t)f);
-    buf_store1(rs_flags, slot, (uint8_t)f);
-    const int count = __popcll(__ballot(grp == 0 && f));
-    buf_store4(rs_cnt, lane == 0 ? (uint32_t)(s * 4) : kOob, (uint32_t)count);
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      const int64_t st = s + t;
+      const bool live = st < sub_end;
+      const int64_t tok = st * kHybridTile + n16;
+      const bool f = (fk[t] || fv[t]) && tok < a.n_tokens;
+      const uint32_t slot = grp == 0 && live ? (uint32_t)tok : kOob;
+      buf_store1(rs_wsf, slot, (uint8_t)f);
+      buf_store1(rs_flags, slot, (uint8_t)f);
+      const int count = __popcll(__ballot(grp == 0 && f));
+      buf_store4(rs_cnt, lane == 0 && live ? (uint32_t)(st * 4) : kOob, (uint32_t)count);
+    }
   };
-  Rows r0, r1, r2;
-  if (sub < sub_end) {
-    fetch(r0, sub);
-    fetch(r1, sub + 1);
-  }
-  for (int64_t s3 = sub; s3 < sub_end; s3 += 3) {
-    fetch(r2, s3 + 2);
-    test(r0, s3);
-    if (s3 + 1 >= sub_end) break;
-    fetch(r0, s3 + 3);
-    test(r1, s3 + 1);
-    if (s3 + 2 >= sub_end) break;
-    fetch(r1, s3 + 4);
-    test(r2, s3 + 2);
+  Rows2 ra, rb;
+  if (sub < sub_end) fetch2(ra, sub);
+  for (int64_t s4 = sub; s4 < sub_end; s4 += 4) {
+    fetch2(rb, s4 + 2);
+    test2(ra, s4);
+    if (s4 + 2 >= sub_end) break;
+    fetch2(ra, s4 + 4);
+    test2(rb, s4 + 2);
   }
 }
 
