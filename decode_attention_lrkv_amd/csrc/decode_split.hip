@@ -12,8 +12,8 @@ namespace {
 // ENC: the appended key has its own encoder (a.enc_k), a separate
 // instantiation so that the plain kernel carries none of its code.
 // EARLY: both chunk buffers are loaded before the fold; chosen by the host
-// when every wave has at least two chunks (a short context, one chunk per
-// wave, runs the smaller kernel without it: measured faster there).
+// when every wave has at least two chunks (with one chunk per wave there is
+// no second chunk to prefetch, and the smaller kernel without it runs).
 template <int KC, int VB, bool ENC, bool EARLY>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void split_bf16_kernel(SplitArgs a) {
