@@ -751,24 +751,36 @@ __device__ __forceinline__ void split_bf16_body(const SplitArgs& a, int wg, int 
   float* po = a.part_o;
   if (FOLD) {
     const int ldb = rv + 8;
+    // the row operand is the same for every dim block: built once per wave,
+    // over the (VB + 1) / 2 blocks of 32 coefficients that cover r_V (a
+    // compile-time count, so the B_V reads below are issued together)
+    constexpr int kLiftK = (VB + 1) / 2;
+    u32x4 a_hi[kLiftK], a_lo[kLiftK];
+#pragma unroll
+    for (int c = 0; c < kLiftK; ++c) {
+      const int k0 = 32 * c + 8 * grp;
+      const bool kv = k0 < rv;   // rv is a multiple of 8: a lane group is all in or all out
+      float v[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) v[e] = (kv && n16 < g) ? s_merged[n16 * 128 + k0 + e] : 0.f;
+      uint32_t hi[4], lo[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        hi[e] = pack_bf16(v[2 * e], v[2 * e + 1]);
+        lo[e] = pack_bf16(v[2 * e] - bf16_lo(hi[e]), v[2 * e + 1] - bf16_hi(hi[e]));
+      }
+      a_hi[c] = u32x4{hi[0], hi[1], hi[2], hi[3]};
+      a_lo[c] = u32x4{lo[0], lo[1], lo[2], lo[3]};
+    }
     for (int nd = wave; nd * 16 < d; nd += kWaves) {
       const int dim = 16 * nd + n16;
       f32x4 o = f32x4{0.f, 0.f, 0.f, 0.f};
-      for (int c = 0; 32 * c < rv; ++c) {
+#pragma unroll
+      for (int c = 0; c < kLiftK; ++c) {
         const int k0 = 32 * c + 8 * grp;
-        const bool kv = k0 < rv;   // rv is a multiple of 8: a lane group is all in or all out
-        float v[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) v[e] = (kv && n16 < g) ? s_merged[n16 * 128 + k0 + e] : 0.f;
-        uint32_t hi[4], lo[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          hi[e] = pack_bf16(v[2 * e], v[2 * e + 1]);
-          lo[e] = pack_bf16(v[2 * e] - bf16_lo(hi[e]), v[2 * e + 1] - bf16_hi(hi[e]));
-        }
-        const u32x4 bvw = kv ? *reinterpret_cast<const u32x4*>(sm.bv + dim * ldb + k0) : u32x4{0u, 0u, 0u, 0u};
-        o = mfma_16x16x32(u32x4{hi[0], hi[1], hi[2], hi[3]}, bvw, o);
-        o = mfma_16x16x32(u32x4{lo[0], lo[1], lo[2], lo[3]}, bvw, o);
+        const u32x4 bvw = k0 < rv ? *reinterpret_cast<const u32x4*>(sm.bv + dim * ldb + k0) : u32x4{0u, 0u, 0u, 0u};
+        o = mfma_16x16x32(a_hi[c], bvw, o);
+        o = mfma_16x16x32(a_lo[c], bvw, o);
       }
       // lane (n16, grp) register i: head 4 grp + i, dim
 #pragma unroll
