@@ -676,24 +676,17 @@ __device__ __forceinline__ void split_bf16_body(const SplitArgs& a, int wg, int 
 
   // --- epilogue
   // 1. Head j of the wave is accumulator row j (high part of p) plus row g + j
-  //    (low part).  Row r lives in lane group r / 4, register r % 4, so for the
-  //    lane holding row 4 grp + i the partner row sits 16 (g + i) / 4 lanes up,
-  //    in register (g + i) % 4 (the same for every lane of the wave).
+  //    (low part).  Row r lives in lane group r / 4, register r % 4; the 2 g
+  //    rows go to LDS as they are and the four-wave merge below adds each
+  //    pair (high + low, the same sum a cross-lane exchange here would form),
+  //    so the wave exchanges nothing between lanes.
   //    The LDS written here (s_acc over the prologue's B_K, s_ml) was last read
   //    before the fold's barrier, so no barrier is needed first.
-  {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int sr = (g + i) & 3;
-      const int src = lane + 16 * ((g + i) >> 2);
+  for (int vb = 0; vb < VB; ++vb)
 #pragma unroll
-      for (int vb = 0; vb < VB; ++vb) {
-        const float v = sr == 0 ? acc[vb][0] : (sr == 1 ? acc[vb][1] : (sr == 2 ? acc[vb][2] : acc[vb][3]));
-        const float lo = __shfl(v, src & 63);
-        if (4 * grp + i < g) s_acc[wave][4 * grp + i][16 * vb + n16] = acc[vb][i] + lo;
-      }
-    }
-  }
+    for (int i = 0; i < 4; ++i)
+      if (4 * grp + i < 2 * g) s_acc[wave][4 * grp + i][16 * vb + n16] = acc[vb][i];
   float l_tot = l_run + __shfl_xor(l_run, 16);
   l_tot += __shfl_xor(l_tot, 32);
   if (lane < g) {
@@ -719,7 +712,7 @@ __device__ __forceinline__ void split_bf16_body(const SplitArgs& a, int wg, int 
 #pragma unroll
     for (int w = 0; w < kWaves; ++w) {
       const float m = s_ml[w][j][0];
-      o = fmaf(m == -INFINITY ? 0.f : exp2_fast(m - M), s_acc[w][j][c], o);
+      o = fmaf(m == -INFINITY ? 0.f : exp2_fast(m - M), s_acc[w][j][c] + s_acc[w][g + j][c], o);
     }
     s_merged[j * 128 + c] = o;
   }
