@@ -38,6 +38,8 @@ namespace lrkv {
 namespace {
 
 constexpr int kWaves = 4;
+// the fold's operand row that carries an appended key (query heads take rows < g <= 8)
+constexpr int kAppRow = 15;
 
 template <typename T>
 __device__ __forceinline__ float load_f(const T* p, int64_t i);
@@ -351,12 +353,23 @@ __device__ __forceinline__ void split_bf16_body(const SplitArgs& a, int wg, int 
     const uint16_t* q = static_cast<const uint16_t*>(a.q) + ((int64_t)b * a.hq + (int64_t)h * g) * (FOLD ? d : rk);
     const int nq = FOLD ? 0 : g * rk / 8;           // <= 128 sixteen-byte pieces
     const u32x4 wq = tid < nq ? *reinterpret_cast<const u32x4*>(q + 8 * tid) : u32x4{0u, 0u, 0u, 0u};
-    // the fold's row operand: lane (n16, grp) holds q[head n16][32 c + 8 grp .. + 7]
-    u32x4 qa[4];
+    // the fold's row operand: lane (n16, grp) holds q[head n16][32 c + 8 grp .. + 7].
+    // Without a separate key encoder the appended token is compressed on the
+    // matrix cores too: its key is row kAppRow of this operand (the fold's
+    // product then also gives c_K = k B_K) and its value row 0 of a second
+    // product against the staged B_V (va).
+    const bool app_mfma = FOLD && !ENC && append;
+    const uint16_t* qrow = n16 < g ? q + n16 * d
+                                   : (app_mfma && n16 == kAppRow ? static_cast<const uint16_t*>(a.k_new) + bh * d
+                                                                  : nullptr);
+    const uint16_t* vrow = app_mfma && n16 == 0 ? static_cast<const uint16_t*>(a.v_new) + bh * d : nullptr;
+    u32x4 qa[4], va[4];
 #pragma unroll
-    for (int c = 0; c < 4; ++c)
-      qa[c] = (FOLD && n16 < g && 32 * c < d) ? *reinterpret_cast<const u32x4*>(q + n16 * d + 32 * c + 8 * grp)
-                                              : u32x4{0u, 0u, 0u, 0u};
+    for (int c = 0; c < 4; ++c) {
+      qa[c] = (FOLD && qrow && 32 * c < d) ? *reinterpret_cast<const u32x4*>(qrow + 32 * c + 8 * grp)
+                                           : u32x4{0u, 0u, 0u, 0u};
+      va[c] = (vrow && 32 * c < d) ? *reinterpret_cast<const u32x4*>(vrow + 32 * c + 8 * grp) : u32x4{0u, 0u, 0u, 0u};
+    }
     constexpr int kBkIter = 8;                      // d * rk / 8 <= 2048 = 8 * 256
     u32x4 wb[kBkIter];
     const uint16_t* bk = FOLD ? static_cast<const uint16_t*>(a.basis_k) + (int64_t)h * d * rk : nullptr;
@@ -375,10 +388,11 @@ __device__ __forceinline__ void split_bf16_body(const SplitArgs& a, int wg, int 
       const int i = tid + 256 * it;
       if (i < nbv) wv[it] = *reinterpret_cast<const u32x4*>(bvs + 8 * i);
     }
-    // the appended token's key and value (float, into the otherwise unused s_q)
+    // with a separate key encoder: the appended token's key and value as
+    // floats (into the otherwise unused s_q) for the vector-ALU compress
     const int e_new = tid & 127;
     float x_new = 0.f;
-    if (append && e_new < d) {
+    if (ENC && append && e_new < d) {
       if (tid < 128) x_new = bf16_to_f32(static_cast<const uint16_t*>(a.k_new)[bh * d + e_new]);
       else x_new = bf16_to_f32(static_cast<const uint16_t*>(a.v_new)[bh * d + e_new]);
     }
@@ -389,7 +403,7 @@ __device__ __forceinline__ void split_bf16_body(const SplitArgs& a, int wg, int 
     } else if (c_begin < c_end) {
       load(ca, c_begin);
     }
-    if (append && e_new < d) s_q[(tid < 128 ? 0 : 128) + e_new] = x_new;
+    if (ENC && append && e_new < d) s_q[(tid < 128 ? 0 : 128) + e_new] = x_new;
     if (tid < nq) {
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
@@ -410,28 +424,56 @@ __device__ __forceinline__ void split_bf16_body(const SplitArgs& a, int wg, int 
     __syncthreads();
     if (FOLD) {
       // on the matrix cores: wave w takes the 16-column blocks w, w + 4, ... of q' = q B_K;
-      // the column operand, lane (n16, grp): B_K[32 c + 8 grp + e][16 nb + n16], e < 8
+      // the column operand, lane (n16, grp): B_K[32 c + 8 grp + e][16 nb + n16], e < 8,
+      // read transposed from the staged rows (two 8-byte reads; a column past
+      // r_K reads other bytes of the staged block, and its result is not kept)
       for (int nb = wave; nb * 16 < rk; nb += kWaves) {
         const int col = 16 * nb + n16;
         f32x4 f = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
           if (32 * c < d) {
-            uint32_t w4[4];
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              const int r0 = 32 * c + 8 * grp + 2 * e;
-              const uint32_t lo = col < rk ? s_bk[r0 * rk + col] : 0u;
-              const uint32_t hi = col < rk ? s_bk[(r0 + 1) * rk + col] : 0u;
-              w4[e] = lo | (hi << 16);
-            }
-            f = mfma_16x16x32(qa[c], u32x4{w4[0], w4[1], w4[2], w4[3]}, f);
+            const uint16_t* src = s_bk + (32 * c + 8 * grp + (n16 >> 2)) * rk + 16 * nb + 4 * (n16 & 3);
+            const u32x2 lo = lds_read_tr16(src);
+            const u32x2 hi = lds_read_tr16(src + 4 * rk);
+            f = mfma_16x16x32(qa[c], u32x4{lo[0], lo[1], hi[0], hi[1]}, f);
           }
         }
         // lane (n16, grp) register i: q' of head 4 grp + i, column col
 #pragma unroll
         for (int i = 0; i < 4; ++i)
           if (4 * grp + i < g && col < rk) s_qf[(4 * grp + i) * rk + col] = f[i] * a.qscale;
+        // row kAppRow: the appended key's coefficient, rounded once, kept
+        // (s_c, for its score) and stored at the appended cache row
+        if (app_mfma && grp == kAppRow / 4 && col < rk) {
+          const uint16_t c16 = f32_to_bf16(f[kAppRow % 4]);
+          s_q[256 + col] = bf16_to_f32(c16);
+          const_cast<uint16_t*>(ck)[append_row * rk + col] = c16;
+        }
+      }
+      if (app_mfma) {
+        // c_V = v B_V: wave w takes the 16-column blocks w, w + 4, ...; the
+        // column operand is read transposed from the staged B_V (pitch rv + 8)
+        const int ldv = rv + 8;
+        for (int nb = wave; nb * 16 < rv; nb += kWaves) {
+          const int col = 16 * nb + n16;
+          f32x4 f = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int c = 0; c < 4; ++c) {
+            if (32 * c < d) {
+              const uint16_t* src = sm.bv + (32 * c + 8 * grp + (n16 >> 2)) * ldv + 16 * nb + 4 * (n16 & 3);
+              const u32x2 lo = lds_read_tr16(src);
+              const u32x2 hi = lds_read_tr16(src + 4 * ldv);
+              f = mfma_16x16x32(va[c], u32x4{lo[0], lo[1], hi[0], hi[1]}, f);
+            }
+          }
+          // row 0 (lane group 0, register 0): the value's coefficient, column col
+          if (grp == 0 && col < rv) {
+            const uint16_t c16 = f32_to_bf16(f[0]);
+            s_q[256 + 128 + col] = bf16_to_f32(c16);
+            const_cast<uint16_t*>(cv)[((append_row >> 3) * rv + col) * 8 + (append_row & 7)] = c16;
+          }
+        }
       }
     } else {
       for (int i = tid; i < g * rk; i += 256) s_qf[i] = s_q[i] * a.qscale;
@@ -463,10 +505,12 @@ __device__ __forceinline__ void split_bf16_body(const SplitArgs& a, int wg, int 
   }
 
   if (append) {
-    // c = round(x E) for the key (threads < 128, column tid) and the value
-    // (threads >= 128, column tid - 128), E the encoder (the basis itself
-    // unless a separate key encoder is given), stored at the appended row; then
-    // the token's score q' . c_K (log2 units), kept with c_V for the epilogue
+    // With a separate key encoder: c = round(x E) for the key (threads < 128,
+    // column tid) and c = round(x B_V) for the value (threads >= 128, column
+    // tid - 128) on the vector ALU, stored at the appended row.  Without one
+    // the prologue's matrix-core products already did this (s_c is complete
+    // since its last barrier).  Then the token's score q' . c_K (log2 units),
+    // kept with c_V for the epilogue.
     const int pa = a.n_parts - 1;
     const int64_t p = append_row;
     float* s_c = s_q + 256;   // past the token's key and value
@@ -513,7 +557,7 @@ __device__ __forceinline__ void split_bf16_body(const SplitArgs& a, int wg, int 
       }
       __syncthreads();
     }
-    if (col < r) {
+    if (ENC && col < r) {
       float acc = 0.f;
       if (kind_v) {
         // four partial sums: the token's compress is on this workgroup's critical path
@@ -540,7 +584,7 @@ __device__ __forceinline__ void split_bf16_body(const SplitArgs& a, int wg, int 
       else
         static_cast<uint16_t*>(const_cast<void*>(a.ck))[(bh * a.cap + p) * rk + col] = c16;
     }
-    __syncthreads();
+    if (ENC) __syncthreads();
     const int64_t row0 = (int64_t)b * a.hq + (int64_t)h * g;
     if (tid < g) {
       float p4[4] = {0.f, 0.f, 0.f, 0.f};

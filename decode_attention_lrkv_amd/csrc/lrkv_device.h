@@ -109,6 +109,20 @@ __device__ __forceinline__ int lds_swz(int row, int col) {
   return line * 128 + (((chunk ^ line) & 15) << 3) + (col & 7);
 }
 
+// Four bfloat16 of a matrix-core operand read transposed from LDS
+// (ds_read_b64_tr_b16).  Within each group of 16 lanes, lane l receives in
+// slot j the element l mod 4 of the 8 bytes that lane 4 j + l / 4 of the
+// group addresses (measured with an in-bounds probe of every lane).  For a
+// row-major [k][n] matrix, lanes n16 = 0..15 of a group pointing at row
+// k0 + n16 / 4, columns n0 + 4 (n16 mod 4) .. + 3, leave lane n16 with
+// rows k0 .. k0 + 3 of column n0 + n16: the k-slots a column operand wants.
+// The address must be 8-byte aligned.
+__device__ __forceinline__ u32x2 lds_read_tr16(const uint16_t* p) {
+  typedef short v4s __attribute__((ext_vector_type(4)));
+  const v4s v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4s*)p);
+  return __builtin_bit_cast(u32x2, v);
+}
+
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 
 __device__ __forceinline__ float wave_max(float v) {
