@@ -488,12 +488,15 @@ __device__ __forceinline__ void split_bf16_body(const SplitArgs& a, int wg, int 
   u32x4 bq_hi[KC], bq_lo[KC];
 #pragma unroll
   for (int c = 0; c < KC; ++c) {
-    float v[8];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const int k = 32 * c + 8 * grp + e;
-      v[e] = (head >= 0 && k < rk) ? s_qf[head * rk + k] : 0.f;
+    // r_K is a multiple of 8: a lane's 8 values are all inside or all past
+    // it, and read as two 16-byte pieces
+    const int k0 = 32 * c + 8 * grp;
+    float4 q0 = make_float4(0.f, 0.f, 0.f, 0.f), q1 = q0;
+    if (head >= 0 && k0 < rk) {
+      q0 = *reinterpret_cast<const float4*>(s_qf + head * rk + k0);
+      q1 = *reinterpret_cast<const float4*>(s_qf + head * rk + k0 + 4);
     }
+    const float v[8] = {q0.x, q0.y, q0.z, q0.w, q1.x, q1.y, q1.z, q1.w};
     uint32_t hi[4], lo[4];
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
