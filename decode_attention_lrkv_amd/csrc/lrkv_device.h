@@ -24,9 +24,13 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
   return __builtin_bit_cast(uint16_t, h);
 }
 
-// Two float32 -> packed bfloat16 pair (a in the low half).
+// Two float32 -> packed bfloat16 pair (a in the low half), round to nearest
+// even: one v_cvt_pk_bf16_f32 for the pair (converting the halves one by one
+// costs two conversions, a shift and an or).
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
+typedef __attribute__((ext_vector_type(2))) float f32x2;
 __device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
-  return (uint32_t)f32_to_bf16(a) | ((uint32_t)f32_to_bf16(b) << 16);
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{a, b}, bf16x2));
 }
 
 // D = A(16x32) * B(32x16) + C on the matrix cores, bf16 in, fp32 accumulate.
