@@ -133,10 +133,13 @@ __device__ void workgroup_partial(const SplitArgs& a, int b, int h, int part, co
 // over the n_parts partials of each of the unit's g query heads; partials of
 // workgroups that saw no token have m_s = -inf and weigh nothing.  Wave w
 // takes heads w, w + 4.  Lane (grp, col) of a wave folds float4 column col of
-// partials grp, grp + 64 / (d / 4), ... into a running (max, sum, output)
-// in ascending order, issuing the loads of sixteen partials at a time, and the
-// lane groups are then combined pairwise (the lower lane's state first, so
-// that both lanes of a pair compute the same bits).
+// partials grp, grp + 64 / (d / 4), ... into a running (max, sum, output),
+// sixteen partials at a time: their loads are issued together, the batch's
+// maximum is taken first, the running state is rescaled to it once and the
+// partials are added with their weights in ascending order (so no step waits
+// for the previous step's maximum).  The lane groups are then combined
+// pairwise (the lower lane's state first, so that both lanes of a pair
+// compute the same bits).
 struct MergeState {
   float m, l;
   f32x4 o;
@@ -180,17 +183,26 @@ __device__ void merge_unit(const MergeArgs& a, int64_t unit) {
         ml[u] = buf_load8(rs_ml, s * 8);
         ov[u] = buf_load16(rs_o, (s * d + 4 * col) * 4);
       }
+      // the batch's maximum first, then every partial's weight at once (no
+      // step waits for the previous one's maximum), in ascending order
+      float mb = st.m;
 #pragma unroll
-      for (int u = 0; u < kU; ++u) {
-        const float ms = __uint_as_float(ml[u][0]);
-        if (s0 + u * groups < S && ms != -INFINITY) {
-          MergeState p;
-          p.m = ms;
-          p.l = __uint_as_float(ml[u][1]);
+      for (int u = 0; u < kU; ++u)
+        if (s0 + u * groups < S) mb = fmaxf(mb, __uint_as_float(ml[u][0]));
+      if (mb != -INFINITY) {
+        const float sc = st.m == -INFINITY ? 0.f : exp2_fast(st.m - mb);
+        st.l *= sc;
 #pragma unroll
-          for (int e = 0; e < 4; ++e) p.o[e] = __uint_as_float(ov[u][e]);
-          st = merge_two(st, p);
+        for (int e = 0; e < 4; ++e) st.o[e] *= sc;
+#pragma unroll
+        for (int u = 0; u < kU; ++u) {
+          const float ms = __uint_as_float(ml[u][0]);
+          const float w = (s0 + u * groups < S && ms != -INFINITY) ? exp2_fast(ms - mb) : 0.f;
+          st.l = fmaf(w, __uint_as_float(ml[u][1]), st.l);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) st.o[e] = fmaf(w, __uint_as_float(ov[u][e]), st.o[e]);
         }
+        st.m = mb;
       }
     }
     for (int off = cols; off < 64; off <<= 1) {
