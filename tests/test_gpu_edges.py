@@ -9,7 +9,8 @@ import torch
 
 import lrkv_synth as synth
 from oracle import lrkv_oracle as O
-from tests.gpu_helpers import DEV, check_decode, round_store, to_dev, to_f64
+from tests.gpu_helpers import DEV, bits, check_decode, round_store, to_dev, to_f64
+from tests.test_gpu_parity_small import check_compress
 
 pytestmark = pytest.mark.gpu
 lrkv = pytest.importorskip("decode_attention_lrkv_amd")
@@ -189,3 +190,58 @@ def test_explicit_scale():
     o_ref, lse_ref = O.decode(q, to_f64(dev["bk"]), ck, to_f64(dev["bv"]), cv, n, scale=0.3)
     o, lse = _run(dev, n, scale=0.3)
     check_decode(to_f64(o), to_f64(lse), o_ref, lse_ref, "bf16", "scale 0.3")
+
+
+@pytest.mark.parametrize("hq,hkv,d,rk,rv,n", [(1, 1, 64, 16, 24, 33), (8, 1, 64, 64, 8, 300),
+                                              (8, 2, 128, 128, 128, 300), (16, 2, 128, 8, 40, 70),
+                                              (2, 1, 128, 24, 40, 2), (32, 4, 64, 64, 64, 1),
+                                              (24, 8, 128, 40, 56, 129), (4, 2, 64, 48, 64, 1000),
+                                              (12, 2, 128, 96, 112, 4097)])
+@pytest.mark.parametrize("enc", [False, True])
+def test_decode_step_shapes(hq, hkv, d, rk, rv, n, enc):
+    """lrkv_decode_step over group sizes, head dims and ranks (the append's
+    product depends on all three): row n - 1 of both caches meets the compress
+    gate, every other row (NaN past the context included) keeps its bits, and
+    the output is the oracle's decode over the n rows.  enc passes the key
+    basis again as the explicit encoder."""
+    B = 2
+    rng = np.random.default_rng(hq * 7919 + d * 31 + rk * 7 + rv + n)
+    cap = (n + 7) // 8 * 8 + 8
+
+    def ortho(r):
+        qm, rr = np.linalg.qr(rng.standard_normal((d, d)))
+        return (qm * np.sign(np.diag(rr)))[:, :r]
+
+    bk_s = round_store(np.stack([ortho(rk) for _ in range(hkv)]), "bf16")
+    bv_s = round_store(np.stack([ortho(rv) for _ in range(hkv)]), "bf16")
+    q_s = round_store(rng.standard_normal((B, hq, d)), "bf16")
+    xk_s = round_store(rng.standard_normal((B, 1, hkv, d)), "bf16")
+    xv_s = round_store(rng.standard_normal((B, 1, hkv, d)), "bf16")
+    ck_s = round_store(rng.standard_normal((B, hkv, n - 1, rk)) * 0.97 ** np.arange(rk), "bf16")
+    cv_s = round_store(rng.standard_normal((B, hkv, n - 1, rv)) * 0.97 ** np.arange(rv), "bf16")
+    ex = synth.bf16_bits_to_f64
+    bk, bv, q, xk, xv = ex(bk_s), ex(bv_s), ex(q_s), ex(xk_s), ex(xv_s)
+    ak, av = O.compress(xk, bk), O.compress(xv, bv)
+    ck_all = np.concatenate([ex(ck_s), O.round_storage(ak, "bf16")], axis=2)
+    cv_all = np.concatenate([ex(cv_s), O.round_storage(av, "bf16")], axis=2)
+    o_ref, lse_ref = O.decode(q, bk, ck_all, bv, cv_all, n)
+
+    ckb = np.full((B, hkv, cap, rk), NAN_BF16, np.uint16)
+    cvb = np.full((B, hkv, cap, rv), NAN_BF16, np.uint16)
+    ckb[:, :, :n - 1] = ck_s
+    cvb[:, :, :n - 1] = cv_s
+    ckd, cvd = to_dev(ckb, "bf16"), to_dev(synth.to_value_octets(cvb), "bf16")
+    bkd = to_dev(bk_s, "bf16")
+    o, lse = lrkv.decode_step(to_dev(q_s, "bf16"), to_dev(xk_s, "bf16"), to_dev(xv_s, "bf16"), bkd, ckd,
+                              to_dev(bv_s, "bf16"), cvd, n, enc_k=bkd if enc else None)
+    torch.cuda.synchronize()
+    what = f"step hq={hq} hkv={hkv} d={d} rk={rk} rv={rv} n={n} enc={enc}"
+    check_compress(to_f64(ckd)[:, :, n - 1:n], ak, xk, bk, "bf16", what + " K row")
+    check_compress(synth.from_value_octets(to_f64(cvd))[:, :, n - 1:n], av, xv, bv, "bf16", what + " V row")
+    after_k = bits(ckd)
+    after_v = synth.from_value_octets(bits(cvd))
+    others = np.ones(cap, bool)
+    others[n - 1] = False
+    assert np.array_equal(after_k[:, :, others], ckb[:, :, others]), what + ": key rows touched"
+    assert np.array_equal(after_v[:, :, others], cvb[:, :, others]), what + ": value rows touched"
+    check_decode(to_f64(o), to_f64(lse), o_ref, lse_ref, "bf16", what)
