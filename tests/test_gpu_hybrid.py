@@ -298,3 +298,44 @@ def test_hybrid_tau_zero_keeps_every_token_full_rank():
     check_decode(np.stack([og[r] for r in rows]), np.array([lg[r] for r in rows]),
                  np.stack([o_ref[r][0] for r in rows]), np.array([o_ref[r][1] for r in rows]),
                  "bf16", "hybrid tau = 0")
+
+
+def test_hybrid_decode_shares_one_workspace_and_replays_in_a_graph():
+    """Calls on two caches that share one workspace give the bits of calls
+    with fresh workspaces, and a captured call replays to the eager bits with
+    eager calls on the same workspace between the replays."""
+    w, inj, k, v, bk, bv, q = _inputs(3000)
+    kd, vd, bkd, bvd, qd = (to_dev(x, "bf16") for x in (k, v, bk, bv, q))
+    caches = []
+    for n in (3000, 1234):
+        c = _new_cache(w, 3000, _round8(len(inj) + 8))
+        lrkv.compress_hybrid(c, kd[:, :n].contiguous(), vd[:, :n].contiguous(), bkd, bvd, TAU, 0)
+        caches.append(c)
+    fresh = [lrkv.decode_attn_hybrid(qd, bkd, bvd, c) for c in caches]
+    need = lrkv.decode_workspace_bytes(w.batch, w.n_q_heads, w.n_kv_heads, w.head_dim, *w.ranks(0), 3000, 0,
+                                       caches[0].side_cap)
+    ws = torch.zeros(need, dtype=torch.uint8, device=DEV)
+    for rep in range(3):
+        for c, (o_ref, l_ref) in zip(caches, fresh):
+            o, lse = lrkv.decode_attn_hybrid(qd, bkd, bvd, c, workspace=ws)
+            torch.cuda.synchronize()
+            assert torch.equal(o.view(torch.int16), o_ref.view(torch.int16)) and torch.equal(lse, l_ref)
+    out = torch.empty_like(qd)
+    lse = torch.empty((w.batch, w.n_q_heads), dtype=torch.float32, device=DEV)
+    stream = torch.cuda.Stream()
+    stream.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(stream):
+        lrkv.decode_attn_hybrid(qd, bkd, bvd, caches[0], out=out, lse=lse, workspace=ws)
+    torch.cuda.current_stream().wait_stream(stream)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        lrkv.decode_attn_hybrid(qd, bkd, bvd, caches[0], out=out, lse=lse, workspace=ws)
+    for rep in range(3):
+        out.zero_()
+        lse.zero_()
+        lrkv.decode_attn_hybrid(qd, bkd, bvd, caches[1], workspace=ws)   # eager work between replays
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out.view(torch.int16), fresh[0][0].view(torch.int16)) and torch.equal(lse, fresh[0][1])
