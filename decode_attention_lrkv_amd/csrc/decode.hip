@@ -21,8 +21,10 @@ void split_bf16_latent_kernel(SplitArgs a) {
 // are divided between the low-rank rows and the full-rank side list (r = d,
 // no fold and no lift, single-buffered so that both fit two waves per SIMD)
 // in proportion to the bytes each list holds, from the counts on the device;
-// within a list, each workgroup takes an equal run of chunks, which its four
-// waves take in turn.  Every workgroup writes partial blockIdx.x.
+// within a list, the workgroups take runs of chunks that differ by at most
+// one chunk (the stream is shared fairly between compute units, so the
+// workgroup with the most bytes ends last), which their four waves take in
+// turn.  Every workgroup writes partial blockIdx.x.
 template <int KC, int VB, int SKC, int SVB>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void split_bf16_hybrid_kernel(SplitArgs lr, SplitArgs side) {
@@ -57,13 +59,13 @@ void split_bf16_hybrid_kernel(SplitArgs lr, SplitArgs side) {
     SplitArgs a = lr;
     a.n_dev = nullptr;
     a.n_static = n_lr;
-    a.chunks_per_split = (int)(((unsigned)ch_lr + (unsigned)p_lr * kWaves - 1) / ((unsigned)p_lr * kWaves));
+    a.list_wgs = p_lr;
     split_bf16_body<KC, VB, true, kStages<KC, VB>, false, true>(a, x, x, sm);
   } else {
     SplitArgs a = side;
     a.n_dev = nullptr;
     a.n_static = n_side;
-    a.chunks_per_split = (int)(((unsigned)ch_side + (unsigned)p_side * kWaves - 1) / ((unsigned)p_side * kWaves));
+    a.list_wgs = p_side;
     split_bf16_body<SKC, SVB, false, 1>(a, x - p_lr, x, sm);
   }
 }

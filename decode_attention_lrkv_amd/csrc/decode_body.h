@@ -315,10 +315,12 @@ __device__ __forceinline__ void split_bf16_body(const SplitArgs& a, int wg, int 
   // cache (measured: 1.4 % faster than one contiguous run per wave with ranks
   // 32/96, where every per-wave run starts at a multiple of 128 KB).  The
   // online softmax does not depend on the order.
+  // With a.list_wgs the workgroups' runs differ by at most one chunk (the
+  // per-workgroup bytes, which set when a workgroup's stream ends, are even).
   const int64_t n_chunks = (n_end + kChunk - 1) / kChunk;
-  const int64_t w_begin = (int64_t)wg * kWaves * cps;
+  const int64_t w_begin = a.list_wgs > 0 ? n_chunks * wg / a.list_wgs : (int64_t)wg * kWaves * cps;
   const int64_t c_begin = w_begin + wave;
-  int64_t c_end = w_begin + (int64_t)kWaves * cps;
+  int64_t c_end = a.list_wgs > 0 ? n_chunks * (wg + 1) / a.list_wgs : w_begin + (int64_t)kWaves * cps;
   if (c_end > n_chunks) c_end = n_chunks;
   constexpr int64_t kStep = kWaves;
 

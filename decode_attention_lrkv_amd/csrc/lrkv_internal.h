@@ -38,6 +38,10 @@ struct SplitArgs {
   // device from the length (chunks_per_split is not used).
   const int32_t* n_ctx_b;
   int chunks_per_split;
+  // > 0: the list's chunks are divided as evenly as whole chunks allow over
+  // this many workgroups (wg in [0, list_wgs) takes chunks
+  // [wg C / list_wgs, (wg + 1) C / list_wgs) of C); chunks_per_split is not used
+  int list_wgs;
   int n_splits;
   int n_parts;           // partials per (b, q head): one per attention workgroup
   float qscale;          // softmax scale * log2(e)
