@@ -378,6 +378,9 @@ def bench_hybrid(torch, lrkv, bm, synth, dev, threads):
                                              threads=threads)).store
     dv = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
     kd, vd = dv(k), dv(v)
+    # three input sets (the token order rotated by a third) so that no call
+    # finds its keys and values in the last-level cache from the call before
+    kvs = [(kd, vd)] + [(torch.roll(kd, j * n // 3, dims=1), torch.roll(vd, j * n // 3, dims=1)) for j in (1, 2)]
     bk, bv, q = dv(synth.basis(w, 0, "k").store), dv(synth.basis(w, 0, "v").store), dv(synth.query(w, 0).store)
     side_cap = 8192
     caches = [lrkv.HybridCache(1, w.n_q_heads, H, d, rk, rv, n, side_cap, dev) for _ in range(3)]
@@ -388,7 +391,7 @@ def bench_hybrid(torch, lrkv, bm, synth, dev, threads):
         c = caches[i % 3]
         c.n_lr.zero_()
         c.n_side.zero_()
-        lrkv.compress_hybrid(c, kd, vd, bk, bv, 0.5, 0, workspace=cws)
+        lrkv.compress_hybrid(c, *kvs[i % 3], bk, bv, 0.5, 0, workspace=cws)
 
     comp_us = _timed(torch, compress)
     n_side = int(caches[0].n_side[0, 0].item())

@@ -312,14 +312,20 @@ void hybrid_select_kernel(HybridArgs a) {
       buf_store4(rs_cnt, lane == 0 && live ? (uint32_t)(st * 4) : kOob, (uint32_t)count);
     }
   };
+  // The pairs of the run are taken last to first: the write kernel walks the
+  // run first to last, so the rows it reads first are the ones read here
+  // last, still in the last-level cache.  A pair index below zero reads
+  // nothing (sub_end is past the run).
+  const int64_t n_pairs = sub < sub_end ? (sub_end - sub + 1) / 2 : 0;
+  auto pair_at = [&](int64_t j) { return j >= 0 ? sub + 2 * j : sub_end; };
   Rows2 ra, rb;
-  if (sub < sub_end) fetch2(ra, sub);
-  for (int64_t s4 = sub; s4 < sub_end; s4 += 4) {
-    fetch2(rb, s4 + 2);
-    test2(ra, s4);
-    if (s4 + 2 >= sub_end) break;
-    fetch2(ra, s4 + 4);
-    test2(rb, s4 + 2);
+  if (n_pairs > 0) fetch2(ra, pair_at(n_pairs - 1));
+  for (int64_t j = n_pairs - 1; j >= 0; j -= 2) {
+    fetch2(rb, pair_at(j - 1));
+    test2(ra, pair_at(j));
+    if (j - 1 < 0) break;
+    fetch2(ra, pair_at(j - 2));
+    test2(rb, pair_at(j - 1));
   }
 }
 
