@@ -200,10 +200,11 @@ def decode_workspace_bytes(batch, n_q_heads, n_kv_heads, head_dim, rank_k, rank_
 
 
 def _workspace(nbytes: int, device, workspace: Optional[torch.Tensor]) -> torch.Tensor:
-    """The caller's workspace, or a new one."""
+    """The caller's workspace, or a new one (zeroed: the hybrid decode's
+    arrival counters at its start must be zero before a first call)."""
     if workspace is not None:
         return workspace
-    return torch.empty(max(nbytes, 16), dtype=torch.uint8, device=device)
+    return torch.zeros(max(nbytes, 16), dtype=torch.uint8, device=device)
 
 
 def decode_attn(q, basis_k, coeff_k, basis_v, coeff_v, n_ctx: int, out=None, lse=None,

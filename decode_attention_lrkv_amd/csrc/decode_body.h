@@ -46,7 +46,13 @@ __device__ __forceinline__ float load_f(const T* p, int64_t i);
 template <>
 __device__ __forceinline__ float load_f<float>(const float* p, int64_t i) { return p[i]; }
 
-__device__ __forceinline__ void store_partial(float* p, float v) { *p = v; }
+// A partial result.  DEVICE: a device-scope store (written through to memory,
+// sc1), for a partial that another workgroup of the same launch merges.
+template <bool DEVICE = false>
+__device__ __forceinline__ void store_partial(float* p, float v) {
+  if (DEVICE) __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  else *p = v;
+}
 
 template <typename T>
 __device__ __forceinline__ void store_f(T* p, int64_t i, float v);
@@ -157,7 +163,7 @@ __device__ __forceinline__ MergeState merge_two(const MergeState& a, const Merge
   return r;
 }
 
-template <typename T>
+template <typename T, bool DEVICE = false>
 __device__ void merge_unit(const MergeArgs& a, int64_t unit) {
   constexpr int kU = 16;
   const int wave = wave_id(), lane = threadIdx.x & 63;
@@ -180,30 +186,33 @@ __device__ void merge_unit(const MergeArgs& a, int64_t unit) {
 #pragma unroll
       for (int u = 0; u < kU; ++u) {
         const uint32_t s = (uint32_t)(s0 + u * groups);
-        ml[u] = buf_load8(rs_ml, s * 8);
-        ov[u] = buf_load16(rs_o, (s * d + 4 * col) * 4);
+        ml[u] = DEVICE ? buf_load8_device(rs_ml, s * 8) : buf_load8(rs_ml, s * 8);
+        ov[u] = DEVICE ? buf_load16_device(rs_o, (s * d + 4 * col) * 4) : buf_load16(rs_o, (s * d + 4 * col) * 4);
       }
       // the batch's maximum first, then every partial's weight at once (no
-      // step waits for the previous one's maximum), in ascending order
+      // step waits for the previous one's maximum), in ascending order.  An
+      // empty partial (max -inf, or past the count) is skipped by a select,
+      // whatever its output words hold (an appended token's slot has none);
+      // no branch depends on the maxima, so every load of the batch issues
+      // before the first use
       float mb = st.m;
 #pragma unroll
       for (int u = 0; u < kU; ++u)
         if (s0 + u * groups < S) mb = fmaxf(mb, __uint_as_float(ml[u][0]));
-      if (mb != -INFINITY) {
-        const float sc = st.m == -INFINITY ? 0.f : exp2_fast(st.m - mb);
-        st.l *= sc;
+      const float sc = st.m == -INFINITY ? 0.f : exp2_fast(st.m - mb);
+      st.l *= sc;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) st.o[e] *= sc;
+      for (int e = 0; e < 4; ++e) st.o[e] *= sc;
 #pragma unroll
-        for (int u = 0; u < kU; ++u) {
-          const float ms = __uint_as_float(ml[u][0]);
-          const float w = (s0 + u * groups < S && ms != -INFINITY) ? exp2_fast(ms - mb) : 0.f;
-          st.l = fmaf(w, __uint_as_float(ml[u][1]), st.l);
+      for (int u = 0; u < kU; ++u) {
+        const float ms = __uint_as_float(ml[u][0]);
+        const bool live = s0 + u * groups < S && ms != -INFINITY;
+        const float w = live ? exp2_fast(ms - mb) : 0.f;
+        st.l = live ? fmaf(w, __uint_as_float(ml[u][1]), st.l) : st.l;
 #pragma unroll
-          for (int e = 0; e < 4; ++e) st.o[e] = fmaf(w, __uint_as_float(ov[u][e]), st.o[e]);
-        }
-        st.m = mb;
+        for (int e = 0; e < 4; ++e) st.o[e] = live ? fmaf(w, __uint_as_float(ov[u][e]), st.o[e]) : st.o[e];
       }
+      st.m = mb;
     }
     for (int off = cols; off < 64; off <<= 1) {
       MergeState other;
@@ -262,7 +271,7 @@ struct SplitSmem {
 // left empty.  ENC: the appended key has a separate encoder (a.enc_k).
 // EARLY (two stages only): both register buffers are loaded before the fold,
 // so that two chunks per wave stream in during the prologue instead of one.
-template <int KC, int VB, bool FOLD, int STAGES, bool ENC = false, bool EARLY = false>
+template <int KC, int VB, bool FOLD, int STAGES, bool ENC = false, bool EARLY = false, bool DEVICE_PARTIAL = false>
 __device__ __forceinline__ void split_bf16_body(const SplitArgs& a, int wg, int part, SplitSmem& sm,
                                                 bool append = false) {
   const int tid = threadIdx.x;
@@ -613,15 +622,15 @@ __device__ __forceinline__ void split_bf16_body(const SplitArgs& a, int wg, int 
       // s_c), before the lift; its own partial slot is marked empty
       s_q[512 + tid] = s;
       if (!a.out) {
-        store_partial(a.part_ml + ((row0 + tid) * a.n_parts + pa) * 2 + 0, -INFINITY);
-        store_partial(a.part_ml + ((row0 + tid) * a.n_parts + pa) * 2 + 1, 0.f);
+        store_partial<DEVICE_PARTIAL>(a.part_ml + ((row0 + tid) * a.n_parts + pa) * 2 + 0, -INFINITY);
+        store_partial<DEVICE_PARTIAL>(a.part_ml + ((row0 + tid) * a.n_parts + pa) * 2 + 1, 0.f);
       }
     }
   } else if (tok_slot && !a.out && tid < g) {
     // no token to append (a device length outside [1, cap]): its slot stays empty
     const int64_t row0 = (int64_t)b * a.hq + (int64_t)h * g;
-    store_partial(a.part_ml + ((row0 + tid) * a.n_parts + a.n_parts - 1) * 2 + 0, -INFINITY);
-    store_partial(a.part_ml + ((row0 + tid) * a.n_parts + a.n_parts - 1) * 2 + 1, 0.f);
+    store_partial<DEVICE_PARTIAL>(a.part_ml + ((row0 + tid) * a.n_parts + a.n_parts - 1) * 2 + 0, -INFINITY);
+    store_partial<DEVICE_PARTIAL>(a.part_ml + ((row0 + tid) * a.n_parts + a.n_parts - 1) * 2 + 1, 0.f);
   }
 
 
@@ -792,8 +801,8 @@ __device__ __forceinline__ void split_bf16_body(const SplitArgs& a, int wg, int 
       s_inv[tid] = L > 0.f ? 1.f / L : 0.f;
       if (a.lse) a.lse[row0 + tid] = L > 0.f ? (M + __log2f(L)) * kLn2 : -INFINITY;
     } else {
-      store_partial(a.part_ml + ((row0 + tid) * a.n_parts + part) * 2 + 0, M);
-      store_partial(a.part_ml + ((row0 + tid) * a.n_parts + part) * 2 + 1, L);
+      store_partial<DEVICE_PARTIAL>(a.part_ml + ((row0 + tid) * a.n_parts + part) * 2 + 0, M);
+      store_partial<DEVICE_PARTIAL>(a.part_ml + ((row0 + tid) * a.n_parts + part) * 2 + 1, L);
     }
   }
   __syncthreads();
@@ -843,14 +852,14 @@ __device__ __forceinline__ void split_bf16_body(const SplitArgs& a, int wg, int 
         if (fin)
           static_cast<uint16_t*>(a.out)[(row0 + 4 * grp + i) * d + dim] = f32_to_bf16(o[i] * s_inv[4 * grp + i]);
         else
-          store_partial(po + ((row0 + 4 * grp + i) * a.n_parts + part) * d + dim, o[i]);
+          store_partial<DEVICE_PARTIAL>(po + ((row0 + 4 * grp + i) * a.n_parts + part) * d + dim, o[i]);
       }
     }
   } else {
     // no lift: the partial is the r_V-wide accumulator (d wide for a full-rank list)
     for (int i = tid; i < g * rv; i += 256) {
       const int j = i / rv, c = i - j * rv;
-      store_partial(po + ((row0 + j) * a.n_parts + part) * rv + c, s_merged[j * 128 + c]);
+      store_partial<DEVICE_PARTIAL>(po + ((row0 + j) * a.n_parts + part) * rv + c, s_merged[j * 128 + c]);
     }
   }
 }

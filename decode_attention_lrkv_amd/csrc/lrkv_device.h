@@ -46,8 +46,12 @@ __device__ __forceinline__ f32x4 mfma_16x16x32(u32x4 a, u32x4 b, f32x4 c) {
 // offset kOob instead of a branch (which keeps the memory-instruction count of
 // a loop body fixed, and the compiler's waits on earlier loads exact).
 constexpr uint32_t kOob = 0x80000000u;
-// cache-policy operand of the buffer intrinsics: bit 1 is nt on gfx950
+// cache-policy operand of the buffer intrinsics: bit 1 is nt on gfx950,
+// bit 4 is sc1, device scope: such a load does not return a line another
+// XCD's L2 may hold stale (each XCD has its own L2), and such a store is
+// written through to memory
 constexpr int kPolicyNt = 2;
+constexpr int kPolicyDevice = 16;
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
@@ -64,6 +68,14 @@ __device__ __forceinline__ u32x4 buf_load16_stream(__amdgpu_buffer_rsrc_t r, uin
 }
 __device__ __forceinline__ u32x2 buf_load8(__amdgpu_buffer_rsrc_t r, uint32_t voff) {
   return __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(r, (int)voff, 0, 0));
+}
+// Device-scope loads (sc1), for data another workgroup of the same launch
+// stored with device scope (see kPolicyDevice).
+__device__ __forceinline__ u32x4 buf_load16_device(__amdgpu_buffer_rsrc_t r, uint32_t voff) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, 0, kPolicyDevice));
+}
+__device__ __forceinline__ u32x2 buf_load8_device(__amdgpu_buffer_rsrc_t r, uint32_t voff) {
+  return __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(r, (int)voff, 0, kPolicyDevice));
 }
 __device__ __forceinline__ uint32_t buf_load4(__amdgpu_buffer_rsrc_t r, uint32_t voff) {
   return __builtin_amdgcn_raw_buffer_load_b32(r, (int)voff, 0, 0);

@@ -61,6 +61,14 @@ struct SplitArgs {
   // out [B, Hq, d] and lse [B, Hq] itself, and no partials or merge are needed.
   void* out;             // or null: write partials
   float* lse;            // or null
+  // Merge in the same launch (hybrid cache): when merge_cnt is non-null,
+  // every workgroup counts its arrival on merge_cnt[b * hkv + h] after its
+  // partial is stored, and the workgroup that arrives last merges the unit's
+  // n_parts partials into merge_out / merge_lse and sets the counter back to
+  // zero.  The counters must be zero when the launch starts.
+  uint32_t* merge_cnt;
+  void* merge_out;       // [B, Hq, d]
+  float* merge_lse;      // [B, Hq] or null
 };
 
 // Log-sum-exp merge of n_parts partials per (b, q head).

@@ -137,9 +137,14 @@ lrkv_status lrkv_compress_kv(const void* xk, const void* xv, const void* basis_k
  * dims->capacity and side_cap instead.  Returns 0 for invalid dims.  The
  * split plan depends on the current device's compute-unit count, so query on
  * the device that will run the call.
- * The workspace is scratch (no initial contents are needed); calls that
+ * The workspace starts with one 32-bit arrival counter per (b, kv head)
+ * (rounded up to 256 bytes) that lrkv_decode_attn_hybrid uses to merge in
+ * its own launch: these words must be zero before a workspace's first hybrid
+ * call (allocate the workspace zeroed), and every call of any decode entry
+ * point leaves them as it found them.  The rest is scratch.  Calls that
  * share a workspace must be ordered on one stream (they must not overlap in
- * time).
+ * time; overlapping hybrid calls on one workspace would also share its
+ * counters).
  */
 size_t lrkv_decode_workspace_bytes(const lrkv_dims* dims, int64_t n_ctx, int64_t side_cap);
 
@@ -353,8 +358,11 @@ lrkv_status lrkv_compress_hybrid(const void* k, const void* v, const void* basis
  * Counts are read on the device; an empty (b, h) gives out = 0, lse = -inf.
  * Each (b, kv head) gets a fixed number of workgroups, divided between the
  * two lists on the device in proportion to the bytes the counts there
- * describe; a second launch merges.  bfloat16 only.
- *   workspace at least lrkv_decode_workspace_bytes(dims, 0, side_cap) bytes.
+ * describe; the workgroup of each (b, kv head) that finishes last merges
+ * the partials in the same launch (one launch per call).  bfloat16 only.
+ *   workspace at least lrkv_decode_workspace_bytes(dims, 0, side_cap) bytes,
+ *             its arrival counters zero (see lrkv_decode_workspace_bytes);
+ *             the call leaves them zero.
  */
 lrkv_status lrkv_decode_attn_hybrid(const void* q, const void* basis_k, const void* coeff_k,
                                     const void* basis_v, const void* coeff_v,

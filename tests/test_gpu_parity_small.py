@@ -180,7 +180,10 @@ def test_decode_step_appends_and_attends(N, layer):
 
 
 def test_decode_step_two_phase_equals_one_call():
-    """lrkv_decode_step_partial + _merge give the bits of lrkv_decode_step."""
+    """lrkv_decode_step_partial + _merge give the bits of lrkv_decode_step,
+    also on a workspace whose bytes all start at 0xFF (float NaN): the
+    appended token's empty partial slot, whose output words the kernels never
+    write, must weigh nothing in the merge whatever those words hold."""
     w = synth.LLAMA_STEP
     layer, N = 1, 3000
     B, H, d = w.batch, w.n_kv_heads, w.head_dim
@@ -194,8 +197,8 @@ def test_decode_step_two_phase_equals_one_call():
     ck1, cv1 = _cache_from_rows(rows_k, rows_v, "bf16", N)
     ck2, cv2 = ck1.clone(), cv1.clone()
     o1, l1 = lrkv.decode_step(qd, kn, vn, bkd, ck1, bvd, cv1, N)
-    ws = torch.empty(lrkv.decode_step_workspace_bytes(B, w.n_q_heads, H, d, rk, rv, N, N), dtype=torch.uint8,
-                     device=DEV)
+    ws = torch.full((lrkv.decode_step_workspace_bytes(B, w.n_q_heads, H, d, rk, rv, N, N),), 0xFF,
+                    dtype=torch.uint8, device=DEV)
     o2 = torch.empty_like(o1)
     l2 = torch.empty_like(l1)
     lrkv.decode_step_partial(qd, kn, vn, bkd, ck2, bvd, cv2, N, ws)
