@@ -39,11 +39,20 @@ void split_bf16_hybrid_kernel(SplitArgs lr, SplitArgs side) {
   // the two lists' lengths, read once as scalars and handed to the body as
   // static lengths (the body reads no count of its own); a cache holds fewer
   // than 2^31 tokens, so 32-bit arithmetic suffices for the division
-  auto count = [](const SplitArgs& a, int64_t bh) {
-    const int n = __builtin_amdgcn_readfirstlane(a.n_dev[bh]);
-    return n < 0 ? 0 : (n > a.cap ? (int)a.cap : n);
-  };
-  const int n_lr = count(lr, bh), n_side = count(side, bh);
+  // Every argument either list reads is loaded here, before the counts are
+  // waited for (left alone, the compiler sinks each argument load into the
+  // branch that first uses it, and the prologue waits for one round trip
+  // after another).
+  asm volatile("" ::"s"(lr.q), "s"(lr.basis_k), "s"(lr.ck), "s"(lr.cv), "s"(lr.basis_v), "s"(lr.part_o),
+               "s"(lr.part_ml), "s"(side.ck), "s"(side.cv), "s"(lr.cap), "s"(side.cap));
+  asm volatile("" ::"s"(lr.rk), "s"(lr.rv), "s"(lr.d), "s"(lr.g), "s"(lr.hq), "s"(lr.n_parts), "s"(lr.qscale));
+  // (both counts' loads issued before either is used: one round trip)
+  const int32_t* cnt_lr = lr.n_dev;
+  const int32_t* cnt_side = side.n_dev;
+  const int raw_lr = __builtin_amdgcn_readfirstlane(cnt_lr[bh]);
+  const int raw_side = __builtin_amdgcn_readfirstlane(cnt_side[bh]);
+  auto clamp = [](int n, int64_t cap) { return n < 0 ? 0 : (n > cap ? (int)cap : n); };
+  const int n_lr = clamp(raw_lr, lr.cap), n_side = clamp(raw_side, side.cap);
   const int ch_lr = (n_lr + kChunk - 1) / kChunk;
   const int ch_side = (n_side + kChunk - 1) / kChunk;
   const int P = gridDim.x;
@@ -64,12 +73,27 @@ void split_bf16_hybrid_kernel(SplitArgs lr, SplitArgs side) {
   if (x < p_lr) {
     SplitArgs a = lr;
     a.n_dev = nullptr;
+    a.n_ctx_b = nullptr;   // (no per-sequence lengths, append, final outputs or
+    a.k_new = nullptr;     // fixed-size runs here: known to the compiler, so their
+    a.out = nullptr;       // branches and argument loads drop out)
+    a.chunks_per_split = 0;
     a.n_static = n_lr;
     a.list_wgs = p_lr;
     split_bf16_body<KC, VB, true, kStages<KC, VB>, false, true, true>(a, x, x, sm);
   } else {
-    SplitArgs a = side;
+    // the side list's own fields; the rest as the low-rank list's
+    SplitArgs a = lr;
+    a.basis_k = nullptr;
+    a.basis_v = nullptr;
+    a.ck = side.ck;
+    a.cv = side.cv;
+    a.cap = side.cap;
+    a.rk = a.rv = lr.d;
     a.n_dev = nullptr;
+    a.n_ctx_b = nullptr;
+    a.k_new = nullptr;
+    a.out = nullptr;
+    a.chunks_per_split = 0;
     a.n_static = n_side;
     a.list_wgs = p_side;
     split_bf16_body<SKC, SVB, false, 1, false, false, true>(a, x - p_lr, x, sm);
