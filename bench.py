@@ -360,6 +360,21 @@ def _timed(torch, fn, iters=TIMED_ITERS, warm=WARM_ITERS):
     return stats([a.elapsed_time(b) * 1e3 for a, b in ev])
 
 
+def _back_to_back(torch, fn, iters=TIMED_ITERS, warm=WARM_ITERS):
+    """Mean microseconds per call of `iters` calls issued in a row between
+    one pair of HIP events on the current stream (after `warm` untimed calls)."""
+    for i in range(warm):
+        fn(i)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for i in range(iters):
+        fn(i)
+    e1.record()
+    torch.cuda.synchronize()
+    return round(e0.elapsed_time(e1) * 1e3 / iters, 3)
+
+
 def bench_hybrid(torch, lrkv, bm, synth, dev, threads):
     """Hybrid cache at 131072 tokens: selection + compaction of every token, then decode.
 
@@ -399,8 +414,9 @@ def bench_hybrid(torch, lrkv, bm, synth, dev, threads):
                       dtype=torch.uint8, device=dev)
     out = torch.empty_like(q)
     lse = torch.empty((1, w.n_q_heads), dtype=torch.float32, device=dev)
-    dec_us = _timed(torch, lambda i: lrkv.decode_attn_hybrid(q, bk, bv, caches[i % 3], out=out, lse=lse,
-                                                             workspace=dws))
+    dec_call = lambda i: lrkv.decode_attn_hybrid(q, bk, bv, caches[i % 3], out=out, lse=lse, workspace=dws)
+    dec_us = _timed(torch, dec_call)
+    dec_b2b = _back_to_back(torch, dec_call)
     comp_bytes = (2 * n * H * d * 2 + (n - n_side) * H * (rk + rv) * 2 + n_side * H * (2 * d * 2 + 4)
                   + H * d * (rk + rv) * 2)
     dec_bytes = bm.decode_bytes(1, w.n_q_heads, H, d, rk, rv, n, side_tokens=n_side)
@@ -411,7 +427,11 @@ def bench_hybrid(torch, lrkv, bm, synth, dev, threads):
             "decode_us": dec_us, "decode_bytes": dec_bytes,
             "decode_GBps": round(dec_bytes / dec_us["mean"] / 1e3, 1),
             "decode_pct_peak": round(100 * dec_bytes / dec_us["mean"] / 1e3 / HBM_PEAK_GBPS, 2),
-            "decode_pct_peak_p50": round(100 * dec_bytes / dec_us["p50"] / 1e3 / HBM_PEAK_GBPS, 2)}
+            "decode_pct_peak_p50": round(100 * dec_bytes / dec_us["p50"] / 1e3 / HBM_PEAK_GBPS, 2),
+            "decode_us_back_to_back": dec_b2b,
+            "decode_pct_peak_back_to_back": round(100 * dec_bytes / dec_b2b / 1e3 / HBM_PEAK_GBPS, 2),
+            "note": "decode_us: each call between its own pair of events (the event commands between calls "
+                    "add about 2 us); decode_us_back_to_back: TIMED_ITERS calls in a row between one pair"}
 
 
 def bench_step_sweep(torch, lrkv, bm, synth, dev, threads):
