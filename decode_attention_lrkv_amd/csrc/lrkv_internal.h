@@ -102,21 +102,23 @@ struct OjaArgs {
   int hkv, d, rank;
   int64_t n_tokens;
   float eta;
-  float* ws;             // [Hkv, n_wg, d * R + R * R] partial sums (R = rank padded to 16)
-  float* ws_sum;         // [Hkv, d * R + R * R] their sums
-  int n_wg;              // stats workgroups per kv head
+  float* ws;             // [Hkv, n_wg, d, d] the runs' partial Gram matrices
+  float* ws_sum;         // [Hkv, d * R + R * R] S1 then S2 (R = rank padded to 16)
+  int n_wg;              // gram workgroups (runs of tokens) per kv head
 };
 // Oja updates of at most this many tokens per head (a decode step's) run as
 // a single launch that needs no workspace.
 constexpr int kOjaSmallTokens = 64;
-// Oja workspace layout: per head and stats workgroup, the partial sums
-// S1 [d][R] then S2 [R][R], R = rank padded to whole 16-column blocks; then
-// per head their sums.
+// Tokens per step of a gram workgroup.
+constexpr int kOjaGramStep = 128;
+// Oja workspace layout: per head and gram workgroup, the partial Gram
+// matrix [d][d]; then per head S1 [d][R] and S2 [R][R], R = rank padded to
+// whole 16-column blocks.
 __host__ __device__ inline int64_t oja_head_floats(int d, int r_pad) { return (int64_t)d * r_pad + (int64_t)r_pad * r_pad; }
 inline int oja_rank_pad(int rank) { return 16 * ((rank + 15) / 16); }
+inline size_t oja_partial_floats(int hkv, int d, int n_wg) { return (size_t)hkv * n_wg * d * d; }
 inline size_t oja_workspace_floats(int hkv, int d, int rank, int n_wg) {
-  const int64_t per_head = oja_head_floats(d, oja_rank_pad(rank));
-  return (size_t)((int64_t)hkv * n_wg * per_head + (int64_t)hkv * per_head);
+  return oja_partial_floats(hkv, d, n_wg) + (size_t)hkv * oja_head_floats(d, oja_rank_pad(rank));
 }
 hipError_t launch_oja_update(const OjaArgs& a, hipStream_t s);
 

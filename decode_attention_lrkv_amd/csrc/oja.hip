@@ -4,21 +4,25 @@
 // (every batch row): Y = X B, then B <- B + eta (X^T Y - B Y^T Y).  The basis
 // is kept in float32 (steps of the size Oja's rule takes fall below bfloat16
 // resolution), and a rounded bfloat16 copy is written for the compress and
-// decode calls.  Three launches, all deterministic:
-//   stats   per (run of 16 W-token steps, kv head).  A step's tokens go to LDS
-//           (as X, and as X^T transposed on the matrix cores; tiles in a
-//           bank-conflict-free swizzled layout), loaded three
-//           steps ahead; each wave owns some 16-column coefficient blocks,
-//           computes their Y on the matrix cores (B split into high and low
-//           bfloat16 parts, held in registers, so Y keeps float32 accuracy),
-//           stores it (again as high + low parts) and accumulates its columns
-//           of S1 = X^T Y [d, r] and its half of the symmetric S2 = Y^T Y
-//           [r, r], contracting over the step's tokens.  The workgroup writes
-//           its partial sums.
-//   reduce  sums every kv head's partials in a fixed order.
-//   apply   B + eta (S1 - B S2) in float32 per 4-row block of B, written
-//           back to the float32 basis and, rounded to nearest even, to the
-//           bfloat16 copy.
+// decode calls.
+//
+// Both statistics are products with the chunk's d x d Gram matrix
+// G = X^T X (associativity):  X^T Y = G B,  Y^T Y = B^T G B.  G does not
+// depend on the rank, its bfloat16 x bfloat16 products are exact in the
+// matrix cores' float32 accumulation, and forming it streams the chunk once.
+// Four launches, all deterministic (fixed summation orders, no atomics):
+//   gram   per (run of 128-token steps, kv head): the run's partial G on the
+//          matrix cores.  A step's tokens are staged in LDS token-major; each
+//          matrix-core operand (16 dims x 8 consecutive tokens per lane
+//          group) is read transposed with ds_read_b64_tr_b16, and the same
+//          operand serves as row operand (G's row block) and as column
+//          operand (its column block).  Loads run two steps ahead.
+//   s1     per 8 rows of G: the runs' partials summed in run order, then
+//          those rows of S1 = G B, float32.
+//   s2     per 4 rows of S2 = B^T S1, float32.
+//   apply  B + eta (S1 - B S2) in float32 per 4-row block of B, written
+//          back to the float32 basis and, rounded to nearest even, to the
+//          bfloat16 copy.
 // Chunks of at most kOjaSmallTokens tokens per head take a single launch
 // instead (oja_small_kernel, the same update in its per-token form).
 #include "lrkv_device.h"
@@ -28,331 +32,261 @@ namespace lrkv {
 
 namespace {
 
-// W waves per stats workgroup; a step is 16 tokens per wave.
-template <int W> constexpr int oja_step() { return 16 * W; }
+// LDS of a gram workgroup: two step tiles of kOjaGramStep token rows, each
+// row 128 elements (256 bytes, one pass of the LDS banks; head_dim 64 uses
+// half of it).  The 16-byte chunks of row t are permuted by an xor with
+// gram_swz(t), an even value that takes eight different values on the rows
+// t0 .. t0 + 3 and t0 + 8 .. t0 + 11 (t0 a multiple of 4): a transposed read
+// of half a wave covers exactly those rows, 32 bytes (two chunks) of each,
+// which then land in sixteen different chunks, i.e. all 64 banks once.
+constexpr int kGramRow = 128;
+__device__ __forceinline__ int gram_swz(int row) { return 2 * ((row & 3) | (((row >> 3) & 1) << 2)); }
+__device__ __forceinline__ int gram_off(int row, int chunk) { return row * kGramRow + ((chunk ^ gram_swz(row)) << 3); }
 
-// The step's bfloat16 tiles use the swizzled LDS layout of lds_swz (rows of
-// 64 or 128 elements), so that the matrix-core operand reads are free of bank
-// conflicts.
-template <int D, int NB, int W>
-struct OjaSmem {
-  static constexpr int R = 16 * NB;        // rank padded to whole 16-column blocks
-  static constexpr int S = oja_step<W>();
-  uint16_t xs[S * D];                      // X of the step, token-major [token][dim] (Y's row operand)
-  uint16_t xt[D * S];                      // X^T of the step: [dim][token] (S1's row operand)
-  uint16_t yt_hi[R * S];                   // Y^T of the step: [coefficient][token], high parts
-  uint16_t yt_lo[R * S];                   // low parts: Y - high
-};
-
-// S2 = Y^T Y is symmetric, so of its 16 x 16 tiles (row block na, column
-// block nb) only one of each mirrored pair is formed: the tiles
-// ((nb + j) mod NB, nb) for j < NB / 2 + 1; when NB is even the tile at
-// j = NB / 2 has its mirror at j = NB / 2 too, so it is formed only for
-// nb < NB / 2.  Every unordered pair of blocks is then formed exactly once,
-// and each column block forms about half a column.  Tiles that are not
-// formed hold no partial sums (their reduced values are never read); the
-// apply step reads them transposed from their mirrors.
-__host__ __device__ constexpr bool oja_s2_formed(int na, int nb, int nb_total) {
-  return ((na - nb + nb_total) % nb_total) < (nb_total + 1) / 2 ||
-         (nb_total % 2 == 0 && (na - nb + nb_total) % nb_total == nb_total / 2 && nb < nb_total / 2);
-}
-
-// Per-head partial sums of one stats workgroup: S1 [D][R] then S2 [R][R]
-// (the tiles oja_s2_formed names; the others are not written); the layout
-// helper oja_head_floats is in lrkv_internal.h.
-
-// Wave w owns the 16-column coefficient blocks w, w + W, ... (NBW of them at
-// most): it keeps their B^T rows in registers for the whole launch, computes
-// their Y for all tokens of a step, and accumulates their columns of S1 and
-// S2, so each Y operand it reads from LDS serves every row block.  W = 8 for
-// ranks above 64 (one block per wave, registers for two waves per SIMD).
-template <int D, int NB, int W>
-__global__ __launch_bounds__(64 * W) void oja_stats_kernel(OjaArgs a) {
-  constexpr int R = 16 * NB;
-  constexpr int NBW = (NB + W - 1) / W;    // coefficient blocks per wave
-  constexpr int KD = D / 32;               // 32-dim k-steps of Y = X B
-  constexpr int STEP = oja_step<W>();
-  constexpr int UNROLL = W == 4 ? 4 : 2;   // token-block and k-step loops (full unroll at 8 waves spills)
-  __shared__ __attribute__((aligned(16))) OjaSmem<D, NB, W> sm;
+// One workgroup per (run of tokens, kv head); wave w owns the row blocks
+// w NI .. w NI + NI - 1 of G (NI = D / 64) and all its column blocks, so each
+// wave forms NI x D / 16 tiles of 16 x 16 (64 accumulators at D = 128).
+template <int D>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void oja_gram_kernel(OjaArgs a) {
+  constexpr int NBLK = D / 16;                       // 16-dim blocks
+  constexpr int NI = NBLK / 4;                       // row blocks per wave
+  constexpr int CPR = D / 8;                         // 16-byte chunks per token row
+  constexpr int PIECES = kOjaGramStep * CPR / 256;   // 16-byte loads per thread per step
+  __shared__ __attribute__((aligned(16))) uint16_t tile[2][kOjaGramStep * kGramRow];
   const int tid = threadIdx.x, wave = wave_id(), lane = tid & 63;
   const int n16 = lane & 15, grp = lane >> 4;
-  const int h = blockIdx.y;
-  const int r = a.rank;
-  // With fewer coefficient blocks than waves (W a multiple of NB), the
-  // G = W / NB waves of a block share its work: wave w takes block w mod NB,
-  // and of the token blocks, S1 row blocks and S2 tiles of that block the
-  // ones numbered part, part + G, ... (part = w / NB).
-  constexpr int G = (NB < W && W % NB == 0) ? W / NB : 1;
-  constexpr int DBW = D / 16 / G;           // S1 row blocks per wave
-  constexpr int NJW = (NB / 2 + G) / G;     // S2 tiles per wave and block
-  const int part = G > 1 ? wave / NB : 0;
-  const int bw = G > 1 ? wave % NB : wave;  // the wave's first coefficient block
+  const int h = blockIdx.y, wg = blockIdx.x;
+  const int64_t n = a.n_tokens;
+  const int64_t t_begin = n * wg / a.n_wg, t_end = n * (wg + 1) / a.n_wg;
+  const int steps = (int)((t_end - t_begin + kOjaGramStep - 1) / kOjaGramStep);
+  const uint16_t* x = static_cast<const uint16_t*>(a.x);
+  const int64_t row_stride = (int64_t)a.hkv * D;   // elements from one token of a head to the next
 
-  // this wave's B^T rows as matrix-core row operands, high and low bfloat16
-  // parts: lane (n16, grp) of block k, step c holds B[32 c + 8 grp + e][16 nb + n16]
-  u32x4 bt_hi[NBW][KD], bt_lo[NBW][KD];
-  {
-    const float* bs = a.basis + (int64_t)h * D * r;
+  // Step s: piece p = tid + 256 u is chunk p % CPR of token p / CPR.  Tokens
+  // past the run (and every token of a step past the last) read zero: the
+  // buffer range ends with the last valid token's row.
+  auto load = [&](u32x4 (&buf)[PIECES], int s) {
+    const int64_t t0 = t_begin + (int64_t)s * kOjaGramStep;
+    const int64_t left = s < steps ? t_end - t0 : 0;
+    const int nt = left < kOjaGramStep ? (int)left : kOjaGramStep;
+    const uint32_t bytes = nt > 0 ? (uint32_t)(((int64_t)(nt - 1) * row_stride + D) * 2) : 0u;
+    const __amdgpu_buffer_rsrc_t rs = make_rsrc(s < steps ? x + (t0 * a.hkv + h) * D : x, bytes);
 #pragma unroll
-    for (int k = 0; k < NBW; ++k) {
-      const int col = 16 * (bw + W * k) + n16;
-#pragma unroll
-      for (int c = 0; c < KD; ++c) {
-        uint32_t hi[4], lo[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int r0 = 32 * c + 8 * grp + 2 * e;
-          const float v0 = col < r ? bs[r0 * r + col] : 0.f;
-          const float v1 = col < r ? bs[(r0 + 1) * r + col] : 0.f;
-          hi[e] = pack_bf16(v0, v1);
-          lo[e] = pack_bf16(v0 - bf16_lo(hi[e]), v1 - bf16_hi(hi[e]));
-        }
-        bt_hi[k][c] = u32x4{hi[0], hi[1], hi[2], hi[3]};
-        bt_lo[k][c] = u32x4{lo[0], lo[1], lo[2], lo[3]};
-      }
+    for (int u = 0; u < PIECES; ++u) {
+      const int p = tid + 256 * u;
+      buf[u] = buf_load16_stream(rs, (uint32_t)(((p / CPR) * row_stride + (p % CPR) * 8) * 2));
     }
-  }
-
-  constexpr int NJ = NB / 2 + 1;            // S2 tiles per column block: row blocks (nb + j) mod NB
-  f32x4 s1[DBW][NBW], s2[NJW][NBW];
+  };
+  auto stage = [&](const u32x4 (&buf)[PIECES], uint16_t* t) {
 #pragma unroll
-  for (int k = 0; k < NBW; ++k) {
-#pragma unroll
-    for (int i = 0; i < DBW; ++i) s1[i][k] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int jj = 0; jj < NJW; ++jj) s2[jj][k] = f32x4{0.f, 0.f, 0.f, 0.f};
-  }
-
-  const int64_t n_tok = a.n_tokens;
-  const int64_t n_steps = (n_tok + STEP - 1) / STEP;
-  const int64_t per_wg = (n_steps + gridDim.x - 1) / gridDim.x;
-  const int64_t s_begin = (int64_t)blockIdx.x * per_wg;
-  const int64_t s_end = s_begin + per_wg < n_steps ? s_begin + per_wg : n_steps;
-
-  // this wave's 16 tokens of a step as loaded: lane (n16, grp) holds token
-  // n16's dims 32 c + 8 grp .. + 7; tokens past the end read zero
-  auto load_x = [&](u32x4 (&xa)[KD], int64_t step) {
-    const int64_t t0 = step * STEP + 16 * wave;
-    const int64_t left = n_tok - t0;
-    const int nt = left <= 0 ? 0 : (left < 16 ? (int)left : 16);
-    const int64_t t_base = nt > 0 ? t0 : 0;
-    const uint16_t* x = static_cast<const uint16_t*>(a.x) + (t_base * a.hkv + h) * D;
-    const uint32_t bytes = nt > 0 ? (uint32_t)(((nt - 1) * a.hkv + 1) * D * 2) : 0u;
-    const __amdgpu_buffer_rsrc_t rs = make_rsrc(x, bytes);
-    const uint32_t voff = (uint32_t)((n16 * a.hkv * D + 8 * grp) * 2);
-#pragma unroll
-    for (int c = 0; c < KD; ++c) xa[c] = buf_load16(rs, voff + 64 * c);
+    for (int u = 0; u < PIECES; ++u) {
+      const int p = tid + 256 * u;
+      *reinterpret_cast<u32x4*>(t + gram_off(p / CPR, p % CPR)) = buf[u];
+    }
+  };
+  // Operand of dim block blk for tokens k0 .. k0 + 31: lane (n16, grp) holds
+  // dim 16 blk + n16 of tokens k0 + 8 grp .. + 7 (two transposed reads of
+  // four tokens each).
+  auto operand = [&](const uint16_t* t, int blk, int k0) {
+    const int c = 2 * blk + ((n16 >> 1) & 1), hf = n16 & 1;
+    const int r = k0 + 8 * grp + (n16 >> 2);
+    const u32x2 lo = lds_read_tr16(t + gram_off(r, c) + 4 * hf);
+    const u32x2 hi = lds_read_tr16(t + gram_off(r + 4, c) + 4 * hf);
+    return u32x4{lo[0], lo[1], hi[0], hi[1]};
   };
 
-  // 32 x 16 slices of the identity as column operands: lane (n16, grp) slot
-  // e of slice hf is 1 where 8 grp + e = 16 hf + n16
-  u32x4 eye[2];
+  f32x4 acc[NI][NBLK];
 #pragma unroll
-  for (int hf = 0; hf < 2; ++hf)
+  for (int i = 0; i < NI; ++i)
 #pragma unroll
-    for (int q = 0; q < 4; ++q)
-      eye[hf][q] = (8 * grp + 2 * q == 16 * hf + n16 ? 0x3F80u : 0u) |
-                   (8 * grp + 2 * q + 1 == 16 * hf + n16 ? 0x3F800000u : 0u);
-  // only waves that own a coefficient block take part in Y, S1 and S2
-  const bool owns = bw < NB;
-
-  // A step's tokens are loaded kAhead steps before it runs, into a ring of
-  // kAhead + 1 register buffers that the loop below rotates by name (a copy
-  // between buffers would wait for the newest load).
-  constexpr int kAhead = 3;
-  static_assert(kAhead == 3, "the ring below has four buffers");
-  u32x4 x0[KD], x1[KD], x2[KD], x3[KD];
-  if (s_begin < s_end) load_x(x0, s_begin);
-  if (s_begin + 1 < s_end) load_x(x1, s_begin + 1);
-  if (s_begin + 2 < s_end) load_x(x2, s_begin + 2);
-  auto run_step = [&](const u32x4 (&xa)[KD], u32x4 (&ahead)[KD], int64_t step) {
-    if (step + kAhead < s_end) load_x(ahead, step + kAhead);
-    // 1. X (token-major) and X^T into LDS.  The wave's own 16 tokens are
-    //    transposed on the matrix cores: X times a slice of the identity puts
-    //    dim 32 c + 16 hf + n16 of tokens 4 grp .. + 3 in lane (n16, grp)
-    //    (exactly for finite tokens: each sum is one product by one and the
-    //    rest products by zero), so
-    //    X^T is stored four tokens at a time
-    const int tok = 16 * wave + n16;
+    for (int j = 0; j < NBLK; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  auto accumulate = [&](const uint16_t* t) {
 #pragma unroll
-    for (int c = 0; c < KD; ++c) {
-      *reinterpret_cast<u32x4*>(&sm.xs[lds_swz<D>(tok, 32 * c + 8 * grp)]) = xa[c];
+    for (int k0 = 0; k0 < kOjaGramStep; k0 += 32) {
+      u32x4 col[NBLK], row[NI];
 #pragma unroll
-      for (int hf = 0; hf < 2; ++hf) {
-        const f32x4 t = mfma_16x16x32(xa[c], eye[hf], f32x4{0.f, 0.f, 0.f, 0.f});
-        const u32x2 w = u32x2{(__float_as_uint(t[0]) >> 16) | (__float_as_uint(t[1]) & 0xFFFF0000u),
-                              (__float_as_uint(t[2]) >> 16) | (__float_as_uint(t[3]) & 0xFFFF0000u)};
-        *reinterpret_cast<u32x2*>(&sm.xt[lds_swz<STEP>(32 * c + 16 * hf + n16, 16 * wave + 4 * grp)]) = w;
-      }
+      for (int j = 0; j < NBLK; ++j) col[j] = operand(t, j, k0);
+#pragma unroll
+      for (int i = 0; i < NI; ++i) row[i] = operand(t, wave * NI + i, k0);
+#pragma unroll
+      for (int i = 0; i < NI; ++i)
+#pragma unroll
+        for (int j = 0; j < NBLK; ++j) acc[i][j] = mfma_16x16x32(row[i], col[j], acc[i][j]);
     }
-    __syncthreads();
-    // 2. Y of this wave's coefficient blocks for the step's W 16-token
-    //    blocks, with the tokens as rows: lane (n16, grp) register i is
-    //    coefficient 16 nb + n16 of token 16 tb + 4 grp + i, so its Y^T row
-    //    is stored four tokens at a time, as high and low parts
-    if (owns) {
-#pragma unroll UNROLL
-      for (int ti = 0; ti < W / G; ++ti) {
-        const int tb = part + G * ti;
-        u32x4 xo[KD];
-#pragma unroll
-        for (int c = 0; c < KD; ++c) xo[c] = *reinterpret_cast<const u32x4*>(&sm.xs[lds_swz<D>(16 * tb + n16, 32 * c + 8 * grp)]);
-#pragma unroll
-        for (int k = 0; k < NBW; ++k) {
-          const int nb = bw + W * k;
-          if (nb < NB) {
-            f32x4 y = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int c = 0; c < KD; ++c) {
-              y = mfma_16x16x32(xo[c], bt_hi[k][c], y);
-              y = mfma_16x16x32(xo[c], bt_lo[k][c], y);
-            }
-            uint32_t hi[4], lo[4];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              hi[i] = f32_to_bf16(y[i]);
-              lo[i] = f32_to_bf16(y[i] - bf16_to_f32((uint16_t)hi[i]));
-            }
-            const int yo = lds_swz<STEP>(16 * nb + n16, 16 * tb + 4 * grp);
-            *reinterpret_cast<u32x2*>(&sm.yt_hi[yo]) = u32x2{hi[0] | (hi[1] << 16), hi[2] | (hi[3] << 16)};
-            *reinterpret_cast<u32x2*>(&sm.yt_lo[yo]) = u32x2{lo[0] | (lo[1] << 16), lo[2] | (lo[3] << 16)};
-          }
-        }
-      }
-    }
-    __syncthreads();
-    // 3. S1 += X^T Y and S2 += Y^T Y over the step's 16 W tokens, for this
-    //    wave's coefficient columns: k-slots are tokens 32 kk + 8 grp .. + 7
-    if (owns) {
-#pragma unroll UNROLL
-      for (int kk = 0; kk < W / 2; ++kk) {
-        const int t = 32 * kk + 8 * grp;
-        u32x4 bh[NBW], bl[NBW];
-#pragma unroll
-        for (int k = 0; k < NBW; ++k) {
-          const int nb = bw + W * k < NB ? bw + W * k : 0;
-          bh[k] = *reinterpret_cast<const u32x4*>(&sm.yt_hi[lds_swz<STEP>(16 * nb + n16, t)]);
-          bl[k] = *reinterpret_cast<const u32x4*>(&sm.yt_lo[lds_swz<STEP>(16 * nb + n16, t)]);
-        }
-#pragma unroll
-        for (int i = 0; i < DBW; ++i) {
-          const int db = part + G * i;
-          const u32x4 xr = *reinterpret_cast<const u32x4*>(&sm.xt[lds_swz<STEP>(16 * db + n16, t)]);
-#pragma unroll
-          for (int k = 0; k < NBW; ++k) {
-            if (bw + W * k < NB) {
-              s1[i][k] = mfma_16x16x32(xr, bh[k], s1[i][k]);
-              s1[i][k] = mfma_16x16x32(xr, bl[k], s1[i][k]);
-            }
-          }
-        }
-#pragma unroll
-        for (int k = 0; k < NBW; ++k) {
-          const int nb = bw + W * k;
-          if (nb < NB) {
-#pragma unroll
-            for (int jj = 0; jj < NJW; ++jj) {
-              const int j = part + G * jj;
-              const int na = (nb + j) % NB;
-              if (j < NJ && oja_s2_formed(na, nb, NB)) {
-                const u32x4 ah = *reinterpret_cast<const u32x4*>(&sm.yt_hi[lds_swz<STEP>(16 * na + n16, t)]);
-                const u32x4 al = *reinterpret_cast<const u32x4*>(&sm.yt_lo[lds_swz<STEP>(16 * na + n16, t)]);
-                s2[jj][k] = mfma_16x16x32(ah, bh[k], s2[jj][k]);
-                s2[jj][k] = mfma_16x16x32(ah, bl[k], s2[jj][k]);
-                s2[jj][k] = mfma_16x16x32(al, bh[k], s2[jj][k]);
-              }
-            }
-          }
-        }
-      }
-    }
-    __syncthreads();   // the next step rewrites X, X^T and Y^T
   };
-  for (int64_t step = s_begin; step < s_end; step += kAhead + 1) {
-    run_step(x0, x3, step);
-    if (step + 1 < s_end) run_step(x1, x0, step + 1);
-    if (step + 2 < s_end) run_step(x2, x1, step + 2);
-    if (step + 3 < s_end) run_step(x3, x2, step + 3);
+  // Two register buffers and two LDS tiles, used in turn: step s is staged
+  // into tile s % 2 from its registers, which then take step s + 2; after
+  // the barrier every wave accumulates the tile.  The barrier also orders
+  // every wave's reads of a tile before that tile is staged again.  (Loads
+  // three steps ahead, with three tiles, measured the same: 32.3 us.)
+  u32x4 b0[PIECES], b1[PIECES];
+  auto step = [&](u32x4 (&buf)[PIECES], int s, uint16_t* t) {
+    stage(buf, t);
+    load(buf, s + 2);
+    __syncthreads();
+    accumulate(t);
+  };
+  load(b0, 0);
+  load(b1, 1);
+  for (int s = 0; s < steps; s += 2) {
+    step(b0, s, tile[0]);
+    if (s + 1 >= steps) break;
+    step(b1, s + 1, tile[1]);
   }
+  // the run's partial G: lane (n16, grp) register e of tile (i, j) is
+  // G[16 (wave NI + i) + 4 grp + e][16 j + n16]
+  float* out = a.ws + ((int64_t)h * a.n_wg + wg) * D * D;
+#pragma unroll
+  for (int i = 0; i < NI; ++i)
+#pragma unroll
+    for (int j = 0; j < NBLK; ++j)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) out[(16 * (wave * NI + i) + 4 * grp + e) * D + 16 * j + n16] = acc[i][j][e];
+}
 
-  // partial sums of this workgroup (zeros when it had no steps); result lane
-  // (n16, grp) register i holds row 4 grp + i, column n16 of its tile
-  float* w1 = a.ws + ((int64_t)h * gridDim.x + blockIdx.x) * oja_head_floats(D, R);
-  float* w2 = w1 + (int64_t)D * R;
+// n floats (a multiple of 4, both ends 16-byte aligned) from global memory
+// to LDS, 16 bytes per load, eight loads per thread in flight before their
+// stores (a load-store loop would wait for each load in turn).
+__device__ __forceinline__ void copy_to_lds(float* dst, const float* src, int n) {
+  const int n4 = n / 4;
+  for (int i0 = threadIdx.x; i0 < n4; i0 += 256 * 8) {
+    f32x4 v[8];
 #pragma unroll
-  for (int k = 0; k < NBW; ++k) {
-    const int nb = bw + W * k;
-    if (nb < NB) {
+    for (int u = 0; u < 8; ++u) {
+      const int i = i0 + 256 * u;
+      v[u] = i < n4 ? reinterpret_cast<const f32x4*>(src)[i] : f32x4{0.f, 0.f, 0.f, 0.f};
+    }
 #pragma unroll
-      for (int di = 0; di < DBW; ++di) {
-        const int db = part + G * di;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) w1[(16 * db + 4 * grp + i) * R + 16 * nb + n16] = s1[di][k][i];
-      }
-#pragma unroll
-      for (int jj = 0; jj < NJW; ++jj) {
-        const int j = part + G * jj;
-        const int na = (nb + j) % NB;
-        if (j < NJ && oja_s2_formed(na, nb, NB)) {
-#pragma unroll
-          for (int i = 0; i < 4; ++i) w2[(16 * na + 4 * grp + i) * R + 16 * nb + n16] = s2[jj][k][i];
-        }
-      }
+    for (int u = 0; u < 8; ++u) {
+      const int i = i0 + 256 * u;
+      if (i < n4) reinterpret_cast<f32x4*>(dst)[i] = v[u];
     }
   }
 }
 
-// Sum of the stats workgroups' partials of every head, in workgroup order.
-__global__ __launch_bounds__(256) void oja_reduce_kernel(OjaArgs a, int64_t per_head) {
-  const int h = blockIdx.y;
-  const int64_t i = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
-  if (i >= per_head) return;
-  f32x4 s = f32x4{0.f, 0.f, 0.f, 0.f};
-  const float* src = a.ws + (int64_t)h * a.n_wg * per_head + i;
-  // the loads of eight partials in flight; the sum keeps workgroup order
-#pragma unroll 8
-  for (int w = 0; w < a.n_wg; ++w) {
-    const f32x4 v = *reinterpret_cast<const f32x4*>(src + (int64_t)w * per_head);
+// Rows row0 .. row0 + kS1Rows - 1 of S1 = G B for one head: the rows of G
+// are the sums of the runs' partials in run order (thread t sums float4
+// column t % 32 of row t / 32, sixteen partials' loads in flight); columns
+// r .. R - 1 of S1 (R = the rank padded to 16) are written as zero.  B is
+// staged in LDS; thread j forms column j of all the rows, so each B element
+// it reads serves kS1Rows products.
+constexpr int kS1Rows = 8;
+__global__ __launch_bounds__(256) void oja_s1_kernel(OjaArgs a, int R) {
+  __shared__ __attribute__((aligned(16))) float s_b[128 * 128];
+  __shared__ __attribute__((aligned(16))) float s_g[kS1Rows][128];
+  const int tid = threadIdx.x;
+  const int h = blockIdx.y, row0 = kS1Rows * blockIdx.x;
+  const int d = a.d, r = a.rank;
+  copy_to_lds(s_b, a.basis + (int64_t)h * d * r, d * r);
+  const int q4 = d / 4;   // float4 columns per row
+  if (tid < kS1Rows * q4) {
+    const int rr = tid / q4, c4 = tid - rr * q4;
+    const f32x4* src = reinterpret_cast<const f32x4*>(a.ws + (int64_t)h * a.n_wg * d * d + (int64_t)(row0 + rr) * d) + c4;
+    const int64_t stride4 = (int64_t)d * d / 4;
+    f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int w0 = 0; w0 < a.n_wg; w0 += 16) {
+      f32x4 v[16];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) s[e] += v[e];
+      for (int u = 0; u < 16; ++u) v[u] = w0 + u < a.n_wg ? src[(int64_t)(w0 + u) * stride4] : f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int u = 0; u < 16; ++u)
+        if (w0 + u < a.n_wg) acc += v[u];
+    }
+    *reinterpret_cast<f32x4*>(&s_g[rr][4 * c4]) = acc;
   }
-  *reinterpret_cast<f32x4*>(a.ws_sum + (int64_t)h * per_head + i) = s;
+  __syncthreads();
+  float* s1 = a.ws_sum + (int64_t)h * oja_head_floats(d, R);
+  for (int j = tid; j < R; j += 256) {
+    float o[kS1Rows];
+#pragma unroll
+    for (int rr = 0; rr < kS1Rows; ++rr) o[rr] = 0.f;
+    if (j < r) {
+      for (int k = 0; k < d; k += 4) {
+        const float b0 = s_b[k * r + j], b1 = s_b[(k + 1) * r + j], b2 = s_b[(k + 2) * r + j],
+                    b3 = s_b[(k + 3) * r + j];
+#pragma unroll
+        for (int rr = 0; rr < kS1Rows; ++rr) {
+          const f32x4 g4 = *reinterpret_cast<const f32x4*>(&s_g[rr][k]);
+          o[rr] = fmaf(g4[3], b3, fmaf(g4[2], b2, fmaf(g4[1], b1, fmaf(g4[0], b0, o[rr]))));
+        }
+      }
+    }
+#pragma unroll
+    for (int rr = 0; rr < kS1Rows; ++rr) s1[(int64_t)(row0 + rr) * R + j] = o[rr];
+  }
+}
+
+// Rows a0 .. a0 + kS2Rows - 1 of S2 = B^T S1 for one head ([R][R] after
+// S1 [d][R]; rows and columns past the rank are zero).  S1 is staged in LDS;
+// thread j forms column j of the rows.
+constexpr int kS2Rows = 4;
+__global__ __launch_bounds__(256) void oja_s2_kernel(OjaArgs a, int R) {
+  __shared__ __attribute__((aligned(16))) float s_s1[128 * 128];
+  __shared__ __attribute__((aligned(16))) float s_b[128][kS2Rows];
+  const int tid = threadIdx.x;
+  const int h = blockIdx.y, a0 = kS2Rows * blockIdx.x;
+  const int d = a.d, r = a.rank;
+  float* sum = a.ws_sum + (int64_t)h * oja_head_floats(d, R);
+  copy_to_lds(s_s1, sum, d * R);
+  const float* bs = a.basis + (int64_t)h * d * r;
+  for (int i = tid; i < d * kS2Rows; i += 256) {
+    const int k = i / kS2Rows, q = i - k * kS2Rows;
+    s_b[k][q] = a0 + q < r ? bs[(int64_t)k * r + a0 + q] : 0.f;
+  }
+  __syncthreads();
+  float* s2 = sum + (int64_t)d * R;
+  for (int j = tid; j < R; j += 256) {
+    f32x4 o = f32x4{0.f, 0.f, 0.f, 0.f};   // rows a0 .. a0 + 3
+    for (int k = 0; k < d; ++k) {
+      const f32x4 b4 = *reinterpret_cast<const f32x4*>(&s_b[k][0]);
+      const float v = s_s1[k * R + j];
+#pragma unroll
+      for (int q = 0; q < kS2Rows; ++q) o[q] = fmaf(b4[q], v, o[q]);
+    }
+#pragma unroll
+    for (int q = 0; q < kS2Rows; ++q) s2[(int64_t)(a0 + q) * R + j] = o[q];
+  }
 }
 
 // B <- B + eta (S1 - B S2) for kOjaRows rows of one head's basis.  The rows
 // are staged in LDS before any is written, and no other workgroup touches
-// them.
+// them; thread j forms column j of the rows.
 constexpr int kOjaRows = 4;
 template <int R>
 __global__ __launch_bounds__(256) void oja_apply_kernel(OjaArgs a) {
-  __shared__ float s_s2[R][R + 1];
-  __shared__ float s_b[kOjaRows][R + 1];
+  __shared__ __attribute__((aligned(16))) float s_s2[R * R];
+  __shared__ __attribute__((aligned(16))) float s_b[kOjaRows][128];
   const int h = blockIdx.y, row0 = kOjaRows * blockIdx.x;
   const int tid = threadIdx.x;
   const int r = a.rank, d = a.d;
   const int64_t per_head = oja_head_floats(d, R);
   const float* sum = a.ws_sum + (int64_t)h * per_head;
   float* bs = a.basis + (int64_t)h * d * r;
-  // tiles that were not formed are the transposes of their mirrors
-  for (int i = tid; i < R * R; i += 256) {
-    const int k = i / R, j = i % R;
-    s_s2[k][j] = oja_s2_formed(k / 16, j / 16, R / 16) ? sum[(int64_t)d * R + i] : sum[(int64_t)d * R + j * R + k];
-  }
+  copy_to_lds(s_s2, sum + (int64_t)d * R, R * R);
   for (int i = tid; i < kOjaRows * r; i += 256) s_b[i / r][i % r] = bs[(int64_t)(row0 + i / r) * r + i % r];
   __syncthreads();
   uint16_t* bb = static_cast<uint16_t*>(a.basis_bf16);
-  for (int i = tid; i < kOjaRows * r; i += 256) {
-    const int rr = i / r, j = i % r;
-    // four partial sums (r is a multiple of 8): no single dependent chain
-    float d4[4] = {0.f, 0.f, 0.f, 0.f};
-    for (int k = 0; k < r; k += 4)
+  for (int j = tid; j < r; j += 256) {
+    float dot[kOjaRows];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) d4[u] = fmaf(s_b[rr][k + u], s_s2[k + u][j], d4[u]);
-    const float dot = (d4[0] + d4[1]) + (d4[2] + d4[3]);
-    const float v = s_b[rr][j] + a.eta * (sum[(int64_t)(row0 + rr) * R + j] - dot);
-    const int64_t o = (int64_t)(row0 + rr) * r + j;
-    bs[o] = v;
-    if (bb) bb[(int64_t)h * d * r + o] = f32_to_bf16(v);
+    for (int rr = 0; rr < kOjaRows; ++rr) dot[rr] = 0.f;
+    for (int k = 0; k < r; k += 4) {   // r is a multiple of 8
+      const float s0 = s_s2[k * R + j], s1 = s_s2[(k + 1) * R + j], s2 = s_s2[(k + 2) * R + j],
+                  s3 = s_s2[(k + 3) * R + j];
+#pragma unroll
+      for (int rr = 0; rr < kOjaRows; ++rr) {
+        const f32x4 b4 = *reinterpret_cast<const f32x4*>(&s_b[rr][k]);
+        dot[rr] = fmaf(b4[3], s3, fmaf(b4[2], s2, fmaf(b4[1], s1, fmaf(b4[0], s0, dot[rr]))));
+      }
+    }
+#pragma unroll
+    for (int rr = 0; rr < kOjaRows; ++rr) {
+      const float v = s_b[rr][j] + a.eta * (sum[(int64_t)(row0 + rr) * R + j] - dot[rr]);
+      const int64_t o = (int64_t)(row0 + rr) * r + j;
+      bs[o] = v;
+      if (bb) bb[(int64_t)h * d * r + o] = f32_to_bf16(v);
+    }
   }
 }
 
@@ -476,15 +410,6 @@ __global__ __launch_bounds__(kOjaSmallThreads) void oja_small_kernel(OjaArgs a) 
 
 }  // namespace
 
-#define LRKV_OJA_CASE4(D, NB)                                                                   \
-  case NB:                                                                                      \
-    hipLaunchKernelGGL((oja_stats_kernel<D, NB, 4>), dim3(a.n_wg, a.hkv), dim3(256), 0, s, a); \
-    break;
-#define LRKV_OJA_CASE8(D, NB)                                                                   \
-  case NB:                                                                                      \
-    hipLaunchKernelGGL((oja_stats_kernel<D, NB, 8>), dim3(a.n_wg, a.hkv), dim3(512), 0, s, a); \
-    break;
-
 hipError_t launch_oja_update(const OjaArgs& a, hipStream_t s) {
   const int nb = (a.rank + 15) / 16;
   if (a.d != 64 && a.d != 128) return hipErrorInvalidValue;
@@ -494,23 +419,16 @@ hipError_t launch_oja_update(const OjaArgs& a, hipStream_t s) {
     else hipLaunchKernelGGL(oja_small_kernel<64>, dim3(a.hkv), dim3(kOjaSmallThreads), 0, s, a);
     return hipGetLastError();
   }
-  if (a.d == 128) {
-    switch (nb) {
-      LRKV_OJA_CASE4(128, 1) LRKV_OJA_CASE4(128, 2) LRKV_OJA_CASE4(128, 3) LRKV_OJA_CASE4(128, 4)
-      LRKV_OJA_CASE8(128, 5) LRKV_OJA_CASE8(128, 6) LRKV_OJA_CASE8(128, 7) LRKV_OJA_CASE8(128, 8)
-      default: return hipErrorInvalidValue;
-    }
-  } else {
-    switch (nb) {
-      LRKV_OJA_CASE4(64, 1) LRKV_OJA_CASE4(64, 2) LRKV_OJA_CASE4(64, 3) LRKV_OJA_CASE4(64, 4)
-      default: return hipErrorInvalidValue;
-    }
-  }
+  if (a.n_wg < 1) return hipErrorInvalidValue;
+  const int R = 16 * nb;
+  if (a.d == 128) hipLaunchKernelGGL(oja_gram_kernel<128>, dim3(a.n_wg, a.hkv), dim3(256), 0, s, a);
+  else hipLaunchKernelGGL(oja_gram_kernel<64>, dim3(a.n_wg, a.hkv), dim3(256), 0, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const int64_t per_head = oja_head_floats(a.d, 16 * nb);
-  const dim3 rgrid((unsigned)((per_head / 4 + 255) / 256), a.hkv);
-  hipLaunchKernelGGL(oja_reduce_kernel, rgrid, dim3(256), 0, s, a, per_head);
+  hipLaunchKernelGGL(oja_s1_kernel, dim3(a.d / kS1Rows, a.hkv), dim3(256), 0, s, a, R);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(oja_s2_kernel, dim3(R / kS2Rows, a.hkv), dim3(256), 0, s, a, R);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   const dim3 agrid((unsigned)(a.d / kOjaRows), a.hkv);

@@ -155,10 +155,11 @@ hipError_t launch_oja_update(const OjaArgs& a, hipStream_t) {
   EXPECT(a.n_tokens >= 1, "Oja update of no tokens launched");
   if (a.n_tokens <= kOjaSmallTokens) return hipSuccess;   // one workgroup per head, no workspace
   const int64_t per_head = oja_head_floats(a.d, oja_rank_pad(a.rank));
-  EXPECT(a.ws_sum == a.ws + (int64_t)a.hkv * a.n_wg * per_head, "Oja sums not after the partials");
-  touch_write(a.ws, (int64_t)a.hkv * a.n_wg * per_head);
+  const int64_t partials = (int64_t)a.hkv * a.n_wg * a.d * a.d;   // the runs' Gram matrices
+  EXPECT(a.ws_sum == a.ws + partials, "Oja sums not after the partials");
+  touch_write(a.ws, partials);
   touch_write(a.ws_sum, (int64_t)a.hkv * per_head);
-  touch_read(a.ws, (int64_t)a.hkv * a.n_wg * per_head);
+  touch_read(a.ws, partials);
   EXPECT(a.n_wg >= 1, "no Oja workgroups");
   return hipSuccess;
 }
