@@ -51,7 +51,9 @@ def parse():
     p.add_argument("--steps", type=int, default=10)
     p.add_argument("--warmup", type=int, default=3)
     p.add_argument("--no-cpu-baseline", action="store_true")
-    p.add_argument("--no-extra", action="store_true", help="skip the hybrid and 32-layer-step figures")
+    p.add_argument("--no-extra", action="store_true", help="skip the variant, hybrid and 32-layer-step figures")
+    p.add_argument("--no-sweep", action="store_true",
+                   help="skip the 32-layer-step figures (their HIP graph replays; for counter passes)")
     p.add_argument("--only", choices=("hybrid", "sweep"),
                    help="run only the hybrid 128K figures or only the 32-layer-step sweep (for profiling)")
     p.add_argument("--cpu-seconds", type=float, default=15.0,
@@ -243,7 +245,8 @@ def main():
     torch.cuda.empty_cache()
     if not args.no_extra:
         result["hybrid_128k"] = bench_hybrid(torch, lrkv, bm, synth, dev, threads)
-        result["step_32layer_sweep"] = bench_step_sweep(torch, lrkv, bm, synth, dev, threads)
+        if not args.no_sweep:
+            result["step_32layer_sweep"] = bench_step_sweep(torch, lrkv, bm, synth, dev, threads)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
     print(json.dumps(result), flush=True)
@@ -328,7 +331,7 @@ def bench_variants(torch, lrkv, bm, synth, dev, layers, ws, dev_bf16):
             "oja_update_decode_GBps": round(oja_dec_bytes / (oja_dec_us["mean"] * 1e-6) / 1e9, 1),
             "note": "same caches and context as the main figure, layers cycled call after call (no prefill "
                     "between them); two launches per decode call; the Oja update is of both bases of a layer "
-                    "(three launches per basis), from its 4096-token prefill chunk and at decode shape "
+                    "(four launches per basis through the Gram matrix), from its 4096-token prefill chunk and at decode shape "
                     "(batch 16 x the step's one appended token)"}
 
 

@@ -17,14 +17,16 @@
 //          group) is read transposed with ds_read_b64_tr_b16, and the same
 //          operand serves as row operand (G's row block) and as column
 //          operand (its column block).  Loads run two steps ahead.
-//   s1     per 8 rows of G: the runs' partials summed in run order, then
-//          those rows of S1 = G B, float32.
+//   s1     per 4 rows of G: the runs' partials summed in a fixed order,
+//          then those rows of S1 = G B, float32.
 //   s2     per 4 rows of S2 = B^T S1, float32.
 //   apply  B + eta (S1 - B S2) in float32 per 4-row block of B, written
 //          back to the float32 basis and, rounded to nearest even, to the
 //          bfloat16 copy.
 // Chunks of at most kOjaSmallTokens tokens per head take a single launch
 // instead (oja_small_kernel, the same update in its per-token form).
+#include <type_traits>
+
 #include "lrkv_device.h"
 #include "lrkv_internal.h"
 
@@ -43,14 +45,11 @@ constexpr int kGramRow = 128;
 __device__ __forceinline__ int gram_swz(int row) { return 2 * ((row & 3) | (((row >> 3) & 1) << 2)); }
 __device__ __forceinline__ int gram_off(int row, int chunk) { return row * kGramRow + ((chunk ^ gram_swz(row)) << 3); }
 
-// One workgroup per (run of tokens, kv head); wave w owns the row blocks
-// w NI .. w NI + NI - 1 of G (NI = D / 64) and all its column blocks, so each
-// wave forms NI x D / 16 tiles of 16 x 16 (64 accumulators at D = 128).
+// One workgroup per (run of tokens, kv head), four waves.
 template <int D>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void oja_gram_kernel(OjaArgs a) {
   constexpr int NBLK = D / 16;                       // 16-dim blocks
-  constexpr int NI = NBLK / 4;                       // row blocks per wave
   constexpr int CPR = D / 8;                         // 16-byte chunks per token row
   constexpr int PIECES = kOjaGramStep * CPR / 256;   // 16-byte loads per thread per step
   __shared__ __attribute__((aligned(16))) uint16_t tile[2][kOjaGramStep * kGramRow];
@@ -96,53 +95,75 @@ void oja_gram_kernel(OjaArgs a) {
     return u32x4{lo[0], lo[1], hi[0], hi[1]};
   };
 
-  f32x4 acc[NI][NBLK];
-#pragma unroll
-  for (int i = 0; i < NI; ++i)
-#pragma unroll
-    for (int j = 0; j < NBLK; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-  auto accumulate = [&](const uint16_t* t) {
-#pragma unroll
-    for (int k0 = 0; k0 < kOjaGramStep; k0 += 32) {
-      u32x4 col[NBLK], row[NI];
-#pragma unroll
-      for (int j = 0; j < NBLK; ++j) col[j] = operand(t, j, k0);
-#pragma unroll
-      for (int i = 0; i < NI; ++i) row[i] = operand(t, wave * NI + i, k0);
-#pragma unroll
-      for (int i = 0; i < NI; ++i)
-#pragma unroll
-        for (int j = 0; j < NBLK; ++j) acc[i][j] = mfma_16x16x32(row[i], col[j], acc[i][j]);
-    }
-  };
-  // Two register buffers and two LDS tiles, used in turn: step s is staged
-  // into tile s % 2 from its registers, which then take step s + 2; after
-  // the barrier every wave accumulates the tile.  The barrier also orders
-  // every wave's reads of a tile before that tile is staged again.  (Loads
-  // three steps ahead, with three tiles, measured the same: 32.3 us.)
+  // G is symmetric, so only its tiles (I, J) with I <= J are formed.  Wave
+  // w < NBLK / 2 owns the row blocks P = w and Q = NBLK - 1 - w: the tiles
+  // (P, J >= P) and (Q, J >= Q), NBLK + 1 of them (9 at D = 128, every wave;
+  // 5 at D = 64, waves 0 and 1), from the column operands J >= P.  The
+  // wave's work is a compile-time function of w, so each wave runs its own
+  // instantiation of the loop (all of them pass the same barriers).
   u32x4 b0[PIECES], b1[PIECES];
-  auto step = [&](u32x4 (&buf)[PIECES], int s, uint16_t* t) {
-    stage(buf, t);
-    load(buf, s + 2);
-    __syncthreads();
-    accumulate(t);
-  };
-  load(b0, 0);
-  load(b1, 1);
-  for (int s = 0; s < steps; s += 2) {
-    step(b0, s, tile[0]);
-    if (s + 1 >= steps) break;
-    step(b1, s + 1, tile[1]);
-  }
-  // the run's partial G: lane (n16, grp) register e of tile (i, j) is
-  // G[16 (wave NI + i) + 4 grp + e][16 j + n16]
   float* out = a.ws + ((int64_t)h * a.n_wg + wg) * D * D;
+  auto run = [&](auto wtag) {
+    constexpr int W = decltype(wtag)::value;
+    constexpr bool kOwns = W < NBLK / 2;
+    constexpr int P = W, Q = NBLK - 1 - W;
+    constexpr int NP = kOwns ? NBLK - P : 0, NQ = kOwns ? NBLK - Q : 0;
+    f32x4 ap[NP > 0 ? NP : 1], aq[NQ > 0 ? NQ : 1];
 #pragma unroll
-  for (int i = 0; i < NI; ++i)
+    for (int j = 0; j < NP; ++j) ap[j] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int j = 0; j < NBLK; ++j)
+    for (int j = 0; j < NQ; ++j) aq[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    auto accumulate = [&](const uint16_t* t) {
+      if (!kOwns) return;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) out[(16 * (wave * NI + i) + 4 * grp + e) * D + 16 * j + n16] = acc[i][j][e];
+      for (int k0 = 0; k0 < kOjaGramStep; k0 += 32) {
+        u32x4 col[NP > 0 ? NP : 1];   // column blocks P .. NBLK - 1
+#pragma unroll
+        for (int j = 0; j < NP; ++j) col[j] = operand(t, P + j, k0);
+#pragma unroll
+        for (int j = 0; j < NP; ++j) ap[j] = mfma_16x16x32(col[0], col[j], ap[j]);
+#pragma unroll
+        for (int j = 0; j < NQ; ++j) aq[j] = mfma_16x16x32(col[Q - P], col[Q - P + j], aq[j]);
+      }
+    };
+    // Two register buffers and two LDS tiles, used in turn: step s is staged
+    // into tile s % 2 from its registers, which then take step s + 2; after
+    // the barrier every wave accumulates the tile.  The barrier also orders
+    // every wave's reads of a tile before that tile is staged again.  (Loads
+    // three steps ahead, with three tiles, measured the same.)
+    auto step = [&](u32x4 (&buf)[PIECES], int s, uint16_t* t) {
+      stage(buf, t);
+      load(buf, s + 2);
+      __syncthreads();
+      accumulate(t);
+    };
+    load(b0, 0);
+    load(b1, 1);
+    for (int s = 0; s < steps; s += 2) {
+      step(b0, s, tile[0]);
+      if (s + 1 >= steps) break;
+      step(b1, s + 1, tile[1]);
+    }
+    // The run's partial G, both triangles: lane (n16, grp) register e of
+    // tile (I, J) is G[16 I + 4 grp + e][16 J + n16]; an off-diagonal tile is
+    // also stored as its mirror, G[16 J + n16][16 I + 4 grp + e .. + 3], four
+    // consecutive floats per lane.
+    auto put = [&](int I, int J, const f32x4& v) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) out[(16 * I + 4 * grp + e) * D + 16 * J + n16] = v[e];
+      if (J != I) *reinterpret_cast<f32x4*>(out + (16 * J + n16) * D + 16 * I + 4 * grp) = v;
+    };
+#pragma unroll
+    for (int j = 0; j < NP; ++j) put(P, P + j, ap[j]);
+#pragma unroll
+    for (int j = 0; j < NQ; ++j) put(Q, Q + j, aq[j]);
+  };
+  switch (wave) {
+    case 0: run(std::integral_constant<int, 0>{}); break;
+    case 1: run(std::integral_constant<int, 1>{}); break;
+    case 2: run(std::integral_constant<int, 2>{}); break;
+    default: run(std::integral_constant<int, 3>{}); break;
+  }
 }
 
 // n floats (a multiple of 4, both ends 16-byte aligned) from global memory
@@ -165,55 +186,66 @@ __device__ __forceinline__ void copy_to_lds(float* dst, const float* src, int n)
   }
 }
 
-// Rows row0 .. row0 + kS1Rows - 1 of S1 = G B for one head: the rows of G
-// are the sums of the runs' partials in run order (thread t sums float4
-// column t % 32 of row t / 32, sixteen partials' loads in flight); columns
-// r .. R - 1 of S1 (R = the rank padded to 16) are written as zero.  B is
-// staged in LDS; thread j forms column j of all the rows, so each B element
-// it reads serves kS1Rows products.
-constexpr int kS1Rows = 8;
+// Rows row0 .. row0 + kS1Rows - 1 of S1 = G B for one head.  The rows of G
+// are the sums of the runs' partials: thread t sums float4 column c4 of row
+// rr over the runs of one parity (t / 128: even or odd runs, sixteen loads
+// in flight), and the row is the even runs' sum plus the odd runs' sum
+// (a fixed order).  Columns r .. R - 1 of S1 (R = the rank padded to 16) are
+// written as zero.  B is staged in LDS; thread j forms column j of all the
+// rows, so each B element it reads serves kS1Rows products.
+constexpr int kS1Rows = 4;
 __global__ __launch_bounds__(256) void oja_s1_kernel(OjaArgs a, int R) {
   __shared__ __attribute__((aligned(16))) float s_b[128 * 128];
-  __shared__ __attribute__((aligned(16))) float s_g[kS1Rows][128];
+  __shared__ __attribute__((aligned(16))) float s_g[2][kS1Rows][128];
   const int tid = threadIdx.x;
   const int h = blockIdx.y, row0 = kS1Rows * blockIdx.x;
   const int d = a.d, r = a.rank;
-  copy_to_lds(s_b, a.basis + (int64_t)h * d * r, d * r);
   const int q4 = d / 4;   // float4 columns per row
-  if (tid < kS1Rows * q4) {
-    const int rr = tid / q4, c4 = tid - rr * q4;
+  const int par = tid >> 7, t = tid & 127;
+  f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+  const bool summer = t < kS1Rows * q4;
+  const int rr = t / q4, c4 = t - rr * q4;
+  if (summer) {
     const f32x4* src = reinterpret_cast<const f32x4*>(a.ws + (int64_t)h * a.n_wg * d * d + (int64_t)(row0 + rr) * d) + c4;
     const int64_t stride4 = (int64_t)d * d / 4;
-    f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
-    for (int w0 = 0; w0 < a.n_wg; w0 += 16) {
+    for (int w0 = par; w0 < a.n_wg; w0 += 32) {
       f32x4 v[16];
 #pragma unroll
-      for (int u = 0; u < 16; ++u) v[u] = w0 + u < a.n_wg ? src[(int64_t)(w0 + u) * stride4] : f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int u = 0; u < 16; ++u) {
+        const int w = w0 + 2 * u;
+        v[u] = w < a.n_wg ? src[(int64_t)w * stride4] : f32x4{0.f, 0.f, 0.f, 0.f};
+      }
 #pragma unroll
       for (int u = 0; u < 16; ++u)
-        if (w0 + u < a.n_wg) acc += v[u];
+        if (w0 + 2 * u < a.n_wg) acc += v[u];
     }
-    *reinterpret_cast<f32x4*>(&s_g[rr][4 * c4]) = acc;
+  }
+  copy_to_lds(s_b, a.basis + (int64_t)h * d * r, d * r);
+  if (summer) *reinterpret_cast<f32x4*>(&s_g[par][rr][4 * c4]) = acc;
+  __syncthreads();
+  for (int i = tid; i < kS1Rows * d; i += 256) {
+    const int r2 = i / d, c = i - r2 * d;
+    s_g[0][r2][c] += s_g[1][r2][c];
   }
   __syncthreads();
   float* s1 = a.ws_sum + (int64_t)h * oja_head_floats(d, R);
   for (int j = tid; j < R; j += 256) {
     float o[kS1Rows];
 #pragma unroll
-    for (int rr = 0; rr < kS1Rows; ++rr) o[rr] = 0.f;
+    for (int q = 0; q < kS1Rows; ++q) o[q] = 0.f;
     if (j < r) {
       for (int k = 0; k < d; k += 4) {
         const float b0 = s_b[k * r + j], b1 = s_b[(k + 1) * r + j], b2 = s_b[(k + 2) * r + j],
                     b3 = s_b[(k + 3) * r + j];
 #pragma unroll
-        for (int rr = 0; rr < kS1Rows; ++rr) {
-          const f32x4 g4 = *reinterpret_cast<const f32x4*>(&s_g[rr][k]);
-          o[rr] = fmaf(g4[3], b3, fmaf(g4[2], b2, fmaf(g4[1], b1, fmaf(g4[0], b0, o[rr]))));
+        for (int q = 0; q < kS1Rows; ++q) {
+          const f32x4 g4 = *reinterpret_cast<const f32x4*>(&s_g[0][q][k]);
+          o[q] = fmaf(g4[3], b3, fmaf(g4[2], b2, fmaf(g4[1], b1, fmaf(g4[0], b0, o[q]))));
         }
       }
     }
 #pragma unroll
-    for (int rr = 0; rr < kS1Rows; ++rr) s1[(int64_t)(row0 + rr) * R + j] = o[rr];
+    for (int q = 0; q < kS1Rows; ++q) s1[(int64_t)(row0 + q) * R + j] = o[q];
   }
 }
 
