@@ -320,6 +320,9 @@ def test_hybrid_decode_shares_one_workspace_and_replays_in_a_graph():
             o, lse = lrkv.decode_attn_hybrid(qd, bkd, bvd, c, workspace=ws)
             torch.cuda.synchronize()
             assert torch.equal(o.view(torch.int16), o_ref.view(torch.int16)) and torch.equal(lse, l_ref)
+            # the in-launch merge's arrival counters (one word per (b, kv head)
+            # at the workspace's start) are back at zero after every call
+            assert not torch.any(ws[:4 * w.batch * w.n_kv_heads]).item()
     out = torch.empty_like(qd)
     lse = torch.empty((w.batch, w.n_q_heads), dtype=torch.float32, device=DEV)
     stream = torch.cuda.Stream()

@@ -57,13 +57,15 @@ def _run(x, b0, eta, workspace=None):
                                        (128, 32, 2, 77, 3), (64, 48, 1, 200, 2), (128, 112, 1, 250, 2),
                                        (64, 16, 2, 3, 2), (128, 128, 1, 64, 1), (128, 8, 3, 20, 4),
                                        (64, 48, 16, 1, 3), (128, 112, 16, 4, 8), (128, 112, 13, 5, 2),
-                                       (64, 64, 8, 8, 1)])
+                                       (64, 64, 8, 8, 1), (128, 40, 3, 3000, 8), (64, 32, 5, 2001, 8)])
 def test_oja_update_small(d, r, B, T, H):
     """Ragged token counts (a last step with 1..63 tokens, or one token), ranks
     that pad to whole 16-column blocks, both head dims; one and two
     coefficient blocks put four and two waves on each block.  Chunks of at
     most 64 tokens per head (here 1 to 64, a decode step's 16 among them) take
-    the single-launch path; 65 tokens (13 x 5) the three-launch one."""
+    the single-launch path; 65 tokens (13 x 5) and more the Gram path, whose
+    runs of 128-token steps end ragged (9000 and 10005 tokens over 32 runs
+    per head: three steps per run, the last one partial)."""
     w = synth.scaled(synth.LLAMA_LAYER, batch=B, n_kv_heads=H, head_dim=d, ranks_even=(r, r), ranks_odd=(r, r))
     x = _tokens(w, 0, "k", T)
     b0 = synth.basis(w, 0, "k").exact
