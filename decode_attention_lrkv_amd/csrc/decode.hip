@@ -25,12 +25,9 @@ void split_bf16_latent_kernel(SplitArgs a) {
 // one chunk (the stream is shared fairly between compute units, so the
 // workgroup with the most bytes ends last), which their four waves take in
 // turn.  Every workgroup writes partial blockIdx.x.
-// With lr.merge_cnt the partials are stored with device scope (written
-// through to memory), each workgroup then counts its arrival, and the last
-// workgroup of the (b, kv head) to arrive merges the partials, loading them
-// with device scope, so that no second launch is needed.  Each wave waits for
-// its own stores before the workgroup barrier that precedes the count, so
-// the count follows every store of the partial.
+// With lr.merge_cnt the last workgroup of each (b, kv head) merges the
+// partials in this launch (merge_in_launch), so that no second launch is
+// needed.
 template <int KC, int VB, int SKC, int SVB>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void split_bf16_hybrid_kernel(SplitArgs lr, SplitArgs side) {
@@ -98,22 +95,7 @@ void split_bf16_hybrid_kernel(SplitArgs lr, SplitArgs side) {
     a.list_wgs = p_side;
     split_bf16_body<SKC, SVB, false, 1, false, false, true>(a, x - p_lr, x, sm);
   }
-  if (lr.merge_cnt == nullptr) return;
-  __shared__ uint32_t s_last;
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  __syncthreads();
-  if (threadIdx.x == 0)
-    s_last = __hip_atomic_fetch_add(lr.merge_cnt + bh, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
-             (uint32_t)(P - 1);
-  __syncthreads();
-  if (!s_last) return;
-  MergeArgs m{};
-  m.part_o = lr.part_o; m.part_ml = lr.part_ml; m.n_parts = P;
-  m.d = lr.d; m.g = lr.g; m.hq = lr.hq; m.hkv = lr.hkv; m.batch = lr.batch;
-  m.out = lr.merge_out; m.lse = lr.merge_lse;
-  merge_unit<uint16_t, true>(m, bh);
-  // every workgroup of the unit has counted: the counter is free for the next launch
-  if (threadIdx.x == 0) __hip_atomic_store(lr.merge_cnt + bh, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (lr.merge_cnt != nullptr) merge_in_launch(lr, bh, P);
 }
 
 // ----------------------------------------------------------------------------

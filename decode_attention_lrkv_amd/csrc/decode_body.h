@@ -231,6 +231,33 @@ __device__ void merge_unit(const MergeArgs& a, int64_t unit) {
   }
 }
 
+// Merge in the attention launch (a.merge_cnt set; the partials were stored
+// with device scope, sc1, written through to memory): each wave waits for
+// its own stores, the workgroup barrier follows, and one thread counts the
+// workgroup's arrival on its unit's counter with a device-scope atomic.  The
+// workgroup that arrives last of `arrivals` merges the unit's a.n_parts
+// partials with device-scope loads (no stale line of another XCD's L2 is
+// returned) into a.merge_out / a.merge_lse and sets the counter back to zero
+// for the next launch.  No fence is needed: the stores are complete at the
+// coherence point before the count, and the loads read from there.
+__device__ __forceinline__ void merge_in_launch(const SplitArgs& a, int64_t bh, int arrivals) {
+  __shared__ uint32_t s_last;
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  if (threadIdx.x == 0)
+    s_last = __hip_atomic_fetch_add(a.merge_cnt + bh, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+             (uint32_t)(arrivals - 1);
+  __syncthreads();
+  if (!s_last) return;
+  MergeArgs m{};
+  m.part_o = a.part_o; m.part_ml = a.part_ml; m.n_parts = a.n_parts;
+  m.d = a.d; m.g = a.g; m.hq = a.hq; m.hkv = a.hkv; m.batch = a.batch;
+  m.out = a.merge_out; m.lse = a.merge_lse;
+  merge_unit<uint16_t, true>(m, bh);
+  // every workgroup of the unit has counted: the counter is free for the next launch
+  if (threadIdx.x == 0) __hip_atomic_store(a.merge_cnt + bh, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 // ----------------------------------------------------------------------------
 // bfloat16 attention kernel (matrix cores)
 // ----------------------------------------------------------------------------

@@ -41,6 +41,7 @@ hipError_t launch_split_bf16(const SplitArgs& a, hipStream_t s) {
   const dim3 grid(a.k_new ? a.n_parts - 1 : a.n_parts, a.hkv, a.batch);
   const int kc = (a.rk + 31) / 32, vb = (a.rv + 15) / 16;
   if (a.basis_k == nullptr || a.basis_v == nullptr || (a.enc_k && !a.k_new)) return hipErrorInvalidValue;
+  if (a.merge_cnt) return launch_split_bf16_merged(a, s);   // decode_split_merged.hip
   // each wave takes chunks_per_split chunks (the plan for the bound when the
   // lengths are on the device, which never gives a wave more)
   const bool early = a.chunks_per_split >= 2;

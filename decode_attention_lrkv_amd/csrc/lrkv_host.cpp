@@ -309,7 +309,8 @@ lrkv_status decode_partial(const void* q, const void* basis_k, const void* coeff
                            lrkv_dtype dtype, void* workspace, const DecodeLayout& L, hipStream_t stream,
                            const char* fn, const void* k_new = nullptr, const void* v_new = nullptr,
                            const void* enc_k = nullptr, void* out = nullptr, float* lse = nullptr,
-                           const int32_t* seq_lens = nullptr) {
+                           const int32_t* seq_lens = nullptr, bool merge_here = false, void* m_out = nullptr,
+                           float* m_lse = nullptr) {
   char* ws = static_cast<char*>(workspace);
   SplitArgs sa{};
   sa.q = q; sa.basis_k = basis_k; sa.ck = coeff_k; sa.cv = coeff_v; sa.basis_v = basis_v;
@@ -331,6 +332,11 @@ lrkv_status decode_partial(const void* q, const void* basis_k, const void* coeff
   sa.out = out;   // final outputs (one attention workgroup per unit), or partials
   sa.lse = lse;
   sa.n_ctx_b = seq_lens;
+  if (merge_here) {   // the launch merges its own partials (see merge_in_step)
+    sa.merge_cnt = reinterpret_cast<uint32_t*>(ws + L.cnt);
+    sa.merge_out = m_out;
+    sa.merge_lse = m_lse;
+  }
   // no basis_k: latent queries (absorbed projections), no fold and no lift
   const hipError_t e = dtype != LRKV_BF16 ? launch_split_f32(sa, stream)
                                           : (basis_k ? launch_split_bf16(sa, stream) : launch_split_bf16_latent(sa, stream));
@@ -350,6 +356,21 @@ lrkv_status decode_merge(void* out, float* lse, const lrkv_dims* dims, lrkv_dtyp
   ma.out = out; ma.lse = lse;
   const hipError_t e = launch_merge(ma, dtype == LRKV_BF16, stream);
   return e == hipSuccess ? LRKV_OK : device_fail(fn, e);
+}
+
+// Whether a bfloat16 attention launch (with B_K, no separate key encoder)
+// merges its partials itself: when it has at most a quarter as many
+// workgroups as the chip has compute units (batch-1 decodes of short and
+// medium contexts, where the second launch is a large part of a layer's
+// time).  Its last workgroup of each unit then merges, and there is no
+// merge launch.  Measured on the batch-1 32-layer step (graph replays,
+// alternating runs on one box): 40 workgroups (2048 tokens) 487.5 against
+// 491.5 us per step (eager 485 against 501), but 136 workgroups (8192
+// tokens) 521.4 against 507.7 us, and in the batched shape slower too.
+bool merge_in_step(const lrkv_dims& d, const DecodeLayout& L, lrkv_dtype dt, const void* enc_k, bool append) {
+  if (dt != LRKV_BF16 || enc_k) return false;
+  const int64_t wgs = (int64_t)d.batch * d.n_kv_heads * (append ? L.parts - 1 : L.parts);
+  return 4 * wgs <= device_cu_count();
 }
 
 }  // namespace
@@ -375,6 +396,9 @@ lrkv_status lrkv_decode_attn(const void* q, const void* basis_k, const void* coe
   if (dtype == LRKV_BF16 && L.parts == 1)   // one workgroup per unit: it writes the outputs, no merge launch
     return decode_partial(q, basis_k, coeff_k, basis_v, coeff_v, dims, n_ctx, scale, dtype, workspace, L, stream,
                           fn, nullptr, nullptr, nullptr, out, lse);
+  if (merge_in_step(*dims, L, dtype, nullptr, false))
+    return decode_partial(q, basis_k, coeff_k, basis_v, coeff_v, dims, n_ctx, scale, dtype, workspace, L, stream,
+                          fn, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, true, out, lse);
   st = decode_partial(q, basis_k, coeff_k, basis_v, coeff_v, dims, n_ctx, scale, dtype, workspace, L, stream, fn);
   if (st != LRKV_OK) return st;
   return decode_merge(out, lse, dims, dtype, workspace, L, stream, fn);
@@ -510,6 +534,9 @@ lrkv_status lrkv_decode_step(const void* q, const void* k_new, const void* v_new
     }
   }
   const DecodeLayout L = step_layout(*dims, n_ctx, dtype);
+  if (merge_in_step(*dims, L, dtype, enc_k, true))
+    return decode_partial(q, basis_k, coeff_k, basis_v, coeff_v, dims, n_ctx, scale, dtype, workspace, L, stream,
+                          fn, k_new, v_new, nullptr, nullptr, nullptr, nullptr, true, out, lse);
   st = step_partial(q, k_new, v_new, basis_k, coeff_k, basis_v, coeff_v, enc_k, dims, n_ctx, scale, dtype, workspace,
                     L, stream, fn);
   if (st != LRKV_OK) return st;
@@ -568,9 +595,10 @@ lrkv_status lrkv_decode_attn_seqlens(const void* q, const void* basis_k, const v
   if (L.parts == 1)
     return decode_partial(q, basis_k, coeff_k, basis_v, coeff_v, dims, max_seq_len, scale, dtype, workspace, L,
                           stream, fn, nullptr, nullptr, nullptr, out, lse, seq_lens);
+  const bool here = merge_in_step(*dims, L, dtype, nullptr, false);
   st = decode_partial(q, basis_k, coeff_k, basis_v, coeff_v, dims, max_seq_len, scale, dtype, workspace, L, stream,
-                      fn, nullptr, nullptr, nullptr, nullptr, nullptr, seq_lens);
-  if (st != LRKV_OK) return st;
+                      fn, nullptr, nullptr, nullptr, nullptr, nullptr, seq_lens, here, out, lse);
+  if (st != LRKV_OK || here) return st;
   return decode_merge(out, lse, dims, dtype, workspace, L, stream, fn);
 }
 
@@ -595,9 +623,10 @@ lrkv_status lrkv_decode_step_seqlens(const void* q, const void* k_new, const voi
                           stream, fn, k_new, v_new, enc_k, out, lse, seq_lens);
   }
   const DecodeLayout L = step_layout(*dims, max_seq_len, dtype);
+  const bool here = merge_in_step(*dims, L, dtype, enc_k, true);
   st = decode_partial(q, basis_k, coeff_k, basis_v, coeff_v, dims, max_seq_len, scale, dtype, workspace, L, stream,
-                      fn, k_new, v_new, enc_k, nullptr, nullptr, seq_lens);
-  if (st != LRKV_OK) return st;
+                      fn, k_new, v_new, enc_k, nullptr, nullptr, seq_lens, here, out, lse);
+  if (st != LRKV_OK || here) return st;
   return decode_merge(out, lse, dims, dtype, workspace, L, stream, fn);
 }
 

@@ -123,6 +123,8 @@ inline size_t oja_workspace_floats(int hkv, int d, int rank, int n_wg) {
 hipError_t launch_oja_update(const OjaArgs& a, hipStream_t s);
 
 hipError_t launch_split_bf16(const SplitArgs& a, hipStream_t s);
+// the same attention with the merge in the launch (a.merge_cnt set)
+hipError_t launch_split_bf16_merged(const SplitArgs& a, hipStream_t s);
 // Hybrid cache: low-rank rows (lr) and full-rank side list (side) in one
 // launch of wgs_per_unit workgroups per (b, kv head), divided between the two
 // lists on the device from the counts there.  Partials go to lr.part_o /

@@ -138,10 +138,11 @@ lrkv_status lrkv_compress_kv(const void* xk, const void* xv, const void* basis_k
  * split plan depends on the current device's compute-unit count, so query on
  * the device that will run the call.
  * The workspace starts with one 32-bit arrival counter per (b, kv head)
- * (rounded up to 256 bytes) that lrkv_decode_attn_hybrid uses to merge in
- * its own launch: these words must be zero before a workspace's first hybrid
- * call (allocate the workspace zeroed), and every call of any decode entry
- * point leaves them as it found them.  The rest is scratch.  Calls that
+ * (rounded up to 256 bytes) that the calls merging in their own launch use
+ * (lrkv_decode_attn_hybrid, and the small bfloat16 launches of
+ * lrkv_decode_attn, lrkv_decode_step and their _seqlens forms): these words
+ * must be zero before a workspace's first call (allocate the workspace
+ * zeroed), and every call of any decode entry point leaves them zero.  The rest is scratch.  Calls that
  * share a workspace must be ordered on one stream (they must not overlap in
  * time; overlapping hybrid calls on one workspace would also share its
  * counters).
@@ -157,8 +158,11 @@ size_t lrkv_decode_workspace_bytes(const lrkv_dims* dims, int64_t n_ctx, int64_t
  * V_hat = C_V B_V^T ("OjaKV" README, StaticPCA: standard attention over
  * keys and values reconstructed from the low-rank cache).  The context is
  * split into chunks attended in parallel (one launch) and the partial
- * results are merged by log-sum-exp (a second launch).  For bfloat16, when
- * one workgroup per (b, kv head) covers the whole context (short contexts),
+ * results are merged by log-sum-exp (a second launch; for bfloat16 launches
+ * of at most a quarter as many workgroups as the GPU has compute units, the
+ * last workgroup of each (b, kv head) merges in the same launch instead,
+ * using the workspace's arrival counters).  For bfloat16, when one
+ * workgroup per (b, kv head) covers the whole context (short contexts),
  * that workgroup normalises and writes out and lse itself: one launch.
  *   q        [B, Hq, d]
  *   basis_k  [Hkv, d, r_K];   coeff_k  key row layout [B, Hkv, capacity, r_K]
@@ -229,15 +233,18 @@ lrkv_status lrkv_decode_attn_latent(const void* q_lat, const void* coeff_k, cons
  * and contributes its softmax term, while the others attend rows
  * [0, n_ctx - 1); a second launch merges.  When one attention workgroup per
  * (b, kv head) covers rows [0, n_ctx - 1) (short contexts), it also appends
- * and writes out and lse itself: one launch.  float32 runs lrkv_compress_kv,
- * then the decode.  The two-phase entry points below always use the
- * partials and the merge launch.
+ * and writes out and lse itself: one launch.  Small bfloat16 launches
+ * without a separate key encoder merge in the launch, as lrkv_decode_attn.
+ * float32 runs lrkv_compress_kv, then the decode.  The two-phase entry
+ * points below always use the partials and the merge launch.
  *   k_new, v_new  [B, Hkv, d] the new token's key and value
  *   basis_k, basis_v  the decoders (fold and lift), as in lrkv_decode_attn
  *   coeff_k, coeff_v  the caches (row n_ctx - 1 is written; rows below are read)
  *   enc_k    [Hkv, d, r_K] encoder of the new key, or NULL when basis_k is an
  *            orthonormal basis that also encodes (the value is encoded by basis_v)
- *   workspace at least lrkv_decode_step_workspace_bytes(dims, n_ctx) bytes
+ *   workspace at least lrkv_decode_step_workspace_bytes(dims, n_ctx) bytes,
+ *             laid out (arrival counters first, zero before the first call)
+ *             as described at lrkv_decode_workspace_bytes
  * Other arguments as lrkv_decode_attn.  Requires 1 <= n_ctx <= capacity.
  */
 size_t lrkv_decode_step_workspace_bytes(const lrkv_dims* dims, int64_t n_ctx);
