@@ -14,7 +14,10 @@ Reported `value`: decode microseconds per layer-step, i.e. one
 lrkv_decode_step per layer (the attention kernel, whose extra workgroup per
 (batch, kv head) compresses and stores the appended token, + the merge
 kernel), averaged over the 32 layers and the timed steps, measured with HIP
-events on the launch stream.  The roofline entry is for the attention kernel
+events on the launch stream around each layer's two launches.  The timed
+steps alternate: in even-numbered ones an extra event between the two
+launches times the attention kernel alone (the roofline's duration), the
+odd-numbered ones give the layer-step figure.  The roofline entry is for the attention kernel
 (split_bf16_kernel, the dominant one): its algorithmic bytes per launch (key
 and value coefficient rows, both bases, the queries, the appended token in and
 its coefficient rows out) over its average launch time.  `cpu_baseline` times the float64 CPU oracle on a
@@ -136,17 +139,18 @@ def main():
         f"workspace {ws_bytes / 2**20:.2f} MiB")
 
     # ---------------- one step: prefill chunk of every layer, then one decode step of every layer
-    def step(ev=None):
+    def step(ev=None, split=True):
         for l, lay in enumerate(layers):
             if ev: ev["pre"][l][0].record()
             lrkv.compress_kv(lay["xk"], lay["xv"], lay["bk"], lay["bv"], lay["ck"], lay["cv"], p0)
             if ev: ev["pre"][l][1].record()
         for l, lay in enumerate(layers):
-            # lrkv_decode_step as its two launches, so that the attention kernel
-            # (which also compresses and stores the appended token) is timed alone
+            # lrkv_decode_step as its two launches; in a split step an event
+            # between them times the attention kernel (which also compresses
+            # and stores the appended token) alone
             if ev: ev["dec"][l][0].record()
             lrkv.decode_step_partial(lay["q"], lay["ak"], lay["av"], lay["bk"], lay["ck"], lay["bv"], lay["cv"], N, ws)
-            if ev: ev["dec"][l][1].record()
+            if ev and split: ev["dec"][l][1].record()
             lrkv.decode_step_merge(lay["out"], lay["lse"], N, ws, H, lay["rk"], lay["rv"], cap)
             if ev: ev["dec"][l][2].record()
 
@@ -158,23 +162,32 @@ def main():
     mk = lambda n: [torch.cuda.Event(enable_timing=True) for _ in range(n)]
     events = [{"pre": [mk(2) for _ in range(L)], "dec": [mk(3) for _ in range(L)]} for _ in range(K)]
     torch.cuda.synchronize()
+    # Even-numbered steps are split (an event between the attention and the
+    # merge launch of every layer, for the kernel's own time); the layer-step
+    # figure comes from the odd-numbered steps, whose two launches follow each
+    # other with no event between them (an event there adds a few us), or
+    # from every step when only one is timed.
+    split = lambda k: k % 2 == 0
     t0 = time.perf_counter()
     for k in range(K):
-        step(events[k])
+        step(events[k], split(k))
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     log(f"timed {K} steps in {wall:.3f}s")
 
     prefill_us, decode_us, attn_us, merge_us = [], [], [], []
     attn_by_par = {0: [], 1: []}
+    whole = [k for k in range(K) if not split(k)] or list(range(K))
     for k in range(K):
         for l in range(L):
             ep, ed = events[k]["pre"][l], events[k]["dec"][l]
             prefill_us.append(ep[0].elapsed_time(ep[1]) * 1e3)
-            attn_us.append(ed[0].elapsed_time(ed[1]) * 1e3)
-            merge_us.append(ed[1].elapsed_time(ed[2]) * 1e3)
-            decode_us.append(ed[0].elapsed_time(ed[2]) * 1e3)
-            attn_by_par[l % 2].append(attn_us[-1])
+            if k in whole:
+                decode_us.append(ed[0].elapsed_time(ed[2]) * 1e3)
+            if split(k):
+                attn_us.append(ed[0].elapsed_time(ed[1]) * 1e3)
+                merge_us.append(ed[1].elapsed_time(ed[2]) * 1e3)
+                attn_by_par[l % 2].append(attn_us[-1])
 
     # ---------------- bytes and rates
     app_bytes = {p: bm.compress_bytes(B, 1, H, d, w.ranks(p)[0]) + bm.compress_bytes(B, 1, H, d, w.ranks(p)[1])
@@ -185,9 +198,9 @@ def main():
                  for p in (0, 1)}
     mean = lambda xs: float(np.mean(xs))
     dec_us = mean(decode_us)
-    dec_gbps = sum((dec_bytes[l % 2] + app_bytes[l % 2]) for l in range(L)) * K / (sum(decode_us) * 1e-6) / 1e9
+    dec_gbps = sum((dec_bytes[l % 2] + app_bytes[l % 2]) for l in range(L)) * len(whole) / (sum(decode_us) * 1e-6) / 1e9
     attn_mean = {p: mean(attn_by_par[p]) for p in (0, 1)}
-    attn_gbps = sum(attn_bytes[l % 2] for l in range(L)) * K / (sum(attn_us) * 1e-6) / 1e9
+    attn_gbps = sum(attn_bytes[l % 2] for l in range(L)) * (len(attn_us) // L) / (sum(attn_us) * 1e-6) / 1e9
     pre_gbps = sum(pre_bytes[l % 2] for l in range(L)) * K / (sum(prefill_us) * 1e-6) / 1e9
     step_decode_us = dec_us * L
     tok_s = B / (step_decode_us * 1e-6)
