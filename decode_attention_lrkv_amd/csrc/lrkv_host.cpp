@@ -65,12 +65,22 @@ struct Plan {
 // Split a context of n_tokens over (units) independent (batch, kv head) rows so
 // that one round of workgroups fills the chip (8 resident waves per compute
 // unit at the split kernel's register use), with at least 4 chunks (128
-// tokens) per split.  LRKV_SPLITS forces the split count.
+// tokens) per split.  When that still leaves several workgroups per unit but
+// few units (batch-1 decodes, bound by each wave's chain of dependent work,
+// not by bytes), the splits go down to one chunk each, as long as the launch
+// keeps to half a round (one workgroup per two compute units): on the
+// batch-1 32-layer step at 2048 tokens (64 chunks per unit) 64 splits per
+// unit took 423.8 us per graph replay against 487.9 us with 16.  A context
+// that one workgroup per unit covers (at most 16 chunks) keeps that single
+// workgroup, which also writes the outputs (no merge): at 256 tokens 342.5
+// against 397 us with more splits.  LRKV_SPLITS forces the split count.
 Plan plan_splits(int64_t units, int64_t n_tokens, int cus, int max_splits) {
   Plan p;
   const int64_t n_chunks = n_tokens > 0 ? cdiv(n_tokens, kChunk) : 1;
-  int64_t s = cdiv((int64_t)cus * 8, units > 0 ? units : 1);
+  const int64_t u = units > 0 ? units : 1;
+  int64_t s = cdiv((int64_t)cus * 8, u);
   s = std::min<int64_t>(s, cdiv(n_chunks, 4));
+  if (s > 4) s = std::max<int64_t>(s, std::min<int64_t>(n_chunks, (int64_t)cus * 2 / u));
   if (const char* env = std::getenv("LRKV_SPLITS")) {
     const long v = std::strtol(env, nullptr, 10);
     if (v > 0) s = v;
