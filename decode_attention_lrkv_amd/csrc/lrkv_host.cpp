@@ -68,19 +68,23 @@ struct Plan {
 // tokens) per split.  When that still leaves several workgroups per unit but
 // few units (batch-1 decodes, bound by each wave's chain of dependent work,
 // not by bytes), the splits go down to one chunk each, as long as the launch
-// keeps to half a round (one workgroup per two compute units): on the
-// batch-1 32-layer step at 2048 tokens (64 chunks per unit) 64 splits per
-// unit took 423.8 us per graph replay against 487.9 us with 16.  A context
-// that one workgroup per unit covers (at most 16 chunks) keeps that single
-// workgroup, which also writes the outputs (no merge): at 256 tokens 342.5
-// against 397 us with more splits.  LRKV_SPLITS forces the split count.
+// keeps to one workgroup per compute unit (one workgroup of four splits per
+// unit kept free for a decode step's appended token): on the batch-1
+// 32-layer step at 2048 tokens (64 chunks per unit) 64 splits per unit took
+// 423.8 us per graph replay against 487.9 us with 16, and at 8192 tokens
+// 124 splits (3 chunks per wave, 184 workgroups) 481.6 against 509.9 us with
+// 64, while 128 splits (2 chunks per wave, 264 workgroups, two on some
+// compute units) took 577 us.  A context that one workgroup per unit covers
+// (at most 16 chunks) keeps that single workgroup, which also writes the
+// outputs (no merge): at 256 tokens 342.5 against 397 us with more splits.
+// LRKV_SPLITS forces the split count.
 Plan plan_splits(int64_t units, int64_t n_tokens, int cus, int max_splits) {
   Plan p;
   const int64_t n_chunks = n_tokens > 0 ? cdiv(n_tokens, kChunk) : 1;
   const int64_t u = units > 0 ? units : 1;
   int64_t s = cdiv((int64_t)cus * 8, u);
   s = std::min<int64_t>(s, cdiv(n_chunks, 4));
-  if (s > 4) s = std::max<int64_t>(s, std::min<int64_t>(n_chunks, (int64_t)cus * 2 / u));
+  if (s > 4) s = std::max<int64_t>(s, std::min<int64_t>(n_chunks, (int64_t)cus * 4 / u - 4));
   if (const char* env = std::getenv("LRKV_SPLITS")) {
     const long v = std::strtol(env, nullptr, 10);
     if (v > 0) s = v;
