@@ -179,13 +179,17 @@ def test_decode_step_appends_and_attends(N, layer):
     check_decode(to_f64(o), to_f64(lse), o_ref, lse_ref, "bf16", f"decode step N={N} layer={layer}")
 
 
-def test_decode_step_two_phase_equals_one_call():
+@pytest.mark.parametrize("h_kv,N", [(8, 3000), (2, 1000), (1, 3000)])
+def test_decode_step_two_phase_equals_one_call(h_kv, N):
     """lrkv_decode_step_partial + _merge give the bits of lrkv_decode_step,
     also on a workspace whose bytes all start at 0xFF (float NaN): the
     appended token's empty partial slot, whose output words the kernels never
-    write, must weigh nothing in the merge whatever those words hold."""
-    w = synth.LLAMA_STEP
-    layer, N = 1, 3000
+    write, must weigh nothing in the merge whatever those words hold.  With
+    one or two kv heads at batch 1 the one call is a launch small enough to
+    merge its own partials (its last workgroup per kv head, device-scope
+    stores and loads), against the two-phase merge launch."""
+    w = synth.scaled(synth.LLAMA_STEP, n_kv_heads=h_kv, n_q_heads=4 * h_kv)
+    layer = 1
     B, H, d = w.batch, w.n_kv_heads, w.head_dim
     rk, rv = w.ranks(layer)
     rows_k = np.zeros((B, H, N, rk)); rows_k[:, :, :N - 1] = _direct_rows(w, layer, "k", N - 1).exact
