@@ -211,6 +211,15 @@ def test_decode_step_two_phase_equals_one_call(h_kv, N):
     assert torch.equal(o1.view(torch.int16), o2.view(torch.int16)) and torch.equal(l1, l2)
     assert torch.equal(ck1.view(torch.int16), ck2.view(torch.int16))
     assert torch.equal(cv1.view(torch.int16), cv2.view(torch.int16))
+    # one-call steps in a row on one zeroed workspace (appending the same token to
+    # the same row again): the same bits each time, and the arrival counters
+    # at the workspace's start are back at zero after each call
+    wz = torch.zeros_like(ws)
+    for _ in range(2):
+        o3, l3 = lrkv.decode_step(qd, kn, vn, bkd, ck1, bvd, cv1, N, workspace=wz)
+        torch.cuda.synchronize()
+        assert torch.equal(o1.view(torch.int16), o3.view(torch.int16)) and torch.equal(l1, l3)
+        assert not torch.any(wz[:4 * B * H]).item()
 
 
 def test_decode_step_float32():
