@@ -393,22 +393,21 @@ __global__ __launch_bounds__(kOjaSmallThreads) void oja_small_kernel(OjaArgs a) 
     *reinterpret_cast<f32x4*>(&s_y[t][c0 + 4]) = f32x4{y[4], y[5], y[6], y[7]};
   }
   __syncthreads();
-  // 3. R = X - Y B^T in place of X: a thread takes one token and 4 dims,
-  //    contracting over the coefficients (both rows contiguous in them)
-  for (int i = tid; i < n * (D / 4); i += kOjaSmallThreads) {
-    const int t = i / (D / 4), e0 = 4 * (i % (D / 4));
-    float acc[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll 2
+  // 3. R = X - Y B^T in place of X: a thread takes one (token, dim),
+  //    contracting over the coefficients; the lanes of a wave take
+  //    consecutive dims of one token, so the Y row is a broadcast and the B
+  //    rows (pitch D + 4 floats) fall in distinct banks (four dims per lane,
+  //    as before, read rows 4 apart: 16-way bank conflicts)
+  for (int i = tid; i < n * D; i += kOjaSmallThreads) {
+    const int t = i / D, e = i % D;
+    float acc = 0.f;
+#pragma unroll 4
     for (int c = 0; c < r; c += 4) {
       const f32x4 yv = *reinterpret_cast<const f32x4*>(&s_y[t][c]);
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const f32x4 bv = *reinterpret_cast<const f32x4*>(&s_b[e0 + q][c]);
-        acc[q] = fmaf(yv[0], bv[0], fmaf(yv[1], bv[1], fmaf(yv[2], bv[2], fmaf(yv[3], bv[3], acc[q]))));
-      }
+      const f32x4 bv = *reinterpret_cast<const f32x4*>(&s_b[e][c]);
+      acc = fmaf(yv[0], bv[0], fmaf(yv[1], bv[1], fmaf(yv[2], bv[2], fmaf(yv[3], bv[3], acc))));
     }
-#pragma unroll
-    for (int q = 0; q < 4; ++q) s_x[t][e0 + q] -= acc[q];
+    s_x[t][e] -= acc;
   }
   __syncthreads();
   // 4. B += eta R^T Y: a thread takes one dim and 8 coefficients,
