@@ -396,18 +396,20 @@ __global__ __launch_bounds__(kOjaSmallThreads) void oja_small_kernel(OjaArgs a) 
   // 3. R = X - Y B^T in place of X: a thread takes one (token, dim),
   //    contracting over the coefficients; the lanes of a wave take
   //    consecutive dims of one token, so the Y row is a broadcast and the B
-  //    rows (pitch D + 4 floats) fall in distinct banks (four dims per lane,
-  //    as before, read rows 4 apart: 16-way bank conflicts)
+  //    rows (pitch D + 4 floats) fall in distinct banks (with four dims per
+  //    lane the rows read together are four apart: 16-way bank conflicts);
+  //    four partial sums, one per float4 lane, keep the chains r / 4 long
   for (int i = tid; i < n * D; i += kOjaSmallThreads) {
     const int t = i / D, e = i % D;
-    float acc = 0.f;
+    f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll 4
     for (int c = 0; c < r; c += 4) {
       const f32x4 yv = *reinterpret_cast<const f32x4*>(&s_y[t][c]);
       const f32x4 bv = *reinterpret_cast<const f32x4*>(&s_b[e][c]);
-      acc = fmaf(yv[0], bv[0], fmaf(yv[1], bv[1], fmaf(yv[2], bv[2], fmaf(yv[3], bv[3], acc))));
+#pragma unroll
+      for (int q = 0; q < 4; ++q) acc[q] = fmaf(yv[q], bv[q], acc[q]);
     }
-    s_x[t][e] -= acc;
+    s_x[t][e] -= (acc[0] + acc[1]) + (acc[2] + acc[3]);
   }
   __syncthreads();
   // 4. B += eta R^T Y: a thread takes one dim and 8 coefficients,
