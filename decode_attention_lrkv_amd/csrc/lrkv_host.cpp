@@ -89,7 +89,12 @@ Plan plan_splits(int64_t units, int64_t n_tokens, int cus, int max_splits) {
   // compute units that finish first (the batched 32K step: 188.8 against
   // 190.4-190.7 us per layer-step, alternating runs on one box; two full
   // rounds 192.3 us).
-  if (2 * u >= cus) s = cdiv((int64_t)cus * 12, u);
+  // (only where whole workgroups of four splits per unit make it at most one
+  // and a half rounds: 768 workgroups at 256 compute units)
+  if (2 * u >= cus) {
+    const int64_t s15 = cdiv((int64_t)cus * 12, u);
+    if (cdiv(s15, 4) * u <= 3 * (int64_t)cus) s = s15;
+  }
   s = std::min<int64_t>(s, cdiv(n_chunks, 4));
   if (s > 4) s = std::max<int64_t>(s, std::min<int64_t>(n_chunks, (int64_t)cus * 4 / u - 4));
   if (const char* env = std::getenv("LRKV_SPLITS")) {
