@@ -344,7 +344,7 @@ def bench_variants(torch, lrkv, bm, synth, dev, layers, ws, dev_bf16):
             "oja_update_decode_GBps": round(oja_dec_bytes / (oja_dec_us["mean"] * 1e-6) / 1e9, 1),
             "note": "same caches and context as the main figure, layers cycled call after call (no prefill "
                     "between them); two launches per decode call; the Oja update is of both bases of a layer "
-                    "(four launches per basis through the Gram matrix), from its 4096-token prefill chunk and at decode shape "
+                    "(three launches per basis through the Gram matrix), from its 4096-token prefill chunk and at decode shape "
                     "(batch 16 x the step's one appended token)"}
 
 

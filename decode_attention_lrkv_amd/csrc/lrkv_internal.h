@@ -103,7 +103,7 @@ struct OjaArgs {
   int64_t n_tokens;
   float eta;
   float* ws;             // [Hkv, n_wg, d, d] the runs' partial Gram matrices
-  float* ws_sum;         // [Hkv, d * R + R * R] S1 then S2 (R = rank padded to 16)
+  float* ws_sum;         // [Hkv, 2 d R] S1 [d][R] then a copy of B [d][r] (R = rank padded to 16)
   int n_wg;              // gram workgroups (runs of tokens) per kv head
 };
 // Oja updates of at most this many tokens per head (a decode step's) run as
@@ -112,9 +112,9 @@ constexpr int kOjaSmallTokens = 64;
 // Tokens per step of a gram workgroup.
 constexpr int kOjaGramStep = 128;
 // Oja workspace layout: per head and gram workgroup, the partial Gram
-// matrix [d][d]; then per head S1 [d][R] and S2 [R][R], R = rank padded to
-// whole 16-column blocks.
-__host__ __device__ inline int64_t oja_head_floats(int d, int r_pad) { return (int64_t)d * r_pad + (int64_t)r_pad * r_pad; }
+// matrix [d][d]; then per head S1 [d][R] (R = rank padded to whole
+// 16-column blocks) and a copy of the basis before the step [d][r].
+__host__ __device__ inline int64_t oja_head_floats(int d, int r_pad) { return 2 * (int64_t)d * r_pad; }
 inline int oja_rank_pad(int rank) { return 16 * ((rank + 15) / 16); }
 inline size_t oja_partial_floats(int hkv, int d, int n_wg) { return (size_t)hkv * n_wg * d * d; }
 inline size_t oja_workspace_floats(int hkv, int d, int rank, int n_wg) {

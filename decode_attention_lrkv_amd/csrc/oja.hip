@@ -10,7 +10,7 @@
 // G = X^T X (associativity):  X^T Y = G B,  Y^T Y = B^T G B.  G does not
 // depend on the rank, its bfloat16 x bfloat16 products are exact in the
 // matrix cores' float32 accumulation, and forming it streams the chunk once.
-// Four launches, all deterministic (fixed summation orders, no atomics):
+// Three launches, all deterministic (fixed summation orders, no atomics):
 //   gram   per (run of 128-token steps, kv head): the run's partial G on the
 //          matrix cores.  A step's tokens are staged in LDS token-major; each
 //          matrix-core operand (16 dims x 8 consecutive tokens per lane
@@ -18,11 +18,14 @@
 //          operand serves as row operand (G's row block) and as column
 //          operand (its column block).  Loads run two steps ahead.
 //   s1     per 4 rows of G: the runs' partials summed in a fixed order,
-//          then those rows of S1 = G B, float32.
-//   s2     per 4 rows of S2 = B^T S1, float32.
-//   apply  B + eta (S1 - B S2) in float32 per 4-row block of B, written
-//          back to the float32 basis and, rounded to nearest even, to the
-//          bfloat16 copy.
+//          then those rows of S1 = G B, float32; the workgroup also copies
+//          its 4 rows of B to the workspace (the basis before the step).
+//   apply  per 4-row block of B: B + eta (S1 - B S2) with
+//          B S2 = B B^T S1 = (B_rows B^T) S1 formed from the copies of B
+//          and S1 (so S2 itself is never formed), float32, written back to
+//          the float32 basis and, rounded to nearest even, to the bfloat16
+//          copy (the copy of B keeps other workgroups' in-place writes out
+//          of each workgroup's reads).
 // Chunks of at most kOjaSmallTokens tokens per head take a single launch
 // instead (oja_small_kernel, the same update in its per-token form).
 #include <type_traits>
@@ -229,6 +232,9 @@ __global__ __launch_bounds__(256) void oja_s1_kernel(OjaArgs a, int R) {
   }
   __syncthreads();
   float* s1 = a.ws_sum + (int64_t)h * oja_head_floats(d, R);
+  // the basis before the step, rows row0 .. row0 + kS1Rows - 1 (from LDS)
+  float* b_old = s1 + (int64_t)d * R;
+  for (int i = tid; i < kS1Rows * r; i += 256) b_old[(int64_t)row0 * r + i] = s_b[row0 * r + i];
   for (int j = tid; j < R; j += 256) {
     float o[kS1Rows];
 #pragma unroll
@@ -249,73 +255,61 @@ __global__ __launch_bounds__(256) void oja_s1_kernel(OjaArgs a, int R) {
   }
 }
 
-// Rows a0 .. a0 + kS2Rows - 1 of S2 = B^T S1 for one head ([R][R] after
-// S1 [d][R]; rows and columns past the rank are zero).  S1 is staged in LDS;
-// thread j forms column j of the rows.
-constexpr int kS2Rows = 4;
-__global__ __launch_bounds__(256) void oja_s2_kernel(OjaArgs a, int R) {
-  __shared__ __attribute__((aligned(16))) float s_s1[128 * 128];
-  __shared__ __attribute__((aligned(16))) float s_b[128][kS2Rows];
-  const int tid = threadIdx.x;
-  const int h = blockIdx.y, a0 = kS2Rows * blockIdx.x;
-  const int d = a.d, r = a.rank;
-  float* sum = a.ws_sum + (int64_t)h * oja_head_floats(d, R);
-  copy_to_lds(s_s1, sum, d * R);
-  const float* bs = a.basis + (int64_t)h * d * r;
-  for (int i = tid; i < d * kS2Rows; i += 256) {
-    const int k = i / kS2Rows, q = i - k * kS2Rows;
-    s_b[k][q] = a0 + q < r ? bs[(int64_t)k * r + a0 + q] : 0.f;
-  }
-  __syncthreads();
-  float* s2 = sum + (int64_t)d * R;
-  for (int j = tid; j < R; j += 256) {
-    f32x4 o = f32x4{0.f, 0.f, 0.f, 0.f};   // rows a0 .. a0 + 3
-    for (int k = 0; k < d; ++k) {
-      const f32x4 b4 = *reinterpret_cast<const f32x4*>(&s_b[k][0]);
-      const float v = s_s1[k * R + j];
-#pragma unroll
-      for (int q = 0; q < kS2Rows; ++q) o[q] = fmaf(b4[q], v, o[q]);
-    }
-#pragma unroll
-    for (int q = 0; q < kS2Rows; ++q) s2[(int64_t)(a0 + q) * R + j] = o[q];
-  }
-}
-
-// B <- B + eta (S1 - B S2) for kOjaRows rows of one head's basis.  The rows
-// are staged in LDS before any is written, and no other workgroup touches
-// them; thread j forms column j of the rows.
+// B <- B + eta (S1 - B S2) for kOjaRows rows of one head's basis, with
+// B_rows S2 = (B_rows B^T) S1: P = B_rows B^T [kOjaRows][d] (thread k forms
+// column k), then thread j forms column j of P S1.  The whole basis before
+// the step and S1 come from the workspace (staged in LDS); the workgroup's
+// rows of the float32 basis are written only after that.
 constexpr int kOjaRows = 4;
 template <int R>
 __global__ __launch_bounds__(256) void oja_apply_kernel(OjaArgs a) {
-  __shared__ __attribute__((aligned(16))) float s_s2[R * R];
-  __shared__ __attribute__((aligned(16))) float s_b[kOjaRows][128];
+  __shared__ __attribute__((aligned(16))) float s_s1[128 * R];
+  __shared__ __attribute__((aligned(16))) float s_bo[128 * R];
+  __shared__ __attribute__((aligned(16))) float s_p[kOjaRows][128];
   const int h = blockIdx.y, row0 = kOjaRows * blockIdx.x;
   const int tid = threadIdx.x;
   const int r = a.rank, d = a.d;
-  const int64_t per_head = oja_head_floats(d, R);
-  const float* sum = a.ws_sum + (int64_t)h * per_head;
-  float* bs = a.basis + (int64_t)h * d * r;
-  copy_to_lds(s_s2, sum + (int64_t)d * R, R * R);
-  for (int i = tid; i < kOjaRows * r; i += 256) s_b[i / r][i % r] = bs[(int64_t)(row0 + i / r) * r + i % r];
+  const float* sum = a.ws_sum + (int64_t)h * oja_head_floats(d, R);
+  const float* b_old = sum + (int64_t)d * R;
+  copy_to_lds(s_s1, sum, d * R);
+  copy_to_lds(s_bo, b_old, d * r);
   __syncthreads();
+  // P = B_rows B^T
+  for (int k = tid; k < d; k += 256) {
+    float p[kOjaRows];
+#pragma unroll
+    for (int q = 0; q < kOjaRows; ++q) p[q] = 0.f;
+    for (int c = 0; c < r; c += 4) {   // r is a multiple of 8
+      const f32x4 bk = *reinterpret_cast<const f32x4*>(&s_bo[k * r + c]);
+#pragma unroll
+      for (int q = 0; q < kOjaRows; ++q) {
+        const f32x4 bq = *reinterpret_cast<const f32x4*>(&s_bo[(row0 + q) * r + c]);
+        p[q] = fmaf(bq[3], bk[3], fmaf(bq[2], bk[2], fmaf(bq[1], bk[1], fmaf(bq[0], bk[0], p[q]))));
+      }
+    }
+#pragma unroll
+    for (int q = 0; q < kOjaRows; ++q) s_p[q][k] = p[q];
+  }
+  __syncthreads();
+  float* bs = a.basis + (int64_t)h * d * r;
   uint16_t* bb = static_cast<uint16_t*>(a.basis_bf16);
   for (int j = tid; j < r; j += 256) {
     float dot[kOjaRows];
 #pragma unroll
-    for (int rr = 0; rr < kOjaRows; ++rr) dot[rr] = 0.f;
-    for (int k = 0; k < r; k += 4) {   // r is a multiple of 8
-      const float s0 = s_s2[k * R + j], s1 = s_s2[(k + 1) * R + j], s2 = s_s2[(k + 2) * R + j],
-                  s3 = s_s2[(k + 3) * R + j];
+    for (int q = 0; q < kOjaRows; ++q) dot[q] = 0.f;
+    for (int k = 0; k < d; k += 4) {
+      const float s0 = s_s1[k * R + j], s1 = s_s1[(k + 1) * R + j], s2 = s_s1[(k + 2) * R + j],
+                  s3 = s_s1[(k + 3) * R + j];
 #pragma unroll
-      for (int rr = 0; rr < kOjaRows; ++rr) {
-        const f32x4 b4 = *reinterpret_cast<const f32x4*>(&s_b[rr][k]);
-        dot[rr] = fmaf(b4[3], s3, fmaf(b4[2], s2, fmaf(b4[1], s1, fmaf(b4[0], s0, dot[rr]))));
+      for (int q = 0; q < kOjaRows; ++q) {
+        const f32x4 p4 = *reinterpret_cast<const f32x4*>(&s_p[q][k]);
+        dot[q] = fmaf(p4[3], s3, fmaf(p4[2], s2, fmaf(p4[1], s1, fmaf(p4[0], s0, dot[q]))));
       }
     }
 #pragma unroll
-    for (int rr = 0; rr < kOjaRows; ++rr) {
-      const float v = s_b[rr][j] + a.eta * (sum[(int64_t)(row0 + rr) * R + j] - dot[rr]);
-      const int64_t o = (int64_t)(row0 + rr) * r + j;
+    for (int q = 0; q < kOjaRows; ++q) {
+      const float v = s_bo[(row0 + q) * r + j] + a.eta * (s_s1[(row0 + q) * R + j] - dot[q]);
+      const int64_t o = (int64_t)(row0 + q) * r + j;
       bs[o] = v;
       if (bb) bb[(int64_t)h * d * r + o] = f32_to_bf16(v);
     }
@@ -468,9 +462,6 @@ hipError_t launch_oja_update(const OjaArgs& a, hipStream_t s) {
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(oja_s1_kernel, dim3(a.d / kS1Rows, a.hkv), dim3(256), 0, s, a, R);
-  e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(oja_s2_kernel, dim3(R / kS2Rows, a.hkv), dim3(256), 0, s, a, R);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   const dim3 agrid((unsigned)(a.d / kOjaRows), a.hkv);

@@ -405,8 +405,8 @@ size_t lrkv_oja_workspace_bytes(int32_t batch, int32_t n_kv_heads, int32_t head_
  * head_dim 64 or 128; rank a multiple of 8, at most head_dim.  The result
  * is deterministic (fixed summation order).  n_tokens = 0 leaves the basis
  * as it is (x may then be NULL).  Up to 64 tokens per head: one launch;
- * more: four (the chunk's Gram matrix G = X^T X per run of tokens, then
- * X^T Y = G B and Y^T Y = B^T G B, then the step).
+ * more: three (the chunk's Gram matrix G = X^T X per run of tokens, then
+ * X^T Y = G B, then the step with B Y^T Y = (B B^T) G B).
  */
 lrkv_status lrkv_oja_update(const void* x, float* basis, void* basis_bf16, int32_t batch,
                             int32_t n_kv_heads, int32_t head_dim, int32_t rank, int64_t n_tokens,
