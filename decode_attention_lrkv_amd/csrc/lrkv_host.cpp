@@ -109,8 +109,9 @@ Plan plan_splits(int64_t units, int64_t n_tokens, int cus, int max_splits) {
   return p;
 }
 
-// Decode workspace: arrival counters [B, Hkv] (uint32, used by the hybrid
-// decode's in-launch merge; zero at rest), the partials [B, Hq, parts, d]
+// Decode workspace: arrival counters [B, Hkv] (uint32, used by the launches
+// that merge in the launch: the hybrid decode and small bfloat16 plain and
+// step launches; zero at rest), the partials [B, Hq, parts, d]
 // and their (max, sum) [B, Hq, parts, 2].  The counters come first in every
 // layout, so calls of any kind that share a workspace leave them alone.
 struct DecodeLayout {

@@ -7,10 +7,13 @@
 // lives in a fixed device array of this library instead.  Each GPU holds its
 // own copy at its own address; the host looks that address up once per device
 // with hipGetSymbolAddress and passes it to the kernels like any workspace.
-// The array keeps the last call's contents; the decode step needs no initial
-// contents in its workspace, so nothing is cleared.  Calls on one GPU share
-// the array, so calls that overlap in time on one GPU (different streams, or
-// different threads without ordering) race.
+// The array keeps the last call's contents.  Its first bytes are the step's
+// per-(b, kv head) arrival counters, which launches that merge their partials
+// in the same launch need at zero: a device global without an initialiser is
+// zero-filled when the code object loads, and every call leaves the counters
+// zero, so nothing is cleared (the partials behind them need no initial
+// contents).  Calls on one GPU share the array, so calls that overlap in time
+// on one GPU (different streams, or different threads without ordering) race.
 #include <mutex>
 
 #include "lrkv.h"

@@ -307,6 +307,8 @@ lrkv_status lrkv_decode_step_seqlens(const void* q, const void* k_new, const voi
  * same kernels and same result as lrkv_decode_step.  The workspace is a fixed
  * device array inside this library of lrkv_decode_step_noalloc_max_bytes()
  * bytes (8 MiB) per GPU, held until the process ends; each GPU has its own.
+ * The array is zero when the library loads, and every call leaves its
+ * arrival counters zero, as lrkv_decode_step requires of a workspace.
  * Calls whose lrkv_decode_step_workspace_bytes(dims, n_ctx) exceeds that size
  * return LRKV_ERR_WORKSPACE_TOO_SMALL before any device call.  The call
  * allocates nothing.  All calls on one GPU share that GPU's array: calls that

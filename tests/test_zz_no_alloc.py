@@ -1,12 +1,16 @@
 """lrkv_decode_step_noalloc (the library's fixed workspace, no allocation)
 against lrkv_decode_step (a caller's workspace) through the C ABI.
 
-Two calls in a row on one GPU, the second with a smaller input: the
-batched-32K shape at 4096 tokens (attention workgroups plus the merge launch)
-and then batch 1 at 300 tokens (one workgroup per (batch, kv head), no merge
-launch).  Both entry points run the same kernels on the same inputs, so the
-outputs, lse and the appended cache rows must agree bit for bit.  A request
-larger than the fixed workspace is refused before any device call.
+Calls in a row on one GPU, each with a smaller input than the one before:
+the batched-32K shape at 4096 tokens (attention workgroups plus the merge
+launch); batch 1 at 896 and then 640 tokens (at most 64 workgroups on a
+256-compute-unit chip, so the last workgroup of each (batch, kv head) merges
+in the launch, counting arrivals in the first bytes of the fixed array: the
+640-token call also shows that the 896-token call left those counters zero);
+and batch 1 at 300 tokens (one workgroup per (batch, kv head), no merge).
+Both entry points run the same kernels on the same inputs, so the outputs,
+lse and the appended cache rows must agree bit for bit.  A request larger
+than the fixed workspace is refused before any device call.
 """
 import ctypes
 
@@ -49,6 +53,7 @@ def _same(a, b):
 @pytest.mark.parametrize("first_then_smaller", [True])
 def test_noalloc_step_equals_the_workspace_step(first_then_smaller):
     cases = [(synth.scaled(synth.BATCHED_32K, n_ctx=(4096,)), 1, 4096, 4096),
+             (synth.LLAMA_STEP, 0, 896, 896), (synth.LLAMA_STEP, 1, 640, 640),
              (synth.LLAMA_STEP, 0, 300, 304)]
     for w, layer, N, cap in cases:
         print(f"noalloc case: batch {w.batch}, N {N}, layer {layer}", flush=True)
