@@ -394,7 +394,12 @@ lrkv_status decode_merge(void* out, float* lse, const lrkv_dims* dims, lrkv_dtyp
 // alternating runs on one box): 40 workgroups (2048 tokens) 487.5 against
 // 491.5 us per step (eager 485 against 501), but 136 workgroups (8192
 // tokens) 521.4 against 507.7 us, and the batched 32K step (512
-// workgroups) 191.4-191.8 against 189.4-189.5 us per layer.
+// workgroups) 191.4-191.8 against 189.4-189.5 us per layer.  (Those
+// workgroup counts are from an earlier split plan: with the plan above, a
+// batch-1 step over 8 kv heads merges in its launch from 17 to 28 chunks
+// (up to 896 tokens; at most 16 chunks take one workgroup per unit, which
+// writes the outputs), and at 2048 tokens takes 136 workgroups and a merge
+// launch.)
 bool merge_in_step(const lrkv_dims& d, const DecodeLayout& L, lrkv_dtype dt, const void* enc_k, bool append) {
   if (dt != LRKV_BF16 || enc_k) return false;
   const int64_t wgs = (int64_t)d.batch * d.n_kv_heads * (append ? L.parts - 1 : L.parts);
