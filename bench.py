@@ -457,7 +457,9 @@ def bench_step_sweep(torch, lrkv, bm, synth, dev, threads):
     entry point as one graph that advances the context by one token per
     replay (the graph appends a token to every layer's cache and increments
     the length); and, for comparison, the unfused sequence (compress launch +
-    decode) as a graph."""
+    decode) as a graph, and the attention alone on latent queries
+    (lrkv_decode_attn_latent per layer: no fold, no lift, no appended token)
+    as a graph."""
     w = synth.LLAMA_STEP
     L, Hq, H, d = w.layers, w.n_q_heads, w.n_kv_heads, w.head_dim
     rk, rv = w.ranks(0)
@@ -503,6 +505,14 @@ def bench_step_sweep(torch, lrkv, bm, synth, dev, threads):
                 lrkv.compress_kv(x["ak"], x["av"], bk, bv, x["ck"], x["cv"], n - 1)
                 lrkv.decode_attn(x["q"], bk, x["ck"], bv, x["cv"], n, out=x["out"], lse=x["lse"], workspace=ws)
 
+        for x in lay:   # latent queries for projections that absorb the bases (no fold, no lift)
+            x["ql"] = x["q"][..., :rk].contiguous()
+            x["ol"] = torch.empty((1, Hq, rv), dtype=torch.bfloat16, device=dev)
+
+        def step_latent(_i=0):   # the attention alone on latent queries (no appended token)
+            for x in lay:
+                lrkv.decode_attn_latent(x["ql"], x["ck"], x["cv"], n, d, out=x["ol"], lse=x["lse"], workspace=ws)
+
         def graph_of(fn):
             s = torch.cuda.Stream()
             with torch.cuda.stream(s):
@@ -518,6 +528,8 @@ def bench_step_sweep(torch, lrkv, bm, synth, dev, threads):
         graph = _timed(torch, lambda i: g.replay())
         g2 = graph_of(step_unfused)
         graph_unfused = _timed(torch, lambda i: g2.replay())
+        g4 = graph_of(step_latent)
+        latent = _timed(torch, lambda i: g4.replay())
         g3 = graph_of(step_advancing)       # the eager warm-up and the capture leave the length at n + 1
         seq_lens.fill_(n)
         torch.cuda.synchronize()
@@ -530,11 +542,13 @@ def bench_step_sweep(torch, lrkv, bm, synth, dev, threads):
                        "advancing_graph_us_per_step": advancing,
                        "advancing_context_range": [n + WARM_ITERS, reached - 1],
                        "unfused_graph_us_per_step": graph_unfused,
+                       "latent_attn_graph_us_per_step": latent,
                        "graph_GBps_effective": round(step_bytes / graph["mean"] / 1e3, 1)}
-        del lay, g, g2, g3, ws
+        del lay, g, g2, g3, g4, ws
         torch.cuda.empty_cache()
     return {"workload": w.name, "layers": L, "by_context": res,
             "note": "working set <= 0.6 GB per step; 'effective' bandwidth can include last-level-cache hits; "
+                    "the latent graph attends rows [0, n) with no appended token; "
                     "the advancing graph appends one token per replay (its context grows from n by "
                     f"{WARM_ITERS} warm-up and {TIMED_ITERS} timed replays)"}
 
