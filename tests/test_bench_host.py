@@ -1,8 +1,9 @@
 """Host-side pieces of the benchmark that run without a GPU: the percentile
 summary and the HIP device attributes it reads the memory clock and bus width
-with."""
+with, and its refusal of more than one GPU."""
 import os
 import subprocess
+import sys
 
 import numpy as np
 import pytest
@@ -58,3 +59,14 @@ def test_traffic_record_is_used_only_for_the_sources_it_was_taken_with(tmp_path,
     with open(csrc / bench.KERNEL_SOURCES[-1], "a") as f:
         f.write("\n// changed\n")
     assert bench.measured_traffic() is None
+
+
+@pytest.mark.parametrize("n", [2, 8])
+def test_bench_refuses_more_than_one_gpu(n):
+    """The decode path runs on one GPU: any other --gpus exits with status 2
+    and a message, before torch or the library is imported."""
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    r = subprocess.run([sys.executable, os.path.join(root, "bench.py"), "--gpus", str(n)], cwd=root,
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2
+    assert "one GPU only" in r.stdout and f"--gpus {n}" in r.stdout
